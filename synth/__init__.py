@@ -1,0 +1,365 @@
+"""Seeded synthetic MoE inputs for the contiguous grouped block-scaled GEMM.
+
+This module only *makes inputs*: routing draws, value draws, group padding and
+the encoding of input values into their storage formats (MXFP8 E4M3 or MXFP4
+E2M1 codes with one E8M0 scale byte per 32 K-elements, or BF16 bits).  It holds
+none of the method's own arithmetic (no GEMM, activation, gating or output
+quantisation), and it imports neither the oracle nor the GPU library; both of
+those take their inputs from here.
+
+Storage conventions (the logical layouts the library's C ABI defines):
+
+* ``a``      (valid_m, K) uint8 E4M3 codes, (valid_m, K/2) uint8 packed E2M1
+             pairs (low nibble = even K element), or (valid_m, K) uint16 BF16 bits
+* ``b``      (L, N, K) / (L, N, K/2) / (L, N, K), same encodings, K-major
+* ``sfa``    (valid_m, K/32) uint8 E8M0 bytes; ``sfb`` (L, N, K/32)
+* ``padded_offsets`` int32 (L,), cumulative group ends, each a multiple of
+  ``m_aligned``; rows of a group are sorted by token id, padding rows follow
+  the routed rows of their group and hold zero codes with scale byte 0.
+* ``alpha`` / ``beta`` float32 (L,), ``prob`` float32 (valid_m,),
+  ``norm_const`` float32 (1,), ``c_in`` (valid_m, 2N) uint16 BF16 bits.
+
+Every draw comes from a numpy PCG64 stream seeded by
+``SeedSequence([seed, stream_id, chunk])``, so a case is a pure function of
+its spec and seed, independent of thread count.
+"""
+from __future__ import annotations
+
+import math
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = ["Case", "CONFIGS", "make_case", "config_spec", "encode_e4m3",
+           "encode_e2m1", "encode_bf16", "mx_quantize"]
+
+# stream ids (one independent PCG64 stream per purpose)
+_S_ROUTE, _S_A, _S_B, _S_ALPHA, _S_PROB, _S_CIN, _S_BETA = range(7)
+_A_CHUNK = 2048  # rows of A generated per independent chunk
+_THREADS = 8
+
+
+def _rng(seed: int, stream: int, chunk: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream, chunk])))
+
+
+# ---------------------------------------------------------------------------
+# storage-format encoders used to *build inputs* (round to nearest, ties to
+# even; inputs are pre-scaled so that no value exceeds the format maximum)
+# ---------------------------------------------------------------------------
+
+def encode_e4m3(v: np.ndarray) -> np.ndarray:
+    """float32 values with |v| <= 448 -> OCP E4M3FN codes (uint8), RNE."""
+    v = np.asarray(v, dtype=np.float32)
+    mag = np.abs(v)
+    bits = mag.view(np.uint32).astype(np.int64)
+    # normal range: keep 3 mantissa bits with round-half-even on the 20 dropped bits
+    rounded = bits + 0x7FFFF + ((bits >> 20) & 1)
+    normal = (rounded >> 20) - (120 << 3)
+    # subnormal range (|v| < 2^-6): integer multiples of 2^-9, RNE via rint
+    sub = np.rint(mag.astype(np.float64) * 512.0).astype(np.int64)
+    code = np.where(mag < 2.0 ** -6, sub, normal)
+    code = np.clip(code, 0, 0x7E)
+    code = code | np.where((v < 0) & (code != 0), 0x80, 0)
+    return code.astype(np.uint8)
+
+
+_E2M1_EDGES_GT = np.array([0.25, 1.25, 2.5, 5.0], dtype=np.float32)   # tie stays (even code below)
+_E2M1_EDGES_GE = np.array([0.75, 1.75, 3.5], dtype=np.float32)        # tie advances (even code above)
+
+
+def encode_e2m1(v: np.ndarray) -> np.ndarray:
+    """float32 values with |v| <= 6 -> E2M1 nibbles (uint8 0..15), RNE.
+
+    Magnitudes by code: 0, 0.5, 1, 1.5, 2, 3, 4, 6.  A value exactly half way
+    between two neighbours goes to the code whose mantissa bit is 0.
+    """
+    v = np.asarray(v, dtype=np.float32)
+    mag = np.abs(v)
+    code = np.zeros(v.shape, dtype=np.uint8)
+    for e in _E2M1_EDGES_GT:
+        code += (mag > e)
+    for e in _E2M1_EDGES_GE:
+        code += (mag >= e)
+    code |= np.where((v < 0) & (code != 0), 8, 0).astype(np.uint8)
+    return code
+
+
+def encode_bf16(v: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bits (uint16), round to nearest even (finite inputs)."""
+    bits = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def mx_quantize(x: np.ndarray, fmt: str):
+    """Quantise float32 rows (..., K) to MX codes + E8M0 bytes per 32 K-elements.
+
+    The block exponent is the smallest power of two 2^e with
+    max|x_blk| / 2^e <= fmt_max (448 for E4M3, 6 for E2M1); the byte is e+127
+    clamped to [0, 254]; an all-zero block gets byte 0.  Elements are x / 2^e
+    rounded to nearest even in the element format.  E2M1 codes are packed two
+    per byte, the even K element in the low nibble.
+    """
+    fmt_max = {"e4m3": 448.0, "e2m1x2": 6.0}[fmt]
+    shp = x.shape
+    k = shp[-1]
+    assert k % 32 == 0
+    blk = x.reshape(shp[:-1] + (k // 32, 32)).astype(np.float32)
+    amax = np.abs(blk).max(axis=-1).astype(np.float64)
+    ratio = amax / fmt_max
+    mant, ex = np.frexp(ratio)              # ratio = mant * 2^ex, mant in [0.5, 1)
+    e = np.where(mant == 0.5, ex - 1, ex)   # ceil(log2(ratio))
+    byte = np.where(amax > 0, np.clip(e + 127, 0, 254), 0).astype(np.int32)
+    scaled = np.ldexp(blk, (127 - byte)[..., None].astype(np.int32)).astype(np.float32)
+    scaled = np.clip(scaled, -fmt_max, fmt_max)
+    if fmt == "e4m3":
+        codes = encode_e4m3(scaled).reshape(shp)
+    else:
+        nib = encode_e2m1(scaled).reshape(shp)
+        codes = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+    return codes, byte.astype(np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# routing
+# ---------------------------------------------------------------------------
+
+def _topk_uniform(rng, tokens, L, topk):
+    """Each token picks `topk` distinct experts uniformly (Gumbel top-k)."""
+    keys = rng.random((tokens, L))
+    return np.argsort(-keys, axis=1, kind="stable")[:, :topk]
+
+
+def _topk_weighted(rng, tokens, L, topk, weights):
+    """Weighted sampling without replacement via Gumbel top-k keys."""
+    w = np.asarray(weights, dtype=np.float64)
+    with np.errstate(divide="ignore"):
+        logw = np.where(w > 0, np.log(np.where(w > 0, w, 1.0)), -np.inf)
+    g = -np.log(-np.log(rng.random((tokens, L))))
+    keys = logw[None, :] + g
+    return np.argsort(-keys, axis=1, kind="stable")[:, :topk]
+
+
+def _softmax(z):
+    z = z - z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+@dataclass
+class Case:
+    name: str
+    seed: int
+    problem: dict
+    arrays: dict
+    counts: np.ndarray          # routed rows per expert (L,)
+    row_valid: np.ndarray       # bool (valid_m,): True for routed rows
+    spec: dict = field(default_factory=dict)
+
+    @property
+    def routed_rows(self) -> int:
+        return int(self.counts.sum())
+
+    @property
+    def flops(self) -> float:
+        """Algorithmic work: 2 * routed rows * N * K (padding rows excluded)."""
+        p = self.problem
+        return 2.0 * self.routed_rows * p["n"] * p["k"]
+
+
+# Workload recipes.  Sizes and distributions follow the MoE configurations the
+# method is exercised on (see the design doc for the recipe of each field).
+CONFIGS = {
+    # gating only, bf16 D + per-group amax
+    "quant_gating_l4": dict(L=4, K=512, N=512, ab="e4m3", act="none", d="bf16", c=None,
+                            routing=("multinomial", 768), alpha=("uniform", 0.5, 2.0),
+                            prob=("uniform",), a_std=1.0, b_std=1.0, seed=101),
+    # FC1 + SwiGLU forward, FP8 D with row and column scale factors
+    "fc1_swiglu_l8": dict(L=8, K=2048, N=2816, ab="e4m3", act="swiglu", d="e4m3", c=None,
+                          routing=("topk", 4096, 2), alpha=("const", 1.0),
+                          prob=("softmax_all",), a_std=1.0, b_std="1/sqrtK", seed=102),
+    # FC2 down projection with Zipf-skewed routing (4 experts forced empty)
+    "fc2_gating_l64_zipf": dict(L=64, K=1408, N=2048, ab="e4m3", act="none", d="bf16", c=None,
+                                routing=("topk_zipf", 16384, 6, 1.1, 4), alpha=("uniform", 0.5, 2.0),
+                                prob=("softmax_picks",), a_std=1.0, b_std="1/sqrtK", seed=103),
+    # sReLU with tanh soft clamp, MXFP4 operands, bf16 C kept, FP8 D
+    "srelu_tanh_fp4_l32": dict(L=32, K=4096, N=4096, ab="e2m1x2", act="srelu", d="e4m3", c="bf16",
+                               routing=("multinomial", 32768), alpha=("const", 1.0),
+                               prob=("uniform",), a_std=1.0, b_std=1.0, clip=6.0, s=8.0, seed=104),
+    # dSwiGLU backward, BF16 operands, dC bf16 + dprob
+    "dswiglu_bf16_l64": dict(L=64, K=2048, N=1408, ab="bf16", act="dswiglu", d="bf16", c=None,
+                             routing=("topk", 16384, 6), alpha=("const", 1.0), beta=("const", 1.0),
+                             prob=("softmax_picks",), a_std=0.1, b_std="1/sqrtK", seed=105),
+    # FC1 + SwiGLU at L=64 (the forward whose backward is dswiglu_bf16_l64)
+    "fc1_swiglu_l64": dict(L=64, K=2048, N=2816, ab="e4m3", act="swiglu", d="e4m3", c=None,
+                           routing=("topk", 16384, 6), alpha=("const", 1.0),
+                           prob=("softmax_all",), a_std=1.0, b_std="1/sqrtK", seed=106),
+}
+
+
+def config_spec(name: str, **overrides) -> dict:
+    spec = dict(CONFIGS[name])
+    spec.update(overrides)
+    spec.setdefault("name", name)
+    return spec
+
+
+def _route(spec, rng):
+    """Return (expert of each routed row, token id, prob) for all routed rows."""
+    L = spec["L"]
+    kind = spec["routing"][0]
+    if kind == "multinomial":
+        rows = spec["routing"][1]
+        counts = rng.multinomial(rows, np.full(L, 1.0 / L))
+        experts = np.repeat(np.arange(L), counts)
+        tokens = np.arange(rows)                   # one row per "token"
+        logits = None
+        picks = None
+    else:
+        tokens_n = spec["routing"][1]
+        topk = spec["routing"][2]
+        if kind == "topk":
+            picks = _topk_uniform(rng, tokens_n, L, topk)
+        elif kind == "topk_zipf":
+            s_exp, n_empty = spec["routing"][3], spec["routing"][4]
+            w = np.arange(1, L + 1, dtype=np.float64) ** (-s_exp)
+            if n_empty:
+                w[-n_empty:] = 0.0                 # lowest-weight ranks never picked
+            perm = rng.permutation(L)              # rank r -> expert perm[r]
+            wexp = np.empty(L)
+            wexp[perm] = w
+            picks = _topk_weighted(rng, tokens_n, L, topk, wexp)
+        else:
+            raise ValueError(kind)
+        logits = rng.standard_normal((tokens_n, L))
+        tok = np.repeat(np.arange(tokens_n), topk)
+        exp_ = picks.reshape(-1)
+        order = np.lexsort((tok, exp_))            # sort by expert, then token
+        experts = exp_[order]
+        tokens = tok[order]
+        counts = np.bincount(experts, minlength=L)
+    # routing probabilities for routed rows
+    pk = spec["prob"][0]
+    if pk == "uniform":
+        prob = None                                # drawn later for every row
+    elif pk == "softmax_all":
+        sm = _softmax(logits)
+        prob = sm[tokens, experts]
+    elif pk == "softmax_picks":
+        lp = np.take_along_axis(logits, picks, axis=1)
+        sm = _softmax(lp)
+        # probability of (token, expert) within that token's picks
+        slot = np.argmax(picks[tokens] == experts[:, None], axis=1)
+        prob = sm[tokens, slot]
+    else:
+        raise ValueError(pk)
+    return experts, tokens, counts, prob
+
+
+def _b_std(spec):
+    s = spec["b_std"]
+    return 1.0 / math.sqrt(spec["K"]) if s == "1/sqrtK" else float(s)
+
+
+def make_case(spec_or_name, seed: int | None = None, **overrides) -> Case:
+    """Build one seeded case from a recipe name (CONFIGS key) or a spec dict.
+
+    Overrides replace recipe fields (e.g. smaller L/K/N/routing for parity
+    tests).  Extra keys: ``m_aligned`` (default 128), ``norm_const`` (1.0).
+    """
+    spec = config_spec(spec_or_name, **overrides) if isinstance(spec_or_name, str) \
+        else dict(spec_or_name, **overrides)
+    if seed is None:
+        seed = spec.get("seed", 0)
+    L, K, N = spec["L"], spec["K"], spec["N"]
+    m_al = spec.get("m_aligned", 128)
+    ab = spec["ab"]
+    rng_route = _rng(seed, _S_ROUTE)
+    experts, tokens, counts, prob_routed = _route(spec, rng_route)
+    if "force_counts" in spec:                     # explicit per-expert row counts (edge cases)
+        counts = np.asarray(spec["force_counts"], dtype=np.int64)
+        experts = np.repeat(np.arange(L), counts)
+        tokens = np.arange(int(counts.sum()))
+        prob_routed = None
+    padded = ((counts + m_al - 1) // m_al) * m_al
+    po = np.cumsum(padded).astype(np.int32)
+    valid_m = int(po[-1]) if L else 0
+    starts = np.concatenate([[0], po[:-1]]).astype(np.int64)
+    # destination row of every routed row
+    rank_in_group = np.arange(len(experts)) - np.repeat(np.concatenate([[0], np.cumsum(counts)[:-1]]), counts)
+    dst = starts[experts] + rank_in_group
+    row_valid = np.zeros(valid_m, dtype=bool)
+    row_valid[dst] = True
+
+    # ---- prob (every row gets a value; padding rows draw U(0,1)) ----
+    rng_p = _rng(seed, _S_PROB)
+    prob = rng_p.random(valid_m).astype(np.float32)
+    if prob_routed is not None:
+        prob[dst] = prob_routed.astype(np.float32)
+
+    # ---- alpha / beta ----
+    def _per_group(desc, stream):
+        if desc[0] == "const":
+            return np.full(L, desc[1], dtype=np.float32)
+        return _rng(seed, stream).uniform(desc[1], desc[2], L).astype(np.float32)
+    alpha = _per_group(spec["alpha"], _S_ALPHA)
+    beta = _per_group(spec.get("beta", ("const", 1.0)), _S_BETA)
+
+    # ---- A: routed rows carry values, padding rows are zero ----
+    a_std = float(spec["a_std"])
+    clip = spec.get("clip")
+    row_chunks = [(r0, min(valid_m, r0 + _A_CHUNK)) for r0 in range(0, valid_m, _A_CHUNK)]
+
+    def _a_chunk(ci):
+        r0, r1 = row_chunks[ci]
+        x = _rng(seed, _S_A, ci).standard_normal((r1 - r0, K), dtype=np.float32)
+        x *= np.float32(a_std)
+        if clip is not None:
+            np.clip(x, -clip, clip, out=x)
+        x[~row_valid[r0:r1]] = 0.0
+        if ab == "bf16":
+            return encode_bf16(x), None
+        return mx_quantize(x, ab)
+
+    def _b_group(g):
+        x = _rng(seed, _S_B, g).standard_normal((N, K), dtype=np.float32)
+        x *= np.float32(_b_std(spec))
+        if clip is not None:
+            np.clip(x, -clip, clip, out=x)
+        if ab == "bf16":
+            return encode_bf16(x), None
+        return mx_quantize(x, ab)
+
+    with ThreadPoolExecutor(_THREADS) as ex:
+        a_parts = list(ex.map(_a_chunk, range(len(row_chunks))))
+        b_parts = list(ex.map(_b_group, range(L)))
+    kb = K // 2 if ab == "e2m1x2" else K
+    adt = np.uint16 if ab == "bf16" else np.uint8
+    a = np.concatenate([p[0] for p in a_parts]) if a_parts else np.zeros((0, kb), adt)
+    b = np.stack([p[0] for p in b_parts])
+    arrays = dict(a=a, b=b, padded_offsets=po, alpha=alpha, prob=prob,
+                  norm_const=np.array([spec.get("norm_const", 1.0)], dtype=np.float32))
+    if ab != "bf16":
+        arrays["sfa"] = (np.concatenate([p[1] for p in a_parts]) if a_parts
+                         else np.zeros((0, K // 32), np.uint8))
+        arrays["sfb"] = np.stack([p[1] for p in b_parts])
+    act = spec["act"]
+    if act == "dswiglu":
+        arrays["beta"] = beta
+        cin_chunks = [(r0, min(valid_m, r0 + _A_CHUNK)) for r0 in range(0, valid_m, _A_CHUNK)]
+
+        def _c_chunk(ci):
+            r0, r1 = cin_chunks[ci]
+            x = _rng(seed, _S_CIN, ci).standard_normal((r1 - r0, 2 * N), dtype=np.float32)
+            return encode_bf16(x)
+        with ThreadPoolExecutor(_THREADS) as ex:
+            parts = list(ex.map(_c_chunk, range(len(cin_chunks))))
+        arrays["c_in"] = np.concatenate(parts) if parts else np.zeros((0, 2 * N), np.uint16)
+
+    problem = dict(num_groups=L, valid_m=valid_m, n=N, k=K, m_aligned=m_al,
+                   ab_dtype=ab, c_dtype=spec.get("c"), d_dtype=spec["d"], act=act,
+                   srelu_tanh_s=float(spec.get("s", 0.0) or 0.0))
+    return Case(name=spec.get("name", "custom"), seed=seed, problem=problem, arrays=arrays,
+                counts=np.asarray(counts), row_valid=row_valid, spec=spec)
