@@ -1,0 +1,152 @@
+/*
+ * moegg.h -- C ABI of libmoegg: the contiguous grouped block-scaled GEMM used
+ * by MoE expert layers, with its fused epilogue, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What one call computes (cuDNN frontend pages "Grouped GEMM + Quant (SM100)",
+ * "Grouped GEMM + SwiGLU (SM100)", "Grouped GEMM + sReLU (SM100)" and
+ * "Grouped GEMM + dGLU (SM100)", §Equations of each):
+ *
+ *   rows m of A in [padded_offsets[g-1], padded_offsets[g]) belong to expert g
+ *   acc[m,n] = sum_k dequant(A[m,k], SFA) * dequant(B[g,n,k], SFB)
+ *   C = alpha_g * acc                       (forward activations)
+ *   R = alpha_g^2 * acc                     (dSwiGLU backward)
+ *   then the activation / gating epilogue selected by `act`, and the output
+ *   formatting selected by `d_dtype`:
+ *     BF16  D (round to nearest even) + per-group amax = max |D| (fp32, before
+ *           rounding) over the group's rows and all output columns;
+ *     E4M3  D and D_col, the same logical output quantised over 32-column row
+ *           blocks (SFD_row) and 32-row column blocks (SFD_col):
+ *           SFD = smallest power of two >= norm_const * amax_blk / 448 (E8M0
+ *           byte, 0 for an all-zero block), D_q = E4M3_rne(D * norm_const / SFD).
+ *
+ * Layouts ("logical" layouts defined by this library; every tensor is dense,
+ * row-major, with no padding between rows):
+ *   A       (valid_m, K)   E4M3 codes, or (valid_m, K/2) packed E2M1 pairs
+ *                          (the even K element in the low nibble), or BF16
+ *   B       (L, N, K)      same encoding as A, K contiguous ("K-major")
+ *   SFA     (valid_m, K/32) E8M0 bytes, one per 32 K-elements (MX formats only)
+ *   SFB     (L, N, K/32)   E8M0 bytes
+ *   padded_offsets (L) int32, cumulative group ends; padded_offsets[L-1] ==
+ *                          valid_m; every entry a multiple of m_aligned and
+ *                          nondecreasing (empty groups repeat the previous end)
+ *   alpha, beta (L) fp32; prob (valid_m) fp32; norm_const (1) fp32
+ *   C       (valid_m, N) BF16                      [optional forward output]
+ *   D, D_col (valid_m, N_out) BF16 or E4M3 codes   N_out = N/2 for SwiGLU,
+ *                                                  2N for dSwiGLU, else N
+ *   SFD_row (valid_m, N_out/32) E8M0; SFD_col (N_out, valid_m/32) E8M0
+ *   amax    (L) fp32, written by the call (zero-filled first)
+ *   C_in    (valid_m, 2N) BF16, saved forward pre-activation [dSwiGLU only]
+ *   dprob   (valid_m) fp32, caller-zeroed, accumulated with atomics [dSwiGLU]
+ *
+ * Ownership: every pointer is a caller-owned device pointer (except the
+ * problem/args structs, which are host memory read during the call only).
+ * The library keeps no pointer after a call returns and allocates no device
+ * memory.  Buffers must stay alive and unchanged until the stream has run
+ * the work.  Calls are asynchronous on `stream` (a hipStream_t; NULL = the
+ * null stream).
+ *
+ * Errors: every shape, dtype, alignment and presence rule is checked on the
+ * host before any HIP call; a failing call returns a status and enqueues
+ * nothing.  padded_offsets values are device data and are not read on the
+ * host (moegg_check_offsets is the opt-in, synchronising validator).
+ * moegg_last_error() returns a thread-local text describing the last failure.
+ */
+#ifndef MOEGG_H_
+#define MOEGG_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOEGG_ABI_VERSION 1
+
+typedef enum moegg_status {
+  MOEGG_OK = 0,
+  MOEGG_ERROR_INVALID_VALUE = 1, /* bad shape, dtype combination, NULL where required */
+  MOEGG_ERROR_MISALIGNED = 2,    /* pointer not 16-byte aligned */
+  MOEGG_ERROR_NOT_SUPPORTED = 3, /* valid per the pages but not built here (e.g. K % 128 != 0) */
+  MOEGG_ERROR_LAUNCH = 4         /* a HIP runtime call failed */
+} moegg_status;
+
+typedef enum moegg_dtype {
+  MOEGG_DT_NONE = 0,
+  MOEGG_DT_E4M3 = 1,   /* OCP E4M3FN: A/B operands (MXFP8) or D/D_col outputs */
+  MOEGG_DT_E2M1X2 = 2, /* packed OCP E2M1 pairs: A/B operands (MXFP4) */
+  MOEGG_DT_BF16 = 3    /* A/B operands (dense BF16 backend) or C / D outputs */
+} moegg_dtype;
+
+typedef enum moegg_act {
+  MOEGG_ACT_NONE = 0,    /* D = prob * C            ("Grouped GEMM + Quant", Step 2)        */
+  MOEGG_ACT_SWIGLU = 1,  /* D = prob * X_b * swish(G_b), pairs [X_b|G_b] of 32 columns
+                            ("Grouped GEMM + SwiGLU", Step 2)                               */
+  MOEGG_ACT_SRELU = 2,   /* D = prob * relu(C)^2, optional tanh soft clamp s
+                            ("Grouped GEMM + sReLU", §Equations / §Tanh soft clamp)          */
+  MOEGG_ACT_DSWIGLU = 3  /* dC = [d_input|d_gate] from R and beta*C_in, dprob += row sums
+                            ("Grouped GEMM + dGLU", BF16 contract, dSwiGLU)                  */
+} moegg_act;
+
+/* Problem description (host struct). */
+typedef struct moegg_problem {
+  int32_t num_groups;   /* L, 1..1024 ("Shapes and Divisibility": expert count <= 1024) */
+  int32_t m_aligned;    /* group row alignment; multiple of 128 here                     */
+  int64_t valid_m;      /* rows of A == padded_offsets[L-1]; multiple of m_aligned       */
+  int32_t n;            /* GEMM N (rows of each expert's B)                               */
+  int32_t k;            /* reduction length K                                             */
+  int32_t ab_dtype;     /* moegg_dtype of A and B: E4M3 | E2M1X2 | BF16                   */
+  int32_t c_dtype;      /* NONE (C not written) | BF16                                    */
+  int32_t d_dtype;      /* BF16 (needs amax) | E4M3 (needs SFD_row, SFD_col, norm_const)  */
+  int32_t act;          /* moegg_act                                                      */
+  float srelu_tanh_s;   /* sReLU soft clamp s; 0 = plain relu^2                           */
+} moegg_problem;
+
+/* Tensor pointers (device memory, caller-owned).  NULL where not used. */
+typedef struct moegg_args {
+  const void* a;
+  const void* b;
+  const uint8_t* sfa;            /* MX operands only */
+  const uint8_t* sfb;            /* MX operands only */
+  const int32_t* padded_offsets;
+  const float* alpha;
+  const float* prob;             /* required ("prob ... Required", Quant page) */
+  const float* beta;             /* dSwiGLU only */
+  const float* norm_const;       /* required iff d_dtype == E4M3 */
+  const void* c_in;              /* dSwiGLU only: saved forward C, BF16 (valid_m, 2N) */
+  void* c;                       /* optional C output (c_dtype BF16) */
+  void* d;                       /* D (or dC for dSwiGLU) */
+  void* d_col;                   /* E4M3 only */
+  uint8_t* sfd_row;              /* E4M3 only */
+  uint8_t* sfd_col;              /* E4M3 only */
+  float* amax;                   /* BF16 D (forward) only */
+  float* dprob;                  /* dSwiGLU only, caller-zeroed */
+} moegg_args;
+
+/* Validate problem + pointers on the host.  No HIP call.  MOEGG_OK if
+ * moegg_run would launch (or, for valid_m == 0, do nothing). */
+moegg_status moegg_check(const moegg_problem* problem, const moegg_args* args);
+
+/* Validate, then enqueue the whole path on `stream` (hipStream_t).  Zero-fills
+ * amax (when used) on the same stream.  valid_m == 0: returns MOEGG_OK and
+ * enqueues nothing. */
+moegg_status moegg_run(const moegg_problem* problem, const moegg_args* args, void* stream);
+
+/* Opt-in validator of device padded_offsets (synchronises `stream`): entries
+ * nondecreasing, multiples of m_aligned, last == valid_m.  MOEGG_OK or
+ * MOEGG_ERROR_INVALID_VALUE. */
+moegg_status moegg_check_offsets(const moegg_problem* problem, const int32_t* padded_offsets,
+                                 void* stream);
+
+/* Output width N_out for a problem (N/2 SwiGLU, 2N dSwiGLU, else N); -1 if invalid act. */
+int64_t moegg_n_out(const moegg_problem* problem);
+
+const char* moegg_status_string(moegg_status status);
+const char* moegg_last_error(void);   /* thread-local detail of the last failure */
+int moegg_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEGG_H_ */

@@ -1,0 +1,61 @@
+// Internal interface between the C-ABI front (moegg_api.cpp) and the HIP
+// kernels (moegg_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moegg {
+
+// Operand family of A/B.
+enum AbKind : int { AB_E4M3 = 0, AB_E2M1 = 1, AB_BF16 = 2 };
+// Epilogue activation.
+enum ActKind : int { ACT_NONE = 0, ACT_SWIGLU = 1, ACT_SRELU = 2, ACT_DSWIGLU = 3 };
+// Output formatting of D.
+enum OutKind : int { OUT_BF16 = 0, OUT_E4M3 = 1 };
+
+// Block tile: BM token rows x BN GEMM columns, 256 threads (4 wave64s).
+constexpr int kBM = 128;
+constexpr int kBN = 256;
+constexpr int kThreads = 256;
+
+// Everything a kernel needs, passed by value (kernel argument segment).
+struct KernelArgs {
+  const uint8_t* a;        // (valid_m, row_bytes)
+  const uint8_t* b;        // (L, n, row_bytes)
+  const uint8_t* sfa;      // (valid_m, ksf)
+  const uint8_t* sfb;      // (L, n, ksf)
+  const int32_t* po;       // (L)
+  const float* alpha;      // (L)
+  const float* prob;       // (valid_m)
+  const float* beta;       // (L) dSwiGLU
+  const float* norm_const; // (1) E4M3 D
+  const uint16_t* c_in;    // (valid_m, 2n) dSwiGLU
+  uint16_t* c;             // (valid_m, n) optional
+  uint8_t* d;              // (valid_m, n_out) bf16 or e4m3
+  uint8_t* d_col;          // (valid_m, n_out) e4m3
+  uint8_t* sfd_row;        // (valid_m, n_out/32)
+  uint8_t* sfd_col;        // (n_out, valid_m/32)
+  float* amax;             // (L)
+  float* dprob;            // (valid_m)
+  int64_t valid_m;
+  int32_t num_groups;
+  int32_t n;
+  int32_t k;
+  int32_t n_out;
+  int32_t row_bytes;       // bytes per row of A and B
+  int32_t ksf;             // scale bytes per row (K/32)
+  int32_t m_tiles;
+  int32_t n_tiles;
+  int32_t k_steps;         // K / elements-per-128-byte-step
+  float srelu_s;
+};
+
+// Launch the grouped GEMM kernel instance for (ab, act, out).  Returns the
+// HIP error of the launch (hipSuccess if enqueued).
+hipError_t launch_grouped_gemm(int ab, int act, int out, const KernelArgs& args, hipStream_t stream);
+
+// Zero `count` floats with a fill kernel (usable under stream capture).
+hipError_t launch_fill_zero(float* ptr, int count, hipStream_t stream);
+
+}  // namespace moegg

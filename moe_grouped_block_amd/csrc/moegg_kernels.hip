@@ -1,0 +1,577 @@
+// HIP kernels of libmoegg for gfx950 (CDNA4): contiguous grouped
+// block-scaled GEMM with fused epilogue.
+//
+// Method ("Grouped GEMM + Quant (SM100)", "Grouped GEMM + SwiGLU (SM100)",
+// "Grouped GEMM + sReLU (SM100)", "Grouped GEMM + dGLU (SM100)", §Equations):
+// rows m of A in [padded_offsets[g-1], padded_offsets[g]) are multiplied by
+// expert g's weight B[g] (N x K, K-major) with per-32-element E8M0 block
+// scales on both operands, scaled by alpha_g (alpha_g^2 for the dSwiGLU
+// backward), then the activation / gating / output-formatting epilogue.
+//
+// Mapping onto CDNA4:
+//  * one workgroup = 4 wave64s = a 128-row x 256-column output tile; a tile
+//    never straddles two experts because groups are padded to a multiple of
+//    128 rows, so the expert index is one per workgroup (binary search of
+//    padded_offsets, wave-uniform).
+//  * the contraction runs on the block-scaled matrix cores:
+//    v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 or E2M1 operands, one E8M0 byte
+//    per lane and operand selects the scale of that lane's 32 K-elements) or
+//    v_mfma_f32_32x32x16_bf16.  The weight tile is the instruction's first
+//    operand and the token tile the second, so an accumulator lane holds one
+//    token row and 16 output columns (4 runs of 4 contiguous columns): row
+//    reductions are lane-local, stores are 8-byte (bf16) / 4-byte (e4m3) runs.
+//  * K advances in steps of 128 bytes per row (128 E4M3, 256 E2M1 or 64 BF16
+//    elements); A/B step tiles are staged global -> registers -> LDS with a
+//    double buffer (row stride 144 B, conflict-free 16-byte LDS reads), one
+//    barrier per step.  Scale bytes go straight to registers.
+//  * the epilogue runs on the fp32 accumulators in registers.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "moegg_internal.h"
+
+namespace moegg {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));   // native vectors (HIP's uint4
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));   // struct defeats SROA)
+
+constexpr int kStride = 144;      // LDS row stride: 128 data bytes + 16 pad
+
+// Unrolled loop whose index is a compile-time constant (instruction
+// immediates such as the MFMA scale byte selectors need one).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRcp448 = 1.0f / 448.0f;   // rcp_max of E4M3, rounded to fp32
+
+// ---------------------------------------------------------------------------
+// device codecs
+// ---------------------------------------------------------------------------
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// E8M0 byte of the smallest power of two >= sf (sf >= 0), clamped to [0, 254].
+__device__ __forceinline__ uint32_t e8m0_ceil(float sf) {
+  const uint32_t u = __float_as_uint(sf);
+  const uint32_t e = u >> 23, m = u & 0x7FFFFFu;
+  uint32_t b = (e == 0) ? (m > 0x400000u ? 1u : 0u) : e + (m != 0u ? 1u : 0u);
+  return b > 254u ? 254u : b;
+}
+
+// 2^(127 - byte), exact.
+__device__ __forceinline__ float e8m0_inverse(uint32_t byte) {
+  return byte < 254u ? __uint_as_float((254u - byte) << 23) : __uint_as_float(0x00400000u);
+}
+
+// Four fp32 -> four E4M3 codes (RNE by the conversion unit, saturated to
+// +-448 beforehand), packed little-endian: a is the lowest byte.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.0f), 448.0f);
+  b = fminf(fmaxf(b, -448.0f), 448.0f);
+  c = fminf(fmaxf(c, -448.0f), 448.0f);
+  d = fminf(fmaxf(d, -448.0f), 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// sigmoid(x) = 1 / (1 + 2^(-x log2 e)); saturates to 0 / 1 at the extremes.
+__device__ __forceinline__ float sigmoid_f(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
+}
+
+// tanh(x) for x >= 0: odd Taylor series below 1/8 (error < 2e-10), else
+// (1 - e^-2x) / (1 + e^-2x).  Result <= 1.
+__device__ __forceinline__ float tanh_nonneg(float x) {
+  const float x2 = x * x;
+  const float series = x * (1.0f + x2 * (-1.0f / 3.0f + x2 * (2.0f / 15.0f + x2 * (-17.0f / 315.0f))));
+  const float e = __builtin_amdgcn_exp2f(-2.0f * kLog2e * x);
+  const float big = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
+  return x < 0.125f ? series : big;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Column offset (within a 32-column MFMA tile) of accumulator element v of
+// this lane: rows of the 32x32 result are spread as 8*(v/4) + 4*(lane/32) + v%4.
+__device__ __forceinline__ int nofs(int v, int hi) { return 8 * (v >> 2) + 4 * hi + (v & 3); }
+
+// Store 16 values of one row (one 32-column tile) as bf16: 4 runs of 4.
+__device__ __forceinline__ void store_bf16_tile(uint8_t* base, int64_t m, int ld, int col, int hi,
+                                                const float* v) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v2u w;
+    w.x = bf16_rne(v[4 * j + 0]) | (bf16_rne(v[4 * j + 1]) << 16);
+    w.y = bf16_rne(v[4 * j + 2]) | (bf16_rne(v[4 * j + 3]) << 16);
+    *reinterpret_cast<v2u*>(base + (m * ld + col + 8 * j + 4 * hi) * 2) = w;
+  }
+}
+
+// FP8 row + column quantisation of one 32-column output tile ("Grouped GEMM +
+// Quant (SM100)", §Equations Step 3 and §Diagram Row/Col Quantize).  The 32
+// rows of the column blocks are the 32 lanes of this half-wave.
+__device__ __forceinline__ void quant_store_tile(const KernelArgs& p, int m, int mblk, int ocol, int hi,
+                                                 int l32, float nc, const float* d) {
+  // row block: 16 values here + 16 in lane ^ 32
+  float ra = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) ra = fmaxf(ra, fabsf(d[v]));
+  ra = fmaxf(ra, __shfl_xor(ra, 32));
+  const uint32_t br = e8m0_ceil((nc * ra) * kRcp448);
+  const float sr = e8m0_inverse(br);
+  const int64_t rowoff = static_cast<int64_t>(m) * p.n_out + ocol + 4 * hi;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = e4m3x4((d[4 * j] * nc) * sr, (d[4 * j + 1] * nc) * sr, (d[4 * j + 2] * nc) * sr,
+                              (d[4 * j + 3] * nc) * sr);
+    *reinterpret_cast<uint32_t*>(p.d + rowoff + 8 * j) = w;
+  }
+  if (hi == 0) p.sfd_row[static_cast<int64_t>(m) * (p.n_out >> 5) + (ocol >> 5)] = static_cast<uint8_t>(br);
+
+  // column blocks: max over the 32 lanes of this half for each element
+  float cm[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float x = fabsf(d[v]);
+    x = fmaxf(x, __shfl_xor(x, 1));
+    x = fmaxf(x, __shfl_xor(x, 2));
+    x = fmaxf(x, __shfl_xor(x, 4));
+    x = fmaxf(x, __shfl_xor(x, 8));
+    x = fmaxf(x, __shfl_xor(x, 16));
+    cm[v] = x;
+  }
+  uint32_t bc[16];
+  float sc[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    bc[v] = e8m0_ceil((nc * cm[v]) * kRcp448);
+    sc[v] = e8m0_inverse(bc[v]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = e4m3x4((d[4 * j] * nc) * sc[4 * j], (d[4 * j + 1] * nc) * sc[4 * j + 1],
+                              (d[4 * j + 2] * nc) * sc[4 * j + 2], (d[4 * j + 3] * nc) * sc[4 * j + 3]);
+    *reinterpret_cast<uint32_t*>(p.d_col + rowoff + 8 * j) = w;
+  }
+  const int64_t mblocks = p.valid_m >> 5;
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    if (l32 == v) p.sfd_col[static_cast<int64_t>(ocol + nofs(v, hi)) * mblocks + mblk] = static_cast<uint8_t>(bc[v]);
+}
+
+// ---------------------------------------------------------------------------
+// the fused kernel
+// ---------------------------------------------------------------------------
+
+template <int AB, int ACT, int OUT>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p) {
+  constexpr int BM = kBM, BN = kBN;
+  constexpr int WN = BN / 2;     // GEMM columns per wave
+  constexpr int TN = WN / 32;    // 32-column MFMA tiles per wave
+  constexpr int TM = 2;          // 32-row MFMA tiles per wave (64 rows)
+  constexpr int A_BYTES = BM * kStride, B_BYTES = BN * kStride;
+  constexpr int A_LD = BM * 8 / kThreads;   // 16-byte chunks per thread per step
+  constexpr int B_LD = BN * 8 / kThreads;
+  constexpr bool MX = AB != AB_BF16;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (A_BYTES + B_BYTES)];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  const int tile = blockIdx.x;
+  const int mt = tile / p.n_tiles;
+  const int nt = tile - mt * p.n_tiles;
+  const int row0 = mt * BM;
+  const int n0 = nt * BN;
+
+  // expert of this row tile: the number of padded_offsets entries <= row0
+  int lo = 0, up = p.num_groups;
+  while (lo < up) {
+    const int mid = (lo + up) >> 1;
+    if (p.po[mid] > row0) up = mid; else lo = mid + 1;
+  }
+  const int g = lo < p.num_groups ? lo : p.num_groups - 1;   // inconsistent offsets never index out of range
+
+  // ---- global -> LDS staging addresses ----
+  const int crow = tid >> 3, ccol = (tid & 7) * 16;
+  const uint8_t* gA = p.a + static_cast<int64_t>(row0 + crow) * p.row_bytes + ccol;
+  const int64_t a_step32 = static_cast<int64_t>(32) * p.row_bytes;
+  const uint8_t* gBg = p.b + static_cast<int64_t>(g) * p.n * p.row_bytes + ccol;
+  int brow[B_LD];
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) brow[i] = min(n0 + crow + 32 * i, p.n - 1);
+  const int lds_st = crow * kStride + ccol;
+
+  v4u ra[A_LD], rb[B_LD];
+  auto gload = [&](int ks) {
+    const int kb = ks * 128;
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const v4u*>(gA + i * a_step32 + kb);
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i)
+      rb[i] = *reinterpret_cast<const v4u*>(gBg + static_cast<int64_t>(brow[i]) * p.row_bytes + kb);
+  };
+  auto sstore = [&](int buf) {
+    uint8_t* sa = smem + buf * A_BYTES;
+    uint8_t* sb = smem + 2 * A_BYTES + buf * B_BYTES;
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) *reinterpret_cast<v4u*>(sa + lds_st + i * 32 * kStride) = ra[i];
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) *reinterpret_cast<v4u*>(sb + lds_st + i * 32 * kStride) = rb[i];
+  };
+
+  // ---- scale bytes: one row per lane and tile; byte 0 / 2 of the shifted
+  //      word are this lane's K-blocks for the two (E4M3) MFMAs of a step ----
+  const uint8_t* sfa_row[TM];
+  const uint8_t* sfb_row[TN];
+  if constexpr (MX) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+      sfa_row[tm] = p.sfa + static_cast<int64_t>(row0 + wm * 64 + tm * 32 + l32) * p.ksf;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      const int r = min(n0 + wn * WN + tn * 32 + l32, p.n - 1);
+      sfb_row[tn] = p.sfb + (static_cast<int64_t>(g) * p.n + r) * p.ksf;
+    }
+  }
+  constexpr int SW = AB == AB_E2M1 ? 2 : 1;   // scale words per row per step
+  uint32_t sa_cur[TM][SW], sb_cur[TN][SW], sa_nxt[TM][SW], sb_nxt[TN][SW];
+  auto sload = [&](int ks, uint32_t (&sa)[TM][SW], uint32_t (&sb)[TN][SW]) {
+    if constexpr (MX) {
+      const int sh = 8 * hi;
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        if constexpr (SW == 1) {
+          sa[tm][0] = *reinterpret_cast<const uint32_t*>(sfa_row[tm] + ks * 4) >> sh;
+        } else {
+          const v2u w = *reinterpret_cast<const v2u*>(sfa_row[tm] + ks * 8);
+          sa[tm][0] = w.x >> sh;
+          sa[tm][1] = w.y >> sh;
+        }
+      }
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        if constexpr (SW == 1) {
+          sb[tn][0] = *reinterpret_cast<const uint32_t*>(sfb_row[tn] + ks * 4) >> sh;
+        } else {
+          const v2u w = *reinterpret_cast<const v2u*>(sfb_row[tn] + ks * 8);
+          sb[tn][0] = w.x >> sh;
+          sb[tn][1] = w.y >> sh;
+        }
+      }
+    }
+  };
+
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
+
+  // ---- main loop ----
+  gload(0);
+  sload(0, sa_cur, sb_cur);
+  sstore(0);
+  __syncthreads();
+  const int a_rd = (wm * 64 + l32) * kStride;
+  const int b_rd = (wn * WN + l32) * kStride;
+  for (int ks = 0; ks < p.k_steps; ++ks) {
+    const int cur = ks & 1;
+    const bool more = ks + 1 < p.k_steps;
+    if (more) {
+      gload(ks + 1);
+      sload(ks + 1, sa_nxt, sb_nxt);
+    }
+    const uint8_t* sa = smem + cur * A_BYTES + a_rd;
+    const uint8_t* sb = smem + 2 * A_BYTES + cur * B_BYTES + b_rd;
+    if constexpr (AB == AB_E4M3) {
+      static_for<0, 2>([&](auto kki) {
+        constexpr int kk = decltype(kki)::value;
+        // 8-bit operands: a lane of half h holds K [16h, 16h+16) and
+        // [32+16h, 48+16h) of the 64-wide window, while its scale byte covers
+        // the 32-element block h; FP4 operands hold [32h, 32h+32) instead.
+        const int off = hi * 16 + kk * 64;
+        v8i fa[TM], fb[TN];
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          const v4u x0 = *reinterpret_cast<const v4u*>(sa + tm * 32 * kStride + off);
+          const v4u x1 = *reinterpret_cast<const v4u*>(sa + tm * 32 * kStride + off + 32);
+          fa[tm] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        }
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const v4u x0 = *reinterpret_cast<const v4u*>(sb + tn * 32 * kStride + off);
+          const v4u x1 = *reinterpret_cast<const v4u*>(sb + tn * 32 * kStride + off + 32);
+          fb[tn] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        }
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn)
+            acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fb[tn], fa[tm], acc[tm][tn], 0, 0, kk * 2, (int)sb_cur[tn][0], kk * 2, (int)sa_cur[tm][0]);
+      });
+    } else if constexpr (AB == AB_E2M1) {
+      static_for<0, 4>([&](auto kki) {
+        constexpr int kk = decltype(kki)::value;
+        const int off = hi * 16 + kk * 32;
+        v8i fa[TM], fb[TN];
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          const v4u x0 = *reinterpret_cast<const v4u*>(sa + tm * 32 * kStride + off);
+          fa[tm] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const v4u x0 = *reinterpret_cast<const v4u*>(sb + tn * 32 * kStride + off);
+          fb[tn] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn)
+            acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fb[tn], fa[tm], acc[tm][tn], 4, 4, (kk & 1) * 2, (int)sb_cur[tn][kk >> 1], (kk & 1) * 2,
+                (int)sa_cur[tm][kk >> 1]);
+      });
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int off = hi * 16 + kk * 32;
+        v8bf fa[TM], fb[TN];
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+          fa[tm] = *reinterpret_cast<const v8bf*>(sa + tm * 32 * kStride + off);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+          fb[tn] = *reinterpret_cast<const v8bf*>(sb + tn * 32 * kStride + off);
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn)
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[tn], fa[tm], acc[tm][tn], 0, 0, 0);
+      }
+    }
+    if (more) {
+      sstore(cur ^ 1);
+      if constexpr (MX) {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+          for (int w = 0; w < SW; ++w) sa_cur[tm][w] = sa_nxt[tm][w];
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int w = 0; w < SW; ++w) sb_cur[tn][w] = sb_nxt[tn][w];
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue ----
+  const float alpha = p.alpha[g];
+  const int mbase = row0 + wm * 64;
+  const int nbase = n0 + wn * WN;
+  float amax_l = 0.0f;
+  float nc = 1.0f;
+  if constexpr (OUT == OUT_E4M3) nc = p.norm_const[0];
+
+  if constexpr (ACT == ACT_DSWIGLU) {
+    // R = alpha^2 acc; X = beta * C_in with blocks [input_b | gate_b]
+    // ("Grouped GEMM + dGLU (SM100)", BF16 contract equations)
+    const float a2 = alpha * alpha;
+    const float beta = p.beta[g];
+    const int ld2 = 2 * p.n;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const int m = mbase + tm * 32 + l32;
+      const float pr = p.prob[m];
+      float dp = 0.0f;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int ncol = nbase + tn * 32;
+        if (ncol >= p.n) continue;
+        const int64_t xoff = static_cast<int64_t>(m) * ld2 + 2 * ncol;   // block b = ncol/32 starts at 64b
+        float xin[16], xg[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const v2u wi = *reinterpret_cast<const v2u*>(p.c_in + xoff + 8 * j + 4 * hi);
+          const v2u wg = *reinterpret_cast<const v2u*>(p.c_in + xoff + 32 + 8 * j + 4 * hi);
+          xin[4 * j + 0] = __uint_as_float(wi.x << 16);
+          xin[4 * j + 1] = __uint_as_float(wi.x & 0xFFFF0000u);
+          xin[4 * j + 2] = __uint_as_float(wi.y << 16);
+          xin[4 * j + 3] = __uint_as_float(wi.y & 0xFFFF0000u);
+          xg[4 * j + 0] = __uint_as_float(wg.x << 16);
+          xg[4 * j + 1] = __uint_as_float(wg.x & 0xFFFF0000u);
+          xg[4 * j + 2] = __uint_as_float(wg.y << 16);
+          xg[4 * j + 3] = __uint_as_float(wg.y & 0xFFFF0000u);
+        }
+        float din[16], dgt[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float r = a2 * acc[tm][tn][v];
+          const float x = beta * xin[v];
+          const float gt = beta * xg[v];
+          const float s = sigmoid_f(gt);
+          const float swish = gt * s;
+          din[v] = r * pr * swish;
+          dgt[v] = r * pr * x * s * (1.0f + gt * (1.0f - s));
+          dp += r * x * swish;
+        }
+        uint8_t* dbase = p.d;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v2u w;
+          w.x = bf16_rne(din[4 * j]) | (bf16_rne(din[4 * j + 1]) << 16);
+          w.y = bf16_rne(din[4 * j + 2]) | (bf16_rne(din[4 * j + 3]) << 16);
+          *reinterpret_cast<v2u*>(dbase + (xoff + 8 * j + 4 * hi) * 2) = w;
+          w.x = bf16_rne(dgt[4 * j]) | (bf16_rne(dgt[4 * j + 1]) << 16);
+          w.y = bf16_rne(dgt[4 * j + 2]) | (bf16_rne(dgt[4 * j + 3]) << 16);
+          *reinterpret_cast<v2u*>(dbase + (xoff + 32 + 8 * j + 4 * hi) * 2) = w;
+        }
+      }
+      dp += __shfl_xor(dp, 32);
+      if (hi == 0) atomicAdd(p.dprob + m, dp);
+    }
+    return;
+  } else {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const int m = mbase + tm * 32 + l32;
+      const int mblk = (mbase + tm * 32) >> 5;
+      const float pr = p.prob[m];
+      if constexpr (ACT == ACT_SWIGLU) {
+        // pairs [X_b | G_b] of 32 columns ("Grouped GEMM + SwiGLU (SM100)", Step 2)
+#pragma unroll
+        for (int tp = 0; tp < TN / 2; ++tp) {
+          const int xcol = nbase + tp * 64;
+          if (xcol >= p.n) continue;
+          float cx[16], cg[16], d[16];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            cx[v] = alpha * acc[tm][2 * tp][v];
+            cg[v] = alpha * acc[tm][2 * tp + 1][v];
+          }
+          if (p.c) {
+            store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, xcol, hi, cx);
+            store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, xcol + 32, hi, cg);
+          }
+#pragma unroll
+          for (int v = 0; v < 16; ++v) d[v] = pr * cx[v] * (cg[v] * sigmoid_f(cg[v]));
+          const int ocol = xcol >> 1;
+          if constexpr (OUT == OUT_BF16) {
+            store_bf16_tile(p.d, m, p.n_out, ocol, hi, d);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) amax_l = fmaxf(amax_l, fabsf(d[v]));
+          } else {
+            quant_store_tile(p, m, mblk, ocol, hi, l32, nc, d);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int ncol = nbase + tn * 32;
+          if (ncol >= p.n) continue;
+          float c[16], d[16];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) c[v] = alpha * acc[tm][tn][v];
+          if (p.c) store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, ncol, hi, c);
+          if constexpr (ACT == ACT_SRELU) {
+            // D = prob * (s * min(tanh(relu(C)/s), 1))^2, or prob * relu(C)^2 for s = 0
+            // ("Grouped GEMM + sReLU (SM100)", §Equations, §Tanh soft clamp)
+            const float s = p.srelu_s;
+            const float rs = s > 0.0f ? 1.0f / s : 0.0f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              float r = fmaxf(c[v], 0.0f);
+              if (s > 0.0f) r = s * fminf(tanh_nonneg(r * rs), 1.0f);
+              d[v] = pr * (r * r);
+            }
+          } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) d[v] = pr * c[v];
+          }
+          if constexpr (OUT == OUT_BF16) {
+            store_bf16_tile(p.d, m, p.n_out, ncol, hi, d);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) amax_l = fmaxf(amax_l, fabsf(d[v]));
+          } else {
+            quant_store_tile(p, m, mblk, ncol, hi, l32, nc, d);
+          }
+        }
+      }
+    }
+    if constexpr (OUT == OUT_BF16) {
+      const float w = wave_max(amax_l);
+      if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(p.amax + g), __float_as_uint(w));
+    }
+  }
+}
+
+__global__ void fill_zero_kernel(float* ptr, int count) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < count) ptr[i] = 0.0f;
+}
+
+template <int AB, int ACT, int OUT>
+hipError_t launch_one(const KernelArgs& a, hipStream_t s) {
+  const int64_t blocks = static_cast<int64_t>(a.m_tiles) * a.n_tiles;
+  hipLaunchKernelGGL((grouped_gemm_kernel<AB, ACT, OUT>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int AB>
+hipError_t launch_ab(int act, int out, const KernelArgs& a, hipStream_t s) {
+  switch (act) {
+    case ACT_NONE: return out == OUT_E4M3 ? launch_one<AB, ACT_NONE, OUT_E4M3>(a, s) : launch_one<AB, ACT_NONE, OUT_BF16>(a, s);
+    case ACT_SWIGLU: return out == OUT_E4M3 ? launch_one<AB, ACT_SWIGLU, OUT_E4M3>(a, s) : launch_one<AB, ACT_SWIGLU, OUT_BF16>(a, s);
+    case ACT_SRELU: return out == OUT_E4M3 ? launch_one<AB, ACT_SRELU, OUT_E4M3>(a, s) : launch_one<AB, ACT_SRELU, OUT_BF16>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm(int ab, int act, int out, const KernelArgs& a, hipStream_t s) {
+  if (act == ACT_DSWIGLU) {
+    if (ab != AB_BF16 || out != OUT_BF16) return hipErrorInvalidValue;
+    return launch_one<AB_BF16, ACT_DSWIGLU, OUT_BF16>(a, s);
+  }
+  switch (ab) {
+    case AB_E4M3: return launch_ab<AB_E4M3>(act, out, a, s);
+    case AB_E2M1: return launch_ab<AB_E2M1>(act, out, a, s);
+    case AB_BF16: return launch_ab<AB_BF16>(act, out, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_fill_zero(float* ptr, int count, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((count + 255) / 256), dim3(256), 0, s, ptr, count);
+  return hipGetLastError();
+}
+
+}  // namespace moegg

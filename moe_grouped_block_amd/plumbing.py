@@ -1,0 +1,79 @@
+"""Device-memory plumbing around the binding (torch used for allocation only).
+
+``to_device`` uploads host arrays in the library's logical layouts;
+``empty_outputs`` allocates the output tensors a problem writes.  Neither
+computes anything of the method.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+_NP2TORCH = {np.dtype(np.uint8): torch.uint8, np.dtype(np.uint16): torch.int16,
+             np.dtype(np.int32): torch.int32, np.dtype(np.float32): torch.float32}
+
+
+def to_device(arrays: dict, device="cuda") -> dict:
+    """numpy arrays -> contiguous device tensors (uint16 bf16 bits travel as int16)."""
+    out = {}
+    for k, v in arrays.items():
+        v = np.ascontiguousarray(v)
+        t = torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v)
+        out[k] = t.to(device, non_blocking=False)
+    return out
+
+
+def n_out(problem: dict) -> int:
+    n = int(problem["n"])
+    return {"none": n, "srelu": n, "swiglu": n // 2, "dswiglu": 2 * n}[problem["act"]]
+
+
+def empty_outputs(problem: dict, device="cuda", fill: int | None = None) -> dict:
+    """Allocate every output the problem writes.  `fill` (a byte value) pre-fills
+    them so a test can see untouched elements; dprob is always zero-filled
+    because the library accumulates into it."""
+    m, n, L = int(problem["valid_m"]), int(problem["n"]), int(problem["num_groups"])
+    no = n_out(problem)
+    out = {}
+
+    def mk(shape, dtype):
+        t = torch.empty(shape, dtype=dtype, device=device)
+        if fill is not None:
+            t.view(torch.uint8).fill_(fill)
+        return t
+    if problem["act"] == "dswiglu":
+        out["d"] = mk((m, no), torch.int16)
+        out["dprob"] = torch.zeros(m, dtype=torch.float32, device=device)
+        return out
+    if problem.get("c_dtype") == "bf16":
+        out["c"] = mk((m, n), torch.int16)
+    if problem["d_dtype"] == "bf16":
+        out["d"] = mk((m, no), torch.int16)
+        out["amax"] = mk((L,), torch.float32)
+    else:
+        out["d"] = mk((m, no), torch.uint8)
+        out["d_col"] = mk((m, no), torch.uint8)
+        out["sfd_row"] = mk((m, no // 32), torch.uint8)
+        out["sfd_col"] = mk((no, m // 32), torch.uint8)
+    return out
+
+
+def inputs_for(problem: dict, dev_arrays: dict) -> dict:
+    """Select the input tensors the problem uses from an uploaded case."""
+    keys = ["a", "b", "padded_offsets", "alpha", "prob"]
+    if problem["ab_dtype"] != "bf16":
+        keys += ["sfa", "sfb"]
+    if problem["d_dtype"] == "e4m3":
+        keys += ["norm_const"]
+    if problem["act"] == "dswiglu":
+        keys += ["beta", "c_in"]
+    return {k: dev_arrays[k] for k in keys}
+
+
+def to_host(outputs: dict) -> dict:
+    """Device outputs -> numpy (int16 bf16 bits come back as uint16)."""
+    res = {}
+    for k, t in outputs.items():
+        a = t.detach().cpu().numpy()
+        res[k] = a.view(np.uint16) if a.dtype == np.int16 else a
+    return res

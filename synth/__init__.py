@@ -169,8 +169,8 @@ class Case:
         return 2.0 * self.routed_rows * p["n"] * p["k"]
 
 
-# Workload recipes.  Sizes and distributions follow the MoE configurations the
-# method is exercised on (see the design doc for the recipe of each field).
+# Workload recipes: expert count, K, N, operand/output formats, routing and the
+# value distributions of the MoE layers the method serves.
 CONFIGS = {
     # gating only, bf16 D + per-group amax
     "quant_gating_l4": dict(L=4, K=512, N=512, ab="e4m3", act="none", d="bf16", c=None,
@@ -199,10 +199,10 @@ CONFIGS = {
 }
 
 
-def config_spec(name: str, **overrides) -> dict:
-    spec = dict(CONFIGS[name])
+def config_spec(config: str, **overrides) -> dict:
+    spec = dict(CONFIGS[config])
     spec.update(overrides)
-    spec.setdefault("name", name)
+    spec.setdefault("name", config)
     return spec
 
 

@@ -1,0 +1,172 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/moegg.h declares, and its host-side validation returns the right
+status for every rule, before any HIP call (no device memory is touched:
+the pointers below are fake, aligned integers)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moegg.h")
+
+import moe_grouped_block_amd as mg  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    if not os.path.exists(mg.lib_path):
+        from moe_grouped_block_amd import build
+        build.build()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*[A-Za-z_][A-Za-z0-9_ \*]*?\b(moegg_[a-z_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_function():
+    names = _declared_functions()
+    assert {"moegg_check", "moegg_run", "moegg_check_offsets", "moegg_n_out", "moegg_status_string",
+            "moegg_last_error", "moegg_abi_version"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", mg.lib_path], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (moegg_[a-z_]+)\b", out))
+    assert set(names) <= exported, set(names) - exported
+    lib = ctypes.CDLL(mg.lib_path)
+    for n in names:
+        getattr(lib, n)
+
+
+def test_version_and_strings():
+    assert mg.moegg_abi_version() == 1
+    for code, name in mg.STATUS.items():
+        assert mg.moegg_status_string(code) == name
+    assert mg.moegg_status_string(99) == "MOEGG_UNKNOWN_STATUS"
+
+
+def test_struct_layout_matches_header():
+    # problem: 2 x int32, int64, 6 x int32, float -> 44 bytes, padded to 48
+    assert ctypes.sizeof(mg.moegg_problem) == 48
+    assert mg.moegg_problem.valid_m.offset == 8
+    assert ctypes.sizeof(mg.moegg_args) == 17 * 8
+
+
+FAKE = 0x7F0000000000            # 16-byte aligned, never dereferenced by moegg_check
+
+
+def _ptrs(names):
+    return {n: FAKE + 0x1000 * i for i, n in enumerate(names)}
+
+
+def _base(kind):
+    if kind == "swiglu_e4m3":
+        p = dict(num_groups=8, m_aligned=128, valid_m=8704, n=2816, k=2048, ab_dtype="e4m3",
+                 c_dtype=None, d_dtype="e4m3", act="swiglu", srelu_tanh_s=0.0)
+        t = _ptrs(["a", "b", "sfa", "sfb", "padded_offsets", "alpha", "prob", "norm_const",
+                   "d", "d_col", "sfd_row", "sfd_col"])
+    elif kind == "gating_bf16":
+        p = dict(num_groups=4, m_aligned=128, valid_m=1024, n=512, k=512, ab_dtype="e4m3",
+                 c_dtype=None, d_dtype="bf16", act="none")
+        t = _ptrs(["a", "b", "sfa", "sfb", "padded_offsets", "alpha", "prob", "d", "amax"])
+    elif kind == "srelu_fp4":
+        p = dict(num_groups=32, m_aligned=128, valid_m=34560, n=4096, k=4096, ab_dtype="e2m1x2",
+                 c_dtype="bf16", d_dtype="e4m3", act="srelu", srelu_tanh_s=8.0)
+        t = _ptrs(["a", "b", "sfa", "sfb", "padded_offsets", "alpha", "prob", "norm_const", "c",
+                   "d", "d_col", "sfd_row", "sfd_col"])
+    else:
+        p = dict(num_groups=64, m_aligned=128, valid_m=102144, n=1408, k=2048, ab_dtype="bf16",
+                 c_dtype=None, d_dtype="bf16", act="dswiglu")
+        t = _ptrs(["a", "b", "padded_offsets", "alpha", "prob", "beta", "c_in", "d", "dprob"])
+    return p, t
+
+
+def _status(p, t):
+    return mg.moegg_check(mg.make_problem(p), mg.make_args(t))
+
+
+@pytest.mark.parametrize("kind", ["swiglu_e4m3", "gating_bf16", "srelu_fp4", "dswiglu"])
+def test_valid_configs_pass(kind):
+    p, t = _base(kind)
+    assert _status(p, t) == 0, mg.moegg_last_error()
+
+
+INVALID, MISALIGNED, NOT_SUPPORTED = 1, 2, 3
+
+CASES = [
+    # (base, problem overrides, tensor overrides, expected status)
+    ("gating_bf16", dict(num_groups=0), {}, INVALID),
+    ("gating_bf16", dict(num_groups=1025), {}, INVALID),
+    ("gating_bf16", dict(n=0), {}, INVALID),
+    ("gating_bf16", dict(valid_m=-128), {}, INVALID),
+    ("gating_bf16", dict(valid_m=1000), {}, INVALID),                  # not a multiple of m_aligned
+    ("gating_bf16", dict(m_aligned=48), {}, INVALID),
+    ("gating_bf16", dict(m_aligned=64, valid_m=1024), {}, NOT_SUPPORTED),
+    ("gating_bf16", dict(k=500), {}, INVALID),                         # K % 32
+    ("gating_bf16", dict(k=544), {}, NOT_SUPPORTED),                   # FP8 step of 128
+    ("srelu_fp4", dict(k=4096 + 128), {}, NOT_SUPPORTED),              # FP4 step of 256
+    ("gating_bf16", dict(n=500), {}, NOT_SUPPORTED),                   # N % 32
+    ("swiglu_e4m3", dict(n=2816 + 32), {}, INVALID),                   # SwiGLU N % 64
+    ("dswiglu", dict(n=1408 + 16), {}, INVALID),                       # dGLU N % 32
+    ("dswiglu", dict(ab_dtype="e4m3"), dict(sfa=FAKE, sfb=FAKE), NOT_SUPPORTED),
+    ("gating_bf16", {}, dict(prob=None), INVALID),                     # prob required
+    ("gating_bf16", {}, dict(amax=None), INVALID),                     # amax for bf16 D
+    ("gating_bf16", {}, dict(sfa=None), INVALID),
+    ("gating_bf16", {}, dict(alpha=None), INVALID),
+    ("swiglu_e4m3", {}, dict(sfd_col=None), INVALID),                  # SFD trio all-or-none
+    ("swiglu_e4m3", {}, dict(norm_const=None), INVALID),
+    ("swiglu_e4m3", {}, dict(d_col=None), INVALID),
+    ("swiglu_e4m3", {}, dict(amax=FAKE), INVALID),
+    ("gating_bf16", {}, dict(norm_const=FAKE), INVALID),
+    ("gating_bf16", {}, dict(a=FAKE + 8), MISALIGNED),
+    ("gating_bf16", {}, dict(d=FAKE + 4), MISALIGNED),
+    ("gating_bf16", {}, dict(prob=FAKE + 2), MISALIGNED),
+    ("srelu_fp4", dict(c_dtype=None), {}, INVALID),                    # c given without c_dtype
+    ("srelu_fp4", {}, dict(c=None), INVALID),
+    ("srelu_fp4", dict(srelu_tanh_s=-1.0), {}, INVALID),
+    ("srelu_fp4", dict(srelu_tanh_s=float("inf")), {}, INVALID),
+    ("dswiglu", {}, dict(beta=None), INVALID),
+    ("dswiglu", {}, dict(c_in=None), INVALID),
+    ("dswiglu", {}, dict(dprob=None), INVALID),
+    ("dswiglu", dict(d_dtype="e4m3"), {}, NOT_SUPPORTED),
+    ("gating_bf16", {}, dict(beta=FAKE), INVALID),                     # dSwiGLU-only input
+    ("gating_bf16", dict(ab_dtype="bf16"), {}, INVALID),               # sfa/sfb with BF16 operands
+    ("gating_bf16", dict(valid_m=2 ** 31), {}, NOT_SUPPORTED),
+]
+
+
+@pytest.mark.parametrize("base,pov,tov,expect", CASES)
+def test_validation_rules(base, pov, tov, expect):
+    p, t = _base(base)
+    p.update(pov)
+    t.update(tov)
+    t = {k: v for k, v in t.items() if v is not None}
+    st = _status(p, t)
+    assert st == expect, (st, mg.moegg_last_error())
+    assert mg.moegg_last_error() != ""
+
+
+def test_run_rejects_before_any_hip_call():
+    # an invalid call must return its status without touching the (absent) GPU
+    p, t = _base("gating_bf16")
+    t.pop("prob")
+    st = mg.moegg_run(mg.make_problem(p), mg.make_args(t), None)
+    assert st == INVALID
+
+
+def test_null_structs():
+    lib = ctypes.CDLL(mg.lib_path)
+    lib.moegg_check.restype = ctypes.c_int
+    assert lib.moegg_check(None, None) == INVALID
+    assert lib.moegg_n_out.restype != 0  # attribute exists
+
+
+def test_n_out():
+    for act, n, expect in [("none", 512, 512), ("swiglu", 2816, 1408), ("srelu", 4096, 4096),
+                           ("dswiglu", 1408, 2816)]:
+        p, _ = _base("gating_bf16")
+        p.update(act=act, n=n)
+        assert mg.moegg_n_out(mg.make_problem(p)) == expect

@@ -1,0 +1,274 @@
+"""GPU parity: the HIP library (through the C ABI) against the oracle.
+
+Small cases run the oracle on every output; full-size workloads compare
+sampled whole 32-row blocks plus properties that hold at any size.  Every case
+prints its name, seed and shape before touching the GPU.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import formats as F
+from parity_util import amax_rule, decode_bf16, pick_row_blocks, rule1, rule2
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+mg = pytest.importorskip("moe_grouped_block_amd")
+from moe_grouped_block_amd import plumbing as pl  # noqa: E402
+
+
+def _announce(case):
+    p = case.problem
+    print(f"\n[gpu-case] {case.name} seed={case.seed} L={p['num_groups']} valid_m={p['valid_m']} "
+          f"n={p['n']} k={p['k']} ab={p['ab_dtype']} act={p['act']} d={p['d_dtype']} c={p.get('c_dtype')}",
+          flush=True)
+
+
+def run_gpu(case, fill=0xA5, times=1):
+    _announce(case)
+    dev = pl.to_device(case.arrays)
+    res = []
+    for _ in range(times):
+        outs = pl.empty_outputs(case.problem, fill=fill)
+        mg.run(case.problem, {**pl.inputs_for(case.problem, dev), **outs})
+        torch.cuda.synchronize()
+        res.append(pl.to_host(outs))
+    return res if times > 1 else res[0]
+
+
+def check_case(case, got, rows=None):
+    """Compare GPU outputs with the oracle on `rows` (default all rows)."""
+    p = case.problem
+    ref = oracle.grouped_gemm(p, case.arrays, rows)
+    r = ref["rows"]
+    grp = ref["group"]
+    stats = {}
+    if p["act"] == "dswiglu":
+        g2 = np.repeat(grp[:, None], ref["dc"].shape[1], axis=1)
+        stats["dc"] = rule1(decode_bf16(got["d"][r]), ref["dc"], g2, "dC")
+        stats["dprob"] = rule1(got["dprob"][r], ref["dprob"], grp, "dprob")
+        return stats
+    if p.get("c_dtype") == "bf16":
+        g2 = np.repeat(grp[:, None], ref["c"].shape[1], axis=1)
+        stats["c"] = rule1(decode_bf16(got["c"][r]), ref["c"], g2, "C")
+    if p["d_dtype"] == "bf16":
+        g2 = np.repeat(grp[:, None], ref["d"].shape[1], axis=1)
+        stats["d"] = rule1(decode_bf16(got["d"][r]), ref["d"], g2, "D")
+        if rows is None:
+            stats["amax"] = amax_rule(got["amax"], ref["amax"])
+    else:
+        nc = float(case.arrays["norm_const"][0])
+        stats["d_row"] = rule2(got["d"][r], got["sfd_row"][r], ref["d"], nc, "row", "D/SFD_row")
+        blocks = np.unique(r // 32)
+        stats["d_col"] = rule2(got["d_col"][r], got["sfd_col"][:, blocks], ref["d"], nc, "col", "D_col/SFD_col")
+    return stats
+
+
+# ---------------------------------------------------------------------------
+# small cases: every output element against the oracle
+# ---------------------------------------------------------------------------
+
+SMALL = {
+    "gating_l4_full": ("quant_gating_l4", {}),
+    "swiglu_fp8_e4m3": ("fc1_swiglu_l8", dict(L=3, K=512, N=320, routing=("topk", 300, 2))),
+    "swiglu_fp8_bf16": ("fc1_swiglu_l8", dict(L=3, K=512, N=320, routing=("topk", 300, 2), d="bf16",
+                                              alpha=("uniform", 0.5, 2.0))),
+    "swiglu_fp8_nc3": ("fc1_swiglu_l8", dict(L=2, K=256, N=256, routing=("topk", 200, 2), norm_const=3.0)),
+    "swiglu_fp4_e4m3_c": ("fc1_swiglu_l8", dict(L=2, ab="e2m1x2", K=512, N=320, routing=("topk", 160, 2),
+                                                b_std=1.0, clip=6.0, c="bf16")),
+    "fc2_zipf_bf16": ("fc2_gating_l64_zipf", dict(L=9, K=384, N=320, routing=("topk_zipf", 400, 3, 1.1, 2))),
+    "gating_fp8_e4m3": ("quant_gating_l4", dict(L=3, K=256, N=288, d="e4m3", routing=("multinomial", 300))),
+    "srelu_fp4_tanh_e4m3": ("srelu_tanh_fp4_l32", dict(L=3, K=1024, N=320, routing=("multinomial", 500))),
+    "srelu_fp4_plain_bf16": ("srelu_tanh_fp4_l32", dict(L=3, K=512, N=256, routing=("multinomial", 300),
+                                                        s=0.0, d="bf16", c=None)),
+    "srelu_fp8_tanh_bf16_c": ("srelu_tanh_fp4_l32", dict(ab="e4m3", L=2, K=512, N=256, clip=None, s=8.0,
+                                                         routing=("multinomial", 300), d="bf16", c="bf16",
+                                                         b_std="1/sqrtK")),
+    "gating_bf16_ops": ("quant_gating_l4", dict(ab="bf16", K=256, N=320, a_std=1.0, b_std=0.1)),
+    "swiglu_bf16_ops_e4m3": ("fc1_swiglu_l8", dict(ab="bf16", L=2, K=192, N=256, routing=("topk", 200, 2))),
+    "dswiglu_bf16": ("dswiglu_bf16_l64", dict(L=5, K=256, N=288, routing=("topk", 200, 3),
+                                              alpha=("uniform", 0.5, 2.0), beta=("uniform", 0.5, 2.0))),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_parity(name):
+    base, over = SMALL[name]
+    case = synth.make_case(base, seed=1000 + sorted(SMALL).index(name), name=name, **over)
+    got = run_gpu(case)
+    stats = check_case(case, got)
+    print(f"[gpu-case] {name} stats {stats}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+
+EDGE = {
+    # empty first / middle / last groups, single-row groups, a group of exactly 128
+    "edge_groups_gating": ("quant_gating_l4", dict(L=7, K=256, N=256, force_counts=[0, 1, 0, 128, 129, 0, 1])),
+    "edge_groups_swiglu_e4m3": ("fc1_swiglu_l8", dict(L=5, K=128, N=128, force_counts=[0, 1, 200, 0, 3])),
+    "edge_l1": ("quant_gating_l4", dict(L=1, K=128, N=64, force_counts=[5])),
+    "edge_n64_swiglu": ("fc1_swiglu_l8", dict(L=2, K=128, N=64, routing=("topk", 100, 1))),
+    "edge_k_one_step_fp4": ("srelu_tanh_fp4_l32", dict(L=2, K=256, N=64, routing=("multinomial", 70))),
+    "edge_k_one_step_bf16": ("dswiglu_bf16_l64", dict(L=2, K=64, N=32, routing=("topk", 50, 1))),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_parity(name):
+    base, over = EDGE[name]
+    case = synth.make_case(base, seed=2000 + sorted(EDGE).index(name), name=name, **over)
+    got = run_gpu(case)
+    check_case(case, got)
+
+
+def test_empty_problem_fills_amax():
+    case = synth.make_case("quant_gating_l4", seed=3, name="all_empty", L=3, force_counts=[0, 0, 0])
+    assert case.problem["valid_m"] == 0
+    _announce(case)
+    dev = pl.to_device({k: v for k, v in case.arrays.items() if v.size})
+    amax = torch.full((3,), 7.0, device="cuda")
+    # zero-row A/prob tensors are represented by any aligned device pointer
+    dummy = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    t = dict(a=dummy, b=dev["b"], sfa=dummy, sfb=dev["sfb"], padded_offsets=dev["padded_offsets"],
+             alpha=dev["alpha"], prob=dummy, d=dummy, amax=amax)
+    mg.run(case.problem, t)
+    torch.cuda.synchronize()
+    assert amax.cpu().tolist() == [0.0, 0.0, 0.0]
+
+
+def test_row_group_map_bit_exact():
+    """alpha_g = 2^g with all-ones data: every row's value is 128 * 2^g, exactly."""
+    counts = [0, 3, 130, 0, 1, 255, 0]
+    L = len(counts)
+    case = synth.make_case("quant_gating_l4", seed=4, name="group_map", L=L, K=128, N=256, force_counts=counts)
+    a = case.arrays
+    valid = case.row_valid
+    a["a"][:] = 0
+    a["a"][valid] = 0x38
+    a["sfa"][:] = 127
+    a["b"][:] = 0x38
+    a["sfb"][:] = 127
+    a["alpha"][:] = (2.0 ** np.arange(L)).astype(np.float32)
+    a["prob"][:] = 1.0
+    got = run_gpu(case)
+    d = decode_bf16(got["d"])
+    grp = oracle.group_of_rows(a["padded_offsets"], np.arange(case.problem["valid_m"]))
+    expect = np.where(valid, 128.0 * 2.0 ** grp, 0.0)
+    assert np.array_equal(d, np.repeat(expect[:, None], 256, axis=1))
+    assert got["amax"].tolist() == [128.0 * 2 ** g if counts[g] else 0.0 for g in range(L)]
+
+
+def test_e4m3_rounding_through_epilogue_bit_exact():
+    """D = prob[m] * 2^e(n) exactly (one nonzero product per dot), so the GPU's
+    fp32 D equals the oracle's float32 D and every code and scale must match
+    bit for bit: this sweeps the conversion's rounding (ties, subnormals)."""
+    rows, n, k = 1024, 256, 128
+    case = synth.make_case("quant_gating_l4", seed=5, name="e4m3_rounding", L=1, K=k, N=n, d="e4m3",
+                           force_counts=[rows])
+    a = case.arrays
+    a["a"][:] = 0
+    a["a"][:, 0] = 0x38                                       # A[m, 0] = 1, rest 0
+    a["sfa"][:] = 127
+    a["b"][:] = 0
+    e = (np.arange(n) % 32) // 2                              # 0..15 per 32-column block
+    a["b"][0, :, 0] = 0x38
+    a["sfb"][0, :, 0] = (127 - e).astype(np.uint8)            # B[n, 0] = 2^-e(n)
+    a["sfb"][0, :, 1:] = 127
+    a["alpha"][:] = 1.0
+    rng = np.random.default_rng(55)
+    prob = rng.uniform(0.5, 1.0, rows).astype(np.float32)
+    # rows whose row-block values land exactly on E4M3 rounding ties: with
+    # prob = mid * 2^-9 the row scale is a power of two that maps prob onto a
+    # midpoint of the top binades
+    pos = F.decode_e4m3(np.arange(0x40, 0x7F))
+    mids = ((pos[:-1] + pos[1:]) / 2)
+    prob[:len(mids)] = (mids * 2.0 ** -9).astype(np.float32)
+    a["prob"][:] = prob
+    got = run_gpu(case)
+    ref = oracle.grouped_gemm(case.problem, a)
+    assert np.array_equal(got["sfd_row"], ref["sfd_row"])
+    assert np.array_equal(got["d"], ref["d_code"])
+    assert np.array_equal(got["sfd_col"], ref["sfd_col"])
+    assert np.array_equal(got["d_col"], ref["d_col_code"])
+
+
+def test_deterministic_repeat():
+    case = synth.make_case("fc1_swiglu_l8", seed=6, name="determinism", L=3, K=256, N=256,
+                           routing=("topk", 300, 2))
+    r1, r2 = run_gpu(case, times=2)
+    for k in r1:
+        assert np.array_equal(r1[k], r2[k]), k
+
+
+def test_dswiglu_dprob_accumulates():
+    """dprob is caller-zeroed and accumulated: a second call adds the same sums."""
+    case = synth.make_case("dswiglu_bf16_l64", seed=7, name="dprob_acc", L=2, K=128, N=64,
+                           routing=("topk", 100, 1))
+    _announce(case)
+    dev = pl.to_device(case.arrays)
+    outs = pl.empty_outputs(case.problem)
+    t = {**pl.inputs_for(case.problem, dev), **outs}
+    mg.run(case.problem, t)
+    torch.cuda.synchronize()
+    once = outs["dprob"].cpu().numpy().copy()
+    mg.run(case.problem, t)
+    torch.cuda.synchronize()
+    twice = outs["dprob"].cpu().numpy()
+    np.testing.assert_allclose(twice, 2 * once, rtol=1e-6, atol=1e-30)
+
+
+def test_check_offsets_on_device():
+    case = synth.make_case("quant_gating_l4", seed=8, name="offsets", L=3, K=128, N=64,
+                           force_counts=[10, 0, 300])
+    _announce(case)
+    po = torch.from_numpy(case.arrays["padded_offsets"]).cuda()
+    prob = mg.make_problem(case.problem)
+    assert mg.moegg_check_offsets(prob, po.data_ptr(), None) == 0
+    bad = po.clone()
+    bad[1] = 64                                   # not a multiple of 128
+    assert mg.moegg_check_offsets(prob, bad.data_ptr(), None) == 1
+    bad = po.clone()
+    bad[2] = bad[1]                               # last != valid_m
+    assert mg.moegg_check_offsets(prob, bad.data_ptr(), None) == 1
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: sampled 32-row blocks + properties at any size
+# ---------------------------------------------------------------------------
+
+FULL = ["fc1_swiglu_l8", "fc2_gating_l64_zipf", "srelu_tanh_fp4_l32", "dswiglu_bf16_l64", "fc1_swiglu_l64"]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    case = synth.make_case(name)
+    got = run_gpu(case, fill=0x5A)
+    rows = pick_row_blocks(case, nblocks=8)
+    stats = check_case(case, got, rows)
+    p = case.problem
+    pad = ~case.row_valid
+    if p["act"] == "dswiglu":
+        assert np.all(got["d"][pad] == 0) and np.all(got["dprob"][pad] == 0)
+    elif p["d_dtype"] == "bf16":
+        d = decode_bf16(got["d"])
+        assert np.all(d[pad] == 0)
+        grp = oracle.group_of_rows(case.arrays["padded_offsets"], np.arange(p["valid_m"]))
+        ref_rows = oracle.grouped_gemm(p, case.arrays, rows)
+        for g in range(p["num_groups"]):
+            sel = grp == g
+            if not sel.any():
+                assert got["amax"][g] == 0.0
+                continue
+            mx = np.abs(d[sel]).max()           # bf16-rounded max vs fp32 amax
+            assert abs(got["amax"][g] - mx) <= mx * 2.0 ** -8, (g, got["amax"][g], mx)
+            sub = ref_rows["group"] == g
+            if sub.any():
+                assert got["amax"][g] >= np.abs(ref_rows["d"][sub]).max() * (1 - 1e-2)
+    else:
+        assert np.all(got["d"][pad] == 0) and np.all(got["sfd_row"][pad] == 0)
+    print(f"[gpu-case] {name} stats {stats}", flush=True)
