@@ -1,0 +1,244 @@
+"""Throughput of the grouped block-scaled GEMM + fused epilogue on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--cold]
+
+A step is one launch of the whole hot path (grouped MXFP8 GEMM, SwiGLU over
+32-column pairs, gating, FP8 row + column quantisation with E8M0 scales) over
+the FC1 + SwiGLU workload at L = 64 experts: 16384 tokens routed top-6
+uniformly (98304 routed rows, each expert padded to a multiple of 128 rows),
+K = 2048, N = 2816 (44 linear/gate pairs of 32 columns), MXFP8 E4M3 operands
+with E8M0 scales per 32 K-elements.  The same line also reports the 8-expert
+FC1 + SwiGLU workload (4096 tokens top-2).  Inputs are synthetic and already
+resident in HBM.  Rank 0 prints one JSON line.
+
+`value` is TFLOP/s over routed rows (2 * routed * N * K per step, padding
+excluded).  `roofline` compares the kernel's achieved rate (HIP events on the
+launch stream) with the dense MXFP8 MFMA peak; `traffic` is read from the
+committed rocprofv3 counter summary when it was taken on the current kernel
+source, else null.  `cpu_baseline` is the float64 oracle on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"e4m3": 5000.0, "e2m1x2": 10100.0, "bf16": 2500.0}   # dense MFMA peaks, MI355X
+HBM_GBS = 8000.0
+KERNEL_SOURCES = ["moe_grouped_block_amd/csrc/moegg_kernels.hip", "moe_grouped_block_amd/csrc/moegg_internal.h"]
+TRAFFIC_FILE = "profiles/grouped_gemm_fc1_swiglu_l64_traffic.md"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it matches
+    the current kernel source and workload."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_work = re.search(r"workload:\s*(\S+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_hash and m_work and m_bytes):
+        return None
+    if m_hash.group(1) != kernel_source_hash() or m_work.group(1) != workload:
+        return None
+    return float(m_bytes.group(1))
+
+
+def algorithmic_bytes(case) -> float:
+    """Each input read once (B only for non-empty experts) + each output written once."""
+    p, a = case.problem, case.arrays
+    nonempty = int((case.counts > 0).sum())
+    L = p["num_groups"]
+    b_bytes = a["b"].nbytes * nonempty / L + (a["sfb"].nbytes * nonempty / L if "sfb" in a else 0)
+    rd = a["a"].nbytes + (a["sfa"].nbytes if "sfa" in a else 0) + b_bytes + a["prob"].nbytes
+    rd += a.get("c_in", a["prob"][:0]).nbytes
+    vm = p["valid_m"]
+    n = p["n"]
+    no = {"none": n, "srelu": n, "swiglu": n // 2, "dswiglu": 2 * n}[p["act"]]
+    if p["act"] == "dswiglu":
+        wr = vm * no * 2 + vm * 4
+    elif p["d_dtype"] == "e4m3":
+        wr = 2 * vm * no + vm * no // 32 + no * vm // 32
+    else:
+        wr = vm * no * 2
+    if p.get("c_dtype") == "bf16":
+        wr += vm * n * 2
+    return float(rd + wr)
+
+
+def cpu_baseline(case, rows_n):
+    """The oracle as it stands on the host cores, on the first `rows_n` rows."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        cores = os.cpu_count() or 1
+    p = case.problem
+    rows_n = min(rows_n, p["valid_m"])
+    rows = np.arange(rows_n)
+    routed = int(case.row_valid[:rows_n].sum())
+    t0 = time.perf_counter()
+    oracle.grouped_gemm(p, case.arrays, rows)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * routed * p["n"] * p["k"]
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"rows [0, {rows_n}) of the workload ({routed} routed rows), one float64 numpy "
+                      f"oracle pass incl. dequantise, GEMM, SwiGLU and FP8 quantisation: {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="fc1_swiglu_l64")
+    ap.add_argument("--also", default="fc1_swiglu_l8", help="comma list of extra workloads to time")
+    ap.add_argument("--cpu-rows", type=int, default=40960, help="rows of the oracle CPU sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true", help="also time launches after an L2/MALL flush")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy 5 times (reference for HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the grouped GEMM is a single-GPU kernel here and "
+              "no multi-GPU path is built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import moe_grouped_block_amd as mg
+    from moe_grouped_block_amd import plumbing as pl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        n = 1 << 27
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": True, "bytes_read_per_copy": 4 * n,
+                          "bytes_written_per_copy": 4 * n, "copies": 5}), flush=True)
+        return
+    if not os.path.exists(mg.lib_path):
+        from moe_grouped_block_amd import build
+        build.build()
+    def measure(name, steps, warmup, cold):
+        case = synth.make_case(name)
+        p = case.problem
+        dev = pl.to_device(case.arrays)
+        outs = pl.empty_outputs(p)
+        tensors = {**pl.inputs_for(p, dev), **outs}
+        stream = torch.cuda.current_stream()
+        prob_s, args_s = mg.make_problem(p), mg.make_args(tensors)
+        handle = stream.cuda_stream
+
+        def step():
+            st = mg.moegg_run(prob_s, args_s, handle)
+            if st != 0:
+                raise mg.MoeggError(st, mg.moegg_last_error())
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = e0.elapsed_time(e1) / steps
+        res = {"case": case, "ms": ms, "wall": wall, "tflops": case.flops / (ms * 1e-3) / 1e12}
+        if cold:
+            flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB > L2 + MALL
+            tot = 0.0
+            for _ in range(10):
+                flush.zero_()
+                a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a0.record(stream)
+                step()
+                a1.record(stream)
+                torch.cuda.synchronize()
+                tot += a0.elapsed_time(a1)
+            res["cold_ms"] = tot / 10
+            del flush
+        del dev, outs, tensors
+        torch.cuda.empty_cache()
+        return res
+
+    main_res = measure(args.workload, args.steps, args.warmup, args.cold)
+    case, ms, wall, value = main_res["case"], main_res["ms"], main_res["wall"], main_res["tflops"]
+    p = case.problem
+    extra = {}
+    if args.cold:
+        extra["cold_ms_per_launch"] = round(main_res["cold_ms"], 5)
+        extra["cold_tflops"] = round(case.flops / (main_res["cold_ms"] * 1e-3) / 1e12, 2)
+    also = {}
+    for name in [x for x in args.also.split(",") if x]:
+        r = measure(name, max(args.steps, 20), args.warmup, args.cold)
+        c = r["case"]
+        also[name] = {"ms_per_step": round(r["ms"], 5), "tflops_routed": round(r["tflops"], 2),
+                      "frac_mxfp8_peak": round(r["tflops"] / PEAK_TFLOPS[c.problem["ab_dtype"]], 4),
+                      "valid_m": c.problem["valid_m"], "routed_rows": c.routed_rows,
+                      "experts": c.problem["num_groups"]}
+        if "cold_ms" in r:
+            also[name]["cold_ms_per_launch"] = round(r["cold_ms"], 5)
+    if also:
+        extra["also"] = also
+
+    peak = PEAK_TFLOPS[p["ab_dtype"]]
+    alg_bytes = algorithmic_bytes(case)
+    t_mfma = case.flops / (peak * 1e12)
+    t_hbm = alg_bytes / (HBM_GBS * 1e9)
+    bound = "mfma" if t_mfma >= t_hbm else "hbm"
+    if bound == "mfma":
+        achieved, pk, unit = value, peak, "TFLOP/s"
+    else:
+        achieved, pk, unit = alg_bytes / (ms * 1e-3) / 1e9, HBM_GBS, "GB/s"
+    roof = {"bound": bound, "achieved": round(achieved, 2), "peak": pk, "unit": unit,
+            "frac": round(achieved / pk, 4), "traffic": read_traffic(args.workload),
+            "algorithmic_bytes": alg_bytes, "algorithmic_flops": case.flops}
+    line = {
+        "metric": "grouped-GEMM TFLOP/s (valid rows) + % MXFP8 MFMA peak, FC1+SwiGLU L=64",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": p["ab_dtype"], "data": "synthetic",
+        "config": {"workload": args.workload, "experts": p["num_groups"], "valid_m": p["valid_m"],
+                   "routed_rows": case.routed_rows, "n": p["n"], "k": p["k"], "act": p["act"],
+                   "d_dtype": p["d_dtype"], "parallelism": "single-gpu"},
+        "roofline": roof,
+        "pct_mxfp8_peak": round(100.0 * value / PEAK_TFLOPS["e4m3"], 2),
+        "wall_s_timed": round(wall, 4),
+    }
+    line.update(extra)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

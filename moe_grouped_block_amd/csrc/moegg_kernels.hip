@@ -42,6 +42,7 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));   // native vectors (H
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));   // struct defeats SROA)
 
 constexpr int kStride = 144;      // LDS row stride: 128 data bytes + 16 pad
+constexpr int kBandM = 8;         // m-tiles per raster band (L2 reuse of B)
 
 // Unrolled loop whose index is a compile-time constant (instruction
 // immediates such as the MFMA scale byte selectors need one).
@@ -183,25 +184,65 @@ __device__ __forceinline__ void quant_store_tile(const KernelArgs& p, int m, int
 // the fused kernel
 // ---------------------------------------------------------------------------
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane i of the wave writes lds_base + 16 i.  `lds_base` must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+// Same with 4 bytes per lane (global_load_lds_dword).
+__device__ __forceinline__ void dma4(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
 template <int AB, int ACT, int OUT>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p) {
   constexpr int BM = kBM, BN = kBN;
   constexpr int WN = BN / 2;     // GEMM columns per wave
   constexpr int TN = WN / 32;    // 32-column MFMA tiles per wave
   constexpr int TM = 2;          // 32-row MFMA tiles per wave (64 rows)
-  constexpr int A_BYTES = BM * kStride, B_BYTES = BN * kStride;
-  constexpr int A_LD = BM * 8 / kThreads;   // 16-byte chunks per thread per step
-  constexpr int B_LD = BN * 8 / kThreads;
   constexpr bool MX = AB != AB_BF16;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (A_BYTES + B_BYTES)];
+  constexpr int SW = AB == AB_E2M1 ? 2 : 1;            // scale words per row per step
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  // scale words per stage: A rows (E4M3: rows 0-127 plus a spare copy written
+  // by waves 2-3 so every wave issues the same loads), then B rows; E2M1 keeps
+  // word w of row r at [w * rows + r]
+  constexpr int SA_BYTES = MX ? 2 * BM * 4 : 4, SB_BYTES = MX ? BN * 4 * SW : 4;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Three-stage LDS ring, one distinct array per stage and operand so the
+  // compiler can tell the stages apart (it then adds no conservative waits
+  // for the direct-to-LDS loads; the explicit waits below order them).
+  // Rows are 128 bytes with the 16-byte chunk c of row r stored at chunk
+  // slot c ^ (r & 7): conflict-free 16-byte reads of 8 consecutive rows.
+  __shared__ __attribute__((aligned(16))) uint8_t sA0[A_BYTES], sA1[A_BYTES], sA2[A_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sB0[B_BYTES], sB1[B_BYTES], sB2[B_BYTES];
+  __shared__ __attribute__((aligned(16))) uint32_t sSA0[SA_BYTES / 4], sSA1[SA_BYTES / 4], sSA2[SA_BYTES / 4];
+  __shared__ __attribute__((aligned(16))) uint32_t sSB0[SB_BYTES / 4], sSB1[SB_BYTES / 4], sSB2[SB_BYTES / 4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, hi = lane >> 5;
 
-  const int tile = blockIdx.x;
-  const int mt = tile / p.n_tiles;
-  const int nt = tile - mt * p.n_tiles;
+  // Workgroup -> tile.  Workgroups are dispatched round-robin over the 8
+  // XCDs (each with its own L2), so XCD x gets the contiguous logical range
+  // [x*q + min(x, r), ...) of the nwg tiles; inside it tiles run in bands of
+  // kBandM m-tiles, m fastest, so the ~32 tiles resident on one XCD are an
+  // 8 (m) x 4 (n) patch that shares each K-slice of A and B through L2.
+  const int nwg = static_cast<int>(gridDim.x);
+  const int wg = static_cast<int>(blockIdx.x);
+  const int xcd = wg & 7, slot = wg >> 3, q = nwg >> 3, r = nwg & 7;
+  const int logical = xcd * q + min(xcd, r) + slot;
+  const int band = logical / (kBandM * p.n_tiles);
+  const int in_band = logical - band * kBandM * p.n_tiles;
+  const int band_rows = min(kBandM, p.m_tiles - band * kBandM);
+  const int nt = in_band / band_rows;
+  const int mt = band * kBandM + (in_band - nt * band_rows);
   const int row0 = mt * BM;
   const int n0 = nt * BN;
 
@@ -213,73 +254,48 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   }
   const int g = lo < p.num_groups ? lo : p.num_groups - 1;   // inconsistent offsets never index out of range
 
-  // ---- global -> LDS staging addresses ----
-  const int crow = tid >> 3, ccol = (tid & 7) * 16;
-  const uint8_t* gA = p.a + static_cast<int64_t>(row0 + crow) * p.row_bytes + ccol;
-  const int64_t a_step32 = static_cast<int64_t>(32) * p.row_bytes;
-  const uint8_t* gBg = p.b + static_cast<int64_t>(g) * p.n * p.row_bytes + ccol;
-  int brow[B_LD];
+  // ---- direct global -> LDS staging ----
+  // One wave instruction fills 8 rows (1 KB).  Wave w fills A rows
+  // [32w, 32w+32) (4 instructions) and B rows [64w, 64w+64) (8 instructions):
+  // lane i writes row 8j + i/8, chunk slot i%8, i.e. logical chunk
+  // (i%8) ^ (i/8) of that row.  Scale words ride along, one dword per lane:
+  // E4M3: every wave loads 64 A rows (waves 2-3 a spare copy) and 64 B rows;
+  // E2M1 (two words per row and step): every wave loads one A plane-half
+  // and 64 B rows of both planes.
+  constexpr int A_INS = BM / 8 / 4, B_INS = BN / 8 / 4;
+  const int lrow = lane >> 3;
+  const int lchunk = ((lane & 7) ^ lrow) * 16;
+  const uint8_t* gA[A_INS];
+  const uint8_t* gB[B_INS];
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) brow[i] = min(n0 + crow + 32 * i, p.n - 1);
-  const int lds_st = crow * kStride + ccol;
+  for (int j = 0; j < A_INS; ++j)
+    gA[j] = p.a + static_cast<int64_t>(row0 + wave * 32 + j * 8 + lrow) * p.row_bytes + lchunk;
+#pragma unroll
+  for (int j = 0; j < B_INS; ++j)
+    gB[j] = p.b + (static_cast<int64_t>(g) * p.n + min(n0 + wave * 64 + j * 8 + lrow, p.n - 1)) * p.row_bytes + lchunk;
+  const uint8_t* gSA = nullptr;
+  const uint8_t* gSB = nullptr;
+  if constexpr (MX) {
+    gSA = p.sfa + static_cast<int64_t>(row0 + (wave & 1) * 64 + lane) * p.ksf + (SW == 2 ? (wave >> 1) * 4 : 0);
+    gSB = p.sfb + (static_cast<int64_t>(g) * p.n + min(n0 + wave * 64 + lane, p.n - 1)) * p.ksf;
+  }
+  // vector-memory instructions per wave per stage (the minimum over waves)
+  constexpr int VM_PER_STAGE = A_INS + B_INS + (AB == AB_E4M3 ? 2 : AB == AB_E2M1 ? 3 : 0);
 
-  v4u ra[A_LD], rb[B_LD];
-  auto gload = [&](int ks) {
+  auto issue = [&](int ks, uint8_t* dA, uint8_t* dB, uint32_t* dSA, uint32_t* dSB) {
     const int kb = ks * 128;
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const v4u*>(gA + i * a_step32 + kb);
+    for (int j = 0; j < A_INS; ++j) dma16(gA[j] + kb, dA + (wave * 32 + j * 8) * 128);
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i)
-      rb[i] = *reinterpret_cast<const v4u*>(gBg + static_cast<int64_t>(brow[i]) * p.row_bytes + kb);
-  };
-  auto sstore = [&](int buf) {
-    uint8_t* sa = smem + buf * A_BYTES;
-    uint8_t* sb = smem + 2 * A_BYTES + buf * B_BYTES;
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) *reinterpret_cast<v4u*>(sa + lds_st + i * 32 * kStride) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) *reinterpret_cast<v4u*>(sb + lds_st + i * 32 * kStride) = rb[i];
-  };
-
-  // ---- scale bytes: one row per lane and tile; byte 0 / 2 of the shifted
-  //      word are this lane's K-blocks for the two (E4M3) MFMAs of a step ----
-  const uint8_t* sfa_row[TM];
-  const uint8_t* sfb_row[TN];
-  if constexpr (MX) {
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-      sfa_row[tm] = p.sfa + static_cast<int64_t>(row0 + wm * 64 + tm * 32 + l32) * p.ksf;
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-      const int r = min(n0 + wn * WN + tn * 32 + l32, p.n - 1);
-      sfb_row[tn] = p.sfb + (static_cast<int64_t>(g) * p.n + r) * p.ksf;
-    }
-  }
-  constexpr int SW = AB == AB_E2M1 ? 2 : 1;   // scale words per row per step
-  uint32_t sa_cur[TM][SW], sb_cur[TN][SW], sa_nxt[TM][SW], sb_nxt[TN][SW];
-  auto sload = [&](int ks, uint32_t (&sa)[TM][SW], uint32_t (&sb)[TN][SW]) {
-    if constexpr (MX) {
-      const int sh = 8 * hi;
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        if constexpr (SW == 1) {
-          sa[tm][0] = *reinterpret_cast<const uint32_t*>(sfa_row[tm] + ks * 4) >> sh;
-        } else {
-          const v2u w = *reinterpret_cast<const v2u*>(sfa_row[tm] + ks * 8);
-          sa[tm][0] = w.x >> sh;
-          sa[tm][1] = w.y >> sh;
-        }
-      }
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        if constexpr (SW == 1) {
-          sb[tn][0] = *reinterpret_cast<const uint32_t*>(sfb_row[tn] + ks * 4) >> sh;
-        } else {
-          const v2u w = *reinterpret_cast<const v2u*>(sfb_row[tn] + ks * 8);
-          sb[tn][0] = w.x >> sh;
-          sb[tn][1] = w.y >> sh;
-        }
-      }
+    for (int j = 0; j < B_INS; ++j) dma16(gB[j] + kb, dB + (wave * 64 + j * 8) * 128);
+    if constexpr (AB == AB_E4M3) {
+      dma4(gSA + ks * 4, dSA + wave * 64);
+      dma4(gSB + ks * 4, dSB + wave * 64);
+    } else if constexpr (AB == AB_E2M1) {
+      // planes: word w of row r at [w * rows + r]
+      dma4(gSA + ks * 8, dSA + (wave >> 1) * BM + (wave & 1) * 64);
+      dma4(gSB + ks * 8, dSB + wave * 64);
+      dma4(gSB + ks * 8 + 4, dSB + BN + wave * 64);
     }
   };
 
@@ -291,40 +307,46 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
 
-  // ---- main loop ----
-  gload(0);
-  sload(0, sa_cur, sb_cur);
-  sstore(0);
-  __syncthreads();
-  const int a_rd = (wm * 64 + l32) * kStride;
-  const int b_rd = (wn * WN + l32) * kStride;
-  for (int ks = 0; ks < p.k_steps; ++ks) {
-    const int cur = ks & 1;
-    const bool more = ks + 1 < p.k_steps;
-    if (more) {
-      gload(ks + 1);
-      sload(ks + 1, sa_nxt, sb_nxt);
+  const int sw = l32 & 7;                     // swizzle of this lane's rows
+  const int a_rd = (wm * 64 + l32) * 128;
+  const int b_rd = (wn * WN + l32) * 128;
+  // One K-step (128 bytes of every row) out of one LDS stage.
+  auto compute = [&](const uint8_t* stA, const uint8_t* stB, const uint32_t* stSA, const uint32_t* stSB) {
+    const uint8_t* sa = stA + a_rd;
+    const uint8_t* sb = stB + b_rd;
+    // scale words: byte 0 / 2 of the shifted word are this lane's K-blocks
+    // for the first / second MFMA of a 128-element E4M3 step (E2M1: two words)
+    uint32_t sca[TM][SW], scb[TN][SW];
+    if constexpr (MX) {
+      const int sh = 8 * hi;
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int w = 0; w < SW; ++w) sca[tm][w] = stSA[w * BM + wm * 64 + tm * 32 + l32] >> sh;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int w = 0; w < SW; ++w) scb[tn][w] = stSB[w * BN + wn * WN + tn * 32 + l32] >> sh;
     }
-    const uint8_t* sa = smem + cur * A_BYTES + a_rd;
-    const uint8_t* sb = smem + 2 * A_BYTES + cur * B_BYTES + b_rd;
     if constexpr (AB == AB_E4M3) {
       static_for<0, 2>([&](auto kki) {
         constexpr int kk = decltype(kki)::value;
         // 8-bit operands: a lane of half h holds K [16h, 16h+16) and
-        // [32+16h, 48+16h) of the 64-wide window, while its scale byte covers
-        // the 32-element block h; FP4 operands hold [32h, 32h+32) instead.
-        const int off = hi * 16 + kk * 64;
+        // [32+16h, 48+16h) of the 64-wide window (chunks h + 4kk and h + 4kk + 2
+        // of the row), while its scale byte covers the 32-element block h;
+        // FP4 operands hold [32h, 32h+32) instead.
+        const int o0 = ((hi + 4 * kk) ^ sw) * 16, o1 = ((hi + 4 * kk + 2) ^ sw) * 16;
         v8i fa[TM], fb[TN];
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
-          const v4u x0 = *reinterpret_cast<const v4u*>(sa + tm * 32 * kStride + off);
-          const v4u x1 = *reinterpret_cast<const v4u*>(sa + tm * 32 * kStride + off + 32);
+          const v4u x0 = *reinterpret_cast<const v4u*>(sa + tm * 32 * 128 + o0);
+          const v4u x1 = *reinterpret_cast<const v4u*>(sa + tm * 32 * 128 + o1);
           fa[tm] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
         }
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-          const v4u x0 = *reinterpret_cast<const v4u*>(sb + tn * 32 * kStride + off);
-          const v4u x1 = *reinterpret_cast<const v4u*>(sb + tn * 32 * kStride + off + 32);
+          const v4u x0 = *reinterpret_cast<const v4u*>(sb + tn * 32 * 128 + o0);
+          const v4u x1 = *reinterpret_cast<const v4u*>(sb + tn * 32 * 128 + o1);
           fb[tn] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
         }
 #pragma unroll
@@ -332,21 +354,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
           for (int tn = 0; tn < TN; ++tn)
             acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                fb[tn], fa[tm], acc[tm][tn], 0, 0, kk * 2, (int)sb_cur[tn][0], kk * 2, (int)sa_cur[tm][0]);
+                fb[tn], fa[tm], acc[tm][tn], 0, 0, kk * 2, (int)scb[tn][0], kk * 2, (int)sca[tm][0]);
       });
     } else if constexpr (AB == AB_E2M1) {
       static_for<0, 4>([&](auto kki) {
         constexpr int kk = decltype(kki)::value;
-        const int off = hi * 16 + kk * 32;
+        const int o0 = ((hi + 2 * kk) ^ sw) * 16;
         v8i fa[TM], fb[TN];
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
-          const v4u x0 = *reinterpret_cast<const v4u*>(sa + tm * 32 * kStride + off);
+          const v4u x0 = *reinterpret_cast<const v4u*>(sa + tm * 32 * 128 + o0);
           fa[tm] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
         }
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-          const v4u x0 = *reinterpret_cast<const v4u*>(sb + tn * 32 * kStride + off);
+          const v4u x0 = *reinterpret_cast<const v4u*>(sb + tn * 32 * 128 + o0);
           fb[tn] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
         }
 #pragma unroll
@@ -354,20 +376,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
           for (int tn = 0; tn < TN; ++tn)
             acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                fb[tn], fa[tm], acc[tm][tn], 4, 4, (kk & 1) * 2, (int)sb_cur[tn][kk >> 1], (kk & 1) * 2,
-                (int)sa_cur[tm][kk >> 1]);
+                fb[tn], fa[tm], acc[tm][tn], 4, 4, (kk & 1) * 2, (int)scb[tn][kk >> 1], (kk & 1) * 2,
+                (int)sca[tm][kk >> 1]);
       });
     } else {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int off = hi * 16 + kk * 32;
+        const int o0 = ((hi + 2 * kk) ^ sw) * 16;
         v8bf fa[TM], fb[TN];
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
-          fa[tm] = *reinterpret_cast<const v8bf*>(sa + tm * 32 * kStride + off);
+          fa[tm] = *reinterpret_cast<const v8bf*>(sa + tm * 32 * 128 + o0);
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
-          fb[tn] = *reinterpret_cast<const v8bf*>(sb + tn * 32 * kStride + off);
+          fb[tn] = *reinterpret_cast<const v8bf*>(sb + tn * 32 * 128 + o0);
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
@@ -375,21 +397,49 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[tn], fa[tm], acc[tm][tn], 0, 0, 0);
       }
     }
-    if (more) {
-      sstore(cur ^ 1);
-      if constexpr (MX) {
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-          for (int w = 0; w < SW; ++w) sa_cur[tm][w] = sa_nxt[tm][w];
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-          for (int w = 0; w < SW; ++w) sb_cur[tn][w] = sb_nxt[tn][w];
-      }
-    }
-    __syncthreads();
+  };
+
+  // ---- main loop: three LDS stages, loads two steps ahead ----
+  // At the top of step ks the wave's outstanding loads are those of stages
+  // ks and ks+1; waiting until only one stage's worth remains and then
+  // meeting at the barrier makes stage ks visible to every wave, and every
+  // wave has finished step ks-1, whose buffer then receives stage ks+2.
+  // The loop is unrolled by three (no exits inside) so every buffer is named
+  // statically; loads past the last stage repeat it (never computed) so the
+  // count of outstanding loads per stage stays the same.  The last 0-2 steps
+  // run after the loop.
+  const int nks = p.k_steps;
+  const int last = nks - 1;
+  issue(0, sA0, sB0, sSA0, sSB0);
+  issue(min(1, last), sA1, sB1, sSA1, sSB1);
+  int ks = 0;
+  for (; ks + 3 <= nks; ks += 3) {
+    wait_vmcnt<VM_PER_STAGE>();
+    __builtin_amdgcn_s_barrier();
+    issue(min(ks + 2, last), sA2, sB2, sSA2, sSB2);
+    compute(sA0, sB0, sSA0, sSB0);
+    wait_vmcnt<VM_PER_STAGE>();
+    __builtin_amdgcn_s_barrier();
+    issue(min(ks + 3, last), sA0, sB0, sSA0, sSB0);
+    compute(sA1, sB1, sSA1, sSB1);
+    wait_vmcnt<VM_PER_STAGE>();
+    __builtin_amdgcn_s_barrier();
+    issue(min(ks + 4, last), sA1, sB1, sSA1, sSB1);
+    compute(sA2, sB2, sSA2, sSB2);
   }
+  if (ks < nks) {                         // one or two steps left: stages in buffers 0 and 1
+    wait_vmcnt<VM_PER_STAGE>();
+    __builtin_amdgcn_s_barrier();
+    compute(sA0, sB0, sSA0, sSB0);
+    if (ks + 1 < nks) {
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      compute(sA1, sB1, sSA1, sSB1);
+    }
+  }
+  // no direct-to-LDS write may still be in flight when the workgroup ends
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
 
   // ---- epilogue ----
   const float alpha = p.alpha[g];
