@@ -79,7 +79,7 @@ moegg_status check_impl(const moegg_problem* pp, const moegg_args* ap) {
     if (p.c_dtype != MOEGG_DT_NONE) return fail(MOEGG_ERROR_INVALID_VALUE, "dSwiGLU writes no C");
   }
   if (p.n % 32 != 0) return fail(MOEGG_ERROR_NOT_SUPPORTED, "n=%d: this build needs n %% 32 == 0", p.n);
-  const int kstep = p.ab_dtype == MOEGG_DT_E4M3 ? 128 : p.ab_dtype == MOEGG_DT_E2M1X2 ? 256 : 64;
+  const int kstep = p.ab_dtype == MOEGG_DT_E4M3 ? 128 : p.ab_dtype == MOEGG_DT_E2M1X2 ? 256 : 64;   // 128-byte steps
   if (p.k % kstep != 0)
     return fail(MOEGG_ERROR_NOT_SUPPORTED, "k=%d: this build needs k %% %d == 0 for this operand type", p.k, kstep);
   if (p.k > (1 << 20)) return fail(MOEGG_ERROR_NOT_SUPPORTED, "k=%d too large", p.k);

@@ -14,10 +14,10 @@ enum ActKind : int { ACT_NONE = 0, ACT_SWIGLU = 1, ACT_SRELU = 2, ACT_DSWIGLU = 
 // Output formatting of D.
 enum OutKind : int { OUT_BF16 = 0, OUT_E4M3 = 1 };
 
-// Block tile: BM token rows x BN GEMM columns, 256 threads (4 wave64s).
+// Block tile: BM token rows x BN GEMM columns, 512 threads (8 wave64s).
 constexpr int kBM = 128;
 constexpr int kBN = 256;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 
 // Everything a kernel needs, passed by value (kernel argument segment).
 struct KernelArgs {
@@ -47,7 +47,7 @@ struct KernelArgs {
   int32_t ksf;             // scale bytes per row (K/32)
   int32_t m_tiles;
   int32_t n_tiles;
-  int32_t k_steps;         // K / elements-per-128-byte-step
+  int32_t k_steps;         // row bytes / 128 (one 128-byte step per row)
   float srelu_s;
 };
 

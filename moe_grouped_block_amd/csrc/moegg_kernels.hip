@@ -41,7 +41,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));   // native vectors (HIP's uint4
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));   // struct defeats SROA)
 
-constexpr int kStride = 144;      // LDS row stride: 128 data bytes + 16 pad
+constexpr int kBK = 128;          // bytes of K per row and pipeline stage (one cache line)
 constexpr int kBandM = 8;         // m-tiles per raster band (L2 reuse of B)
 
 // Unrolled loop whose index is a compile-time constant (instruction
@@ -106,10 +106,40 @@ __device__ __forceinline__ float tanh_nonneg(float x) {
   return x < 0.125f ? series : big;
 }
 
+// Cross-lane helpers on the VALU (DPP and the gfx950 permlane swaps), no LDS.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Max over the 32 lanes of each half-wave (lanes 0-31 and 32-63 separately):
+// pairs, quads, 8-lane halves of a row (mirror), 16-lane rows (mirror), then
+// rows 0/1 and 2/3 exchanged by v_permlane16_swap.
+__device__ __forceinline__ float half_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));     // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));     // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));    // row_half_mirror
+  x = fmaxf(x, dpp_f<0x140>(x));    // row_mirror
+  const v2u sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw.x), __uint_as_float(sw.y));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = half_max(v);
+  const v2u sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(sw.x), __uint_as_float(sw.y));
+}
+
+// Sum of the two halves' values (lane l and lane l ^ 32), in every lane.
+__device__ __forceinline__ float halves_sum(float v) {
+  const v2u sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(sw.x) + __uint_as_float(sw.y);
+}
+
+// Max of the two halves' values, in every lane.
+__device__ __forceinline__ float halves_max(float v) {
+  const v2u sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(sw.x), __uint_as_float(sw.y));
 }
 
 // Column offset (within a 32-column MFMA tile) of accumulator element v of
@@ -129,15 +159,15 @@ __device__ __forceinline__ void store_bf16_tile(uint8_t* base, int64_t m, int ld
 }
 
 // FP8 row + column quantisation of one 32-column output tile ("Grouped GEMM +
-// Quant (SM100)", §Equations Step 3 and §Diagram Row/Col Quantize).  The 32
-// rows of the column blocks are the 32 lanes of this half-wave.
+// Quant (SM100)", §Equations Step 3 and §Diagram Row/Col Quantize).  A row
+// block is this lane's 16 values plus those of lane ^ 32; a column block is
+// one accumulator element over the 32 lanes of this half-wave.
 __device__ __forceinline__ void quant_store_tile(const KernelArgs& p, int m, int mblk, int ocol, int hi,
                                                  int l32, float nc, const float* d) {
-  // row block: 16 values here + 16 in lane ^ 32
   float ra = 0.0f;
 #pragma unroll
   for (int v = 0; v < 16; ++v) ra = fmaxf(ra, fabsf(d[v]));
-  ra = fmaxf(ra, __shfl_xor(ra, 32));
+  ra = halves_max(ra);
   const uint32_t br = e8m0_ceil((nc * ra) * kRcp448);
   const float sr = e8m0_inverse(br);
   const int64_t rowoff = static_cast<int64_t>(m) * p.n_out + ocol + 4 * hi;
@@ -149,24 +179,16 @@ __device__ __forceinline__ void quant_store_tile(const KernelArgs& p, int m, int
   }
   if (hi == 0) p.sfd_row[static_cast<int64_t>(m) * (p.n_out >> 5) + (ocol >> 5)] = static_cast<uint8_t>(br);
 
-  // column blocks: max over the 32 lanes of this half for each element
-  float cm[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    float x = fabsf(d[v]);
-    x = fmaxf(x, __shfl_xor(x, 1));
-    x = fmaxf(x, __shfl_xor(x, 2));
-    x = fmaxf(x, __shfl_xor(x, 4));
-    x = fmaxf(x, __shfl_xor(x, 8));
-    x = fmaxf(x, __shfl_xor(x, 16));
-    cm[v] = x;
-  }
-  uint32_t bc[16];
+  // column scales; lane l32 < 16 of each half keeps the byte of its element l32
+  const int idx = l32 & 15;
+  uint32_t bsel = 0;
   float sc[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    bc[v] = e8m0_ceil((nc * cm[v]) * kRcp448);
-    sc[v] = e8m0_inverse(bc[v]);
+    const float cm = half_max(fabsf(d[v]));
+    const uint32_t b = e8m0_ceil((nc * cm) * kRcp448);
+    sc[v] = e8m0_inverse(b);
+    bsel = idx == v ? b : bsel;
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -174,10 +196,8 @@ __device__ __forceinline__ void quant_store_tile(const KernelArgs& p, int m, int
                               (d[4 * j + 2] * nc) * sc[4 * j + 2], (d[4 * j + 3] * nc) * sc[4 * j + 3]);
     *reinterpret_cast<uint32_t*>(p.d_col + rowoff + 8 * j) = w;
   }
-  const int64_t mblocks = p.valid_m >> 5;
-#pragma unroll
-  for (int v = 0; v < 16; ++v)
-    if (l32 == v) p.sfd_col[static_cast<int64_t>(ocol + nofs(v, hi)) * mblocks + mblk] = static_cast<uint8_t>(bc[v]);
+  if (l32 < 16)
+    p.sfd_col[static_cast<int64_t>(ocol + nofs(idx, hi)) * (p.valid_m >> 5) + mblk] = static_cast<uint8_t>(bsel);
 }
 
 // ---------------------------------------------------------------------------
@@ -202,38 +222,41 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 template <int AB, int ACT, int OUT>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p) {
-  constexpr int BM = kBM, BN = kBN;
-  constexpr int WN = BN / 2;     // GEMM columns per wave
-  constexpr int TN = WN / 32;    // 32-column MFMA tiles per wave
-  constexpr int TM = 2;          // 32-row MFMA tiles per wave (64 rows)
+  constexpr int BM = kBM, BN = kBN, BK = kBK;
+  constexpr int NW = kThreads / 64;  // 8 waves: 2 (m) x 4 (n), two per SIMD
+  constexpr int WM = BM / 2;         // rows per wave (64)
+  constexpr int WN = BN / 4;         // GEMM columns per wave (64)
+  constexpr int TM = WM / 32;        // 32-row MFMA tiles per wave
+  constexpr int TN = WN / 32;        // 32-column MFMA tiles per wave
   constexpr bool MX = AB != AB_BF16;
-  constexpr int SW = AB == AB_E2M1 ? 2 : 1;            // scale words per row per step
-  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-  // scale words per stage: A rows (E4M3: rows 0-127 plus a spare copy written
-  // by waves 2-3 so every wave issues the same loads), then B rows; E2M1 keeps
-  // word w of row r at [w * rows + r]
-  constexpr int SA_BYTES = MX ? 2 * BM * 4 : 4, SB_BYTES = MX ? BN * 4 * SW : 4;
+  constexpr int SW = AB == AB_E2M1 ? 2 : 1;          // scale words per row per step
+  constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
+  // scale words per stage, word w of row r at [w * rows + r]; the A area has
+  // spare room so that every wave issues the same number of loads
+  constexpr int SA_WORDS = MX ? 4 * BM : 1, SB_WORDS = MX ? SW * BN : 1;
 
-  // Three-stage LDS ring, one distinct array per stage and operand so the
-  // compiler can tell the stages apart (it then adds no conservative waits
-  // for the direct-to-LDS loads; the explicit waits below order them).
-  // Rows are 128 bytes with the 16-byte chunk c of row r stored at chunk
-  // slot c ^ (r & 7): conflict-free 16-byte reads of 8 consecutive rows.
+  // Three-stage LDS ring (about 150 KB: one workgroup per CU), one distinct
+  // array per stage and operand: the compiler can then tell the stages apart
+  // and adds no conservative waits for the direct-to-LDS loads (the explicit
+  // waits below order them).  Rows are BK = 128 bytes, a whole cache line, so
+  // every load instruction moves whole lines; the 16-byte chunk c of row r
+  // sits at chunk slot c ^ (r & 7), so 16-byte reads of 8 consecutive rows
+  // hit 8 distinct bank groups.
   __shared__ __attribute__((aligned(16))) uint8_t sA0[A_BYTES], sA1[A_BYTES], sA2[A_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sB0[B_BYTES], sB1[B_BYTES], sB2[B_BYTES];
-  __shared__ __attribute__((aligned(16))) uint32_t sSA0[SA_BYTES / 4], sSA1[SA_BYTES / 4], sSA2[SA_BYTES / 4];
-  __shared__ __attribute__((aligned(16))) uint32_t sSB0[SB_BYTES / 4], sSB1[SB_BYTES / 4], sSB2[SB_BYTES / 4];
+  __shared__ __attribute__((aligned(16))) uint32_t sSA0[SA_WORDS], sSA1[SA_WORDS], sSA2[SA_WORDS];
+  __shared__ __attribute__((aligned(16))) uint32_t sSB0[SB_WORDS], sSB1[SB_WORDS], sSB2[SB_WORDS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int l32 = lane & 31, hi = lane >> 5;
 
   // Workgroup -> tile.  Workgroups are dispatched round-robin over the 8
   // XCDs (each with its own L2), so XCD x gets the contiguous logical range
   // [x*q + min(x, r), ...) of the nwg tiles; inside it tiles run in bands of
-  // kBandM m-tiles, m fastest, so the ~32 tiles resident on one XCD are an
-  // 8 (m) x 4 (n) patch that shares each K-slice of A and B through L2.
+  // kBandM m-tiles, m fastest, so the tiles resident on one XCD form a
+  // compact patch that shares each K-slice of A and B through L2.
   const int nwg = static_cast<int>(gridDim.x);
   const int wg = static_cast<int>(blockIdx.x);
   const int xcd = wg & 7, slot = wg >> 3, q = nwg >> 3, r = nwg & 7;
@@ -256,46 +279,67 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 
   // ---- direct global -> LDS staging ----
   // One wave instruction fills 8 rows (1 KB).  Wave w fills A rows
-  // [32w, 32w+32) (4 instructions) and B rows [64w, 64w+64) (8 instructions):
-  // lane i writes row 8j + i/8, chunk slot i%8, i.e. logical chunk
-  // (i%8) ^ (i/8) of that row.  Scale words ride along, one dword per lane:
-  // E4M3: every wave loads 64 A rows (waves 2-3 a spare copy) and 64 B rows;
-  // E2M1 (two words per row and step): every wave loads one A plane-half
-  // and 64 B rows of both planes.
-  constexpr int A_INS = BM / 8 / 4, B_INS = BN / 8 / 4;
+  // [16w, 16w+16) (2 instructions) and B rows [32w, 32w+32) (4
+  // instructions): lane i writes row 8j + i/8, chunk slot i%8, i.e. logical
+  // chunk (i%8) ^ (i/8) of that row.  Scale dwords ride along, one per lane:
+  // E4M3 (one dword per row and step): waves 0-1 load A rows, waves 2-5 B
+  // rows, waves 6-7 a spare copy of A; E2M1 (two dwords per row and step):
+  // two loads per wave covering both words of A and B.
+  constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;
   const int lrow = lane >> 3;
   const int lchunk = ((lane & 7) ^ lrow) * 16;
   const uint8_t* gA[A_INS];
   const uint8_t* gB[B_INS];
 #pragma unroll
   for (int j = 0; j < A_INS; ++j)
-    gA[j] = p.a + static_cast<int64_t>(row0 + wave * 32 + j * 8 + lrow) * p.row_bytes + lchunk;
+    gA[j] = p.a + static_cast<int64_t>(row0 + wave * (8 * A_INS) + j * 8 + lrow) * p.row_bytes + lchunk;
 #pragma unroll
   for (int j = 0; j < B_INS; ++j)
-    gB[j] = p.b + (static_cast<int64_t>(g) * p.n + min(n0 + wave * 64 + j * 8 + lrow, p.n - 1)) * p.row_bytes + lchunk;
-  const uint8_t* gSA = nullptr;
-  const uint8_t* gSB = nullptr;
+    gB[j] = p.b + (static_cast<int64_t>(g) * p.n + min(n0 + wave * (8 * B_INS) + j * 8 + lrow, p.n - 1)) *
+                      p.row_bytes + lchunk;
+  // scale loads: for load slot u of this wave, the source row pointer and the
+  // LDS word offset (rows of A: 128, of B: 256; 64 rows per load)
+  constexpr int S_LOADS = AB == AB_E4M3 ? 1 : AB == AB_E2M1 ? 2 : 0;
+  const uint8_t* gS[S_LOADS > 0 ? S_LOADS : 1];
+  int sdst[S_LOADS > 0 ? S_LOADS : 1];
+  bool sisA[S_LOADS > 0 ? S_LOADS : 1];
   if constexpr (MX) {
-    gSA = p.sfa + static_cast<int64_t>(row0 + (wave & 1) * 64 + lane) * p.ksf + (SW == 2 ? (wave >> 1) * 4 : 0);
-    gSB = p.sfb + (static_cast<int64_t>(g) * p.n + min(n0 + wave * 64 + lane, p.n - 1)) * p.ksf;
+#pragma unroll
+    for (int u = 0; u < S_LOADS; ++u) {
+      // job = (wave * S_LOADS + u): E4M3 jobs 0-1 A rows, 2-5 B rows, 6-7 spare
+      // A; E2M1 jobs 0-3 A (word, half), 4-11 B (word, quarter), 12-15 spare A
+      const int job = wave * S_LOADS + u;
+      int word, rowsel, isA;
+      if (AB == AB_E4M3) {
+        isA = job < 2 || job >= 6;
+        word = 0;
+        rowsel = job < 2 ? job * 64 : job >= 6 ? (job - 6) * 64 : (job - 2) * 64;
+        sdst[u] = job < 2 ? job * 64 : job >= 6 ? 2 * BM + (job - 6) * 64 : (job - 2) * 64;
+      } else {
+        isA = job < 4 || job >= 12;
+        const int aj = job < 4 ? job : job - 12, bj = job - 4;
+        word = isA ? aj >> 1 : bj >> 2;
+        rowsel = isA ? (aj & 1) * 64 : (bj & 3) * 64;
+        sdst[u] = isA ? (job < 4 ? word * BM + rowsel : 2 * BM + word * BM + rowsel) : word * BN + rowsel;
+      }
+      sisA[u] = isA;
+      gS[u] = isA ? p.sfa + static_cast<int64_t>(row0 + rowsel + lane) * p.ksf + word * 4
+                  : p.sfb + (static_cast<int64_t>(g) * p.n + min(n0 + rowsel + lane, p.n - 1)) * p.ksf + word * 4;
+    }
   }
-  // vector-memory instructions per wave per stage (the minimum over waves)
-  constexpr int VM_PER_STAGE = A_INS + B_INS + (AB == AB_E4M3 ? 2 : AB == AB_E2M1 ? 3 : 0);
+  // vector-memory instructions per wave per stage
+  constexpr int VM_PER_STAGE = A_INS + B_INS + S_LOADS;
 
   auto issue = [&](int ks, uint8_t* dA, uint8_t* dB, uint32_t* dSA, uint32_t* dSB) {
-    const int kb = ks * 128;
+    const int kb = ks * BK;
 #pragma unroll
-    for (int j = 0; j < A_INS; ++j) dma16(gA[j] + kb, dA + (wave * 32 + j * 8) * 128);
+    for (int j = 0; j < A_INS; ++j) dma16(gA[j] + kb, dA + (wave * (8 * A_INS) + j * 8) * BK);
 #pragma unroll
-    for (int j = 0; j < B_INS; ++j) dma16(gB[j] + kb, dB + (wave * 64 + j * 8) * 128);
-    if constexpr (AB == AB_E4M3) {
-      dma4(gSA + ks * 4, dSA + wave * 64);
-      dma4(gSB + ks * 4, dSB + wave * 64);
-    } else if constexpr (AB == AB_E2M1) {
-      // planes: word w of row r at [w * rows + r]
-      dma4(gSA + ks * 8, dSA + (wave >> 1) * BM + (wave & 1) * 64);
-      dma4(gSB + ks * 8, dSB + wave * 64);
-      dma4(gSB + ks * 8 + 4, dSB + BN + wave * 64);
+    for (int j = 0; j < B_INS; ++j) dma16(gB[j] + kb, dB + (wave * (8 * B_INS) + j * 8) * BK);
+    if constexpr (MX) {
+#pragma unroll
+      for (int u = 0; u < S_LOADS; ++u)
+        dma4(gS[u] + ks * 4 * SW, (sisA[u] ? dSA : dSB) + sdst[u]);
     }
   };
 
@@ -308,21 +352,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
 
   const int sw = l32 & 7;                     // swizzle of this lane's rows
-  const int a_rd = (wm * 64 + l32) * 128;
-  const int b_rd = (wn * WN + l32) * 128;
-  // One K-step (128 bytes of every row) out of one LDS stage.
+  const int a_rd = (wm * WM + l32) * BK;
+  const int b_rd = (wn * WN + l32) * BK;
+  // One K-step (BK bytes of every row) out of one LDS stage.
   auto compute = [&](const uint8_t* stA, const uint8_t* stB, const uint32_t* stSA, const uint32_t* stSB) {
     const uint8_t* sa = stA + a_rd;
     const uint8_t* sb = stB + b_rd;
     // scale words: byte 0 / 2 of the shifted word are this lane's K-blocks
-    // for the first / second MFMA of a 128-element E4M3 step (E2M1: two words)
+    // for the first / second 64-element window of a word's four blocks
     uint32_t sca[TM][SW], scb[TN][SW];
     if constexpr (MX) {
       const int sh = 8 * hi;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-        for (int w = 0; w < SW; ++w) sca[tm][w] = stSA[w * BM + wm * 64 + tm * 32 + l32] >> sh;
+        for (int w = 0; w < SW; ++w) sca[tm][w] = stSA[w * BM + wm * WM + tm * 32 + l32] >> sh;
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
@@ -332,21 +376,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       static_for<0, 2>([&](auto kki) {
         constexpr int kk = decltype(kki)::value;
         // 8-bit operands: a lane of half h holds K [16h, 16h+16) and
-        // [32+16h, 48+16h) of the 64-wide window (chunks h + 4kk and h + 4kk + 2
-        // of the row), while its scale byte covers the 32-element block h;
-        // FP4 operands hold [32h, 32h+32) instead.
+        // [32+16h, 48+16h) of the 64-wide window (chunks h + 4kk and
+        // h + 4kk + 2 of the row), while its scale byte covers the 32-element
+        // block h of the window; FP4 operands hold [32h, 32h+32) instead.
         const int o0 = ((hi + 4 * kk) ^ sw) * 16, o1 = ((hi + 4 * kk + 2) ^ sw) * 16;
         v8i fa[TM], fb[TN];
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
-          const v4u x0 = *reinterpret_cast<const v4u*>(sa + tm * 32 * 128 + o0);
-          const v4u x1 = *reinterpret_cast<const v4u*>(sa + tm * 32 * 128 + o1);
+          const v4u x0 = *reinterpret_cast<const v4u*>(sa + tm * 32 * BK + o0);
+          const v4u x1 = *reinterpret_cast<const v4u*>(sa + tm * 32 * BK + o1);
           fa[tm] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
         }
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-          const v4u x0 = *reinterpret_cast<const v4u*>(sb + tn * 32 * 128 + o0);
-          const v4u x1 = *reinterpret_cast<const v4u*>(sb + tn * 32 * 128 + o1);
+          const v4u x0 = *reinterpret_cast<const v4u*>(sb + tn * 32 * BK + o0);
+          const v4u x1 = *reinterpret_cast<const v4u*>(sb + tn * 32 * BK + o1);
           fb[tn] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
         }
 #pragma unroll
@@ -363,12 +407,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         v8i fa[TM], fb[TN];
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
-          const v4u x0 = *reinterpret_cast<const v4u*>(sa + tm * 32 * 128 + o0);
+          const v4u x0 = *reinterpret_cast<const v4u*>(sa + tm * 32 * BK + o0);
           fa[tm] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
         }
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-          const v4u x0 = *reinterpret_cast<const v4u*>(sb + tn * 32 * 128 + o0);
+          const v4u x0 = *reinterpret_cast<const v4u*>(sb + tn * 32 * BK + o0);
           fb[tn] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
         }
 #pragma unroll
@@ -386,10 +430,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         v8bf fa[TM], fb[TN];
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
-          fa[tm] = *reinterpret_cast<const v8bf*>(sa + tm * 32 * 128 + o0);
+          fa[tm] = *reinterpret_cast<const v8bf*>(sa + tm * 32 * BK + o0);
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
-          fb[tn] = *reinterpret_cast<const v8bf*>(sb + tn * 32 * 128 + o0);
+          fb[tn] = *reinterpret_cast<const v8bf*>(sb + tn * 32 * BK + o0);
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
@@ -439,11 +483,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   }
   // no direct-to-LDS write may still be in flight when the workgroup ends
   wait_vmcnt<0>();
-  __builtin_amdgcn_s_barrier();
 
   // ---- epilogue ----
   const float alpha = p.alpha[g];
-  const int mbase = row0 + wm * 64;
+  const int mbase = row0 + wm * WM;
   const int nbase = n0 + wn * WN;
   float amax_l = 0.0f;
   float nc = 1.0f;
@@ -503,7 +546,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           *reinterpret_cast<v2u*>(dbase + (xoff + 32 + 8 * j + 4 * hi) * 2) = w;
         }
       }
-      dp += __shfl_xor(dp, 32);
+      dp = halves_sum(dp);
       if (hi == 0) atomicAdd(p.dprob + m, dp);
     }
     return;
