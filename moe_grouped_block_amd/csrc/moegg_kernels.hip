@@ -240,8 +240,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   // and adds no conservative waits for the direct-to-LDS loads (the explicit
   // waits below order them).  Rows are BK = 128 bytes, a whole cache line, so
   // every load instruction moves whole lines; the 16-byte chunk c of row r
-  // sits at chunk slot c ^ (r & 7), so 16-byte reads of 8 consecutive rows
-  // hit 8 distinct bank groups.
+  // sits at chunk slot c ^ ((r >> 1) & 7).  The LDS has 64 four-byte banks
+  // (256 bytes), so two consecutive 128-byte rows fill one bank window and a
+  // 16-lane group of 16-byte reads (16 consecutive rows, one chunk each) hits
+  // 16 distinct bank quads.
   __shared__ __attribute__((aligned(16))) uint8_t sA0[A_BYTES], sA1[A_BYTES], sA2[A_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sB0[B_BYTES], sB1[B_BYTES], sB2[B_BYTES];
   __shared__ __attribute__((aligned(16))) uint32_t sSA0[SA_WORDS], sSA1[SA_WORDS], sSA2[SA_WORDS];
@@ -280,23 +282,26 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   // ---- direct global -> LDS staging ----
   // One wave instruction fills 8 rows (1 KB).  Wave w fills A rows
   // [16w, 16w+16) (2 instructions) and B rows [32w, 32w+32) (4
-  // instructions): lane i writes row 8j + i/8, chunk slot i%8, i.e. logical
-  // chunk (i%8) ^ (i/8) of that row.  Scale dwords ride along, one per lane:
+  // instructions): lane i writes row r = 8j + i/8, chunk slot i%8, i.e.
+  // logical chunk (i%8) ^ ((r >> 1) & 7) of that row.  Scale dwords ride along, one per lane:
   // E4M3 (one dword per row and step): waves 0-1 load A rows, waves 2-5 B
   // rows, waves 6-7 a spare copy of A; E2M1 (two dwords per row and step):
   // two loads per wave covering both words of A and B.
   constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;
   const int lrow = lane >> 3;
-  const int lchunk = ((lane & 7) ^ lrow) * 16;
   const uint8_t* gA[A_INS];
   const uint8_t* gB[B_INS];
 #pragma unroll
-  for (int j = 0; j < A_INS; ++j)
-    gA[j] = p.a + static_cast<int64_t>(row0 + wave * (8 * A_INS) + j * 8 + lrow) * p.row_bytes + lchunk;
+  for (int j = 0; j < A_INS; ++j) {
+    const int r = wave * (8 * A_INS) + j * 8 + lrow;             // row in the tile
+    gA[j] = p.a + static_cast<int64_t>(row0 + r) * p.row_bytes + (((lane & 7) ^ ((r >> 1) & 7)) * 16);
+  }
 #pragma unroll
-  for (int j = 0; j < B_INS; ++j)
-    gB[j] = p.b + (static_cast<int64_t>(g) * p.n + min(n0 + wave * (8 * B_INS) + j * 8 + lrow, p.n - 1)) *
-                      p.row_bytes + lchunk;
+  for (int j = 0; j < B_INS; ++j) {
+    const int r = wave * (8 * B_INS) + j * 8 + lrow;
+    gB[j] = p.b + (static_cast<int64_t>(g) * p.n + min(n0 + r, p.n - 1)) * p.row_bytes +
+            (((lane & 7) ^ ((r >> 1) & 7)) * 16);
+  }
   // scale loads: for load slot u of this wave, the source row pointer and the
   // LDS word offset (rows of A: 128, of B: 256; 64 rows per load)
   constexpr int S_LOADS = AB == AB_E4M3 ? 1 : AB == AB_E2M1 ? 2 : 0;
@@ -351,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
 
-  const int sw = l32 & 7;                     // swizzle of this lane's rows
+  const int sw = (l32 >> 1) & 7;              // swizzle of this lane's rows (tiles start at multiples of 32)
   const int a_rd = (wm * WM + l32) * BK;
   const int b_rd = (wn * WN + l32) * BK;
   // One K-step (BK bytes of every row) out of one LDS stage.
