@@ -25,6 +25,18 @@ moegg_status fail(moegg_status st, const char* fmt, ...) {
   return st;
 }
 
+// Compute units of the current device (cached per device id), 0 on error.
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev] = cus;
+  return cus;
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int64_t n_out_of(const moegg_problem& p) {
@@ -49,8 +61,9 @@ moegg_status check_impl(const moegg_problem* pp, const moegg_args* ap) {
   if (p.valid_m < 0) return fail(MOEGG_ERROR_INVALID_VALUE, "valid_m=%lld negative", (long long)p.valid_m);
   if (p.m_aligned <= 0 || p.m_aligned % 32 != 0)
     return fail(MOEGG_ERROR_INVALID_VALUE, "m_aligned=%d must be a positive multiple of 32", p.m_aligned);
-  if (p.m_aligned % moegg::kBM != 0)
-    return fail(MOEGG_ERROR_NOT_SUPPORTED, "m_aligned=%d: this build needs a multiple of %d", p.m_aligned, moegg::kBM);
+  if (p.m_aligned % moegg::kRowBlock != 0)
+    return fail(MOEGG_ERROR_NOT_SUPPORTED, "m_aligned=%d: this build needs a multiple of %d", p.m_aligned,
+                moegg::kRowBlock);
   if (p.valid_m % p.m_aligned != 0)
     return fail(MOEGG_ERROR_INVALID_VALUE, "valid_m=%lld not a multiple of m_aligned=%d", (long long)p.valid_m, p.m_aligned);
   if (p.valid_m > (int64_t)INT32_MAX)
@@ -175,8 +188,13 @@ moegg_status moegg_run(const moegg_problem* problem, const moegg_args* args, voi
   k.row_bytes = ab == moegg::AB_E4M3 ? p.k : ab == moegg::AB_E2M1 ? p.k / 2 : 2 * p.k;
   k.ksf = p.k / 32;
   k.k_steps = k.row_bytes / 128;
-  k.m_tiles = static_cast<int32_t>(p.valid_m / moegg::kBM);
   k.n_tiles = (p.n + moegg::kBN - 1) / moegg::kBN;
+  // persistent grid: one workgroup per CU, never more than there are tiles
+  // (at most (valid_m / 128 + L) / 2 row tiles, each n_tiles wide)
+  const int64_t max_tiles = ((p.valid_m / moegg::kRowBlock + p.num_groups + 1) / 2) * k.n_tiles;
+  const int cus = device_cus();
+  if (cus <= 0) return fail(MOEGG_ERROR_LAUNCH, "cannot query the device's compute units");
+  k.grid = static_cast<int32_t>(max_tiles < cus ? max_tiles : cus);
   k.srelu_s = p.srelu_tanh_s;
   const int out = p.d_dtype == MOEGG_DT_E4M3 ? moegg::OUT_E4M3 : moegg::OUT_BF16;
   hipError_t e = moegg::launch_grouped_gemm(ab, p.act, out, k, stream);

@@ -15,8 +15,11 @@ enum ActKind : int { ACT_NONE = 0, ACT_SWIGLU = 1, ACT_SRELU = 2, ACT_DSWIGLU = 
 enum OutKind : int { OUT_BF16 = 0, OUT_E4M3 = 1 };
 
 // Block tile: BM token rows x BN GEMM columns, 512 threads (8 wave64s).
-constexpr int kBM = 128;
+// Experts are cut into 256-row tiles plus at most one 128-row tile, so the
+// row alignment of every expert (m_aligned) must be a multiple of kRowBlock.
+constexpr int kBM = 256;
 constexpr int kBN = 256;
+constexpr int kRowBlock = 128;
 constexpr int kThreads = 512;
 
 // Everything a kernel needs, passed by value (kernel argument segment).
@@ -45,9 +48,9 @@ struct KernelArgs {
   int32_t n_out;
   int32_t row_bytes;       // bytes per row of A and B
   int32_t ksf;             // scale bytes per row (K/32)
-  int32_t m_tiles;
-  int32_t n_tiles;
+  int32_t n_tiles;         // ceil(n / kBN)
   int32_t k_steps;         // row bytes / 128 (one 128-byte step per row)
+  int32_t grid;            // persistent workgroups launched (>= 1)
   float srelu_s;
 };
 

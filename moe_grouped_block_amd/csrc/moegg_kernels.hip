@@ -9,22 +9,28 @@
 // backward), then the activation / gating / output-formatting epilogue.
 //
 // Mapping onto CDNA4:
-//  * one workgroup = 4 wave64s = a 128-row x 256-column output tile; a tile
-//    never straddles two experts because groups are padded to a multiple of
-//    128 rows, so the expert index is one per workgroup (binary search of
-//    padded_offsets, wave-uniform).
+//  * persistent workgroups, one per CU (8 wave64s, about 140 KB of LDS),
+//    walk a list of 256 x 256 output tiles.  A tile never straddles two
+//    experts: expert g's padded rows are cut into 256-row tiles plus one
+//    128-row tile when its row count is an odd number of 128-row blocks.
+//    Each workgroup builds the per-expert tile prefix sums in LDS from
+//    padded_offsets once and maps a linear tile index to (expert, first row,
+//    first column) by binary search.  Linear tile indices are handed out so
+//    that the workgroups resident on one XCD (one L2) work on a compact patch
+//    of neighbouring tiles at any time.
 //  * the contraction runs on the block-scaled matrix cores:
 //    v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 or E2M1 operands, one E8M0 byte
 //    per lane and operand selects the scale of that lane's 32 K-elements) or
 //    v_mfma_f32_32x32x16_bf16.  The weight tile is the instruction's first
 //    operand and the token tile the second, so an accumulator lane holds one
 //    token row and 16 output columns (4 runs of 4 contiguous columns): row
-//    reductions are lane-local, stores are 8-byte (bf16) / 4-byte (e4m3) runs.
+//    reductions are lane-local.
 //  * K advances in steps of 128 bytes per row (128 E4M3, 256 E2M1 or 64 BF16
-//    elements); A/B step tiles are staged global -> registers -> LDS with a
-//    double buffer (row stride 144 B, conflict-free 16-byte LDS reads), one
-//    barrier per step.  Scale bytes go straight to registers.
-//  * the epilogue runs on the fp32 accumulators in registers.
+//    elements).  Two LDS stages (A, B and their scale words) are filled by
+//    direct global -> LDS loads one step ahead; the first stage of the next
+//    tile is loaded while the current tile's epilogue runs.
+//  * the epilogue works on the fp32 accumulators in registers; column
+//    blocks of the FP8 output are reduced through a per-wave LDS transpose.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,12 +43,15 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));   // native vectors (HIP's uint4
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));   // struct defeats SROA)
 
 constexpr int kBK = 128;          // bytes of K per row and pipeline stage (one cache line)
 constexpr int kBandM = 8;         // m-tiles per raster band (L2 reuse of B)
+constexpr int kTPitch = 36;       // floats per row of the epilogue transpose (see quant_tile)
+constexpr int kScratch = 8192;    // bytes of epilogue scratch per wave
 
 // Unrolled loop whose index is a compile-time constant (instruction
 // immediates such as the MFMA scale byte selectors need one).
@@ -142,9 +151,16 @@ __device__ __forceinline__ float halves_max(float v) {
   return fmaxf(__uint_as_float(sw.x), __uint_as_float(sw.y));
 }
 
-// Column offset (within a 32-column MFMA tile) of accumulator element v of
-// this lane: rows of the 32x32 result are spread as 8*(v/4) + 4*(lane/32) + v%4.
-__device__ __forceinline__ int nofs(int v, int hi) { return 8 * (v >> 2) + 4 * hi + (v & 3); }
+// The value lane l ^ 32 holds, in every lane.
+__device__ __forceinline__ uint32_t other_half(uint32_t v, int hi) {
+  const v2u sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return hi ? sw.x : sw.y;
+}
+
+// max(|a|, |b|, c) (one v_max3_f32 with abs modifiers).
+__device__ __forceinline__ float max_abs2(float c, float a, float b) {
+  return fmaxf(fmaxf(fabsf(a), fabsf(b)), c);
+}
 
 // Store 16 values of one row (one 32-column tile) as bf16: 4 runs of 4.
 __device__ __forceinline__ void store_bf16_tile(uint8_t* base, int64_t m, int ld, int col, int hi,
@@ -158,46 +174,80 @@ __device__ __forceinline__ void store_bf16_tile(uint8_t* base, int64_t m, int ld
   }
 }
 
-// FP8 row + column quantisation of one 32-column output tile ("Grouped GEMM +
-// Quant (SM100)", §Equations Step 3 and §Diagram Row/Col Quantize).  A row
-// block is this lane's 16 values plus those of lane ^ 32; a column block is
-// one accumulator element over the 32 lanes of this half-wave.
-__device__ __forceinline__ void quant_store_tile(const KernelArgs& p, int m, int mblk, int ocol, int hi,
-                                                 int l32, float nc, const float* d) {
+// Store one row's 32 E4M3 codes of a 32-column tile.  This lane holds the
+// codes of columns 8j + 4*hi + [0, 4) (w[j]); after one exchange with lane
+// l ^ 32 (same row), lane hi = 0 stores columns [0, 16) and lane hi = 1
+// columns [16, 32), one 16-byte store each.
+__device__ __forceinline__ void store_e4m3_row(uint8_t* dst_row, int hi, const uint32_t* w) {
+  const uint32_t r0 = other_half(hi ? w[0] : w[2], hi);   // hi=0 gets the partner's w0, hi=1 its w2
+  const uint32_t r1 = other_half(hi ? w[1] : w[3], hi);
+  v4u o;
+  o.x = hi ? r0 : w[0];
+  o.y = hi ? w[2] : r0;
+  o.z = hi ? r1 : w[1];
+  o.w = hi ? w[3] : r1;
+  *reinterpret_cast<v4u*>(dst_row + 16 * hi) = o;
+}
+
+// FP8 row + column quantisation of one 32 x 32 output tile ("Grouped GEMM +
+// Quant (SM100)", §Equations Step 3 and §Diagram Row/Col Quantize).
+// dn[v] = D * norm_const for row m (this lane's row) and column
+// 8*(v/4) + 4*hi + v%4 of the tile.  A row block is one row's 32 values
+// (this lane and lane ^ 32); a column block is one column over the tile's 32
+// rows, reduced through the wave's LDS scratch:
+//   T: 32 rows x kTPitch floats, row r at T + r * kTPitch (16-byte writes of
+//      4 columns; the pitch keeps every 16-lane group of writes on distinct
+//      banks),
+//   S: 32 floats, the inverse column scales.
+// Lanes 0-31 read rows 0-15 of column l, lanes 32-63 rows 24-31 then 16-23,
+// so that both halves of a 64-lane read hit complementary bank ranges.
+// Returns the E8M0 byte of this lane's column (l % 32) block.
+__device__ __forceinline__ uint32_t quant_tile(const KernelArgs& p, float* T, float* S, int m, int ocol, int hi,
+                                               int l32, const float* dn) {
+  // ---- row block ----
   float ra = 0.0f;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) ra = fmaxf(ra, fabsf(d[v]));
+  for (int v = 0; v < 16; v += 2) ra = max_abs2(ra, dn[v], dn[v + 1]);
   ra = halves_max(ra);
-  const uint32_t br = e8m0_ceil((nc * ra) * kRcp448);
+  const uint32_t br = e8m0_ceil(ra * kRcp448);
   const float sr = e8m0_inverse(br);
-  const int64_t rowoff = static_cast<int64_t>(m) * p.n_out + ocol + 4 * hi;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t w = e4m3x4((d[4 * j] * nc) * sr, (d[4 * j + 1] * nc) * sr, (d[4 * j + 2] * nc) * sr,
-                              (d[4 * j + 3] * nc) * sr);
-    *reinterpret_cast<uint32_t*>(p.d + rowoff + 8 * j) = w;
-  }
-  if (hi == 0) p.sfd_row[static_cast<int64_t>(m) * (p.n_out >> 5) + (ocol >> 5)] = static_cast<uint8_t>(br);
 
-  // column scales; lane l32 < 16 of each half keeps the byte of its element l32
-  const int idx = l32 & 15;
-  uint32_t bsel = 0;
+  // ---- column blocks through LDS ----
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<v4f*>(T + l32 * kTPitch + 8 * j + 4 * hi) = v4f{dn[4 * j], dn[4 * j + 1], dn[4 * j + 2], dn[4 * j + 3]};
+  float cm = 0.0f;
+  const float* c0 = T + l32 + (hi ? 24 * kTPitch : 0);      // rows [0, 8) / [24, 32)
+  const float* c1 = T + l32 + (hi ? 8 * kTPitch : 0);       // rows [8, 16) / [16, 24) at r + 8
+#pragma unroll
+  for (int r = 0; r < 8; r += 2) cm = max_abs2(cm, c0[r * kTPitch], c0[(r + 1) * kTPitch]);
+#pragma unroll
+  for (int r = 8; r < 16; r += 2) cm = max_abs2(cm, c1[r * kTPitch], c1[(r + 1) * kTPitch]);
+  cm = halves_max(cm);
+  const uint32_t bc = e8m0_ceil(cm * kRcp448);
+  if (hi == 0) S[l32] = e8m0_inverse(bc);
   float sc[16];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const float cm = half_max(fabsf(d[v]));
-    const uint32_t b = e8m0_ceil((nc * cm) * kRcp448);
-    sc[v] = e8m0_inverse(b);
-    bsel = idx == v ? b : bsel;
+  for (int j = 0; j < 4; ++j) {
+    const v4f s4 = *reinterpret_cast<const v4f*>(S + 8 * j + 4 * hi);
+    sc[4 * j] = s4.x;
+    sc[4 * j + 1] = s4.y;
+    sc[4 * j + 2] = s4.z;
+    sc[4 * j + 3] = s4.w;
   }
+
+  uint32_t wr[4], wc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t w = e4m3x4((d[4 * j] * nc) * sc[4 * j], (d[4 * j + 1] * nc) * sc[4 * j + 1],
-                              (d[4 * j + 2] * nc) * sc[4 * j + 2], (d[4 * j + 3] * nc) * sc[4 * j + 3]);
-    *reinterpret_cast<uint32_t*>(p.d_col + rowoff + 8 * j) = w;
+    wr[j] = e4m3x4(dn[4 * j] * sr, dn[4 * j + 1] * sr, dn[4 * j + 2] * sr, dn[4 * j + 3] * sr);
+    wc[j] = e4m3x4(dn[4 * j] * sc[4 * j], dn[4 * j + 1] * sc[4 * j + 1], dn[4 * j + 2] * sc[4 * j + 2],
+                   dn[4 * j + 3] * sc[4 * j + 3]);
   }
-  if (l32 < 16)
-    p.sfd_col[static_cast<int64_t>(ocol + nofs(idx, hi)) * (p.valid_m >> 5) + mblk] = static_cast<uint8_t>(bsel);
+  const int64_t rowoff = static_cast<int64_t>(m) * p.n_out + ocol;
+  store_e4m3_row(p.d + rowoff, hi, wr);
+  store_e4m3_row(p.d_col + rowoff, hi, wc);
+  if (hi == 0) p.sfd_row[static_cast<int64_t>(m) * (p.n_out >> 5) + (ocol >> 5)] = static_cast<uint8_t>(br);
+  return bc;
 }
 
 // ---------------------------------------------------------------------------
@@ -220,147 +270,201 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
+// One output tile: rows [row0, row0 + rows) of expert g, GEMM columns
+// [n0, n0 + 256).  rows is 0 (nothing to store), 128 or 256.
+struct Tile {
+  int g, row0, rows, n0;
+};
+
 template <int AB, int ACT, int OUT>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p) {
   constexpr int BM = kBM, BN = kBN, BK = kBK;
-  constexpr int NW = kThreads / 64;  // 8 waves: 2 (m) x 4 (n), two per SIMD
-  constexpr int WM = BM / 2;         // rows per wave (64)
+  constexpr int NW = kThreads / 64;  // 8 waves: 2 (m) x 4 (n), waves w and w+4 share a SIMD
+  constexpr int WM = BM / 2;         // rows per wave (128)
   constexpr int WN = BN / 4;         // GEMM columns per wave (64)
-  constexpr int TM = WM / 32;        // 32-row MFMA tiles per wave
-  constexpr int TN = WN / 32;        // 32-column MFMA tiles per wave
+  constexpr int TM = WM / 32;        // 32-row MFMA tiles per wave (4)
+  constexpr int TN = WN / 32;        // 32-column MFMA tiles per wave (2)
   constexpr bool MX = AB != AB_BF16;
   constexpr int SW = AB == AB_E2M1 ? 2 : 1;          // scale words per row per step
   constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
-  // scale words per stage, word w of row r at [w * rows + r]; the A area has
-  // spare room so that every wave issues the same number of loads
-  constexpr int SA_WORDS = MX ? 4 * BM : 1, SB_WORDS = MX ? SW * BN : 1;
+  constexpr int SA_WORDS = MX ? SW * BM : 1, SB_WORDS = MX ? SW * BN : 1;
+  static_assert(NW == 8 && TM == 4 && TN == 2, "tile shape");
+  static_assert(4 * kScratch <= A_BYTES && 4 * kScratch <= B_BYTES, "epilogue scratch lives in stage 1");
 
-  // Three-stage LDS ring (about 150 KB: one workgroup per CU), one distinct
-  // array per stage and operand: the compiler can then tell the stages apart
-  // and adds no conservative waits for the direct-to-LDS loads (the explicit
-  // waits below order them).  Rows are BK = 128 bytes, a whole cache line, so
-  // every load instruction moves whole lines; the 16-byte chunk c of row r
-  // sits at chunk slot c ^ ((r >> 1) & 7).  The LDS has 64 four-byte banks
-  // (256 bytes), so two consecutive 128-byte rows fill one bank window and a
-  // 16-lane group of 16-byte reads (16 consecutive rows, one chunk each) hits
-  // 16 distinct bank quads.
-  __shared__ __attribute__((aligned(16))) uint8_t sA0[A_BYTES], sA1[A_BYTES], sA2[A_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t sB0[B_BYTES], sB1[B_BYTES], sB2[B_BYTES];
-  __shared__ __attribute__((aligned(16))) uint32_t sSA0[SA_WORDS], sSA1[SA_WORDS], sSA2[SA_WORDS];
-  __shared__ __attribute__((aligned(16))) uint32_t sSB0[SB_WORDS], sSB1[SB_WORDS], sSB2[SB_WORDS];
+  // Two LDS stages (about 66 KB each), one distinct array per stage and
+  // operand: the compiler can then tell the stages apart and adds no
+  // conservative waits for the direct-to-LDS loads (the explicit waits below
+  // order them).  Rows are BK = 128 bytes, a whole cache line, so every load
+  // instruction moves whole lines; the 16-byte chunk c of row r sits at chunk
+  // slot c ^ ((r >> 1) & 7).  The LDS has 64 four-byte banks (256 bytes), so
+  // two consecutive 128-byte rows fill one bank window and a 16-lane group of
+  // 16-byte reads (16 consecutive rows, one chunk each) hits 16 distinct bank
+  // quads.  Stage 1's A and B areas double as the epilogue scratch.
+  __shared__ __attribute__((aligned(16))) uint8_t sA0[A_BYTES], sA1[A_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sB0[B_BYTES], sB1[B_BYTES];
+  __shared__ __attribute__((aligned(16))) uint32_t sSA0[SA_WORDS], sSA1[SA_WORDS];
+  __shared__ __attribute__((aligned(16))) uint32_t sSB0[SB_WORDS], sSB1[SB_WORDS];
+  __shared__ int32_t sTiles[1025];   // m-tiles before expert g, g = 0..L
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int l32 = lane & 31, hi = lane >> 5;
+  const int L = p.num_groups;
+  const int vm = static_cast<int>(p.valid_m);
 
-  // Workgroup -> tile.  Workgroups are dispatched round-robin over the 8
-  // XCDs (each with its own L2), so XCD x gets the contiguous logical range
-  // [x*q + min(x, r), ...) of the nwg tiles; inside it tiles run in bands of
-  // kBandM m-tiles, m fastest, so the tiles resident on one XCD form a
-  // compact patch that shares each K-slice of A and B through L2.
+  // ---- per-expert tile prefix sums (once per workgroup) ----
+  // expert g owns P_g = (po[g] - po[g-1]) / 128 row blocks -> ceil(P_g / 2)
+  // m-tiles.  Counts are clamped so that inconsistent offsets can neither
+  // overflow the sums nor address rows outside [0, valid_m).
+  if (wave == 0) {
+    int base = 0;
+    for (int c0 = 0; c0 < L; c0 += 64) {
+      const int gi = c0 + lane;
+      int cnt = 0;
+      if (gi < L) {
+        const int end = p.po[gi], beg = gi ? p.po[gi - 1] : 0;
+        const int blocks = min(max(end - beg, 0) >> 7, vm >> 7);
+        cnt = (blocks + 1) >> 1;
+      }
+      int x = cnt;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+      }
+      if (gi < L) sTiles[gi + 1] = min(base + x, 1 << 30);
+      base = min(base + __shfl(x, 63), 1 << 30);
+    }
+    if (lane == 0) sTiles[0] = 0;
+  }
+  __syncthreads();
+  const int m_tiles = sTiles[L];
+  const int64_t n_tiles = p.n_tiles;
+  const int64_t total = static_cast<int64_t>(m_tiles) * n_tiles;
+
+  // Linear tile index -> tile.  Workgroups are dispatched round-robin over
+  // the 8 XCDs (each with its own L2): workgroup w runs on XCD w % 8.  The
+  // workgroups of XCD x take the contiguous slots [x*q + min(x, r), ...) of
+  // the nwg slots, and pass i of slot s handles linear tile i * nwg + s, so
+  // the tiles in flight on one XCD are consecutive.  Linear tiles run in
+  // bands of kBandM m-tiles, m fastest, so consecutive tiles share B (same
+  // expert and columns) or A (same rows) through L2.
   const int nwg = static_cast<int>(gridDim.x);
   const int wg = static_cast<int>(blockIdx.x);
-  const int xcd = wg & 7, slot = wg >> 3, q = nwg >> 3, r = nwg & 7;
-  const int logical = xcd * q + min(xcd, r) + slot;
-  const int band = logical / (kBandM * p.n_tiles);
-  const int in_band = logical - band * kBandM * p.n_tiles;
-  const int band_rows = min(kBandM, p.m_tiles - band * kBandM);
-  const int nt = in_band / band_rows;
-  const int mt = band * kBandM + (in_band - nt * band_rows);
-  const int row0 = mt * BM;
-  const int n0 = nt * BN;
-
-  // expert of this row tile: the number of padded_offsets entries <= row0
-  int lo = 0, up = p.num_groups;
-  while (lo < up) {
-    const int mid = (lo + up) >> 1;
-    if (p.po[mid] > row0) up = mid; else lo = mid + 1;
-  }
-  const int g = lo < p.num_groups ? lo : p.num_groups - 1;   // inconsistent offsets never index out of range
+  const int slot = [&] {
+    const int xcd = wg & 7, j = wg >> 3, q = nwg >> 3, r = nwg & 7;
+    return xcd * q + min(xcd, r) + j;
+  }();
+  auto tile_of = [&](int64_t t) __attribute__((always_inline)) -> Tile {
+    const int64_t band_size = static_cast<int64_t>(kBandM) * n_tiles;
+    const int band = static_cast<int>(t / band_size);
+    const int in_band = static_cast<int>(t - band * band_size);
+    const int band_rows = min(kBandM, m_tiles - band * kBandM);
+    const int nt = in_band / band_rows;
+    const int mt = band * kBandM + (in_band - nt * band_rows);
+    // expert: the largest g with sTiles[g] <= mt (empty experts skipped)
+    int lo = 0, up = L;
+    while (up - lo > 1) {
+      const int mid = (lo + up) >> 1;
+      if (sTiles[mid] <= mt) lo = mid; else up = mid;
+    }
+    Tile tl;
+    tl.g = __builtin_amdgcn_readfirstlane(lo);
+    // first row: a multiple of 128 in [0, valid_m - 128] whatever the offsets
+    // hold (valid_m is a positive multiple of 128 here); rows past the
+    // expert's end or valid_m are not stored
+    const int64_t beg = lo ? p.po[lo - 1] : 0, end = p.po[lo];
+    const int64_t jt = min(mt - sTiles[lo], vm >> 8);
+    const int r0 = static_cast<int>(min((max(beg, int64_t{0}) + jt * BM) & ~int64_t{127}, int64_t{vm - 128}));
+    const int64_t rows = min(min(int64_t{BM}, end - r0), int64_t{vm - r0});
+    tl.row0 = __builtin_amdgcn_readfirstlane(r0);
+    tl.rows = __builtin_amdgcn_readfirstlane(static_cast<int>(max(rows, int64_t{0})) & ~127);
+    tl.n0 = __builtin_amdgcn_readfirstlane(nt * BN);
+    return tl;
+  };
 
   // ---- direct global -> LDS staging ----
   // One wave instruction fills 8 rows (1 KB).  Wave w fills A rows
-  // [16w, 16w+16) (2 instructions) and B rows [32w, 32w+32) (4
-  // instructions): lane i writes row r = 8j + i/8, chunk slot i%8, i.e.
-  // logical chunk (i%8) ^ ((r >> 1) & 7) of that row.  Scale dwords ride along, one per lane:
-  // E4M3 (one dword per row and step): waves 0-1 load A rows, waves 2-5 B
-  // rows, waves 6-7 a spare copy of A; E2M1 (two dwords per row and step):
-  // two loads per wave covering both words of A and B.
+  // [32w, 32w+32) and B rows [32w, 32w+32) (4 instructions each): lane i
+  // writes row r = 8j + i/8 of its group, chunk slot i%8, i.e. logical chunk
+  // (i%8) ^ ((r >> 1) & 7) of that row.  A rows past the tile's valid rows
+  // repeat its last row and B rows past N repeat row N-1 (loaded, never
+  // stored).  Scale dwords ride along, one per lane: E4M3 (one dword per row
+  // and step): waves 0-3 load A rows, waves 4-7 B rows; E2M1 (two dwords):
+  // two loads per wave; BF16 has none.
   constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;
-  const int lrow = lane >> 3;
-  const uint8_t* gA[A_INS];
-  const uint8_t* gB[B_INS];
-#pragma unroll
-  for (int j = 0; j < A_INS; ++j) {
-    const int r = wave * (8 * A_INS) + j * 8 + lrow;             // row in the tile
-    gA[j] = p.a + static_cast<int64_t>(row0 + r) * p.row_bytes + (((lane & 7) ^ ((r >> 1) & 7)) * 16);
-  }
-#pragma unroll
-  for (int j = 0; j < B_INS; ++j) {
-    const int r = wave * (8 * B_INS) + j * 8 + lrow;
-    gB[j] = p.b + (static_cast<int64_t>(g) * p.n + min(n0 + r, p.n - 1)) * p.row_bytes +
-            (((lane & 7) ^ ((r >> 1) & 7)) * 16);
-  }
-  // scale loads: for load slot u of this wave, the source row pointer and the
-  // LDS word offset (rows of A: 128, of B: 256; 64 rows per load)
   constexpr int S_LOADS = AB == AB_E4M3 ? 1 : AB == AB_E2M1 ? 2 : 0;
-  const uint8_t* gS[S_LOADS > 0 ? S_LOADS : 1];
-  int sdst[S_LOADS > 0 ? S_LOADS : 1];
-  bool sisA[S_LOADS > 0 ? S_LOADS : 1];
-  if constexpr (MX) {
-#pragma unroll
-    for (int u = 0; u < S_LOADS; ++u) {
-      // job = (wave * S_LOADS + u): E4M3 jobs 0-1 A rows, 2-5 B rows, 6-7 spare
-      // A; E2M1 jobs 0-3 A (word, half), 4-11 B (word, quarter), 12-15 spare A
-      const int job = wave * S_LOADS + u;
-      int word, rowsel, isA;
-      if (AB == AB_E4M3) {
-        isA = job < 2 || job >= 6;
-        word = 0;
-        rowsel = job < 2 ? job * 64 : job >= 6 ? (job - 6) * 64 : (job - 2) * 64;
-        sdst[u] = job < 2 ? job * 64 : job >= 6 ? 2 * BM + (job - 6) * 64 : (job - 2) * 64;
-      } else {
-        isA = job < 4 || job >= 12;
-        const int aj = job < 4 ? job : job - 12, bj = job - 4;
-        word = isA ? aj >> 1 : bj >> 2;
-        rowsel = isA ? (aj & 1) * 64 : (bj & 3) * 64;
-        sdst[u] = isA ? (job < 4 ? word * BM + rowsel : 2 * BM + word * BM + rowsel) : word * BN + rowsel;
-      }
-      sisA[u] = isA;
-      gS[u] = isA ? p.sfa + static_cast<int64_t>(row0 + rowsel + lane) * p.ksf + word * 4
-                  : p.sfb + (static_cast<int64_t>(g) * p.n + min(n0 + rowsel + lane, p.n - 1)) * p.ksf + word * 4;
-    }
-  }
-  // vector-memory instructions per wave per stage
-  constexpr int VM_PER_STAGE = A_INS + B_INS + S_LOADS;
+  constexpr int SL = S_LOADS > 0 ? S_LOADS : 1;
+  constexpr int S_HALF = AB == AB_E4M3 ? 4 : 8;      // scale jobs of A (the rest are B's)
+  const int lrow = lane >> 3;
 
-  auto issue = [&](int ks, uint8_t* dA, uint8_t* dB, uint32_t* dSA, uint32_t* dSB) {
-    const int kb = ks * BK;
+  struct Src {
+    const uint8_t* a;    // wave-uniform bases
+    const uint8_t* b;
+    uint32_t oa[A_INS];  // per-lane byte offsets
+    uint32_t ob[B_INS];
+    const uint8_t* s[SL];
+  };
+  auto make_src = [&](const Tile& tl) __attribute__((always_inline)) {
+    Src s;
+    s.a = p.a + static_cast<int64_t>(tl.row0) * p.row_bytes;
+    s.b = p.b + (static_cast<int64_t>(tl.g) * p.n + tl.n0) * p.row_bytes;
+    const int alast = max(min(tl.rows, vm - tl.row0), 1) - 1;   // last loadable row of the tile
+    const int blast = p.n - 1 - tl.n0;
 #pragma unroll
-    for (int j = 0; j < A_INS; ++j) dma16(gA[j] + kb, dA + (wave * (8 * A_INS) + j * 8) * BK);
+    for (int j = 0; j < A_INS; ++j) {
+      const int r = wave * (8 * A_INS) + j * 8 + lrow;
+      s.oa[j] = static_cast<uint32_t>(min(r, alast) * p.row_bytes + (((lane & 7) ^ ((r >> 1) & 7)) * 16));
+    }
 #pragma unroll
-    for (int j = 0; j < B_INS; ++j) dma16(gB[j] + kb, dB + (wave * (8 * B_INS) + j * 8) * BK);
+    for (int j = 0; j < B_INS; ++j) {
+      const int r = wave * (8 * B_INS) + j * 8 + lrow;
+      s.ob[j] = static_cast<uint32_t>(min(r, blast) * p.row_bytes + (((lane & 7) ^ ((r >> 1) & 7)) * 16));
+    }
     if constexpr (MX) {
 #pragma unroll
-      for (int u = 0; u < S_LOADS; ++u)
-        dma4(gS[u] + ks * 4 * SW, (sisA[u] ? dSA : dSB) + sdst[u]);
+      for (int u = 0; u < S_LOADS; ++u) {
+        // job (wave * S_LOADS + u): E4M3 jobs 0-3 A rows, 4-7 B rows;
+        // E2M1 jobs 0-7 A (word, quarter), 8-15 B (word, quarter)
+        const int job = wave * S_LOADS + u;
+        const bool isA = job < S_HALF;
+        const int jj = isA ? job : job - S_HALF;
+        const int word = jj >> 2, rowsel = (jj & 3) * 64 + lane;
+        s.s[u] = isA ? p.sfa + static_cast<int64_t>(tl.row0 + min(rowsel, alast)) * p.ksf + word * 4
+                     : p.sfb + (static_cast<int64_t>(tl.g) * p.n + tl.n0 + min(rowsel, blast)) * p.ksf + word * 4;
+      }
+    }
+    return s;
+  };
+
+  auto issue = [&](const Src& s, int ks, uint8_t* dA, uint8_t* dB, uint32_t* dSA, uint32_t* dSB)
+      __attribute__((always_inline)) {
+    const int kb = ks * BK;
+#pragma unroll
+    for (int j = 0; j < A_INS; ++j) dma16(s.a + s.oa[j] + kb, dA + (wave * (8 * A_INS) + j * 8) * BK);
+#pragma unroll
+    for (int j = 0; j < B_INS; ++j) dma16(s.b + s.ob[j] + kb, dB + (wave * (8 * B_INS) + j * 8) * BK);
+    if constexpr (MX) {
+#pragma unroll
+      for (int u = 0; u < S_LOADS; ++u) {
+        // LDS words: word w of row r at [w * rows + r], 64 rows per load
+        const int job = wave * S_LOADS + u;
+        const bool isA = job < S_HALF;
+        const int jj = isA ? job : job - S_HALF;
+        uint32_t* dst = (isA ? dSA : dSB) + (jj >> 2) * (isA ? BM : BN) + (jj & 3) * 64;
+        dma4(s.s[u] + ks * 4 * SW, dst);
+      }
     }
   };
 
   v16f acc[TM][TN];
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
-
   const int sw = (l32 >> 1) & 7;              // swizzle of this lane's rows (tiles start at multiples of 32)
   const int a_rd = (wm * WM + l32) * BK;
   const int b_rd = (wn * WN + l32) * BK;
   // One K-step (BK bytes of every row) out of one LDS stage.
-  auto compute = [&](const uint8_t* stA, const uint8_t* stB, const uint32_t* stSA, const uint32_t* stSB) {
+  auto compute = [&](const uint8_t* stA, const uint8_t* stB, const uint32_t* stSA, const uint32_t* stSB)
+      __attribute__((always_inline)) {
     const uint8_t* sa = stA + a_rd;
     const uint8_t* sb = stB + b_rd;
     // scale words: byte 0 / 2 of the shifted word are this lane's K-blocks
@@ -404,6 +508,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           for (int tn = 0; tn < TN; ++tn)
             acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 fb[tn], fa[tm], acc[tm][tn], 0, 0, kk * 2, (int)scb[tn][0], kk * 2, (int)sca[tm][0]);
+        // keep the next window's fragments out of this window's registers
+        __builtin_amdgcn_sched_barrier(0);
       });
     } else if constexpr (AB == AB_E2M1) {
       static_for<0, 4>([&](auto kki) {
@@ -427,6 +533,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 fb[tn], fa[tm], acc[tm][tn], 4, 4, (kk & 1) * 2, (int)scb[tn][kk >> 1], (kk & 1) * 2,
                 (int)sca[tm][kk >> 1]);
+        __builtin_amdgcn_sched_barrier(0);
       });
     } else {
 #pragma unroll
@@ -444,189 +551,246 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
           for (int tn = 0; tn < TN; ++tn)
             acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[tn], fa[tm], acc[tm][tn], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
 
-  // ---- main loop: three LDS stages, loads two steps ahead ----
-  // At the top of step ks the wave's outstanding loads are those of stages
-  // ks and ks+1; waiting until only one stage's worth remains and then
-  // meeting at the barrier makes stage ks visible to every wave, and every
-  // wave has finished step ks-1, whose buffer then receives stage ks+2.
-  // The loop is unrolled by three (no exits inside) so every buffer is named
-  // statically; loads past the last stage repeat it (never computed) so the
-  // count of outstanding loads per stage stays the same.  The last 0-2 steps
-  // run after the loop.
-  const int nks = p.k_steps;
-  const int last = nks - 1;
-  issue(0, sA0, sB0, sSA0, sSB0);
-  issue(min(1, last), sA1, sB1, sSA1, sSB1);
-  int ks = 0;
-  for (; ks + 3 <= nks; ks += 3) {
-    wait_vmcnt<VM_PER_STAGE>();
-    __builtin_amdgcn_s_barrier();
-    issue(min(ks + 2, last), sA2, sB2, sSA2, sSB2);
-    compute(sA0, sB0, sSA0, sSB0);
-    wait_vmcnt<VM_PER_STAGE>();
-    __builtin_amdgcn_s_barrier();
-    issue(min(ks + 3, last), sA0, sB0, sSA0, sSB0);
-    compute(sA1, sB1, sSA1, sSB1);
-    wait_vmcnt<VM_PER_STAGE>();
-    __builtin_amdgcn_s_barrier();
-    issue(min(ks + 4, last), sA1, sB1, sSA1, sSB1);
-    compute(sA2, sB2, sSA2, sSB2);
-  }
-  if (ks < nks) {                         // one or two steps left: stages in buffers 0 and 1
-    wait_vmcnt<VM_PER_STAGE>();
-    __builtin_amdgcn_s_barrier();
-    compute(sA0, sB0, sSA0, sSB0);
-    if (ks + 1 < nks) {
-      wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-      compute(sA1, sB1, sSA1, sSB1);
-    }
-  }
-  // no direct-to-LDS write may still be in flight when the workgroup ends
-  wait_vmcnt<0>();
-
-  // ---- epilogue ----
-  const float alpha = p.alpha[g];
-  const int mbase = row0 + wm * WM;
-  const int nbase = n0 + wn * WN;
-  float amax_l = 0.0f;
+  // ---- epilogue of one tile (accumulators -> outputs) ----
   float nc = 1.0f;
   if constexpr (OUT == OUT_E4M3) nc = p.norm_const[0];
+  // this wave's epilogue scratch: 8 KB of stage 1 (free once every wave has
+  // finished the tile's last K-step)
+  float* scratch = reinterpret_cast<float*>(wave < 4 ? sA1 + wave * kScratch : sB1 + (wave - 4) * kScratch);
+  float* sT = scratch;
+  float* sS = scratch + 32 * kTPitch;
 
-  if constexpr (ACT == ACT_DSWIGLU) {
-    // R = alpha^2 acc; X = beta * C_in with blocks [input_b | gate_b]
-    // ("Grouped GEMM + dGLU (SM100)", BF16 contract equations)
-    const float a2 = alpha * alpha;
-    const float beta = p.beta[g];
-    const int ld2 = 2 * p.n;
+  auto epilogue = [&](const Tile& tl) __attribute__((always_inline)) {
+    if (wm * WM >= tl.rows) return;     // rows of a 128-row tile (or an empty one) handled by wm = 0
+    const int g = tl.g;
+    const float alpha = p.alpha[g];
+    const int mbase = tl.row0 + wm * WM;
+    const int nbase = tl.n0 + wn * WN;
+    float pr[TM];
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      const int m = mbase + tm * 32 + l32;
-      const float pr = p.prob[m];
-      float dp = 0.0f;
+    for (int tm = 0; tm < TM; ++tm) pr[tm] = p.prob[mbase + tm * 32 + l32];
+
+    if constexpr (ACT == ACT_DSWIGLU) {
+      // R = alpha^2 acc; X = beta * C_in with blocks [input_b | gate_b]
+      // ("Grouped GEMM + dGLU (SM100)", BF16 contract equations)
+      const float a2 = alpha * alpha;
+      const float beta = p.beta[g];
+      const int ld2 = 2 * p.n;
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const int ncol = nbase + tn * 32;
-        if (ncol >= p.n) continue;
-        const int64_t xoff = static_cast<int64_t>(m) * ld2 + 2 * ncol;   // block b = ncol/32 starts at 64b
-        float xin[16], xg[16];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v2u wi = *reinterpret_cast<const v2u*>(p.c_in + xoff + 8 * j + 4 * hi);
-          const v2u wg = *reinterpret_cast<const v2u*>(p.c_in + xoff + 32 + 8 * j + 4 * hi);
-          xin[4 * j + 0] = __uint_as_float(wi.x << 16);
-          xin[4 * j + 1] = __uint_as_float(wi.x & 0xFFFF0000u);
-          xin[4 * j + 2] = __uint_as_float(wi.y << 16);
-          xin[4 * j + 3] = __uint_as_float(wi.y & 0xFFFF0000u);
-          xg[4 * j + 0] = __uint_as_float(wg.x << 16);
-          xg[4 * j + 1] = __uint_as_float(wg.x & 0xFFFF0000u);
-          xg[4 * j + 2] = __uint_as_float(wg.y << 16);
-          xg[4 * j + 3] = __uint_as_float(wg.y & 0xFFFF0000u);
-        }
-        float din[16], dgt[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float r = a2 * acc[tm][tn][v];
-          const float x = beta * xin[v];
-          const float gt = beta * xg[v];
-          const float s = sigmoid_f(gt);
-          const float swish = gt * s;
-          din[v] = r * pr * swish;
-          dgt[v] = r * pr * x * s * (1.0f + gt * (1.0f - s));
-          dp += r * x * swish;
-        }
-        uint8_t* dbase = p.d;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v2u w;
-          w.x = bf16_rne(din[4 * j]) | (bf16_rne(din[4 * j + 1]) << 16);
-          w.y = bf16_rne(din[4 * j + 2]) | (bf16_rne(din[4 * j + 3]) << 16);
-          *reinterpret_cast<v2u*>(dbase + (xoff + 8 * j + 4 * hi) * 2) = w;
-          w.x = bf16_rne(dgt[4 * j]) | (bf16_rne(dgt[4 * j + 1]) << 16);
-          w.y = bf16_rne(dgt[4 * j + 2]) | (bf16_rne(dgt[4 * j + 3]) << 16);
-          *reinterpret_cast<v2u*>(dbase + (xoff + 32 + 8 * j + 4 * hi) * 2) = w;
-        }
-      }
-      dp = halves_sum(dp);
-      if (hi == 0) atomicAdd(p.dprob + m, dp);
-    }
-    return;
-  } else {
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      const int m = mbase + tm * 32 + l32;
-      const int mblk = (mbase + tm * 32) >> 5;
-      const float pr = p.prob[m];
-      if constexpr (ACT == ACT_SWIGLU) {
-        // pairs [X_b | G_b] of 32 columns ("Grouped GEMM + SwiGLU (SM100)", Step 2)
-#pragma unroll
-        for (int tp = 0; tp < TN / 2; ++tp) {
-          const int xcol = nbase + tp * 64;
-          if (xcol >= p.n) continue;
-          float cx[16], cg[16], d[16];
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            cx[v] = alpha * acc[tm][2 * tp][v];
-            cg[v] = alpha * acc[tm][2 * tp + 1][v];
-          }
-          if (p.c) {
-            store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, xcol, hi, cx);
-            store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, xcol + 32, hi, cg);
-          }
-#pragma unroll
-          for (int v = 0; v < 16; ++v) d[v] = pr * cx[v] * (cg[v] * sigmoid_f(cg[v]));
-          const int ocol = xcol >> 1;
-          if constexpr (OUT == OUT_BF16) {
-            store_bf16_tile(p.d, m, p.n_out, ocol, hi, d);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) amax_l = fmaxf(amax_l, fabsf(d[v]));
-          } else {
-            quant_store_tile(p, m, mblk, ocol, hi, l32, nc, d);
-          }
-        }
-      } else {
+      for (int tm = 0; tm < TM; ++tm) {
+        const int m = mbase + tm * 32 + l32;
+        float dp = 0.0f;
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           const int ncol = nbase + tn * 32;
           if (ncol >= p.n) continue;
-          float c[16], d[16];
+          const int64_t xoff = static_cast<int64_t>(m) * ld2 + 2 * ncol;   // block b = ncol/32 starts at 64b
+          float xin[16], xg[16];
 #pragma unroll
-          for (int v = 0; v < 16; ++v) c[v] = alpha * acc[tm][tn][v];
-          if (p.c) store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, ncol, hi, c);
-          if constexpr (ACT == ACT_SRELU) {
-            // D = prob * (s * min(tanh(relu(C)/s), 1))^2, or prob * relu(C)^2 for s = 0
-            // ("Grouped GEMM + sReLU (SM100)", §Equations, §Tanh soft clamp)
-            const float s = p.srelu_s;
-            const float rs = s > 0.0f ? 1.0f / s : 0.0f;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              float r = fmaxf(c[v], 0.0f);
-              if (s > 0.0f) r = s * fminf(tanh_nonneg(r * rs), 1.0f);
-              d[v] = pr * (r * r);
-            }
-          } else {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) d[v] = pr * c[v];
+          for (int j = 0; j < 4; ++j) {
+            const v2u wi = *reinterpret_cast<const v2u*>(p.c_in + xoff + 8 * j + 4 * hi);
+            const v2u wg = *reinterpret_cast<const v2u*>(p.c_in + xoff + 32 + 8 * j + 4 * hi);
+            xin[4 * j + 0] = __uint_as_float(wi.x << 16);
+            xin[4 * j + 1] = __uint_as_float(wi.x & 0xFFFF0000u);
+            xin[4 * j + 2] = __uint_as_float(wi.y << 16);
+            xin[4 * j + 3] = __uint_as_float(wi.y & 0xFFFF0000u);
+            xg[4 * j + 0] = __uint_as_float(wg.x << 16);
+            xg[4 * j + 1] = __uint_as_float(wg.x & 0xFFFF0000u);
+            xg[4 * j + 2] = __uint_as_float(wg.y << 16);
+            xg[4 * j + 3] = __uint_as_float(wg.y & 0xFFFF0000u);
           }
-          if constexpr (OUT == OUT_BF16) {
-            store_bf16_tile(p.d, m, p.n_out, ncol, hi, d);
+          float din[16], dgt[16];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) amax_l = fmaxf(amax_l, fabsf(d[v]));
-          } else {
-            quant_store_tile(p, m, mblk, ncol, hi, l32, nc, d);
+          for (int v = 0; v < 16; ++v) {
+            const float r = a2 * acc[tm][tn][v];
+            const float x = beta * xin[v];
+            const float gt = beta * xg[v];
+            const float s = sigmoid_f(gt);
+            const float swish = gt * s;
+            din[v] = r * pr[tm] * swish;
+            dgt[v] = r * pr[tm] * x * s * (1.0f + gt * (1.0f - s));
+            dp += r * x * swish;
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v2u w;
+            w.x = bf16_rne(din[4 * j]) | (bf16_rne(din[4 * j + 1]) << 16);
+            w.y = bf16_rne(din[4 * j + 2]) | (bf16_rne(din[4 * j + 3]) << 16);
+            *reinterpret_cast<v2u*>(p.d + (xoff + 8 * j + 4 * hi) * 2) = w;
+            w.x = bf16_rne(dgt[4 * j]) | (bf16_rne(dgt[4 * j + 1]) << 16);
+            w.y = bf16_rne(dgt[4 * j + 2]) | (bf16_rne(dgt[4 * j + 3]) << 16);
+            *reinterpret_cast<v2u*>(p.d + (xoff + 32 + 8 * j + 4 * hi) * 2) = w;
           }
         }
+        dp = halves_sum(dp);
+        if (hi == 0) atomicAdd(p.dprob + m, dp);
+      }
+    } else {
+      float amax_l = 0.0f;
+      const int mblk0 = mbase >> 5;
+      // output column tiles of this wave: SwiGLU turns a [X_b | G_b] pair of
+      // 32-column MFMA tiles into one
+      constexpr int TO = ACT == ACT_SWIGLU ? TN / 2 : TN;
+#pragma unroll
+      for (int to = 0; to < TO; ++to) {
+        const int gcol = nbase + (ACT == ACT_SWIGLU ? 64 : 32) * to;   // first GEMM column
+        if (gcol >= p.n) continue;
+        const int ocol = ACT == ACT_SWIGLU ? gcol >> 1 : gcol;
+        uint32_t colw = 0;                                             // E8M0 bytes of 4 column blocks
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          const int m = mbase + tm * 32 + l32;
+          float d[16];
+          if constexpr (ACT == ACT_SWIGLU) {
+            // pairs [X_b | G_b] of 32 columns ("Grouped GEMM + SwiGLU (SM100)",
+            // Step 2): D = prob * (alpha X) * silu(alpha G), times norm_const
+            // for FP8 output, evaluated as (X G) (prob nc alpha^2) sigmoid(alpha G)
+            const v16f& ax = acc[tm][2 * to];
+            const v16f& ag = acc[tm][2 * to + 1];
+            if (p.c) {
+              float cx[16], cg[16];
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                cx[v] = alpha * ax[v];
+                cg[v] = alpha * ag[v];
+              }
+              store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, gcol, hi, cx);
+              store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, gcol + 32, hi, cg);
+            }
+            const float f = pr[tm] * nc * (alpha * alpha);
+            const float nal = -alpha * kLog2e;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(ag[v] * nal));
+              d[v] = ((ax[v] * ag[v]) * f) * s;
+            }
+          } else {
+            float c[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) c[v] = alpha * acc[tm][to][v];
+            if (p.c) store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, gcol, hi, c);
+            const float f = pr[tm] * nc;
+            if constexpr (ACT == ACT_SRELU) {
+              // D = prob * (s * min(tanh(relu(C)/s), 1))^2, or prob * relu(C)^2 for s = 0
+              // ("Grouped GEMM + sReLU (SM100)", §Equations, §Tanh soft clamp)
+              const float s = p.srelu_s;
+              const float rs = s > 0.0f ? 1.0f / s : 0.0f;
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                float r = fmaxf(c[v], 0.0f);
+                if (s > 0.0f) r = s * fminf(tanh_nonneg(r * rs), 1.0f);
+                d[v] = f * (r * r);
+              }
+            } else {
+#pragma unroll
+              for (int v = 0; v < 16; ++v) d[v] = f * c[v];
+            }
+          }
+          if constexpr (OUT == OUT_BF16) {
+            store_bf16_tile(p.d, m, p.n_out, ocol, hi, d);
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) amax_l = max_abs2(amax_l, d[v], d[v + 1]);
+          } else {
+            const uint32_t bc = quant_tile(p, sT, sS, m, ocol, hi, l32, d);
+            colw |= bc << (8 * tm);
+          }
+        }
+        if constexpr (OUT == OUT_E4M3) {
+          // column l32's scale bytes of the wave's 4 consecutive 32-row blocks
+          if (hi == 0)
+            *reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(ocol + l32) * (vm >> 5) + mblk0) = colw;
+        }
+      }
+      if constexpr (OUT == OUT_BF16) {
+        const float w = wave_max(amax_l);
+        if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(p.amax + g), __float_as_uint(w));
       }
     }
-    if constexpr (OUT == OUT_BF16) {
-      const float w = wave_max(amax_l);
-      if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(p.amax + g), __float_as_uint(w));
+  };
+
+  // ---- persistent tile loop ----
+  // Two LDS stages, loads one step ahead.  At the top of step ks the wave's
+  // only outstanding loads are those of stage ks (and stores of the previous
+  // tile's epilogue); waiting for them and meeting at the barrier makes stage
+  // ks visible to every wave, and every wave has finished step ks-1 (and the
+  // previous epilogue), whose buffer then receives stage ks+1.  The K loop is
+  // unrolled by two (no exits inside) so every buffer is named statically; a
+  // tile's last step loads the next tile's first stage into buffer 0 (or the
+  // current tile's again when there is none), so every tile starts in buffer
+  // 0 and its epilogue can use buffer 1.  Odd and even step counts get their
+  // own copy of the loop.
+  const int nks = p.k_steps;
+  int64_t t = slot;
+  if (t >= total) return;
+  Tile cur = tile_of(t);
+  Src src = make_src(cur);
+  issue(src, 0, sA0, sB0, sSA0, sSB0);
+
+  auto run = [&](auto odd_c) __attribute__((always_inline)) {
+    constexpr bool ODD = decltype(odd_c)::value;
+    while (true) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
+      const int64_t t_next = t + nwg;
+      const bool has_next = t_next < total;
+      const Tile nxt = tile_of(has_next ? t_next : t);
+      for (int ks = 0; ks < nks - 2; ks += 2) {
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        issue(src, ks + 1, sA1, sB1, sSA1, sSB1);
+        compute(sA0, sB0, sSA0, sSB0);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        issue(src, ks + 2, sA0, sB0, sSA0, sSB0);
+        compute(sA1, sB1, sSA1, sSB1);
+      }
+      if constexpr (!ODD) {
+        // steps nks-2 (buffer 0) and nks-1 (buffer 1)
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        issue(src, nks - 1, sA1, sB1, sSA1, sSB1);
+        compute(sA0, sB0, sSA0, sSB0);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        src = make_src(nxt);
+        issue(src, 0, sA0, sB0, sSA0, sSB0);
+        compute(sA1, sB1, sSA1, sSB1);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+      } else {
+        // step nks-1 (buffer 0)
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        compute(sA0, sB0, sSA0, sSB0);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        src = make_src(nxt);
+        issue(src, 0, sA0, sB0, sSA0, sSB0);
+      }
+      // materialise the accumulators here: otherwise the last step's MFMAs
+      // sink into the epilogue's branches and keep their operands alive
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) asm volatile("" : "+v"(acc[tm][tn]));
+      epilogue(cur);
+      if (!has_next) break;
+      t = t_next;
+      cur = nxt;
     }
-  }
+  };
+  if (nks & 1) run(std::true_type{}); else run(std::false_type{});
+  // no direct-to-LDS write may still be in flight when the workgroup ends
+  wait_vmcnt<0>();
 }
 
 __global__ void fill_zero_kernel(float* ptr, int count) {
@@ -636,8 +800,7 @@ __global__ void fill_zero_kernel(float* ptr, int count) {
 
 template <int AB, int ACT, int OUT>
 hipError_t launch_one(const KernelArgs& a, hipStream_t s) {
-  const int64_t blocks = static_cast<int64_t>(a.m_tiles) * a.n_tiles;
-  hipLaunchKernelGGL((grouped_gemm_kernel<AB, ACT, OUT>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<AB, ACT, OUT>), dim3(static_cast<unsigned>(a.grid)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -654,6 +817,7 @@ hipError_t launch_ab(int act, int out, const KernelArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_grouped_gemm(int ab, int act, int out, const KernelArgs& a, hipStream_t s) {
+  if (a.grid <= 0) return hipErrorInvalidValue;
   if (act == ACT_DSWIGLU) {
     if (ab != AB_BF16 || out != OUT_BF16) return hipErrorInvalidValue;
     return launch_one<AB_BF16, ACT_DSWIGLU, OUT_BF16>(a, s);
