@@ -88,16 +88,30 @@ __device__ __forceinline__ float e8m0_inverse(uint32_t byte) {
   return byte < 254u ? __uint_as_float((254u - byte) << 23) : __uint_as_float(0x00400000u);
 }
 
-// Four fp32 -> four E4M3 codes (RNE by the conversion unit, saturated to
-// +-448 beforehand), packed little-endian: a is the lowest byte.
+// E8M0 byte -> its value 2^(byte - 127) as fp32 (byte 0 is the subnormal
+// 2^-127), the form the scaled conversions take.
+__device__ __forceinline__ float e8m0_value(uint32_t byte) {
+  return __uint_as_float(byte ? byte << 23 : 0x00400000u);
+}
+
+// Four fp32 -> four E4M3 codes, RNE by the conversion unit, packed
+// little-endian (a is the lowest byte).  The inputs are block-scaled values,
+// |x| <= 448 (1 + 2^-22) for finite D, which the conversion rounds to +-448;
+// non-finite D gives the E4M3 NaN code.
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  a = fminf(fmaxf(a, -448.0f), 448.0f);
-  b = fminf(fmaxf(b, -448.0f), 448.0f);
-  c = fminf(fmaxf(c, -448.0f), 448.0f);
-  d = fminf(fmaxf(d, -448.0f), 448.0f);
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return static_cast<uint32_t>(w);
+}
+
+// Same for x / 2^(byte - 127) with the block scale folded into the conversion
+// (v_cvt_scalef32_pk_fp8_f32 takes the exponent of `scale`): equal to
+// e4m3x4(x * 2^(127 - byte)) for every finite x.
+__device__ __forceinline__ uint32_t e4m3x4_scaled(float a, float b, float c, float d, float scale) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  v2s w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, a, b, scale, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, scale, true);
+  return static_cast<uint32_t>(static_cast<uint16_t>(w.x)) | (static_cast<uint32_t>(static_cast<uint16_t>(w.y)) << 16);
 }
 
 // sigmoid(x) = 1 / (1 + 2^(-x log2 e)); saturates to 0 / 1 at the extremes.
@@ -175,18 +189,16 @@ __device__ __forceinline__ void store_bf16_tile(uint8_t* base, int64_t m, int ld
 }
 
 // Store one row's 32 E4M3 codes of a 32-column tile.  This lane holds the
-// codes of columns 8j + 4*hi + [0, 4) (w[j]); after one exchange with lane
-// l ^ 32 (same row), lane hi = 0 stores columns [0, 16) and lane hi = 1
-// columns [16, 32), one 16-byte store each.
+// codes of columns 8j + 4*hi + [0, 4) (w[j]).  v_permlane32_swap(x, y)
+// exchanges x of lanes 32-63 with y of lanes 0-31: with x = w[j], y = w[j+2]
+// lane hi = 0 ends with (own w[j], partner's w[j]) = columns 8j + [0, 8) and
+// lane hi = 1 with (partner's w[j+2], own w[j+2]) = columns 16 + 8j + [0, 8),
+// so lane hi = 0 stores columns [0, 16) and lane hi = 1 columns [16, 32),
+// one 16-byte store each.
 __device__ __forceinline__ void store_e4m3_row(uint8_t* dst_row, int hi, const uint32_t* w) {
-  const uint32_t r0 = other_half(hi ? w[0] : w[2], hi);   // hi=0 gets the partner's w0, hi=1 its w2
-  const uint32_t r1 = other_half(hi ? w[1] : w[3], hi);
-  v4u o;
-  o.x = hi ? r0 : w[0];
-  o.y = hi ? w[2] : r0;
-  o.z = hi ? r1 : w[1];
-  o.w = hi ? w[3] : r1;
-  *reinterpret_cast<v4u*>(dst_row + 16 * hi) = o;
+  const v2u s0 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+  const v2u s1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+  *reinterpret_cast<v4u*>(dst_row + 16 * hi) = v4u{s0.x, s0.y, s1.x, s1.y};
 }
 
 // FP8 row + column quantisation of one 32 x 32 output tile ("Grouped GEMM +
@@ -210,7 +222,7 @@ __device__ __forceinline__ uint32_t quant_tile(const KernelArgs& p, float* T, fl
   for (int v = 0; v < 16; v += 2) ra = max_abs2(ra, dn[v], dn[v + 1]);
   ra = halves_max(ra);
   const uint32_t br = e8m0_ceil(ra * kRcp448);
-  const float sr = e8m0_inverse(br);
+  const float sr = e8m0_value(br);
 
   // ---- column blocks through LDS ----
 #pragma unroll
@@ -226,22 +238,15 @@ __device__ __forceinline__ uint32_t quant_tile(const KernelArgs& p, float* T, fl
   cm = halves_max(cm);
   const uint32_t bc = e8m0_ceil(cm * kRcp448);
   if (hi == 0) S[l32] = e8m0_inverse(bc);
-  float sc[16];
+  v4f sc[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const v4f s4 = *reinterpret_cast<const v4f*>(S + 8 * j + 4 * hi);
-    sc[4 * j] = s4.x;
-    sc[4 * j + 1] = s4.y;
-    sc[4 * j + 2] = s4.z;
-    sc[4 * j + 3] = s4.w;
-  }
+  for (int j = 0; j < 4; ++j) sc[j] = *reinterpret_cast<const v4f*>(S + 8 * j + 4 * hi);
 
   uint32_t wr[4], wc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    wr[j] = e4m3x4(dn[4 * j] * sr, dn[4 * j + 1] * sr, dn[4 * j + 2] * sr, dn[4 * j + 3] * sr);
-    wc[j] = e4m3x4(dn[4 * j] * sc[4 * j], dn[4 * j + 1] * sc[4 * j + 1], dn[4 * j + 2] * sc[4 * j + 2],
-                   dn[4 * j + 3] * sc[4 * j + 3]);
+    wr[j] = e4m3x4_scaled(dn[4 * j], dn[4 * j + 1], dn[4 * j + 2], dn[4 * j + 3], sr);
+    wc[j] = e4m3x4(dn[4 * j] * sc[j].x, dn[4 * j + 1] * sc[j].y, dn[4 * j + 2] * sc[j].z, dn[4 * j + 3] * sc[j].w);
   }
   const int64_t rowoff = static_cast<int64_t>(m) * p.n_out + ocol;
   store_e4m3_row(p.d + rowoff, hi, wr);
@@ -398,6 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   constexpr int SL = S_LOADS > 0 ? S_LOADS : 1;
   constexpr int S_HALF = AB == AB_E4M3 ? 4 : 8;      // scale jobs of A (the rest are B's)
   const int lrow = lane >> 3;
+  const int nks_all = p.k_steps;
 
   struct Src {
     const uint8_t* a;    // wave-uniform bases
@@ -438,24 +444,30 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
     return s;
   };
 
-  auto issue = [&](const Src& s, int ks, uint8_t* dA, uint8_t* dB, uint32_t* dSA, uint32_t* dSB)
+  // Load i of a stage (0 <= i < VM_STAGE): A rows, B rows, scale words.
+  constexpr int VM_STAGE = A_INS + B_INS + S_LOADS;
+  auto issue_one = [&](const Src& s, int ks, int i, uint8_t* dA, uint8_t* dB, uint32_t* dSA, uint32_t* dSB)
       __attribute__((always_inline)) {
     const int kb = ks * BK;
-#pragma unroll
-    for (int j = 0; j < A_INS; ++j) dma16(s.a + s.oa[j] + kb, dA + (wave * (8 * A_INS) + j * 8) * BK);
-#pragma unroll
-    for (int j = 0; j < B_INS; ++j) dma16(s.b + s.ob[j] + kb, dB + (wave * (8 * B_INS) + j * 8) * BK);
-    if constexpr (MX) {
-#pragma unroll
-      for (int u = 0; u < S_LOADS; ++u) {
-        // LDS words: word w of row r at [w * rows + r], 64 rows per load
-        const int job = wave * S_LOADS + u;
-        const bool isA = job < S_HALF;
-        const int jj = isA ? job : job - S_HALF;
-        uint32_t* dst = (isA ? dSA : dSB) + (jj >> 2) * (isA ? BM : BN) + (jj & 3) * 64;
-        dma4(s.s[u] + ks * 4 * SW, dst);
-      }
+    if (i < A_INS) {
+      dma16(s.a + s.oa[i] + kb, dA + (wave * (8 * A_INS) + i * 8) * BK);
+    } else if (i < A_INS + B_INS) {
+      const int j = i - A_INS;
+      dma16(s.b + s.ob[j] + kb, dB + (wave * (8 * B_INS) + j * 8) * BK);
+    } else if constexpr (MX) {
+      // LDS words: word w of row r at [w * rows + r], 64 rows per load
+      const int u = i - A_INS - B_INS;
+      const int job = wave * S_LOADS + u;
+      const bool isA = job < S_HALF;
+      const int jj = isA ? job : job - S_HALF;
+      uint32_t* dst = (isA ? dSA : dSB) + (jj >> 2) * (isA ? BM : BN) + (jj & 3) * 64;
+      dma4(s.s[u] + ks * 4 * SW, dst);
     }
+  };
+  auto issue = [&](const Src& s, int ks, uint8_t* dA, uint8_t* dB, uint32_t* dSA, uint32_t* dSB)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < VM_STAGE; ++i) issue_one(s, ks, i, dA, dB, dSA, dSB);
   };
 
   v16f acc[TM][TN];
@@ -463,8 +475,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   const int a_rd = (wm * WM + l32) * BK;
   const int b_rd = (wn * WN + l32) * BK;
   // One K-step (BK bytes of every row) out of one LDS stage.
-  auto compute = [&](const uint8_t* stA, const uint8_t* stB, const uint32_t* stSA, const uint32_t* stSB)
-      __attribute__((always_inline)) {
+  // `hook(g)` runs right after the step's MFMA number g (0, 1, ...).
+  auto compute = [&](const uint8_t* stA, const uint8_t* stB, const uint32_t* stSA, const uint32_t* stSB,
+                     auto&& hook) __attribute__((always_inline)) {
     const uint8_t* sa = stA + a_rd;
     const uint8_t* sb = stB + b_rd;
     // scale words: byte 0 / 2 of the shifted word are this lane's K-blocks
@@ -505,11 +518,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-          for (int tn = 0; tn < TN; ++tn)
+          for (int tn = 0; tn < TN; ++tn) {
             acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 fb[tn], fa[tm], acc[tm][tn], 0, 0, kk * 2, (int)scb[tn][0], kk * 2, (int)sca[tm][0]);
-        // keep the next window's fragments out of this window's registers
-        __builtin_amdgcn_sched_barrier(0);
+            hook((kk * TM + tm) * TN + tn);
+          }
       });
     } else if constexpr (AB == AB_E2M1) {
       static_for<0, 4>([&](auto kki) {
@@ -529,11 +542,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-          for (int tn = 0; tn < TN; ++tn)
+          for (int tn = 0; tn < TN; ++tn) {
             acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 fb[tn], fa[tm], acc[tm][tn], 4, 4, (kk & 1) * 2, (int)scb[tn][kk >> 1], (kk & 1) * 2,
                 (int)sca[tm][kk >> 1]);
-        __builtin_amdgcn_sched_barrier(0);
+            hook((kk * TM + tm) * TN + tn);
+          }
       });
     } else {
 #pragma unroll
@@ -549,9 +563,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-          for (int tn = 0; tn < TN; ++tn)
+          for (int tn = 0; tn < TN; ++tn) {
             acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[tn], fa[tm], acc[tm][tn], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+            hook((kk * TM + tm) * TN + tn);
+          }
       }
     }
   };
@@ -565,15 +580,28 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   float* sT = scratch;
   float* sS = scratch + 32 * kTPitch;
 
-  auto epilogue = [&](const Tile& tl) __attribute__((always_inline)) {
+  // Per-tile epilogue factors, loaded before the tile's last K-step so that
+  // their latency hides behind it: alpha_g and prob of this lane's 4 rows.
+  struct EpiIn {
+    float alpha;
+    float pr[TM];
+  };
+  auto epi_in = [&](const Tile& tl) __attribute__((always_inline)) {
+    EpiIn e;
+    e.alpha = p.alpha[tl.g];
+    const int mb = min(tl.row0 + wm * WM, vm - WM);      // rows of idle waves: any valid ones
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) e.pr[tm] = p.prob[mb + tm * 32 + l32];
+    return e;
+  };
+
+  auto epilogue = [&](const Tile& tl, const EpiIn& ein) __attribute__((always_inline)) {
     if (wm * WM >= tl.rows) return;     // rows of a 128-row tile (or an empty one) handled by wm = 0
     const int g = tl.g;
-    const float alpha = p.alpha[g];
+    const float alpha = ein.alpha;
     const int mbase = tl.row0 + wm * WM;
     const int nbase = tl.n0 + wn * WN;
-    float pr[TM];
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) pr[tm] = p.prob[mbase + tm * 32 + l32];
+    const float* pr = ein.pr;
 
     if constexpr (ACT == ACT_DSWIGLU) {
       // R = alpha^2 acc; X = beta * C_in with blocks [input_b | gate_b]
@@ -667,7 +695,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
               const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(ag[v] * nal));
-              d[v] = ((ax[v] * ag[v]) * f) * s;
+              d[v] = (ax[v] * ag[v]) * (f * s);
             }
           } else {
             float c[16];
@@ -715,10 +743,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 
   // ---- persistent tile loop ----
   // Two LDS stages, loads one step ahead.  At the top of step ks the wave's
-  // only outstanding loads are those of stage ks (and stores of the previous
-  // tile's epilogue); waiting for them and meeting at the barrier makes stage
-  // ks visible to every wave, and every wave has finished step ks-1 (and the
-  // previous epilogue), whose buffer then receives stage ks+1.  The K loop is
+  // only outstanding loads are stage ks's (a tile's first step also waits
+  // out the previous epilogue's stores); waiting for them and meeting at the
+  // barrier makes stage ks visible to every wave, and every wave has
+  // finished step ks-1 (and the previous epilogue), whose buffer then
+  // receives stage ks+1.  The K loop is
   // unrolled by two (no exits inside) so every buffer is named statically; a
   // tile's last step loads the next tile's first stage into buffer 0 (or the
   // current tile's again when there is none), so every tile starts in buffer
@@ -743,34 +772,39 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       const int64_t t_next = t + nwg;
       const bool has_next = t_next < total;
       const Tile nxt = tile_of(has_next ? t_next : t);
+      auto no_loads = [](int) {};
+      // stage 0 and whatever the previous epilogue left in flight
+      wait_vmcnt<0>();
       for (int ks = 0; ks < nks - 2; ks += 2) {
+        __builtin_amdgcn_sched_barrier(0);   // keep the wait below the previous step's MFMAs
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        issue(src, ks + 1, sA1, sB1, sSA1, sSB1);
-        compute(sA0, sB0, sSA0, sSB0);
+        issue(src, ks + 1, sA1, sB1, sSA1, sSB1); compute(sA0, sB0, sSA0, sSB0, no_loads);
+        __builtin_amdgcn_sched_barrier(0);   // keep the wait below the previous step's MFMAs
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        issue(src, ks + 2, sA0, sB0, sSA0, sSB0);
-        compute(sA1, sB1, sSA1, sSB1);
+        issue(src, ks + 2, sA0, sB0, sSA0, sSB0); compute(sA1, sB1, sSA1, sSB1, no_loads);
       }
+      const EpiIn ein = epi_in(cur);
       if constexpr (!ODD) {
         // steps nks-2 (buffer 0) and nks-1 (buffer 1)
+        __builtin_amdgcn_sched_barrier(0);   // keep the wait below the previous step's MFMAs
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        issue(src, nks - 1, sA1, sB1, sSA1, sSB1);
-        compute(sA0, sB0, sSA0, sSB0);
+        issue(src, nks - 1, sA1, sB1, sSA1, sSB1); compute(sA0, sB0, sSA0, sSB0, no_loads);
+        __builtin_amdgcn_sched_barrier(0);   // keep the wait below the previous step's MFMAs
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         src = make_src(nxt);
-        issue(src, 0, sA0, sB0, sSA0, sSB0);
-        compute(sA1, sB1, sSA1, sSB1);
+        issue(src, 0, sA0, sB0, sSA0, sSB0); compute(sA1, sB1, sSA1, sSB1, no_loads);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
       } else {
         // step nks-1 (buffer 0)
+        __builtin_amdgcn_sched_barrier(0);   // keep the wait below the previous step's MFMAs
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        compute(sA0, sB0, sSA0, sSB0);
+        compute(sA0, sB0, sSA0, sSB0, no_loads);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         src = make_src(nxt);
@@ -782,7 +816,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) asm volatile("" : "+v"(acc[tm][tn]));
-      epilogue(cur);
+      epilogue(cur, ein);
       if (!has_next) break;
       t = t_next;
       cur = nxt;
