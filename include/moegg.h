@@ -25,8 +25,14 @@
  *   A       (valid_m, K)   E4M3 codes, or (valid_m, K/2) packed E2M1 pairs
  *                          (the even K element in the low nibble), or BF16
  *   B       (L, N, K)      same encoding as A, K contiguous ("K-major")
- *   SFA     (valid_m, K/32) E8M0 bytes, one per 32 K-elements (MX formats only)
- *   SFB     (L, N, K/32)   E8M0 bytes
+ *   SFA     E8M0 bytes, one per 32 K-elements of each row of A (MX formats
+ *           only), stored as K/128 planes of 32-bit words: the byte of row r
+ *           and K-block kb (kb = k / 32) is at byte offset
+ *           4 * ((kb / 4) * valid_m + r) + kb % 4, i.e. a (K/128, valid_m, 4)
+ *           array.  One plane holds the scales of 128 consecutive K elements
+ *           of every row, so the scales a row tile needs for one K-step are
+ *           contiguous.  (The logical view is the pages' (valid_m, K/32).)
+ *   SFB     the same for the rows of B: (K/128, L*N, 4), row index g*N + n
  *   padded_offsets (L) int32, cumulative group ends; padded_offsets[L-1] ==
  *                          valid_m; every entry a multiple of m_aligned and
  *                          nondecreasing (empty groups repeat the previous end)
@@ -61,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MOEGG_ABI_VERSION 1
+#define MOEGG_ABI_VERSION 2
 
 typedef enum moegg_status {
   MOEGG_OK = 0,
@@ -106,8 +112,8 @@ typedef struct moegg_problem {
 typedef struct moegg_args {
   const void* a;
   const void* b;
-  const uint8_t* sfa;            /* MX operands only */
-  const uint8_t* sfb;            /* MX operands only */
+  const uint8_t* sfa;            /* MX operands only; (K/128, valid_m, 4) word planes */
+  const uint8_t* sfb;            /* MX operands only; (K/128, L*N, 4) word planes */
   const int32_t* padded_offsets;
   const float* alpha;
   const float* prob;             /* required ("prob ... Required", Quant page) */

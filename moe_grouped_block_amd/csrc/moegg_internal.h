@@ -26,8 +26,8 @@ constexpr int kThreads = 512;
 struct KernelArgs {
   const uint8_t* a;        // (valid_m, row_bytes)
   const uint8_t* b;        // (L, n, row_bytes)
-  const uint8_t* sfa;      // (valid_m, ksf)
-  const uint8_t* sfb;      // (L, n, ksf)
+  const uint8_t* sfa;      // (K/128, valid_m, 4): 32-bit word planes
+  const uint8_t* sfb;      // (K/128, L*n, 4)
   const int32_t* po;       // (L)
   const float* alpha;      // (L)
   const float* prob;       // (valid_m)

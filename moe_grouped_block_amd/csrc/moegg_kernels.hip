@@ -437,8 +437,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         const bool isA = job < S_HALF;
         const int jj = isA ? job : job - S_HALF;
         const int word = jj >> 2, rowsel = (jj & 3) * 64 + lane;
-        s.s[u] = isA ? p.sfa + static_cast<int64_t>(tl.row0 + min(rowsel, alast)) * p.ksf + word * 4
-                     : p.sfb + (static_cast<int64_t>(tl.g) * p.n + tl.n0 + min(rowsel, blast)) * p.ksf + word * 4;
+        // word planes: word j of row r at 4 * (j * rows + r) (rows = valid_m for
+        // SFA, L * N for SFB); step ks uses planes SW*ks .. SW*ks + SW-1
+        s.s[u] = isA ? p.sfa + (static_cast<int64_t>(word) * vm + tl.row0 + min(rowsel, alast)) * 4
+                     : p.sfb + (static_cast<int64_t>(word) * p.num_groups * p.n +
+                                static_cast<int64_t>(tl.g) * p.n + tl.n0 + min(rowsel, blast)) * 4;
       }
     }
     return s;
@@ -461,7 +464,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       const bool isA = job < S_HALF;
       const int jj = isA ? job : job - S_HALF;
       uint32_t* dst = (isA ? dSA : dSB) + (jj >> 2) * (isA ? BM : BN) + (jj & 3) * 64;
-      dma4(s.s[u] + ks * 4 * SW, dst);
+      const int64_t plane = isA ? static_cast<int64_t>(vm) * 4 : static_cast<int64_t>(p.num_groups) * p.n * 4;
+      dma4(s.s[u] + static_cast<int64_t>(ks) * SW * plane, dst);
     }
   };
   auto issue = [&](const Src& s, int ks, uint8_t* dA, uint8_t* dB, uint32_t* dSA, uint32_t* dSB)

@@ -1,6 +1,7 @@
 """Device-memory plumbing around the binding (torch used for allocation only).
 
-``to_device`` uploads host arrays in the library's logical layouts;
+``to_device`` uploads host arrays in the library's ABI layouts (the
+generator's logical (rows, K/32) scale arrays become word planes);
 ``empty_outputs`` allocates the output tensors a problem writes.  Neither
 computes anything of the method.
 """
@@ -13,10 +14,24 @@ _NP2TORCH = {np.dtype(np.uint8): torch.uint8, np.dtype(np.uint16): torch.int16,
              np.dtype(np.int32): torch.int32, np.dtype(np.float32): torch.float32}
 
 
+def scale_planes(sf: np.ndarray) -> np.ndarray:
+    """Logical E8M0 scales (..., rows, K/32) -> the ABI's word planes
+    (K/128, rows_total, 4): byte kb of row r moves to [kb // 4, r, kb % 4]."""
+    kb = sf.shape[-1]
+    rows = int(np.prod(sf.shape[:-1]))
+    if kb % 4:
+        raise ValueError("K/32 must be a multiple of 4")
+    return np.ascontiguousarray(sf.reshape(rows, kb // 4, 4).transpose(1, 0, 2))
+
+
 def to_device(arrays: dict, device="cuda") -> dict:
-    """numpy arrays -> contiguous device tensors (uint16 bf16 bits travel as int16)."""
+    """numpy arrays -> contiguous device tensors in the ABI's layouts: scale
+    arrays (sfa, sfb) are rearranged into word planes, bf16 bits travel as
+    int16."""
     out = {}
     for k, v in arrays.items():
+        if k in ("sfa", "sfb") and v.size:
+            v = scale_planes(v)
         v = np.ascontiguousarray(v)
         t = torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v)
         out[k] = t.to(device, non_blocking=False)

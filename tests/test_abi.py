@@ -42,7 +42,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_strings():
-    assert mg.moegg_abi_version() == 1
+    assert mg.moegg_abi_version() == 2
     for code, name in mg.STATUS.items():
         assert mg.moegg_status_string(code) == name
     assert mg.moegg_status_string(99) == "MOEGG_UNKNOWN_STATUS"
