@@ -310,6 +310,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   __shared__ __attribute__((aligned(16))) uint32_t sSA0[SA_WORDS], sSA1[SA_WORDS];
   __shared__ __attribute__((aligned(16))) uint32_t sSB0[SB_WORDS], sSB1[SB_WORDS];
   __shared__ int32_t sTiles[1025];   // m-tiles before expert g, g = 0..L
+  __shared__ float sPr[kThreads / 64][kBM / 2];   // prob of each wave's 128 rows (epilogue)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -584,28 +585,38 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   float* sT = scratch;
   float* sS = scratch + 32 * kTPitch;
 
-  // Per-tile epilogue factors, loaded before the tile's last K-step so that
-  // their latency hides behind it: alpha_g and prob of this lane's 4 rows.
+  // Per-tile epilogue factors: alpha_g (a scalar load issued before the
+  // tile's last K-step) and prob of the wave's 128 rows, copied to LDS by two
+  // direct loads issued just before the next tile's first stage, so that no
+  // register holds them across the last K-step.
   struct EpiIn {
     float alpha;
-    float pr[TM];
   };
   auto epi_in = [&](const Tile& tl) __attribute__((always_inline)) {
     EpiIn e;
     e.alpha = p.alpha[tl.g];
-    const int mb = min(tl.row0 + wm * WM, vm - WM);      // rows of idle waves: any valid ones
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) e.pr[tm] = p.prob[mb + tm * 32 + l32];
     return e;
+  };
+  auto load_prob = [&](const Tile& tl) __attribute__((always_inline)) {
+    const int mb = min(tl.row0 + wm * WM, vm - WM);      // rows of idle waves: any valid ones
+    dma4(p.prob + mb + lane, sPr[wave]);
+    dma4(p.prob + mb + 64 + lane, sPr[wave] + 64);
   };
 
   auto epilogue = [&](const Tile& tl, const EpiIn& ein) __attribute__((always_inline)) {
     if (wm * WM >= tl.rows) return;     // rows of a 128-row tile (or an empty one) handled by wm = 0
+    // lane-dependent addresses are rebuilt here from an opaque copy of the
+    // lane id rather than kept live (and spilled) across the K loop
+    int lid = lane;
+    asm volatile("" : "+v"(lid));
+    const int l32 = lid & 31, hi = lid >> 5;
     const int g = tl.g;
     const float alpha = ein.alpha;
     const int mbase = tl.row0 + wm * WM;
     const int nbase = tl.n0 + wn * WN;
-    const float* pr = ein.pr;
+    float pr[TM];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) pr[tm] = sPr[wave][tm * 32 + l32];
 
     if constexpr (ACT == ACT_DSWIGLU) {
       // R = alpha^2 acc; X = beta * C_in with blocks [input_b | gate_b]
@@ -800,6 +811,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         src = make_src(nxt);
+        load_prob(cur);
         issue(src, 0, sA0, sB0, sSA0, sSB0); compute(sA1, sB1, sSA1, sSB1, no_loads);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
@@ -812,6 +824,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         src = make_src(nxt);
+        load_prob(cur);
         issue(src, 0, sA0, sB0, sSA0, sSB0);
       }
       // materialise the accumulators here: otherwise the last step's MFMAs
