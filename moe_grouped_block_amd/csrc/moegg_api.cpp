@@ -192,6 +192,9 @@ moegg_status moegg_run(const moegg_problem* problem, const moegg_args* args, voi
   // persistent grid: one workgroup per CU, never more than there are tiles
   // (at most (valid_m / 128 + L) / 2 row tiles, each n_tiles wide)
   const int64_t max_tiles = ((p.valid_m / moegg::kRowBlock + p.num_groups + 1) / 2) * k.n_tiles;
+  if (max_tiles >= (int64_t{1} << 31))
+    return fail(MOEGG_ERROR_NOT_SUPPORTED, "valid_m=%lld x n=%d: more than 2^31 output tiles",
+                (long long)p.valid_m, p.n);
   const int cus = device_cus();
   if (cus <= 0) return fail(MOEGG_ERROR_LAUNCH, "cannot query the device's compute units");
   k.grid = static_cast<int32_t>(max_tiles < cus ? max_tiles : cus);

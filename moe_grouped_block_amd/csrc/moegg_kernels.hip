@@ -346,8 +346,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   }
   __syncthreads();
   const int m_tiles = sTiles[L];
-  const int64_t n_tiles = p.n_tiles;
-  const int64_t total = static_cast<int64_t>(m_tiles) * n_tiles;
+  const int n_tiles = p.n_tiles;
+  // the host guarantees (valid_m / 128 + L) / 2 * n_tiles < 2^31
+  const int total = __builtin_amdgcn_readfirstlane(m_tiles * n_tiles);
 
   // Linear tile index -> tile.  Workgroups are dispatched round-robin over
   // the 8 XCDs (each with its own L2): workgroup w runs on XCD w % 8.  The
@@ -362,10 +363,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
     const int xcd = wg & 7, j = wg >> 3, q = nwg >> 3, r = nwg & 7;
     return xcd * q + min(xcd, r) + j;
   }();
-  auto tile_of = [&](int64_t t) __attribute__((always_inline)) -> Tile {
-    const int64_t band_size = static_cast<int64_t>(kBandM) * n_tiles;
-    const int band = static_cast<int>(t / band_size);
-    const int in_band = static_cast<int>(t - band * band_size);
+  auto tile_of = [&](int t) __attribute__((always_inline)) -> Tile {
+    const int band_size = kBandM * n_tiles;
+    const int band = t / band_size;
+    const int in_band = t - band * band_size;
     const int band_rows = min(kBandM, m_tiles - band * kBandM);
     const int nt = in_band / band_rows;
     const int mt = band * kBandM + (in_band - nt * band_rows);
@@ -414,6 +415,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
     const uint8_t* s[SL];
   };
   auto make_src = [&](const Tile& tl) __attribute__((always_inline)) {
+    // per-lane values are rebuilt from an opaque copy of the lane id instead
+    // of being kept live (and spilled) across the K loop
+    int lid = lane;
+    asm volatile("" : "+v"(lid));
+    const int lrow = lid >> 3;
     Src s;
     s.a = p.a + static_cast<int64_t>(tl.row0) * p.row_bytes;
     s.b = p.b + (static_cast<int64_t>(tl.g) * p.n + tl.n0) * p.row_bytes;
@@ -422,12 +428,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
     for (int j = 0; j < A_INS; ++j) {
       const int r = wave * (8 * A_INS) + j * 8 + lrow;
-      s.oa[j] = static_cast<uint32_t>(min(r, alast) * p.row_bytes + (((lane & 7) ^ ((r >> 1) & 7)) * 16));
+      s.oa[j] = static_cast<uint32_t>(min(r, alast) * p.row_bytes + (((lid & 7) ^ ((r >> 1) & 7)) * 16));
     }
 #pragma unroll
     for (int j = 0; j < B_INS; ++j) {
       const int r = wave * (8 * B_INS) + j * 8 + lrow;
-      s.ob[j] = static_cast<uint32_t>(min(r, blast) * p.row_bytes + (((lane & 7) ^ ((r >> 1) & 7)) * 16));
+      s.ob[j] = static_cast<uint32_t>(min(r, blast) * p.row_bytes + (((lid & 7) ^ ((r >> 1) & 7)) * 16));
     }
     if constexpr (MX) {
 #pragma unroll
@@ -437,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         const int job = wave * S_LOADS + u;
         const bool isA = job < S_HALF;
         const int jj = isA ? job : job - S_HALF;
-        const int word = jj >> 2, rowsel = (jj & 3) * 64 + lane;
+        const int word = jj >> 2, rowsel = (jj & 3) * 64 + lid;
         // word planes: word j of row r at 4 * (j * rows + r) (rows = valid_m for
         // SFA, L * N for SFB); step ks uses planes SW*ks .. SW*ks + SW-1
         s.s[u] = isA ? p.sfa + (static_cast<int64_t>(word) * vm + tl.row0 + min(rowsel, alast)) * 4
@@ -476,15 +482,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   };
 
   v16f acc[TM][TN];
-  const int sw = (l32 >> 1) & 7;              // swizzle of this lane's rows (tiles start at multiples of 32)
-  const int a_rd = (wm * WM + l32) * BK;
-  const int b_rd = (wn * WN + l32) * BK;
   // One K-step (BK bytes of every row) out of one LDS stage.
   // `hook(g)` runs right after the step's MFMA number g (0, 1, ...).
   auto compute = [&](const uint8_t* stA, const uint8_t* stB, const uint32_t* stSA, const uint32_t* stSB,
                      auto&& hook) __attribute__((always_inline)) {
-    const uint8_t* sa = stA + a_rd;
-    const uint8_t* sb = stB + b_rd;
+    // this lane's LDS addresses, rebuilt every step from an opaque copy of
+    // the lane id (a few VALU) instead of occupying registers across the
+    // persistent loop
+    int lid = lane;
+    asm volatile("" : "+v"(lid));
+    const int l32 = lid & 31, hi = lid >> 5;
+    const int sw = (l32 >> 1) & 7;              // swizzle of this lane's rows (tiles start at multiples of 32)
+    const uint8_t* sa = stA + (wm * WM + l32) * BK;
+    const uint8_t* sb = stB + (wn * WN + l32) * BK;
     // scale words: byte 0 / 2 of the shifted word are this lane's K-blocks
     // for the first / second 64-element window of a word's four blocks
     uint32_t sca[TM][SW], scb[TN][SW];
@@ -769,7 +779,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   // 0 and its epilogue can use buffer 1.  Odd and even step counts get their
   // own copy of the loop.
   const int nks = p.k_steps;
-  int64_t t = slot;
+  int t = __builtin_amdgcn_readfirstlane(slot);
   if (t >= total) return;
   Tile cur = tile_of(t);
   Src src = make_src(cur);
@@ -784,7 +794,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
-      const int64_t t_next = t + nwg;
+      const int t_next = t + nwg;
       const bool has_next = t_next < total;
       const Tile nxt = tile_of(has_next ? t_next : t);
       auto no_loads = [](int) {};
