@@ -798,17 +798,34 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       const bool has_next = t_next < total;
       const Tile nxt = tile_of(has_next ? t_next : t);
       auto no_loads = [](int) {};
+      // a stage's loads in two halves: the first before the step's MFMAs,
+      // the rest after the first K-window's MFMAs
+      constexpr int VM_FIRST = (VM_STAGE + 1) / 2;
+      auto second_half = [&](int ksl, uint8_t* dA, uint8_t* dB, uint32_t* dSA, uint32_t* dSB)
+          __attribute__((always_inline)) {
+        return [&, ksl, dA, dB, dSA, dSB](int gi) __attribute__((always_inline)) {
+          if (gi == TM * TN - 1) {
+#pragma unroll
+            for (int i = VM_FIRST; i < VM_STAGE; ++i) issue_one(src, ksl, i, dA, dB, dSA, dSB);
+          }
+        };
+      };
+      auto first_half = [&](int ksl, uint8_t* dA, uint8_t* dB, uint32_t* dSA, uint32_t* dSB)
+          __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < VM_FIRST; ++i) issue_one(src, ksl, i, dA, dB, dSA, dSB);
+      };
       // stage 0 and whatever the previous epilogue left in flight
       wait_vmcnt<0>();
       for (int ks = 0; ks < nks - 2; ks += 2) {
         __builtin_amdgcn_sched_barrier(0);   // keep the wait below the previous step's MFMAs
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        issue(src, ks + 1, sA1, sB1, sSA1, sSB1); compute(sA0, sB0, sSA0, sSB0, no_loads);
+        first_half(ks + 1, sA1, sB1, sSA1, sSB1); compute(sA0, sB0, sSA0, sSB0, second_half(ks + 1, sA1, sB1, sSA1, sSB1));
         __builtin_amdgcn_sched_barrier(0);   // keep the wait below the previous step's MFMAs
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        issue(src, ks + 2, sA0, sB0, sSA0, sSB0); compute(sA1, sB1, sSA1, sSB1, no_loads);
+        first_half(ks + 2, sA0, sB0, sSA0, sSB0); compute(sA1, sB1, sSA1, sSB1, second_half(ks + 2, sA0, sB0, sSA0, sSB0));
       }
       const EpiIn ein = epi_in(cur);
       if constexpr (!ODD) {
@@ -816,13 +833,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         __builtin_amdgcn_sched_barrier(0);   // keep the wait below the previous step's MFMAs
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        issue(src, nks - 1, sA1, sB1, sSA1, sSB1); compute(sA0, sB0, sSA0, sSB0, no_loads);
+        first_half(nks - 1, sA1, sB1, sSA1, sSB1); compute(sA0, sB0, sSA0, sSB0, second_half(nks - 1, sA1, sB1, sSA1, sSB1));
         __builtin_amdgcn_sched_barrier(0);   // keep the wait below the previous step's MFMAs
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         src = make_src(nxt);
         load_prob(cur);
-        issue(src, 0, sA0, sB0, sSA0, sSB0); compute(sA1, sB1, sSA1, sSB1, no_loads);
+        first_half(0, sA0, sB0, sSA0, sSB0); compute(sA1, sB1, sSA1, sSB1, second_half(0, sA0, sB0, sSA0, sSB0));
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
       } else {
