@@ -292,20 +292,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   constexpr bool MX = AB != AB_BF16;
   constexpr int SW = AB == AB_E2M1 ? 2 : 1;          // scale words per row per step
   constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
+  constexpr int AH_BYTES = A_BYTES / 2;              // one of the two A row halves
   constexpr int SA_WORDS = MX ? SW * BM : 1, SB_WORDS = MX ? SW * BN : 1;
   static_assert(NW == 8 && TM == 4 && TN == 2, "tile shape");
-  static_assert(4 * kScratch <= A_BYTES && 4 * kScratch <= B_BYTES, "epilogue scratch lives in stage 1");
+  static_assert(2 * kScratch <= AH_BYTES && 4 * kScratch <= B_BYTES, "epilogue scratch lives in stage 1");
 
-  // Two LDS stages (about 66 KB each), one distinct array per stage and
-  // operand: the compiler can then tell the stages apart and adds no
+  // Two LDS stages (about 66 KB each), one distinct array per stage, operand
+  // and A row half: the compiler can then tell them apart and adds no
   // conservative waits for the direct-to-LDS loads (the explicit waits below
-  // order them).  Rows are BK = 128 bytes, a whole cache line, so every load
-  // instruction moves whole lines; the 16-byte chunk c of row r sits at chunk
-  // slot c ^ ((r >> 1) & 7).  The LDS has 64 four-byte banks (256 bytes), so
-  // two consecutive 128-byte rows fill one bank window and a 16-lane group of
+  // order them).  A's rows are split by bit 6 of the tile row: rows with it
+  // clear (the first two 32-row MFMA tiles of each wave row) sit in sAl,
+  // the others in sAh, each half at index (r & 63) | ((r >> 1) & 64).
+  // Rows are BK = 128 bytes, a whole cache line, so every load instruction
+  // moves whole lines; the 16-byte chunk c of array row i sits at chunk slot
+  // c ^ ((i >> 1) & 7).  The LDS has 64 four-byte banks (256 bytes), so two
+  // consecutive 128-byte rows fill one bank window and a 16-lane group of
   // 16-byte reads (16 consecutive rows, one chunk each) hits 16 distinct bank
   // quads.  Stage 1's A and B areas double as the epilogue scratch.
-  __shared__ __attribute__((aligned(16))) uint8_t sA0[A_BYTES], sA1[A_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sAl0[AH_BYTES], sAh0[AH_BYTES], sAl1[AH_BYTES], sAh1[AH_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sB0[B_BYTES], sB1[B_BYTES];
   __shared__ __attribute__((aligned(16))) uint32_t sSA0[SA_WORDS], sSA1[SA_WORDS];
   __shared__ __attribute__((aligned(16))) uint32_t sSB0[SB_WORDS], sSB1[SB_WORDS];
@@ -392,26 +396,27 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   };
 
   // ---- direct global -> LDS staging ----
-  // One wave instruction fills 8 rows (1 KB).  Wave w fills A rows
-  // [32w, 32w+32) and B rows [32w, 32w+32) (4 instructions each): lane i
-  // writes row r = 8j + i/8 of its group, chunk slot i%8, i.e. logical chunk
-  // (i%8) ^ ((r >> 1) & 7) of that row.  A rows past the tile's valid rows
+  // One wave instruction fills 8 rows (1 KB): lane i writes row 8j + i/8 of
+  // its group, chunk slot i%8, i.e. logical chunk (i%8) ^ ((row >> 1) & 7).
+  // Wave w fills B rows [32w, 32w+32) (4 instructions) and rows
+  // [16w, 16w+16) of each A half (2 + 2).  A rows past the tile's valid rows
   // repeat its last row and B rows past N repeat row N-1 (loaded, never
   // stored).  Scale dwords ride along, one per lane: E4M3 (one dword per row
   // and step): waves 0-3 load A rows, waves 4-7 B rows; E2M1 (two dwords):
   // two loads per wave; BF16 has none.
-  constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;
+  // A stage's loads come in two sets: the early set (B, the low A half and
+  // all scale words: everything the first operand cluster of a step reads)
+  // and the late set (the high A half, read by the second cluster).
   constexpr int S_LOADS = AB == AB_E4M3 ? 1 : AB == AB_E2M1 ? 2 : 0;
   constexpr int SL = S_LOADS > 0 ? S_LOADS : 1;
   constexpr int S_HALF = AB == AB_E4M3 ? 4 : 8;      // scale jobs of A (the rest are B's)
-  const int lrow = lane >> 3;
-  const int nks_all = p.k_steps;
+  constexpr int N_EARLY = 2 + 4 + S_LOADS, N_LATE = 2;
 
   struct Src {
     const uint8_t* a;    // wave-uniform bases
     const uint8_t* b;
-    uint32_t oa[A_INS];  // per-lane byte offsets
-    uint32_t ob[B_INS];
+    uint32_t oa[4];      // per-lane byte offsets: low half j = 0, 1; high half 2, 3
+    uint32_t ob[4];
     const uint8_t* s[SL];
   };
   auto make_src = [&](const Tile& tl) __attribute__((always_inline)) {
@@ -426,13 +431,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
     const int alast = max(min(tl.rows, vm - tl.row0), 1) - 1;   // last loadable row of the tile
     const int blast = p.n - 1 - tl.n0;
 #pragma unroll
-    for (int j = 0; j < A_INS; ++j) {
-      const int r = wave * (8 * A_INS) + j * 8 + lrow;
-      s.oa[j] = static_cast<uint32_t>(min(r, alast) * p.row_bytes + (((lid & 7) ^ ((r >> 1) & 7)) * 16));
+    for (int j = 0; j < 4; ++j) {
+      const int i = wave * 16 + (j & 1) * 8 + lrow;              // row within the half
+      const int r = (i & 63) | ((j >> 1) << 6) | ((i & 64) << 1);
+      s.oa[j] = static_cast<uint32_t>(min(r, alast) * p.row_bytes + (((lid & 7) ^ ((i >> 1) & 7)) * 16));
     }
 #pragma unroll
-    for (int j = 0; j < B_INS; ++j) {
-      const int r = wave * (8 * B_INS) + j * 8 + lrow;
+    for (int j = 0; j < 4; ++j) {
+      const int r = wave * 32 + j * 8 + lrow;
       s.ob[j] = static_cast<uint32_t>(min(r, blast) * p.row_bytes + (((lid & 7) ^ ((r >> 1) & 7)) * 16));
     }
     if constexpr (MX) {
@@ -454,136 +460,166 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
     return s;
   };
 
-  // Load i of a stage (0 <= i < VM_STAGE): A rows, B rows, scale words.
-  constexpr int VM_STAGE = A_INS + B_INS + S_LOADS;
-  auto issue_one = [&](const Src& s, int ks, int i, uint8_t* dA, uint8_t* dB, uint32_t* dSA, uint32_t* dSB)
-      __attribute__((always_inline)) {
+  // One LDS stage: the two A halves, B, scale words.
+  struct Stage {
+    uint8_t* al;
+    uint8_t* ah;
+    uint8_t* b;
+    uint32_t* sa;
+    uint32_t* sb;
+  };
+  const Stage st0{sAl0, sAh0, sB0, sSA0, sSB0};
+  const Stage st1{sAl1, sAh1, sB1, sSA1, sSB1};
+  auto issue_early = [&](const Src& s, int ks, const Stage& d) __attribute__((always_inline)) {
     const int kb = ks * BK;
-    if (i < A_INS) {
-      dma16(s.a + s.oa[i] + kb, dA + (wave * (8 * A_INS) + i * 8) * BK);
-    } else if (i < A_INS + B_INS) {
-      const int j = i - A_INS;
-      dma16(s.b + s.ob[j] + kb, dB + (wave * (8 * B_INS) + j * 8) * BK);
-    } else if constexpr (MX) {
-      // LDS words: word w of row r at [w * rows + r], 64 rows per load
-      const int u = i - A_INS - B_INS;
-      const int job = wave * S_LOADS + u;
-      const bool isA = job < S_HALF;
-      const int jj = isA ? job : job - S_HALF;
-      uint32_t* dst = (isA ? dSA : dSB) + (jj >> 2) * (isA ? BM : BN) + (jj & 3) * 64;
-      const int64_t plane = isA ? static_cast<int64_t>(vm) * 4 : static_cast<int64_t>(p.num_groups) * p.n * 4;
-      dma4(s.s[u] + static_cast<int64_t>(ks) * SW * plane, dst);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(s.a + s.oa[j] + kb, d.al + (wave * 16 + j * 8) * BK);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(s.b + s.ob[j] + kb, d.b + (wave * 32 + j * 8) * BK);
+    if constexpr (MX) {
+#pragma unroll
+      for (int u = 0; u < S_LOADS; ++u) {
+        // LDS words: word w of row r at [w * rows + r], 64 rows per load
+        const int job = wave * S_LOADS + u;
+        const bool isA = job < S_HALF;
+        const int jj = isA ? job : job - S_HALF;
+        uint32_t* dst = (isA ? d.sa : d.sb) + (jj >> 2) * (isA ? BM : BN) + (jj & 3) * 64;
+        const int64_t plane = isA ? static_cast<int64_t>(vm) * 4 : static_cast<int64_t>(p.num_groups) * p.n * 4;
+        dma4(s.s[u] + static_cast<int64_t>(ks) * SW * plane, dst);
+      }
     }
   };
-  auto issue = [&](const Src& s, int ks, uint8_t* dA, uint8_t* dB, uint32_t* dSA, uint32_t* dSB)
-      __attribute__((always_inline)) {
+  auto issue_late = [&](const Src& s, int ks, const Stage& d) __attribute__((always_inline)) {
+    const int kb = ks * BK;
 #pragma unroll
-    for (int i = 0; i < VM_STAGE; ++i) issue_one(s, ks, i, dA, dB, dSA, dSB);
+    for (int j = 0; j < 2; ++j) dma16(s.a + s.oa[2 + j] + kb, d.ah + (wave * 16 + j * 8) * BK);
+  };
+  auto issue = [&](const Src& s, int ks, const Stage& d) __attribute__((always_inline)) {
+    issue_early(s, ks, d);
+    issue_late(s, ks, d);
   };
 
   v16f acc[TM][TN];
-  // One K-step (BK bytes of every row) out of one LDS stage.
-  // `hook(g)` runs right after the step's MFMA number g (0, 1, ...).
-  auto compute = [&](const uint8_t* stA, const uint8_t* stB, const uint32_t* stSA, const uint32_t* stSB,
-                     auto&& hook) __attribute__((always_inline)) {
-    // this lane's LDS addresses, rebuilt every step from an opaque copy of
-    // the lane id (a few VALU) instead of occupying registers across the
-    // persistent loop
+  // The K loop runs in clusters: an M cluster reads operands from LDS into
+  // registers and issues direct loads, a C cluster runs MFMAs only.  Step s
+  // is M0 (B and the A tiles 0, 1 of the wave, all scale words), C0 (those
+  // A tiles), M1 (A tiles 2, 3), C1 (those, with B still in registers).  The
+  // two waves sharing a SIMD (w and w + 4) run one cluster apart, so one of
+  // them issues MFMAs while the other reads LDS and issues loads.
+  // A lane's 16-byte pieces of a 32-row tile for one step: chunks hi + 2c,
+  // c = 0..3.  E4M3 window kk uses pieces 2kk, 2kk+1 (K [16hi, 16hi+16) and
+  // [32+16hi, 48+16hi) of the window; its scale byte covers the 32-element
+  // block hi of the window); E2M1 (32 elements) and BF16 (8 elements) window
+  // kk use piece kk.
+  typedef v4u Pieces[4];
+  auto read_tile = [&](const uint8_t* base, int l32, int hi, Pieces& x) __attribute__((always_inline)) {
+    const int sw = (l32 >> 1) & 7;      // swizzle of this lane's rows (tiles start at multiples of 32)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[c] = *reinterpret_cast<const v4u*>(base + (((hi + 2 * c) ^ sw) * 16));
+  };
+  auto settle = [&](Pieces& x) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(x[c]));
+  };
+  struct Ops0 {
+    Pieces a[2], b[TN];
+    uint32_t sa[TM][SW], sb[TN][SW];
+  };
+  struct Ops1 {
+    Pieces a[2];
+  };
+  // M0: B, A tiles 0, 1 and the scale words (fin0 waits for them and
+  // shifts the scale words so that byte 0 / 2 is this lane's block of an
+  // even / odd window)
+  auto read0 = [&](const Stage& st) __attribute__((always_inline)) {
     int lid = lane;
     asm volatile("" : "+v"(lid));
     const int l32 = lid & 31, hi = lid >> 5;
-    const int sw = (l32 >> 1) & 7;              // swizzle of this lane's rows (tiles start at multiples of 32)
-    const uint8_t* sa = stA + (wm * WM + l32) * BK;
-    const uint8_t* sb = stB + (wn * WN + l32) * BK;
-    // scale words: byte 0 / 2 of the shifted word are this lane's K-blocks
-    // for the first / second 64-element window of a word's four blocks
-    uint32_t sca[TM][SW], scb[TN][SW];
+    Ops0 o;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) read_tile(st.b + (wn * WN + tn * 32 + l32) * BK, l32, hi, o.b[tn]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) read_tile(st.al + (wm * 64 + t * 32 + l32) * BK, l32, hi, o.a[t]);
     if constexpr (MX) {
-      const int sh = 8 * hi;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-        for (int w = 0; w < SW; ++w) sca[tm][w] = stSA[w * BM + wm * WM + tm * 32 + l32] >> sh;
+        for (int w = 0; w < SW; ++w) o.sa[tm][w] = st.sa[w * BM + wm * WM + tm * 32 + l32];
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-        for (int w = 0; w < SW; ++w) scb[tn][w] = stSB[w * BN + wn * WN + tn * 32 + l32] >> sh;
+        for (int w = 0; w < SW; ++w) o.sb[tn][w] = st.sb[w * BN + wn * WN + tn * 32 + l32];
     }
-    if constexpr (AB == AB_E4M3) {
-      static_for<0, 2>([&](auto kki) {
-        constexpr int kk = decltype(kki)::value;
-        // 8-bit operands: a lane of half h holds K [16h, 16h+16) and
-        // [32+16h, 48+16h) of the 64-wide window (chunks h + 4kk and
-        // h + 4kk + 2 of the row), while its scale byte covers the 32-element
-        // block h of the window; FP4 operands hold [32h, 32h+32) instead.
-        const int o0 = ((hi + 4 * kk) ^ sw) * 16, o1 = ((hi + 4 * kk + 2) ^ sw) * 16;
-        v8i fa[TM], fb[TN];
+    return o;
+  };
+  auto fin0 = [&](Ops0& o) __attribute__((always_inline)) {
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-          const v4u x0 = *reinterpret_cast<const v4u*>(sa + tm * 32 * BK + o0);
-          const v4u x1 = *reinterpret_cast<const v4u*>(sa + tm * 32 * BK + o1);
-          fa[tm] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    for (int tn = 0; tn < TN; ++tn) settle(o.b[tn]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) settle(o.a[t]);
+    if constexpr (MX) {
+      int lid = lane;
+      asm volatile("" : "+v"(lid));
+      const int sh = 8 * (lid >> 5);
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int w = 0; w < SW; ++w) {
+          asm volatile("" : "+v"(o.sa[tm][w]));
+          o.sa[tm][w] >>= sh;
         }
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int w = 0; w < SW; ++w) {
+          asm volatile("" : "+v"(o.sb[tn][w]));
+          o.sb[tn][w] >>= sh;
+        }
+    }
+  };
+  // M1: A tiles 2, 3
+  auto read1 = [&](const Stage& st) __attribute__((always_inline)) {
+    int lid = lane;
+    asm volatile("" : "+v"(lid));
+    const int l32 = lid & 31, hi = lid >> 5;
+    Ops1 o;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) read_tile(st.ah + (wm * 64 + t * 32 + l32) * BK, l32, hi, o.a[t]);
+    return o;
+  };
+  auto fin1 = [&](Ops1& o) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) settle(o.a[t]);
+  };
+  // C cluster: MFMA tiles tm0, tm0 + 1 (A pieces a[0], a[1]) x all tn, all
+  // windows of the step
+  auto mma = [&](int tm0, const Pieces* a, const Ops0& o0) __attribute__((always_inline)) {
+    constexpr int NWIN = AB == AB_E4M3 ? 2 : 4;
+    static_for<0, NWIN>([&](auto kc) {
+      constexpr int kk = decltype(kc)::value;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-          const v4u x0 = *reinterpret_cast<const v4u*>(sb + tn * 32 * BK + o0);
-          const v4u x1 = *reinterpret_cast<const v4u*>(sb + tn * 32 * BK + o1);
-          fb[tn] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        }
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-          for (int tn = 0; tn < TN; ++tn) {
-            acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                fb[tn], fa[tm], acc[tm][tn], 0, 0, kk * 2, (int)scb[tn][0], kk * 2, (int)sca[tm][0]);
-            hook((kk * TM + tm) * TN + tn);
+          v16f& c = acc[tm0 + t][tn];
+          if constexpr (AB == AB_E4M3) {
+            const v4u a0 = a[t][2 * kk], a1 = a[t][2 * kk + 1], b0 = o0.b[tn][2 * kk], b1 = o0.b[tn][2 * kk + 1];
+            const v8i fa{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+            const v8i fb{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, c, 0, 0, kk * 2, (int)o0.sb[tn][0], kk * 2,
+                                                                (int)o0.sa[tm0 + t][0]);
+          } else if constexpr (AB == AB_E2M1) {
+            const v4u a0 = a[t][kk], b0 = o0.b[tn][kk];
+            const v8i fa{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
+            const v8i fb{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
+            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, c, 4, 4, (kk & 1) * 2, (int)o0.sb[tn][kk >> 1],
+                                                                (kk & 1) * 2, (int)o0.sa[tm0 + t][kk >> 1]);
+          } else {
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, o0.b[tn][kk]),
+                                                        __builtin_bit_cast(v8bf, a[t][kk]), c, 0, 0, 0);
           }
-      });
-    } else if constexpr (AB == AB_E2M1) {
-      static_for<0, 4>([&](auto kki) {
-        constexpr int kk = decltype(kki)::value;
-        const int o0 = ((hi + 2 * kk) ^ sw) * 16;
-        v8i fa[TM], fb[TN];
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-          const v4u x0 = *reinterpret_cast<const v4u*>(sa + tm * 32 * BK + o0);
-          fa[tm] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
         }
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          const v4u x0 = *reinterpret_cast<const v4u*>(sb + tn * 32 * BK + o0);
-          fb[tn] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-          for (int tn = 0; tn < TN; ++tn) {
-            acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                fb[tn], fa[tm], acc[tm][tn], 4, 4, (kk & 1) * 2, (int)scb[tn][kk >> 1], (kk & 1) * 2,
-                (int)sca[tm][kk >> 1]);
-            hook((kk * TM + tm) * TN + tn);
-          }
-      });
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int o0 = ((hi + 2 * kk) ^ sw) * 16;
-        v8bf fa[TM], fb[TN];
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-          fa[tm] = *reinterpret_cast<const v8bf*>(sa + tm * 32 * BK + o0);
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-          fb[tn] = *reinterpret_cast<const v8bf*>(sb + tn * 32 * BK + o0);
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-          for (int tn = 0; tn < TN; ++tn) {
-            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[tn], fa[tm], acc[tm][tn], 0, 0, 0);
-            hook((kk * TM + tm) * TN + tn);
-          }
-      }
-    }
+    });
   };
 
   // ---- epilogue of one tile (accumulators -> outputs) ----
@@ -591,7 +627,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   if constexpr (OUT == OUT_E4M3) nc = p.norm_const[0];
   // this wave's epilogue scratch: 8 KB of stage 1 (free once every wave has
   // finished the tile's last K-step)
-  float* scratch = reinterpret_cast<float*>(wave < 4 ? sA1 + wave * kScratch : sB1 + (wave - 4) * kScratch);
+  float* scratch = reinterpret_cast<float*>(wave < 2   ? sAl1 + wave * kScratch
+                                            : wave < 4 ? sAh1 + (wave - 2) * kScratch
+                                                       : sB1 + (wave - 4) * kScratch);
   float* sT = scratch;
   float* sS = scratch + 32 * kTPitch;
 
@@ -767,106 +805,145 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   };
 
   // ---- persistent tile loop ----
-  // Two LDS stages, loads one step ahead.  At the top of step ks the wave's
-  // only outstanding loads are stage ks's (a tile's first step also waits
-  // out the previous epilogue's stores); waiting for them and meeting at the
-  // barrier makes stage ks visible to every wave, and every wave has
-  // finished step ks-1 (and the previous epilogue), whose buffer then
-  // receives stage ks+1.  The K loop is
-  // unrolled by two (no exits inside) so every buffer is named statically; a
-  // tile's last step loads the next tile's first stage into buffer 0 (or the
-  // current tile's again when there is none), so every tile starts in buffer
-  // 0 and its epilogue can use buffer 1.  Odd and even step counts get their
-  // own copy of the loop.
+  // Two LDS stages.  Every cluster ends at a workgroup barrier; waves 4-7
+  // pass one extra barrier at the start of a tile and waves 0-3 one at its
+  // end, so between two barriers one wave of each SIMD is in a C cluster and
+  // the other in an M cluster.  A stage's early set (read in M0) is free once
+  // both wave groups have passed M0, its late set once both have passed M1.
+  //
+  // Even step counts >= 4: stage s+2's early set is issued in M1(s) into the
+  // buffer of stage s, its late set in M0(s+1); M1(s) waits for stage s+1's
+  // early set and M0(s+1) for its late set, so every load has about four
+  // clusters to arrive and the barrier after the wait publishes it before
+  // any wave reads it.  A tile's last two steps load the next tile's first
+  // stage into buffer 0 (the current tile's again when there is none), so
+  // every tile starts in buffer 0; the tile's first M0 loads stage 1 whole
+  // into buffer 1, which the previous epilogue used as scratch.
+  // Other step counts: stage s+1 is loaded whole in M0(s) and waited for in
+  // M1(s); the next tile's first stage is loaded during the epilogue.
+  // The K loop is unrolled by two (no exits inside) so every buffer is named
+  // statically.
   const int nks = p.k_steps;
   int t = __builtin_amdgcn_readfirstlane(slot);
   if (t >= total) return;
   Tile cur = tile_of(t);
   Src src = make_src(cur);
-  issue(src, 0, sA0, sB0, sSA0, sSB0);
+  issue(src, 0, st0);
 
-  auto run = [&](auto odd_c) __attribute__((always_inline)) {
-    constexpr bool ODD = decltype(odd_c)::value;
+  auto sync = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // pin the accumulators after each MFMA cluster (the MFMAs are pure
+  // operations that the compiler would otherwise sink past the barriers,
+  // out of their cluster and into the code after the K loop)
+  auto pin_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) asm volatile("" : "+v"(acc[tm][tn]));
+  };
+  constexpr int VMW = N_EARLY + N_LATE;
+  using NoWait = std::integral_constant<int, -1>;
+  using WaitStage = std::integral_constant<int, VMW>;
+  using WaitAll = std::integral_constant<int, 0>;
+  auto no_loads = []() __attribute__((always_inline)) {};
+  // one K-step out of stage `st`: loads0 / loads1 run in M0 / M1 after the
+  // LDS reads are issued, then the cluster waits until at most W0 / W1 of
+  // this wave's loads are outstanding (no wait for -1)
+  auto step = [&](const Stage& st, auto&& loads0, auto w0c, auto&& loads1, auto w1c) __attribute__((always_inline)) {
+    constexpr int W0 = decltype(w0c)::value, W1 = decltype(w1c)::value;
+    Ops0 o0 = read0(st);
+    loads0();
+    fin0(o0);
+    if constexpr (W0 >= 0) wait_vmcnt<W0>();
+    sync();
+    mma(0, o0.a, o0);
+    pin_acc();
+    sync();
+    Ops1 o1 = read1(st);
+    loads1();
+    fin1(o1);
+    if constexpr (W1 >= 0) wait_vmcnt<W1>();
+    sync();
+    mma(2, o1.a, o0);
+    pin_acc();
+    sync();
+  };
+  auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
+  };
+
+  auto run = [&](auto fast_c) __attribute__((always_inline)) {
+    constexpr bool FAST = decltype(fast_c)::value;
     while (true) {
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
+      zero_acc();
       const int t_next = t + nwg;
       const bool has_next = t_next < total;
       const Tile nxt = tile_of(has_next ? t_next : t);
-      auto no_loads = [](int) {};
-      // a stage's loads in two halves: the first before the step's MFMAs,
-      // the rest after the first K-window's MFMAs
-      constexpr int VM_FIRST = (VM_STAGE + 1) / 2;
-      auto second_half = [&](int ksl, uint8_t* dA, uint8_t* dB, uint32_t* dSA, uint32_t* dSB)
-          __attribute__((always_inline)) {
-        return [&, ksl, dA, dB, dSA, dSB](int gi) __attribute__((always_inline)) {
-          if (gi == TM * TN - 1) {
-#pragma unroll
-            for (int i = VM_FIRST; i < VM_STAGE; ++i) issue_one(src, ksl, i, dA, dB, dSA, dSB);
-          }
-        };
-      };
-      auto first_half = [&](int ksl, uint8_t* dA, uint8_t* dB, uint32_t* dSA, uint32_t* dSB)
-          __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < VM_FIRST; ++i) issue_one(src, ksl, i, dA, dB, dSA, dSB);
-      };
-      // stage 0 and whatever the previous epilogue left in flight
+      // stage 0 (and whatever the previous epilogue left in flight) complete
+      // and visible, the previous epilogue's scratch free
       wait_vmcnt<0>();
-      for (int ks = 0; ks < nks - 2; ks += 2) {
-        __builtin_amdgcn_sched_barrier(0);   // keep the wait below the previous step's MFMAs
-        wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        first_half(ks + 1, sA1, sB1, sSA1, sSB1); compute(sA0, sB0, sSA0, sSB0, second_half(ks + 1, sA1, sB1, sSA1, sSB1));
-        __builtin_amdgcn_sched_barrier(0);   // keep the wait below the previous step's MFMAs
-        wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        first_half(ks + 2, sA0, sB0, sSA0, sSB0); compute(sA1, sB1, sSA1, sSB1, second_half(ks + 2, sA0, sB0, sSA0, sSB0));
-      }
-      const EpiIn ein = epi_in(cur);
-      if constexpr (!ODD) {
-        // steps nks-2 (buffer 0) and nks-1 (buffer 1)
-        __builtin_amdgcn_sched_barrier(0);   // keep the wait below the previous step's MFMAs
-        wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        first_half(nks - 1, sA1, sB1, sSA1, sSB1); compute(sA0, sB0, sSA0, sSB0, second_half(nks - 1, sA1, sB1, sSA1, sSB1));
-        __builtin_amdgcn_sched_barrier(0);   // keep the wait below the previous step's MFMAs
-        wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        src = make_src(nxt);
-        load_prob(cur);
-        first_half(0, sA0, sB0, sSA0, sSB0); compute(sA1, sB1, sSA1, sSB1, second_half(0, sA0, sB0, sSA0, sSB0));
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_barrier();
+      sync();
+      if (wm) sync();
+      if constexpr (FAST) {
+        step(st0, [&]() __attribute__((always_inline)) { issue(src, 1, st1); }, NoWait{},
+             [&]() __attribute__((always_inline)) { issue_early(src, 2, st0); }, WaitStage{});
+        step(st1, [&]() __attribute__((always_inline)) { issue_late(src, 2, st0); }, WaitStage{},
+             [&]() __attribute__((always_inline)) { issue_early(src, 3, st1); }, WaitStage{});
+        for (int ks = 2; ks < nks - 2; ks += 2) {
+          step(st0, [&]() __attribute__((always_inline)) { issue_late(src, ks + 1, st1); }, WaitStage{},
+               [&]() __attribute__((always_inline)) { issue_early(src, ks + 2, st0); }, WaitStage{});
+          step(st1, [&]() __attribute__((always_inline)) { issue_late(src, ks + 2, st0); }, WaitStage{},
+               [&]() __attribute__((always_inline)) { issue_early(src, ks + 3, st1); }, WaitStage{});
+        }
+        const EpiIn ein = epi_in(cur);
+        step(st0, [&]() __attribute__((always_inline)) { issue_late(src, nks - 1, st1); }, WaitStage{},
+             [&]() __attribute__((always_inline)) {
+               src = make_src(nxt);
+               issue_early(src, 0, st0);
+             },
+             WaitStage{});
+        step(st1, [&]() __attribute__((always_inline)) {
+               load_prob(cur);
+               issue_late(src, 0, st0);
+             },
+             std::integral_constant<int, VMW + 2>{}, no_loads, NoWait{});
+        if (!wm) sync();
+        wait_vmcnt<N_LATE>();      // prob (issued before the next tile's late set)
+        epilogue(cur, ein);
       } else {
-        // step nks-1 (buffer 0)
-        __builtin_amdgcn_sched_barrier(0);   // keep the wait below the previous step's MFMAs
-        wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        compute(sA0, sB0, sSA0, sSB0, no_loads);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_barrier();
+        int ks = 0;
+        for (; ks + 2 < nks; ks += 2) {
+          step(st0, [&]() __attribute__((always_inline)) { issue(src, ks + 1, st1); }, NoWait{}, no_loads, WaitAll{});
+          step(st1, [&]() __attribute__((always_inline)) { issue(src, ks + 2, st0); }, NoWait{}, no_loads, WaitAll{});
+        }
+        const EpiIn ein = epi_in(cur);
+        if (nks - ks == 2) {
+          step(st0, [&]() __attribute__((always_inline)) { issue(src, ks + 1, st1); }, NoWait{}, no_loads, WaitAll{});
+          step(st1, no_loads, NoWait{}, no_loads, NoWait{});
+        } else {
+          step(st0, no_loads, NoWait{}, no_loads, NoWait{});
+        }
+        if (!wm) sync();
         src = make_src(nxt);
         load_prob(cur);
-        issue(src, 0, sA0, sB0, sSA0, sSB0);
+        issue(src, 0, st0);
+        wait_vmcnt<VMW>();         // prob (issued before the next tile's first stage)
+        epilogue(cur, ein);
       }
-      // materialise the accumulators here: otherwise the last step's MFMAs
-      // sink into the epilogue's branches and keep their operands alive
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) asm volatile("" : "+v"(acc[tm][tn]));
-      epilogue(cur, ein);
       if (!has_next) break;
       t = t_next;
       cur = nxt;
     }
   };
-  if (nks & 1) run(std::true_type{}); else run(std::false_type{});
+  if ((nks & 1) == 0 && nks >= 4) run(std::true_type{}); else run(std::false_type{});
   // no direct-to-LDS write may still be in flight when the workgroup ends
   wait_vmcnt<0>();
 }

@@ -7,7 +7,8 @@ none of the method's own arithmetic (no GEMM, activation, gating or output
 quantisation), and it imports neither the oracle nor the GPU library; both of
 those take their inputs from here.
 
-Storage conventions (the logical layouts the library's C ABI defines):
+Storage conventions (logical layouts; the C ABI stores the scale arrays as
+K-block word planes, which the device plumbing builds on upload):
 
 * ``a``      (valid_m, K) uint8 E4M3 codes, (valid_m, K/2) uint8 packed E2M1
              pairs (low nibble = even K element), or (valid_m, K) uint16 BF16 bits
