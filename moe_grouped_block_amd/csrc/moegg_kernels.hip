@@ -410,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   constexpr int S_LOADS = AB == AB_E4M3 ? 1 : AB == AB_E2M1 ? 2 : 0;
   constexpr int SL = S_LOADS > 0 ? S_LOADS : 1;
   constexpr int S_HALF = AB == AB_E4M3 ? 4 : 8;      // scale jobs of A (the rest are B's)
-  constexpr int N_EARLY = 2 + 4 + S_LOADS, N_LATE = 2;
+  constexpr int N_EA = 2 + S_LOADS, N_EB = 4, N_EARLY = N_EA + N_EB, N_LATE = 2;
 
   struct Src {
     const uint8_t* a;    // wave-uniform bases
@@ -470,12 +470,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   };
   const Stage st0{sAl0, sAh0, sB0, sSA0, sSB0};
   const Stage st1{sAl1, sAh1, sB1, sSA1, sSB1};
-  auto issue_early = [&](const Src& s, int ks, const Stage& d) __attribute__((always_inline)) {
+  // early set, first part: the low A half and the scale words
+  auto issue_ea = [&](const Src& s, int ks, const Stage& d) __attribute__((always_inline)) {
     const int kb = ks * BK;
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16(s.a + s.oa[j] + kb, d.al + (wave * 16 + j * 8) * BK);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(s.b + s.ob[j] + kb, d.b + (wave * 32 + j * 8) * BK);
     if constexpr (MX) {
 #pragma unroll
       for (int u = 0; u < S_LOADS; ++u) {
@@ -489,14 +488,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       }
     }
   };
-  auto issue_late = [&](const Src& s, int ks, const Stage& d) __attribute__((always_inline)) {
-    const int kb = ks * BK;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) dma16(s.a + s.oa[2 + j] + kb, d.ah + (wave * 16 + j * 8) * BK);
+  // early set, second part: B row load j (0..3)
+  auto issue_eb = [&](const Src& s, int ks, const Stage& d, int j) __attribute__((always_inline)) {
+    dma16(s.b + s.ob[j] + ks * BK, d.b + (wave * 32 + j * 8) * BK);
   };
+  // late set: high A half load j (0..1)
+  auto issue_l = [&](const Src& s, int ks, const Stage& d, int j) __attribute__((always_inline)) {
+    dma16(s.a + s.oa[2 + j] + ks * BK, d.ah + (wave * 16 + j * 8) * BK);
+  };
+  // a whole stage, in the order early (first part, second part), late
   auto issue = [&](const Src& s, int ks, const Stage& d) __attribute__((always_inline)) {
-    issue_early(s, ks, d);
-    issue_late(s, ks, d);
+    issue_ea(s, ks, d);
+#pragma unroll
+    for (int j = 0; j < N_EB; ++j) issue_eb(s, ks, d, j);
+#pragma unroll
+    for (int j = 0; j < N_LATE; ++j) issue_l(s, ks, d, j);
   };
 
   v16f acc[TM][TN];
@@ -593,14 +599,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   };
   // C cluster: MFMA tiles tm0, tm0 + 1 (A pieces a[0], a[1]) x all tn, all
   // windows of the step
-  auto mma = [&](int tm0, const Pieces* a, const Ops0& o0) __attribute__((always_inline)) {
-    constexpr int NWIN = AB == AB_E4M3 ? 2 : 4;
+  // `hook(i)` runs right after the cluster's MFMA number i (0 .. NMMA-1)
+  constexpr int NWIN = AB == AB_E4M3 ? 2 : 4;
+  constexpr int NMMA = NWIN * 2 * TN;
+  auto mma = [&](int tm0, const Pieces* a, const Ops0& o0, auto&& hook) __attribute__((always_inline)) {
     static_for<0, NWIN>([&](auto kc) {
       constexpr int kk = decltype(kc)::value;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
+          const int mi = (kk * 2 + t) * TN + tn;
           v16f& c = acc[tm0 + t][tn];
           if constexpr (AB == AB_E4M3) {
             const v4u a0 = a[t][2 * kk], a1 = a[t][2 * kk + 1], b0 = o0.b[tn][2 * kk], b1 = o0.b[tn][2 * kk + 1];
@@ -618,6 +627,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, o0.b[tn][kk]),
                                                         __builtin_bit_cast(v8bf, a[t][kk]), c, 0, 0, 0);
           }
+          hook(mi);
         }
     });
   };
@@ -844,30 +854,43 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) asm volatile("" : "+v"(acc[tm][tn]));
   };
-  constexpr int VMW = N_EARLY + N_LATE;
   using NoWait = std::integral_constant<int, -1>;
-  using WaitStage = std::integral_constant<int, VMW>;
   using WaitAll = std::integral_constant<int, 0>;
+  // steady state: M0(s) waits for stage s's late set, M1(s) for stage s+1's
+  // early set (see the issue order in the loop below)
+  using WaitM0 = std::integral_constant<int, N_EARLY>;
+  using WaitM1 = std::integral_constant<int, N_LATE + N_EA>;
   auto no_loads = []() __attribute__((always_inline)) {};
-  // one K-step out of stage `st`: loads0 / loads1 run in M0 / M1 after the
-  // LDS reads are issued, then the cluster waits until at most W0 / W1 of
-  // this wave's loads are outstanding (no wait for -1)
-  auto step = [&](const Stage& st, auto&& loads0, auto w0c, auto&& loads1, auto w1c) __attribute__((always_inline)) {
+  auto no_hook = [](int) __attribute__((always_inline)) {};
+  // hook issuing N loads spread evenly over a C cluster's MFMAs
+  auto spread = [&](auto nc, auto&& f) __attribute__((always_inline)) {
+    constexpr int N = decltype(nc)::value;
+    return [&f](int i) __attribute__((always_inline)) {
+      constexpr int gap = NMMA / N;
+      if (i % gap == 0 && i / gap < N) f(i / gap);
+    };
+  };
+  // one K-step out of stage `st`: m0 / m1 issue loads in the M clusters
+  // after the LDS reads, c0 / c1 are hooks run between the MFMAs of the C
+  // clusters; the M clusters then wait until at most W0 / W1 of this wave's
+  // loads are outstanding (no wait for -1)
+  auto step = [&](const Stage& st, auto&& m0, auto&& c0, auto&& m1, auto&& c1, auto w0c, auto w1c)
+      __attribute__((always_inline)) {
     constexpr int W0 = decltype(w0c)::value, W1 = decltype(w1c)::value;
     Ops0 o0 = read0(st);
-    loads0();
+    m0();
     fin0(o0);
     if constexpr (W0 >= 0) wait_vmcnt<W0>();
     sync();
-    mma(0, o0.a, o0);
+    mma(0, o0.a, o0, c0);
     pin_acc();
     sync();
     Ops1 o1 = read1(st);
-    loads1();
+    m1();
     fin1(o1);
     if constexpr (W1 >= 0) wait_vmcnt<W1>();
     sync();
-    mma(2, o1.a, o0);
+    mma(2, o1.a, o0, c1);
     pin_acc();
     sync();
   };
@@ -893,49 +916,62 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       sync();
       if (wm) sync();
       if constexpr (FAST) {
-        step(st0, [&]() __attribute__((always_inline)) { issue(src, 1, st1); }, NoWait{},
-             [&]() __attribute__((always_inline)) { issue_early(src, 2, st0); }, WaitStage{});
-        step(st1, [&]() __attribute__((always_inline)) { issue_late(src, 2, st0); }, WaitStage{},
-             [&]() __attribute__((always_inline)) { issue_early(src, 3, st1); }, WaitStage{});
+        // stage s+2: early first part in M1(s), B in C1(s), late set in C0(s+1)
+        using I2 = std::integral_constant<int, N_LATE>;
+        using I4 = std::integral_constant<int, N_EB>;
+        step(st0, [&]() __attribute__((always_inline)) { issue(src, 1, st1); }, no_hook,
+             [&]() __attribute__((always_inline)) { issue_ea(src, 2, st0); },
+             spread(I4{}, [&](int j) __attribute__((always_inline)) { issue_eb(src, 2, st0, j); }), NoWait{}, WaitM1{});
+        step(st1, no_loads, spread(I2{}, [&](int j) __attribute__((always_inline)) { issue_l(src, 2, st0, j); }),
+             [&]() __attribute__((always_inline)) { issue_ea(src, 3, st1); },
+             spread(I4{}, [&](int j) __attribute__((always_inline)) { issue_eb(src, 3, st1, j); }), WaitM0{}, WaitM1{});
         for (int ks = 2; ks < nks - 2; ks += 2) {
-          step(st0, [&]() __attribute__((always_inline)) { issue_late(src, ks + 1, st1); }, WaitStage{},
-               [&]() __attribute__((always_inline)) { issue_early(src, ks + 2, st0); }, WaitStage{});
-          step(st1, [&]() __attribute__((always_inline)) { issue_late(src, ks + 2, st0); }, WaitStage{},
-               [&]() __attribute__((always_inline)) { issue_early(src, ks + 3, st1); }, WaitStage{});
+          step(st0, no_loads, spread(I2{}, [&](int j) __attribute__((always_inline)) { issue_l(src, ks + 1, st1, j); }),
+               [&]() __attribute__((always_inline)) { issue_ea(src, ks + 2, st0); },
+               spread(I4{}, [&](int j) __attribute__((always_inline)) { issue_eb(src, ks + 2, st0, j); }), WaitM0{},
+               WaitM1{});
+          step(st1, no_loads, spread(I2{}, [&](int j) __attribute__((always_inline)) { issue_l(src, ks + 2, st0, j); }),
+               [&]() __attribute__((always_inline)) { issue_ea(src, ks + 3, st1); },
+               spread(I4{}, [&](int j) __attribute__((always_inline)) { issue_eb(src, ks + 3, st1, j); }), WaitM0{},
+               WaitM1{});
         }
         const EpiIn ein = epi_in(cur);
-        step(st0, [&]() __attribute__((always_inline)) { issue_late(src, nks - 1, st1); }, WaitStage{},
+        step(st0, no_loads, spread(I2{}, [&](int j) __attribute__((always_inline)) { issue_l(src, nks - 1, st1, j); }),
              [&]() __attribute__((always_inline)) {
                src = make_src(nxt);
-               issue_early(src, 0, st0);
+               issue_ea(src, 0, st0);
              },
-             WaitStage{});
-        step(st1, [&]() __attribute__((always_inline)) {
-               load_prob(cur);
-               issue_late(src, 0, st0);
-             },
-             std::integral_constant<int, VMW + 2>{}, no_loads, NoWait{});
+             spread(I4{}, [&](int j) __attribute__((always_inline)) { issue_eb(src, 0, st0, j); }), WaitM0{}, WaitM1{});
+        step(st1, no_loads,
+             spread(I2{}, [&](int j) __attribute__((always_inline)) {
+               if (j == 0) load_prob(cur);
+               issue_l(src, 0, st0, j);
+             }),
+             no_loads, no_hook, WaitM0{}, NoWait{});
         if (!wm) sync();
         wait_vmcnt<N_LATE>();      // prob (issued before the next tile's late set)
         epilogue(cur, ein);
       } else {
         int ks = 0;
         for (; ks + 2 < nks; ks += 2) {
-          step(st0, [&]() __attribute__((always_inline)) { issue(src, ks + 1, st1); }, NoWait{}, no_loads, WaitAll{});
-          step(st1, [&]() __attribute__((always_inline)) { issue(src, ks + 2, st0); }, NoWait{}, no_loads, WaitAll{});
+          step(st0, [&]() __attribute__((always_inline)) { issue(src, ks + 1, st1); }, no_hook, no_loads, no_hook,
+               NoWait{}, WaitAll{});
+          step(st1, [&]() __attribute__((always_inline)) { issue(src, ks + 2, st0); }, no_hook, no_loads, no_hook,
+               NoWait{}, WaitAll{});
         }
         const EpiIn ein = epi_in(cur);
         if (nks - ks == 2) {
-          step(st0, [&]() __attribute__((always_inline)) { issue(src, ks + 1, st1); }, NoWait{}, no_loads, WaitAll{});
-          step(st1, no_loads, NoWait{}, no_loads, NoWait{});
+          step(st0, [&]() __attribute__((always_inline)) { issue(src, ks + 1, st1); }, no_hook, no_loads, no_hook,
+               NoWait{}, WaitAll{});
+          step(st1, no_loads, no_hook, no_loads, no_hook, NoWait{}, NoWait{});
         } else {
-          step(st0, no_loads, NoWait{}, no_loads, NoWait{});
+          step(st0, no_loads, no_hook, no_loads, no_hook, NoWait{}, NoWait{});
         }
         if (!wm) sync();
         src = make_src(nxt);
         load_prob(cur);
         issue(src, 0, st0);
-        wait_vmcnt<VMW>();         // prob (issued before the next tile's first stage)
+        wait_vmcnt<N_EARLY + N_LATE>();   // prob (issued before the next tile's first stage)
         epilogue(cur, ein);
       }
       if (!has_next) break;
