@@ -865,7 +865,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   // hook issuing N loads spread evenly over a C cluster's MFMAs
   auto spread = [&](auto nc, auto&& f) __attribute__((always_inline)) {
     constexpr int N = decltype(nc)::value;
-    return [&f](int i) __attribute__((always_inline)) {
+    return [f](int i) __attribute__((always_inline)) {
       constexpr int gap = NMMA / N;
       if (i % gap == 0 && i / gap < N) f(i / gap);
     };
@@ -903,8 +903,37 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
   };
 
-  auto run = [&](auto fast_c) __attribute__((always_inline)) {
-    constexpr bool FAST = decltype(fast_c)::value;
+  // Stage s+2 is loaded during step s: its early first part in M1(s), its
+  // B rows in C1(s), its late set in C0(s+1).  Hooks and waits of a
+  // steady-state pair of steps (s even in buffer 0, s+1 in buffer 1):
+  using I2 = std::integral_constant<int, N_LATE>;
+  using I4 = std::integral_constant<int, N_EB>;
+  auto lhook = [&](int ks, Stage d) __attribute__((always_inline)) {
+    return spread(I2{}, [&, ks, d](int j) __attribute__((always_inline)) { issue_l(src, ks, d, j); });
+  };
+  auto ehook = [&](int ks, Stage d) __attribute__((always_inline)) {
+    return spread(I4{}, [&, ks, d](int j) __attribute__((always_inline)) { issue_eb(src, ks, d, j); });
+  };
+  // steps 0 and 1 of a tile (stage 0 resident): stage 1 whole in M0(0)
+  auto first_pair = [&]() __attribute__((always_inline)) {
+    step(st0, [&]() __attribute__((always_inline)) { issue(src, 1, st1); }, no_hook,
+         [&]() __attribute__((always_inline)) { issue_ea(src, 2, st0); }, ehook(2, st0), NoWait{}, WaitM1{});
+    step(st1, no_loads, lhook(2, st0), [&]() __attribute__((always_inline)) { issue_ea(src, 3, st1); }, ehook(3, st1),
+         WaitM0{}, WaitM1{});
+  };
+  // steps ks (buffer 0) and ks+1 (buffer 1), loading stages up to ks+3
+  auto mid_pair = [&](int ks) __attribute__((always_inline)) {
+    step(st0, no_loads, lhook(ks + 1, st1), [&]() __attribute__((always_inline)) { issue_ea(src, ks + 2, st0); },
+         ehook(ks + 2, st0), WaitM0{}, WaitM1{});
+    step(st1, no_loads, lhook(ks + 2, st0), [&]() __attribute__((always_inline)) { issue_ea(src, ks + 3, st1); },
+         ehook(ks + 3, st1), WaitM0{}, WaitM1{});
+  };
+
+  // MODE 0: even step counts >= 4, the next tile's first stage loaded
+  // during the last two steps; MODE 1: odd step counts >= 3 and MODE 2: one
+  // or two steps, the next tile's first stage loaded during the epilogue.
+  auto run = [&](auto mode_c) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_c)::value;
     while (true) {
       zero_acc();
       const int t_next = t + nwg;
@@ -915,33 +944,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       wait_vmcnt<0>();
       sync();
       if (wm) sync();
-      if constexpr (FAST) {
-        // stage s+2: early first part in M1(s), B in C1(s), late set in C0(s+1)
-        using I2 = std::integral_constant<int, N_LATE>;
-        using I4 = std::integral_constant<int, N_EB>;
-        step(st0, [&]() __attribute__((always_inline)) { issue(src, 1, st1); }, no_hook,
-             [&]() __attribute__((always_inline)) { issue_ea(src, 2, st0); },
-             spread(I4{}, [&](int j) __attribute__((always_inline)) { issue_eb(src, 2, st0, j); }), NoWait{}, WaitM1{});
-        step(st1, no_loads, spread(I2{}, [&](int j) __attribute__((always_inline)) { issue_l(src, 2, st0, j); }),
-             [&]() __attribute__((always_inline)) { issue_ea(src, 3, st1); },
-             spread(I4{}, [&](int j) __attribute__((always_inline)) { issue_eb(src, 3, st1, j); }), WaitM0{}, WaitM1{});
-        for (int ks = 2; ks < nks - 2; ks += 2) {
-          step(st0, no_loads, spread(I2{}, [&](int j) __attribute__((always_inline)) { issue_l(src, ks + 1, st1, j); }),
-               [&]() __attribute__((always_inline)) { issue_ea(src, ks + 2, st0); },
-               spread(I4{}, [&](int j) __attribute__((always_inline)) { issue_eb(src, ks + 2, st0, j); }), WaitM0{},
-               WaitM1{});
-          step(st1, no_loads, spread(I2{}, [&](int j) __attribute__((always_inline)) { issue_l(src, ks + 2, st0, j); }),
-               [&]() __attribute__((always_inline)) { issue_ea(src, ks + 3, st1); },
-               spread(I4{}, [&](int j) __attribute__((always_inline)) { issue_eb(src, ks + 3, st1, j); }), WaitM0{},
-               WaitM1{});
-        }
+      if constexpr (MODE == 0) {
+        first_pair();
+        for (int ks = 2; ks < nks - 2; ks += 2) mid_pair(ks);
         const EpiIn ein = epi_in(cur);
-        step(st0, no_loads, spread(I2{}, [&](int j) __attribute__((always_inline)) { issue_l(src, nks - 1, st1, j); }),
+        step(st0, no_loads, lhook(nks - 1, st1),
              [&]() __attribute__((always_inline)) {
                src = make_src(nxt);
                issue_ea(src, 0, st0);
              },
-             spread(I4{}, [&](int j) __attribute__((always_inline)) { issue_eb(src, 0, st0, j); }), WaitM0{}, WaitM1{});
+             ehook(0, st0), WaitM0{}, WaitM1{});
         step(st1, no_loads,
              spread(I2{}, [&](int j) __attribute__((always_inline)) {
                if (j == 0) load_prob(cur);
@@ -952,21 +964,32 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         wait_vmcnt<N_LATE>();      // prob (issued before the next tile's late set)
         epilogue(cur, ein);
       } else {
-        int ks = 0;
-        for (; ks + 2 < nks; ks += 2) {
-          step(st0, [&]() __attribute__((always_inline)) { issue(src, ks + 1, st1); }, no_hook, no_loads, no_hook,
-               NoWait{}, WaitAll{});
-          step(st1, [&]() __attribute__((always_inline)) { issue(src, ks + 2, st0); }, no_hook, no_loads, no_hook,
-               NoWait{}, WaitAll{});
+        if constexpr (MODE == 1) {
+          // steps 0 .. nks-4 in pairs, then nks-3 (buffer 0), nks-2 (buffer 1)
+          // and nks-1 (buffer 0), which load nothing beyond stage nks-1
+          if (nks > 3) first_pair();
+          for (int ks = 2; ks < nks - 3; ks += 2) mid_pair(ks);
+          if (nks > 3) {
+            step(st0, no_loads, lhook(nks - 2, st1),
+                 [&]() __attribute__((always_inline)) { issue_ea(src, nks - 1, st0); }, ehook(nks - 1, st0), WaitM0{},
+                 WaitM1{});
+          } else {
+            step(st0, [&]() __attribute__((always_inline)) { issue(src, 1, st1); }, no_hook,
+                 [&]() __attribute__((always_inline)) { issue_ea(src, 2, st0); }, ehook(2, st0), NoWait{}, WaitM1{});
+          }
+          step(st1, no_loads, lhook(nks - 1, st0), no_loads, no_hook, WaitM0{},
+               std::integral_constant<int, N_LATE>{});
+          step(st0, no_loads, no_hook, no_loads, no_hook, WaitAll{}, NoWait{});
+        } else {
+          if (nks == 2) {
+            step(st0, [&]() __attribute__((always_inline)) { issue(src, 1, st1); }, no_hook, no_loads, no_hook,
+                 NoWait{}, WaitAll{});
+            step(st1, no_loads, no_hook, no_loads, no_hook, NoWait{}, NoWait{});
+          } else {
+            step(st0, no_loads, no_hook, no_loads, no_hook, NoWait{}, NoWait{});
+          }
         }
         const EpiIn ein = epi_in(cur);
-        if (nks - ks == 2) {
-          step(st0, [&]() __attribute__((always_inline)) { issue(src, ks + 1, st1); }, no_hook, no_loads, no_hook,
-               NoWait{}, WaitAll{});
-          step(st1, no_loads, no_hook, no_loads, no_hook, NoWait{}, NoWait{});
-        } else {
-          step(st0, no_loads, no_hook, no_loads, no_hook, NoWait{}, NoWait{});
-        }
         if (!wm) sync();
         src = make_src(nxt);
         load_prob(cur);
@@ -979,7 +1002,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       cur = nxt;
     }
   };
-  if ((nks & 1) == 0 && nks >= 4) run(std::true_type{}); else run(std::false_type{});
+  if ((nks & 1) == 0 && nks >= 4) run(std::integral_constant<int, 0>{});
+  else if (nks >= 3) run(std::integral_constant<int, 1>{});
+  else run(std::integral_constant<int, 2>{});
   // no direct-to-LDS write may still be in flight when the workgroup ends
   wait_vmcnt<0>();
 }
