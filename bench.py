@@ -112,7 +112,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fc1_swiglu_l64")
-    ap.add_argument("--also", default="fc1_swiglu_l8", help="comma list of extra workloads to time")
+    ap.add_argument("--also", default="fc1_swiglu_l8,fc1_swiglu_l64:discrete",
+                    help="comma list of extra workloads to time; a ':discrete' suffix passes the expert "
+                         "weights as per-expert allocations (b_ptrs / sfb_ptrs)")
     ap.add_argument("--cpu-rows", type=int, default=40960, help="rows of the oracle CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", action="store_true", help="also time launches after an L2/MALL flush")
@@ -145,11 +147,21 @@ def main():
         from moe_grouped_block_amd import build
         build.build()
     def measure(name, steps, warmup, cold):
-        case = synth.make_case(name)
+        base, _, mode = name.partition(":")
+        case = synth.make_case(base)
         p = case.problem
         dev = pl.to_device(case.arrays)
         outs = pl.empty_outputs(p)
-        tensors = {**pl.inputs_for(p, dev), **outs}
+        keep = None
+        if mode == "discrete":
+            ptrs, keep = pl.discrete_weights(p, case.arrays, seed=case.seed)
+            del dev["b"]
+            dev.pop("sfb", None)
+            tensors = {**pl.inputs_for(p, dev, discrete=ptrs), **outs}
+        elif mode:
+            raise SystemExit(f"unknown workload mode {mode!r}")
+        else:
+            tensors = {**pl.inputs_for(p, dev), **outs}
         stream = torch.cuda.current_stream()
         prob_s, args_s = mg.make_problem(p), mg.make_args(tensors)
         handle = stream.cuda_stream
@@ -186,7 +198,7 @@ def main():
                 tot += a0.elapsed_time(a1)
             res["cold_ms"] = tot / 10
             del flush
-        del dev, outs, tensors
+        del dev, outs, tensors, keep
         torch.cuda.empty_cache()
         return res
 

@@ -33,6 +33,13 @@
  *           of every row, so the scales a row tile needs for one K-step are
  *           contiguous.  (The logical view is the pages' (valid_m, K/32).)
  *   SFB     the same for the rows of B: (K/128, L*N, 4), row index g*N + n
+ *   Discrete weights (the pages' b_ptrs / sfb_ptrs mode, "Grouped GEMM +
+ *   sReLU (SM100)", §Discrete-weight wrapper): instead of B and SFB the
+ *   caller passes device arrays of L device pointers; b_ptrs[g] points to
+ *   expert g's (N, K) weights in B's encoding and sfb_ptrs[g] (MX only) to
+ *   its scales as (K/128, N, 4) word planes.  Each pointer must be 16-byte
+ *   aligned (the kernel ignores its low 4 bits); entries of experts with no
+ *   rows are never read.
  *   padded_offsets (L) int32, cumulative group ends; padded_offsets[L-1] ==
  *                          valid_m; every entry a multiple of m_aligned and
  *                          nondecreasing (empty groups repeat the previous end)
@@ -67,7 +74,7 @@
 extern "C" {
 #endif
 
-#define MOEGG_ABI_VERSION 2
+#define MOEGG_ABI_VERSION 3
 
 typedef enum moegg_status {
   MOEGG_OK = 0,
@@ -127,6 +134,8 @@ typedef struct moegg_args {
   uint8_t* sfd_col;              /* E4M3 only */
   float* amax;                   /* BF16 D (forward) only */
   float* dprob;                  /* dSwiGLU only, caller-zeroed */
+  const void* const* b_ptrs;     /* discrete weights instead of b: (L) device array, 8-byte aligned */
+  const uint8_t* const* sfb_ptrs;/* discrete weights, MX only, instead of sfb: (L) device array */
 } moegg_args;
 
 /* Validate problem + pointers on the host.  No HIP call.  MOEGG_OK if

@@ -32,7 +32,7 @@ STATUS = {0: "MOEGG_OK", 1: "MOEGG_ERROR_INVALID_VALUE", 2: "MOEGG_ERROR_MISALIG
           3: "MOEGG_ERROR_NOT_SUPPORTED", 4: "MOEGG_ERROR_LAUNCH"}
 
 ARG_FIELDS = ("a", "b", "sfa", "sfb", "padded_offsets", "alpha", "prob", "beta", "norm_const",
-              "c_in", "c", "d", "d_col", "sfd_row", "sfd_col", "amax", "dprob")
+              "c_in", "c", "d", "d_col", "sfd_row", "sfd_col", "amax", "dprob", "b_ptrs", "sfb_ptrs")
 
 
 class moegg_problem(ctypes.Structure):

@@ -101,11 +101,20 @@ moegg_status check_impl(const moegg_problem* pp, const moegg_args* ap) {
     return fail(MOEGG_ERROR_INVALID_VALUE, "E4M3 D needs N_out %% 32 == 0 (row blocks), N_out=%lld", (long long)n_out);
 
   // --- presence ---------------------------------------------------------------
-  if (!a.a || !a.b || !a.padded_offsets || !a.alpha || !a.d)
-    return fail(MOEGG_ERROR_INVALID_VALUE, "a, b, padded_offsets, alpha and d are required");
+  if (!a.a || !a.padded_offsets || !a.alpha || !a.d)
+    return fail(MOEGG_ERROR_INVALID_VALUE, "a, padded_offsets, alpha and d are required");
+  if ((a.b != nullptr) == (a.b_ptrs != nullptr))
+    return fail(MOEGG_ERROR_INVALID_VALUE, "exactly one of b (dense weights) and b_ptrs (discrete) is required");
   if (!a.prob) return fail(MOEGG_ERROR_INVALID_VALUE, "prob is required (pass ones for no gating)");
-  if (mx && (!a.sfa || !a.sfb)) return fail(MOEGG_ERROR_INVALID_VALUE, "MX operands need sfa and sfb");
-  if (!mx && (a.sfa || a.sfb)) return fail(MOEGG_ERROR_INVALID_VALUE, "BF16 operands take no sfa/sfb");
+  if (a.b) {
+    if (a.sfb_ptrs) return fail(MOEGG_ERROR_INVALID_VALUE, "sfb_ptrs is for discrete weights (b_ptrs) only");
+    if (mx && (!a.sfa || !a.sfb)) return fail(MOEGG_ERROR_INVALID_VALUE, "MX operands need sfa and sfb");
+    if (!mx && (a.sfa || a.sfb)) return fail(MOEGG_ERROR_INVALID_VALUE, "BF16 operands take no sfa/sfb");
+  } else {
+    if (a.sfb) return fail(MOEGG_ERROR_INVALID_VALUE, "discrete weights take sfb_ptrs, not sfb");
+    if (mx && (!a.sfa || !a.sfb_ptrs)) return fail(MOEGG_ERROR_INVALID_VALUE, "MX operands need sfa and sfb_ptrs");
+    if (!mx && (a.sfa || a.sfb_ptrs)) return fail(MOEGG_ERROR_INVALID_VALUE, "BF16 operands take no sfa/sfb_ptrs");
+  }
   if (p.c_dtype == MOEGG_DT_BF16 && !a.c) return fail(MOEGG_ERROR_INVALID_VALUE, "c_dtype BF16 needs c");
   if (p.c_dtype == MOEGG_DT_NONE && a.c) return fail(MOEGG_ERROR_INVALID_VALUE, "c given but c_dtype NONE");
   const int nq = (a.sfd_row != nullptr) + (a.sfd_col != nullptr) + (a.norm_const != nullptr);
@@ -134,6 +143,9 @@ moegg_status check_impl(const moegg_problem* pp, const moegg_args* ap) {
   const void* small[] = {a.padded_offsets, a.alpha, a.prob, a.beta, a.norm_const, a.amax, a.dprob};
   for (const void* q : small)
     if (q && !aligned(q, 4)) return fail(MOEGG_ERROR_MISALIGNED, "vector pointer %p not 4-byte aligned", q);
+  const void* ptr_arrays[] = {a.b_ptrs, a.sfb_ptrs};
+  for (const void* q : ptr_arrays)
+    if (q && !aligned(q, 8)) return fail(MOEGG_ERROR_MISALIGNED, "pointer array %p not 8-byte aligned", q);
   return MOEGG_OK;
 }
 
@@ -166,6 +178,9 @@ moegg_status moegg_run(const moegg_problem* problem, const moegg_args* args, voi
   k.b = static_cast<const uint8_t*>(a.b);
   k.sfa = a.sfa;
   k.sfb = a.sfb;
+  k.b_ptrs = reinterpret_cast<const uint8_t* const*>(a.b_ptrs);
+  k.sfb_ptrs = a.sfb_ptrs;
+  k.sfb_rows = a.b_ptrs ? p.n : static_cast<int64_t>(p.num_groups) * p.n;
   k.po = a.padded_offsets;
   k.alpha = a.alpha;
   k.prob = a.prob;

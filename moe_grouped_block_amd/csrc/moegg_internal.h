@@ -28,6 +28,9 @@ struct KernelArgs {
   const uint8_t* b;        // (L, n, row_bytes)
   const uint8_t* sfa;      // (K/128, valid_m, 4): 32-bit word planes
   const uint8_t* sfb;      // (K/128, L*n, 4)
+  const uint8_t* const* b_ptrs;     // discrete weights: (L) per-expert (n, row_bytes), or null
+  const uint8_t* const* sfb_ptrs;   // discrete weights: (L) per-expert (K/128, n, 4), or null
+  int64_t sfb_rows;                 // rows of one SFB word plane: L*n dense, n discrete
   const int32_t* po;       // (L)
   const float* alpha;      // (L)
   const float* prob;       // (valid_m)

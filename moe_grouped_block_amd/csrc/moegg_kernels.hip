@@ -427,7 +427,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
     const int lrow = lid >> 3;
     Src s;
     s.a = p.a + static_cast<int64_t>(tl.row0) * p.row_bytes;
-    s.b = p.b + (static_cast<int64_t>(tl.g) * p.n + tl.n0) * p.row_bytes;
+    // dense weights: expert g's rows follow the previous experts'; discrete
+    // weights: its own allocation (low 4 bits cleared: 16-byte aligned loads)
+    const uint8_t* bg = p.b_ptrs ? reinterpret_cast<const uint8_t*>(
+                                       reinterpret_cast<uintptr_t>(p.b_ptrs[tl.g]) & ~uintptr_t{15})
+                                 : p.b + static_cast<int64_t>(tl.g) * p.n * p.row_bytes;
+    s.b = bg + static_cast<int64_t>(tl.n0) * p.row_bytes;
     const int alast = max(min(tl.rows, vm - tl.row0), 1) - 1;   // last loadable row of the tile
     const int blast = p.n - 1 - tl.n0;
 #pragma unroll
@@ -451,10 +456,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         const int jj = isA ? job : job - S_HALF;
         const int word = jj >> 2, rowsel = (jj & 3) * 64 + lid;
         // word planes: word j of row r at 4 * (j * rows + r) (rows = valid_m for
-        // SFA, L * N for SFB); step ks uses planes SW*ks .. SW*ks + SW-1
+        // SFA, sfb_rows for SFB: L * N dense with row g * N + n, N discrete);
+        // step ks uses planes SW*ks .. SW*ks + SW-1
+        const uint8_t* sg = p.sfb_ptrs ? reinterpret_cast<const uint8_t*>(
+                                             reinterpret_cast<uintptr_t>(p.sfb_ptrs[tl.g]) & ~uintptr_t{15})
+                                       : p.sfb + static_cast<int64_t>(tl.g) * p.n * 4;
         s.s[u] = isA ? p.sfa + (static_cast<int64_t>(word) * vm + tl.row0 + min(rowsel, alast)) * 4
-                     : p.sfb + (static_cast<int64_t>(word) * p.num_groups * p.n +
-                                static_cast<int64_t>(tl.g) * p.n + tl.n0 + min(rowsel, blast)) * 4;
+                     : sg + (static_cast<int64_t>(word) * p.sfb_rows + tl.n0 + min(rowsel, blast)) * 4;
       }
     }
     return s;
@@ -483,7 +491,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         const bool isA = job < S_HALF;
         const int jj = isA ? job : job - S_HALF;
         uint32_t* dst = (isA ? d.sa : d.sb) + (jj >> 2) * (isA ? BM : BN) + (jj & 3) * 64;
-        const int64_t plane = isA ? static_cast<int64_t>(vm) * 4 : static_cast<int64_t>(p.num_groups) * p.n * 4;
+        const int64_t plane = isA ? static_cast<int64_t>(vm) * 4 : p.sfb_rows * 4;
         dma4(s.s[u] + static_cast<int64_t>(ks) * SW * plane, dst);
       }
     }

@@ -38,6 +38,38 @@ def to_device(arrays: dict, device="cuda") -> dict:
     return out
 
 
+def discrete_weights(problem: dict, arrays: dict, device="cuda", seed: int = 0, null_empty=None):
+    """Per-expert allocations for the discrete-weight mode.
+
+    Expert g's weights (N, row units) and, for MX operands, its scales as
+    (K/128, N, 4) word planes get allocations of their own, made in a
+    shuffled expert order with spacers between them, so their addresses are
+    neither contiguous nor ascending.  Returns (pointer tensors {"b_ptrs",
+    "sfb_ptrs"}, list of tensors to keep alive).  Experts listed in
+    `null_empty` get a null pointer (allowed for experts without rows)."""
+    L = int(problem["num_groups"])
+    mx = problem["ab_dtype"] != "bf16"
+    order = np.random.default_rng(seed).permutation(L)
+    null_empty = set(null_empty or ())
+    keep, bptr, sptr = [], [0] * L, [0] * L
+    for g in order:
+        keep.append(torch.empty(4096 + 256 * int(g), dtype=torch.uint8, device=device))   # spacer
+        if g in null_empty:
+            continue
+        b = np.ascontiguousarray(arrays["b"][g])
+        tb = torch.from_numpy(b.view(np.int16) if b.dtype == np.uint16 else b).to(device)
+        keep.append(tb)
+        bptr[g] = tb.data_ptr()
+        if mx:
+            ts = torch.from_numpy(scale_planes(arrays["sfb"][g])).to(device)
+            keep.append(ts)
+            sptr[g] = ts.data_ptr()
+    ptrs = {"b_ptrs": torch.tensor(bptr, dtype=torch.int64, device=device)}
+    if mx:
+        ptrs["sfb_ptrs"] = torch.tensor(sptr, dtype=torch.int64, device=device)
+    return ptrs, keep
+
+
 def n_out(problem: dict) -> int:
     n = int(problem["n"])
     return {"none": n, "srelu": n, "swiglu": n // 2, "dswiglu": 2 * n}[problem["act"]]
@@ -73,11 +105,16 @@ def empty_outputs(problem: dict, device="cuda", fill: int | None = None) -> dict
     return out
 
 
-def inputs_for(problem: dict, dev_arrays: dict) -> dict:
-    """Select the input tensors the problem uses from an uploaded case."""
+def inputs_for(problem: dict, dev_arrays: dict, discrete: dict | None = None) -> dict:
+    """Select the input tensors the problem uses from an uploaded case;
+    `discrete` (pointer tensors from discrete_weights) replaces b and sfb."""
     keys = ["a", "b", "padded_offsets", "alpha", "prob"]
     if problem["ab_dtype"] != "bf16":
         keys += ["sfa", "sfb"]
+    if discrete is not None:
+        keys = [k for k in keys if k not in ("b", "sfb")]
+        return {**{k: dev_arrays[k] for k in keys + [k for k in ("norm_const",) if problem["d_dtype"] == "e4m3"]
+                   + (["beta", "c_in"] if problem["act"] == "dswiglu" else [])}, **discrete}
     if problem["d_dtype"] == "e4m3":
         keys += ["norm_const"]
     if problem["act"] == "dswiglu":

@@ -42,7 +42,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_strings():
-    assert mg.moegg_abi_version() == 2
+    assert mg.moegg_abi_version() == 3
     for code, name in mg.STATUS.items():
         assert mg.moegg_status_string(code) == name
     assert mg.moegg_status_string(99) == "MOEGG_UNKNOWN_STATUS"
@@ -52,7 +52,8 @@ def test_struct_layout_matches_header():
     # problem: 2 x int32, int64, 6 x int32, float -> 44 bytes, padded to 48
     assert ctypes.sizeof(mg.moegg_problem) == 48
     assert mg.moegg_problem.valid_m.offset == 8
-    assert ctypes.sizeof(mg.moegg_args) == 17 * 8
+    assert ctypes.sizeof(mg.moegg_args) == 19 * 8
+    assert mg.moegg_args.b_ptrs.offset == 17 * 8 and mg.moegg_args.sfb_ptrs.offset == 18 * 8
 
 
 FAKE = 0x7F0000000000            # 16-byte aligned, never dereferenced by moegg_check
@@ -94,7 +95,7 @@ def test_valid_configs_pass(kind):
     assert _status(p, t) == 0, mg.moegg_last_error()
 
 
-INVALID, MISALIGNED, NOT_SUPPORTED = 1, 2, 3
+OK, INVALID, MISALIGNED, NOT_SUPPORTED = 0, 1, 2, 3
 
 CASES = [
     # (base, problem overrides, tensor overrides, expected status)
@@ -135,6 +136,16 @@ CASES = [
     ("gating_bf16", {}, dict(beta=FAKE), INVALID),                     # dSwiGLU-only input
     ("gating_bf16", dict(ab_dtype="bf16"), {}, INVALID),               # sfa/sfb with BF16 operands
     ("gating_bf16", dict(valid_m=2 ** 31), {}, NOT_SUPPORTED),
+    # discrete weights (b_ptrs / sfb_ptrs instead of b / sfb)
+    ("gating_bf16", {}, dict(b=None, sfb=None, b_ptrs=FAKE + 0x20000, sfb_ptrs=FAKE + 0x21000), OK),
+    ("dswiglu", {}, dict(b=None, b_ptrs=FAKE + 0x20000), OK),
+    ("gating_bf16", {}, dict(b_ptrs=FAKE + 0x20000), INVALID),               # both b and b_ptrs
+    ("gating_bf16", {}, dict(b=None), INVALID),                              # neither
+    ("gating_bf16", {}, dict(b=None, b_ptrs=FAKE + 0x20000), INVALID),       # dense sfb with b_ptrs
+    ("gating_bf16", {}, dict(b=None, sfb=None, b_ptrs=FAKE + 0x20000), INVALID),   # MX without sfb_ptrs
+    ("gating_bf16", {}, dict(sfb_ptrs=FAKE + 0x21000), INVALID),             # sfb_ptrs with dense b
+    ("dswiglu", {}, dict(b=None, b_ptrs=FAKE + 0x20000, sfb_ptrs=FAKE + 0x21000), INVALID),   # BF16 + sfb_ptrs
+    ("gating_bf16", {}, dict(b=None, sfb=None, b_ptrs=FAKE + 0x20004, sfb_ptrs=FAKE + 0x21000), MISALIGNED),
 ]
 
 
@@ -146,7 +157,8 @@ def test_validation_rules(base, pov, tov, expect):
     t = {k: v for k, v in t.items() if v is not None}
     st = _status(p, t)
     assert st == expect, (st, mg.moegg_last_error())
-    assert mg.moegg_last_error() != ""
+    if expect != OK:
+        assert mg.moegg_last_error() != ""
 
 
 def test_run_rejects_before_any_hip_call():
