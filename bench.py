@@ -112,7 +112,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fc1_swiglu_l64")
-    ap.add_argument("--also", default="fc1_swiglu_l8,fc1_swiglu_l64:discrete",
+    ap.add_argument("--also", default="fc1_swiglu_l8,fc1_swiglu_l64:discrete,dswiglu_mxfp8_l64",
                     help="comma list of extra workloads to time; a ':discrete' suffix passes the expert "
                          "weights as per-expert allocations (b_ptrs / sfb_ptrs)")
     ap.add_argument("--cpu-rows", type=int, default=40960, help="rows of the oracle CPU sample")

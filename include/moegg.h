@@ -48,7 +48,11 @@
  *   D, D_col (valid_m, N_out) BF16 or E4M3 codes   N_out = N/2 for SwiGLU,
  *                                                  2N for dSwiGLU, else N
  *   SFD_row (valid_m, N_out/32) E8M0; SFD_col (N_out, valid_m/32) E8M0
- *   amax    (L) fp32, written by the call (zero-filled first)
+ *   amax    (L) fp32, written by the call (zero-filled first); for dSwiGLU
+ *           with MX operands and a BF16 dC, (L, 2): max |d_input| and max
+ *           |d_gate| over the group's rows (the block-scaled dGLU contract's
+ *           amax of shape (L, 2, 1); which quantity each entry holds is this
+ *           library's reading)
  *   C_in    (valid_m, 2N) BF16, saved forward pre-activation [dSwiGLU only]
  *   dprob   (valid_m) fp32, caller-zeroed, accumulated with atomics [dSwiGLU]
  *
@@ -98,7 +102,9 @@ typedef enum moegg_act {
   MOEGG_ACT_SRELU = 2,   /* D = prob * relu(C)^2, optional tanh soft clamp s
                             ("Grouped GEMM + sReLU", §Equations / §Tanh soft clamp)          */
   MOEGG_ACT_DSWIGLU = 3  /* dC = [d_input|d_gate] from R and beta*C_in, dprob += row sums
-                            ("Grouped GEMM + dGLU", BF16 contract, dSwiGLU)                  */
+                            ("Grouped GEMM + dGLU", BF16 contract and block-scaled contract,
+                            dSwiGLU): BF16 operands -> BF16 dC; MX operands -> BF16 dC + amax
+                            (L, 2), or E4M3 dC as D/D_col with SFD_row/SFD_col             */
 } moegg_act;
 
 /* Problem description (host struct). */
@@ -132,7 +138,7 @@ typedef struct moegg_args {
   void* d_col;                   /* E4M3 only */
   uint8_t* sfd_row;              /* E4M3 only */
   uint8_t* sfd_col;              /* E4M3 only */
-  float* amax;                   /* BF16 D (forward) only */
+  float* amax;                   /* BF16 D: (L), or (L, 2) for dSwiGLU with MX operands */
   float* dprob;                  /* dSwiGLU only, caller-zeroed */
   const void* const* b_ptrs;     /* discrete weights instead of b: (L) device array, 8-byte aligned */
   const uint8_t* const* sfb_ptrs;/* discrete weights, MX only, instead of sfb: (L) device array */

@@ -86,9 +86,8 @@ moegg_status check_impl(const moegg_problem* pp, const moegg_args* ap) {
     return fail(MOEGG_ERROR_INVALID_VALUE, "SwiGLU needs n %% 64 == 0 (32-column pairs), n=%d", p.n);
   if (p.act == MOEGG_ACT_DSWIGLU) {
     if (p.n % 32 != 0) return fail(MOEGG_ERROR_INVALID_VALUE, "dSwiGLU needs n %% 32 == 0, n=%d", p.n);
-    if (p.ab_dtype != MOEGG_DT_BF16)
-      return fail(MOEGG_ERROR_NOT_SUPPORTED, "dSwiGLU is built for the BF16 backend only");
-    if (p.d_dtype != MOEGG_DT_BF16) return fail(MOEGG_ERROR_NOT_SUPPORTED, "dSwiGLU output must be BF16");
+    if (!mx && p.d_dtype != MOEGG_DT_BF16)
+      return fail(MOEGG_ERROR_NOT_SUPPORTED, "dSwiGLU with BF16 operands writes a BF16 dC only");
     if (p.c_dtype != MOEGG_DT_NONE) return fail(MOEGG_ERROR_INVALID_VALUE, "dSwiGLU writes no C");
   }
   if (p.n % 32 != 0) return fail(MOEGG_ERROR_NOT_SUPPORTED, "n=%d: this build needs n %% 32 == 0", p.n);
@@ -125,13 +124,13 @@ moegg_status check_impl(const moegg_problem* pp, const moegg_args* ap) {
   } else {
     if (nq != 0 || a.d_col)
       return fail(MOEGG_ERROR_INVALID_VALUE, "d_col/sfd_row/sfd_col/norm_const are for E4M3 D only");
-    if (p.act != MOEGG_ACT_DSWIGLU && !a.amax)
+    if ((p.act != MOEGG_ACT_DSWIGLU || mx) && !a.amax)
       return fail(MOEGG_ERROR_INVALID_VALUE, "BF16 D needs amax");
   }
   if (p.act == MOEGG_ACT_DSWIGLU) {
     if (!a.beta || !a.c_in || !a.dprob)
       return fail(MOEGG_ERROR_INVALID_VALUE, "dSwiGLU needs beta, c_in and dprob");
-    if (a.amax) return fail(MOEGG_ERROR_INVALID_VALUE, "dSwiGLU writes no amax");
+    if (!mx && a.amax) return fail(MOEGG_ERROR_INVALID_VALUE, "dSwiGLU with BF16 operands writes no amax");
   } else if (a.beta || a.c_in || a.dprob) {
     return fail(MOEGG_ERROR_INVALID_VALUE, "beta/c_in/dprob are for dSwiGLU only");
   }
@@ -168,7 +167,9 @@ moegg_status moegg_run(const moegg_problem* problem, const moegg_args* args, voi
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
 
   if (a.amax) {
-    hipError_t e = moegg::launch_fill_zero(a.amax, p.num_groups, stream);
+    // (L) per group, or (L, 2) for dSwiGLU: [d_input blocks, d_gate blocks]
+    const int count = p.act == MOEGG_ACT_DSWIGLU ? 2 * p.num_groups : p.num_groups;
+    hipError_t e = moegg::launch_fill_zero(a.amax, count, stream);
     if (e != hipSuccess) return fail(MOEGG_ERROR_LAUNCH, "amax fill: %s", hipGetErrorString(e));
   }
   if (p.valid_m == 0) return MOEGG_OK;

@@ -216,6 +216,9 @@ __device__ __forceinline__ void store_e4m3_row(uint8_t* dst_row, int hi, const u
 // Returns the E8M0 byte of this lane's column (l % 32) block.
 __device__ __forceinline__ uint32_t quant_tile(const KernelArgs& p, float* T, float* S, int m, int ocol, int hi,
                                                int l32, const float* dn) {
+  // the previous call's cross-lane reads of T and S stay ahead of this
+  // call's writes
+  __builtin_amdgcn_wave_barrier();
   // ---- row block ----
   float ra = 0.0f;
 #pragma unroll
@@ -228,6 +231,10 @@ __device__ __forceinline__ uint32_t quant_tile(const KernelArgs& p, float* T, fl
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     *reinterpret_cast<v4f*>(T + l32 * kTPitch + 8 * j + 4 * hi) = v4f{dn[4 * j], dn[4 * j + 1], dn[4 * j + 2], dn[4 * j + 3]};
+  // lanes read what other lanes of the wave wrote: keep the compiler from
+  // moving LDS accesses across this point (the LDS executes one wave's
+  // accesses in order)
+  __builtin_amdgcn_wave_barrier();
   float cm = 0.0f;
   const float* c0 = T + l32 + (hi ? 24 * kTPitch : 0);      // rows [0, 8) / [24, 32)
   const float* c1 = T + l32 + (hi ? 8 * kTPitch : 0);       // rows [8, 16) / [16, 24) at r + 8
@@ -238,6 +245,7 @@ __device__ __forceinline__ uint32_t quant_tile(const KernelArgs& p, float* T, fl
   cm = halves_max(cm);
   const uint32_t bc = e8m0_ceil(cm * kRcp448);
   if (hi == 0) S[l32] = e8m0_inverse(bc);
+  __builtin_amdgcn_wave_barrier();
   v4f sc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) sc[j] = *reinterpret_cast<const v4f*>(S + 8 * j + 4 * hi);
@@ -279,6 +287,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // [n0, n0 + 256).  rows is 0 (nothing to store), 128 or 256.
 struct Tile {
   int g, row0, rows, n0;
+  const uint8_t* bg;    // expert g's weights (row 0) and SFB words (row 0 of plane 0)
+  const uint8_t* sg;
 };
 
 template <int AB, int ACT, int OUT>
@@ -392,6 +402,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
     tl.row0 = __builtin_amdgcn_readfirstlane(r0);
     tl.rows = __builtin_amdgcn_readfirstlane(static_cast<int>(max(rows, int64_t{0})) & ~127);
     tl.n0 = __builtin_amdgcn_readfirstlane(nt * BN);
+    // dense weights: expert g's rows follow the previous experts'; discrete
+    // weights: its own allocations (low 4 bits cleared: 16-byte aligned
+    // loads).  Resolved here, at tile set-up, so that the operand loads of
+    // the K loop need no branch.
+    if (p.b_ptrs) {
+      tl.bg = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(p.b_ptrs[tl.g]) & ~uintptr_t{15});
+      tl.sg = p.sfb_ptrs ? reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(p.sfb_ptrs[tl.g]) &
+                                                            ~uintptr_t{15})
+                         : nullptr;
+    } else {
+      tl.bg = p.b + static_cast<int64_t>(tl.g) * p.n * p.row_bytes;
+      tl.sg = p.sfb ? p.sfb + static_cast<int64_t>(tl.g) * p.n * 4 : nullptr;
+    }
     return tl;
   };
 
@@ -427,12 +450,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
     const int lrow = lid >> 3;
     Src s;
     s.a = p.a + static_cast<int64_t>(tl.row0) * p.row_bytes;
-    // dense weights: expert g's rows follow the previous experts'; discrete
-    // weights: its own allocation (low 4 bits cleared: 16-byte aligned loads)
-    const uint8_t* bg = p.b_ptrs ? reinterpret_cast<const uint8_t*>(
-                                       reinterpret_cast<uintptr_t>(p.b_ptrs[tl.g]) & ~uintptr_t{15})
-                                 : p.b + static_cast<int64_t>(tl.g) * p.n * p.row_bytes;
-    s.b = bg + static_cast<int64_t>(tl.n0) * p.row_bytes;
+    s.b = tl.bg + static_cast<int64_t>(tl.n0) * p.row_bytes;
     const int alast = max(min(tl.rows, vm - tl.row0), 1) - 1;   // last loadable row of the tile
     const int blast = p.n - 1 - tl.n0;
 #pragma unroll
@@ -458,11 +476,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         // word planes: word j of row r at 4 * (j * rows + r) (rows = valid_m for
         // SFA, sfb_rows for SFB: L * N dense with row g * N + n, N discrete);
         // step ks uses planes SW*ks .. SW*ks + SW-1
-        const uint8_t* sg = p.sfb_ptrs ? reinterpret_cast<const uint8_t*>(
-                                             reinterpret_cast<uintptr_t>(p.sfb_ptrs[tl.g]) & ~uintptr_t{15})
-                                       : p.sfb + static_cast<int64_t>(tl.g) * p.n * 4;
         s.s[u] = isA ? p.sfa + (static_cast<int64_t>(word) * vm + tl.row0 + min(rowsel, alast)) * 4
-                     : sg + (static_cast<int64_t>(word) * p.sfb_rows + tl.n0 + min(rowsel, blast)) * 4;
+                     : tl.sg + (static_cast<int64_t>(word) * p.sfb_rows + tl.n0 + min(rowsel, blast)) * 4;
       }
     }
     return s;
@@ -686,10 +701,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 
     if constexpr (ACT == ACT_DSWIGLU) {
       // R = alpha^2 acc; X = beta * C_in with blocks [input_b | gate_b]
-      // ("Grouped GEMM + dGLU (SM100)", BF16 contract equations)
+      // ("Grouped GEMM + dGLU (SM100)", BF16 contract equations and the
+      // block-scaled contract's Step 2): d_input = R prob swish(gate),
+      // d_gate = R prob input s (1 + gate (1 - s)), dprob += R input swish
       const float a2 = alpha * alpha;
       const float beta = p.beta[g];
       const int ld2 = 2 * p.n;
+      // block-scaled operands with a BF16 output: amax per group of the
+      // d_input blocks and of the d_gate blocks (amax of shape (L, 2))
+      constexpr bool AMAX2 = MX && OUT == OUT_BF16;
+      float amax_in = 0.0f, amax_gt = 0.0f;
+      uint32_t colw_in[TN], colw_gt[TN];      // E4M3: column scale bytes of 4 row blocks
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) colw_in[tn] = colw_gt[tn] = 0;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
         const int m = mbase + tm * 32 + l32;
@@ -698,6 +722,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         for (int tn = 0; tn < TN; ++tn) {
           const int ncol = nbase + tn * 32;
           if (ncol >= p.n) continue;
+          // keep this tile's C_in loads here (hoisting every tile's loads
+          // ahead of the FP8 quantisation would spill)
+          if constexpr (OUT == OUT_E4M3) asm volatile("" ::: "memory");
           const int64_t xoff = static_cast<int64_t>(m) * ld2 + 2 * ncol;   // block b = ncol/32 starts at 64b
           float xin[16], xg[16];
 #pragma unroll
@@ -725,19 +752,59 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             dgt[v] = r * pr[tm] * x * s * (1.0f + gt * (1.0f - s));
             dp += r * x * swish;
           }
+          if constexpr (OUT == OUT_BF16) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            v2u w;
-            w.x = bf16_rne(din[4 * j]) | (bf16_rne(din[4 * j + 1]) << 16);
-            w.y = bf16_rne(din[4 * j + 2]) | (bf16_rne(din[4 * j + 3]) << 16);
-            *reinterpret_cast<v2u*>(p.d + (xoff + 8 * j + 4 * hi) * 2) = w;
-            w.x = bf16_rne(dgt[4 * j]) | (bf16_rne(dgt[4 * j + 1]) << 16);
-            w.y = bf16_rne(dgt[4 * j + 2]) | (bf16_rne(dgt[4 * j + 3]) << 16);
-            *reinterpret_cast<v2u*>(p.d + (xoff + 32 + 8 * j + 4 * hi) * 2) = w;
+            for (int j = 0; j < 4; ++j) {
+              v2u w;
+              w.x = bf16_rne(din[4 * j]) | (bf16_rne(din[4 * j + 1]) << 16);
+              w.y = bf16_rne(din[4 * j + 2]) | (bf16_rne(din[4 * j + 3]) << 16);
+              *reinterpret_cast<v2u*>(p.d + (xoff + 8 * j + 4 * hi) * 2) = w;
+              w.x = bf16_rne(dgt[4 * j]) | (bf16_rne(dgt[4 * j + 1]) << 16);
+              w.y = bf16_rne(dgt[4 * j + 2]) | (bf16_rne(dgt[4 * j + 3]) << 16);
+              *reinterpret_cast<v2u*>(p.d + (xoff + 32 + 8 * j + 4 * hi) * 2) = w;
+            }
+            if constexpr (AMAX2) {
+#pragma unroll
+              for (int v = 0; v < 16; v += 2) {
+                amax_in = max_abs2(amax_in, din[v], din[v + 1]);
+                amax_gt = max_abs2(amax_gt, dgt[v], dgt[v + 1]);
+              }
+            }
+          } else {
+            // FP8 dC: each 32-column output block quantised by rows and
+            // columns like a forward D ("Grouped GEMM + dGLU (SM100)",
+            // block-scaled Step 3)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              din[v] *= nc;
+              dgt[v] *= nc;
+            }
+            colw_in[tn] |= quant_tile(p, sT, sS, m, 2 * ncol, hi, l32, din) << (8 * tm);
+            colw_gt[tn] |= quant_tile(p, sT, sS, m, 2 * ncol + 32, hi, l32, dgt) << (8 * tm);
           }
         }
         dp = halves_sum(dp);
         if (hi == 0) atomicAdd(p.dprob + m, dp);
+      }
+      if constexpr (OUT == OUT_E4M3) {
+        // column l32's scale bytes of the wave's 4 consecutive 32-row blocks
+        const int mblk0 = mbase >> 5;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int ncol = nbase + tn * 32;
+          if (ncol >= p.n || hi != 0) continue;
+          *reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(2 * ncol + l32) * (vm >> 5) + mblk0) =
+              colw_in[tn];
+          *reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(2 * ncol + 32 + l32) * (vm >> 5) + mblk0) =
+              colw_gt[tn];
+        }
+      }
+      if constexpr (AMAX2) {
+        const float wi = wave_max(amax_in), wg = wave_max(amax_gt);
+        if (lane == 0) {
+          atomicMax(reinterpret_cast<unsigned int*>(p.amax + 2 * g), __float_as_uint(wi));
+          atomicMax(reinterpret_cast<unsigned int*>(p.amax + 2 * g + 1), __float_as_uint(wg));
+        }
       }
     } else {
       float amax_l = 0.0f;
@@ -938,8 +1005,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   };
 
   // MODE 0: even step counts >= 4, the next tile's first stage loaded
-  // during the last two steps; MODE 1: odd step counts >= 3 and MODE 2: one
-  // or two steps, the next tile's first stage loaded during the epilogue.
+  // during the last two steps; MODE 1: odd step counts >= 5, MODE 3: three
+  // steps and MODE 2: one or two steps, the next tile's first stage loaded
+  // during the epilogue.  (No mode branches on the step count between
+  // different step bodies: such branches make the register allocator spill.)
   auto run = [&](auto mode_c) __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode_c)::value;
     while (true) {
@@ -972,12 +1041,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         wait_vmcnt<N_LATE>();      // prob (issued before the next tile's late set)
         epilogue(cur, ein);
       } else {
-        if constexpr (MODE == 1) {
+        if constexpr (MODE == 1 || MODE == 3) {
           // steps 0 .. nks-4 in pairs, then nks-3 (buffer 0), nks-2 (buffer 1)
           // and nks-1 (buffer 0), which load nothing beyond stage nks-1
-          if (nks > 3) first_pair();
-          for (int ks = 2; ks < nks - 3; ks += 2) mid_pair(ks);
-          if (nks > 3) {
+          // (MODE 1: odd nks >= 5; MODE 3: nks == 3, whose step 0 loads
+          // stage 1 whole)
+          if constexpr (MODE == 1) {
+            first_pair();
+            for (int ks = 2; ks < nks - 3; ks += 2) mid_pair(ks);
             step(st0, no_loads, lhook(nks - 2, st1),
                  [&]() __attribute__((always_inline)) { issue_ea(src, nks - 1, st0); }, ehook(nks - 1, st0), WaitM0{},
                  WaitM1{});
@@ -1011,7 +1082,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
     }
   };
   if ((nks & 1) == 0 && nks >= 4) run(std::integral_constant<int, 0>{});
-  else if (nks >= 3) run(std::integral_constant<int, 1>{});
+  else if (nks >= 5) run(std::integral_constant<int, 1>{});
+  else if (nks == 3) run(std::integral_constant<int, 3>{});
   else run(std::integral_constant<int, 2>{});
   // no direct-to-LDS write may still be in flight when the workgroup ends
   wait_vmcnt<0>();
@@ -1043,8 +1115,17 @@ hipError_t launch_ab(int act, int out, const KernelArgs& a, hipStream_t s) {
 hipError_t launch_grouped_gemm(int ab, int act, int out, const KernelArgs& a, hipStream_t s) {
   if (a.grid <= 0) return hipErrorInvalidValue;
   if (act == ACT_DSWIGLU) {
-    if (ab != AB_BF16 || out != OUT_BF16) return hipErrorInvalidValue;
-    return launch_one<AB_BF16, ACT_DSWIGLU, OUT_BF16>(a, s);
+    switch (ab) {
+      case AB_BF16:
+        return out == OUT_BF16 ? launch_one<AB_BF16, ACT_DSWIGLU, OUT_BF16>(a, s) : hipErrorInvalidValue;
+      case AB_E4M3:
+        return out == OUT_E4M3 ? launch_one<AB_E4M3, ACT_DSWIGLU, OUT_E4M3>(a, s)
+                               : launch_one<AB_E4M3, ACT_DSWIGLU, OUT_BF16>(a, s);
+      case AB_E2M1:
+        return out == OUT_E4M3 ? launch_one<AB_E2M1, ACT_DSWIGLU, OUT_E4M3>(a, s)
+                               : launch_one<AB_E2M1, ACT_DSWIGLU, OUT_BF16>(a, s);
+      default: return hipErrorInvalidValue;
+    }
   }
   switch (ab) {
     case AB_E4M3: return launch_ab<AB_E4M3>(act, out, a, s);

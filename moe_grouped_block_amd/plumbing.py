@@ -89,8 +89,16 @@ def empty_outputs(problem: dict, device="cuda", fill: int | None = None) -> dict
             t.view(torch.uint8).fill_(fill)
         return t
     if problem["act"] == "dswiglu":
-        out["d"] = mk((m, no), torch.int16)
         out["dprob"] = torch.zeros(m, dtype=torch.float32, device=device)
+        if problem["d_dtype"] == "e4m3":
+            out["d"] = mk((m, no), torch.uint8)
+            out["d_col"] = mk((m, no), torch.uint8)
+            out["sfd_row"] = mk((m, no // 32), torch.uint8)
+            out["sfd_col"] = mk((no, m // 32), torch.uint8)
+        else:
+            out["d"] = mk((m, no), torch.int16)
+            if problem["ab_dtype"] != "bf16":
+                out["amax"] = mk((L, 2), torch.float32)
         return out
     if problem.get("c_dtype") == "bf16":
         out["c"] = mk((m, n), torch.int16)

@@ -38,6 +38,10 @@ reason, in the design notes of the repository):
 * sReLU tanh clamp: t = tanh(relu(C)/s) capped at 1, c = s*t, D = prob*c^2.
 * amax is the max |D| (before any output rounding) over the group's rows and
   all output columns; an empty group reports 0.
+* Block-scaled dSwiGLU with a BF16 dC reports amax of shape (L, 2) (the dGLU
+  page's block-scaled outputs): entry 0 is max |d_input| over the group's
+  rows and its input blocks, entry 1 max |d_gate| over its gate blocks.  With
+  an FP8 dC, dC is quantised by rows and columns exactly like a forward D.
 """
 from __future__ import annotations
 
@@ -234,26 +238,41 @@ def grouped_gemm(problem: dict, arrays: dict, rows=None) -> dict:
     out = {"rows": rows, "group": grp, "acc": acc}
 
     if act == "dswiglu":
+        # "Grouped GEMM + dGLU (SM100)": R_g = alpha_g^2 A_g B_g^T (BF16 contract;
+        # block-scaled Step 1 with dequantised A, B), then Step 2
         rmat = (alpha ** 2)[:, None] * acc
         beta = np.asarray(arrays["beta"], dtype=np.float64)[grp]
         x_saved = beta[:, None] * F.decode_bf16(arrays["c_in"][rows])
         dc, dprob = dswiglu(rmat, x_saved, prob)
         out.update(r=rmat, dc=dc, dprob=dprob, dc_bits=F.encode_bf16(dc))
-        return out
-
-    c = alpha[:, None] * acc
-    out["c"] = c
-    if problem.get("c_dtype") == "bf16":
-        out["c_bits"] = F.encode_bf16(c)
-    if act == "none":
-        d = prob[:, None] * c
-    elif act == "swiglu":
-        d = swiglu(c, prob)
-    elif act == "srelu":
-        d = srelu(c, prob, float(problem.get("srelu_tanh_s", 0.0)))
+        if ab == "bf16":
+            return out
+        # block-scaled backend: output formatting of dC (Step 3)
+        d = dc
+        if problem["d_dtype"] == "bf16":
+            halves = np.abs(dc).reshape(len(rows), -1, 2, 32)
+            amax2 = np.zeros((L, 2), dtype=np.float64)
+            for g in np.unique(grp):
+                sel = halves[grp == g]
+                if sel.size:
+                    amax2[g] = sel.max(axis=(0, 1, 3))
+            out["amax2"] = amax2
+            return out
+        out["d"] = d
     else:
-        raise ValueError(act)
-    out["d"] = d
+        c = alpha[:, None] * acc
+        out["c"] = c
+        if problem.get("c_dtype") == "bf16":
+            out["c_bits"] = F.encode_bf16(c)
+        if act == "none":
+            d = prob[:, None] * c
+        elif act == "swiglu":
+            d = swiglu(c, prob)
+        elif act == "srelu":
+            d = srelu(c, prob, float(problem.get("srelu_tanh_s", 0.0)))
+        else:
+            raise ValueError(act)
+        out["d"] = d
 
     if problem["d_dtype"] == "bf16":
         out["d_bits"] = F.encode_bf16(d)

@@ -193,6 +193,11 @@ CONFIGS = {
     "dswiglu_bf16_l64": dict(L=64, K=2048, N=1408, ab="bf16", act="dswiglu", d="bf16", c=None,
                              routing=("topk", 16384, 6), alpha=("const", 1.0), beta=("const", 1.0),
                              prob=("softmax_picks",), a_std=0.1, b_std="1/sqrtK", seed=105),
+    # dSwiGLU backward on the block-scaled backend: MXFP8 upstream gradient
+    # and weights, FP8 dC with row / column scale factors
+    "dswiglu_mxfp8_l64": dict(L=64, K=2048, N=1408, ab="e4m3", act="dswiglu", d="e4m3", c=None,
+                              routing=("topk", 16384, 6), alpha=("const", 1.0), beta=("const", 1.0),
+                              prob=("softmax_picks",), a_std=0.1, b_std="1/sqrtK", seed=107),
     # FC1 + SwiGLU at L=64 (the forward whose backward is dswiglu_bf16_l64)
     "fc1_swiglu_l64": dict(L=64, K=2048, N=2816, ab="e4m3", act="swiglu", d="e4m3", c=None,
                            routing=("topk", 16384, 6), alpha=("const", 1.0),

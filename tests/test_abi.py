@@ -112,7 +112,14 @@ CASES = [
     ("gating_bf16", dict(n=500), {}, NOT_SUPPORTED),                   # N % 32
     ("swiglu_e4m3", dict(n=2816 + 32), {}, INVALID),                   # SwiGLU N % 64
     ("dswiglu", dict(n=1408 + 16), {}, INVALID),                       # dGLU N % 32
-    ("dswiglu", dict(ab_dtype="e4m3"), dict(sfa=FAKE, sfb=FAKE), NOT_SUPPORTED),
+    ("dswiglu", dict(ab_dtype="e4m3"), dict(sfa=FAKE, sfb=FAKE), INVALID),            # MX + bf16 dC needs amax
+    ("dswiglu", dict(ab_dtype="e4m3"), dict(sfa=FAKE, sfb=FAKE, amax=FAKE), OK),
+    ("dswiglu", dict(ab_dtype="e4m3", d_dtype="e4m3"),
+     dict(sfa=FAKE, sfb=FAKE, d_col=FAKE + 0x40000, sfd_row=FAKE + 0x50000, sfd_col=FAKE + 0x60000,
+          norm_const=FAKE + 0x70000), OK),
+    ("dswiglu", dict(ab_dtype="e4m3", d_dtype="e4m3"),
+     dict(sfa=FAKE, sfb=FAKE, d_col=FAKE + 0x40000, sfd_row=FAKE + 0x50000, sfd_col=FAKE + 0x60000), INVALID),
+    ("dswiglu", {}, dict(amax=FAKE), INVALID),                                   # BF16 operands: no amax
     ("gating_bf16", {}, dict(prob=None), INVALID),                     # prob required
     ("gating_bf16", {}, dict(amax=None), INVALID),                     # amax for bf16 D
     ("gating_bf16", {}, dict(sfa=None), INVALID),

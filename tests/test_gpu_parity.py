@@ -46,9 +46,18 @@ def check_case(case, got, rows=None):
     grp = ref["group"]
     stats = {}
     if p["act"] == "dswiglu":
+        stats["dprob"] = rule1(got["dprob"][r], ref["dprob"], grp, "dprob")
+        if p["d_dtype"] == "e4m3":
+            nc = float(case.arrays["norm_const"][0])
+            stats["d_row"] = rule2(got["d"][r], got["sfd_row"][r], ref["dc"], nc, "row", "dC/SFD_row")
+            blocks = np.unique(r // 32)
+            stats["d_col"] = rule2(got["d_col"][r], got["sfd_col"][:, blocks], ref["dc"], nc, "col",
+                                   "dC_col/SFD_col")
+            return stats
         g2 = np.repeat(grp[:, None], ref["dc"].shape[1], axis=1)
         stats["dc"] = rule1(decode_bf16(got["d"][r]), ref["dc"], g2, "dC")
-        stats["dprob"] = rule1(got["dprob"][r], ref["dprob"], grp, "dprob")
+        if "amax2" in ref and rows is None:
+            stats["amax2"] = amax_rule(got["amax"].reshape(-1), ref["amax2"].reshape(-1))
         return stats
     if p.get("c_dtype") == "bf16":
         g2 = np.repeat(grp[:, None], ref["c"].shape[1], axis=1)
@@ -90,6 +99,19 @@ SMALL = {
     "swiglu_bf16_ops_e4m3": ("fc1_swiglu_l8", dict(ab="bf16", L=2, K=192, N=256, routing=("topk", 200, 2))),
     "dswiglu_bf16": ("dswiglu_bf16_l64", dict(L=5, K=256, N=288, routing=("topk", 200, 3),
                                               alpha=("uniform", 0.5, 2.0), beta=("uniform", 0.5, 2.0))),
+    # block-scaled dSwiGLU ("Grouped GEMM + dGLU (SM100)", block-scaled contract):
+    # step counts 8 (even), 5 (odd), 3 and 2 exercise every load schedule
+    "dswiglu_mxfp8_e4m3": ("dswiglu_mxfp8_l64", dict(L=5, K=1024, N=288, routing=("topk", 200, 3),
+                                                     alpha=("uniform", 0.5, 2.0), beta=("uniform", 0.5, 2.0))),
+    "dswiglu_mxfp8_e4m3_odd": ("dswiglu_mxfp8_l64", dict(L=3, K=640, N=256, routing=("topk", 150, 2),
+                                                         norm_const=2.0)),
+    "dswiglu_mxfp8_bf16_amax": ("dswiglu_mxfp8_l64", dict(L=4, K=384, N=320, d="bf16", routing=("topk", 200, 2),
+                                                          alpha=("uniform", 0.5, 2.0))),
+    "dswiglu_mxfp4_e4m3": ("dswiglu_mxfp8_l64", dict(ab="e2m1x2", L=3, K=512, N=256, routing=("topk", 150, 2),
+                                                     a_std=1.0, b_std=1.0, clip=6.0)),
+    "dswiglu_mxfp4_bf16_amax": ("dswiglu_mxfp8_l64", dict(ab="e2m1x2", d="bf16", L=3, K=1024, N=288,
+                                                          routing=("topk", 150, 2), a_std=1.0, b_std=1.0,
+                                                          clip=6.0)),
 }
 
 
@@ -288,7 +310,8 @@ def test_check_offsets_on_device():
 # full-size workloads: sampled 32-row blocks + properties at any size
 # ---------------------------------------------------------------------------
 
-FULL = ["fc1_swiglu_l8", "fc2_gating_l64_zipf", "srelu_tanh_fp4_l32", "dswiglu_bf16_l64", "fc1_swiglu_l64"]
+FULL = ["fc1_swiglu_l8", "fc2_gating_l64_zipf", "srelu_tanh_fp4_l32", "dswiglu_bf16_l64", "fc1_swiglu_l64",
+        "dswiglu_mxfp8_l64"]
 
 
 @pytest.mark.slow
@@ -314,7 +337,8 @@ def test_full_size_sampled(name):
     pad = ~case.row_valid
     if p["act"] == "dswiglu":
         # padding rows have A = 0, so R = 0: dC and dprob are (signed) zeros
-        assert np.all(decode_bf16(got["d"][pad]) == 0) and np.all(got["dprob"][pad] == 0)
+        dpad = F.decode_e4m3(got["d"][pad]) if p["d_dtype"] == "e4m3" else decode_bf16(got["d"][pad])
+        assert np.all(dpad == 0) and np.all(got["dprob"][pad] == 0)
     elif p["d_dtype"] == "bf16":
         d = decode_bf16(got["d"])
         assert np.all(d[pad] == 0)

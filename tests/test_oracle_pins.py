@@ -296,6 +296,45 @@ def test_dswiglu_alpha_squared_and_beta_placement():
     np.testing.assert_allclose(out["dprob"], 32 * 9.0 * 0.5 * 0.5 * s, rtol=1e-14)
 
 
+def _bs_dswiglu_case(d_dtype):
+    """Two experts of 2 rows, MXFP8 A = 1.0 and B = 1/32 (scale byte 122), K = 64:
+    acc = 2; alpha = (0.5, 1) -> R = (0.5, 2).  C_in: input blocks 2.0, gate
+    blocks 0.0 (beta 1), so swish(gate) = 0 and sigmoid(gate) = 1/2:
+    d_input = 0, d_gate = R * prob * 2 * 1/2 = R * prob, dprob = 0."""
+    m, k, n = 4, 64, 32
+    a, sfa = _const_mx(m, k, 0x38, 127)
+    b, sfb = _const_mx(2 * n, k, 0x38, 122)
+    c_in = np.zeros((m, 2 * n), np.uint16)
+    c_in[:, :32] = 0x4000
+    arr = dict(a=a, sfa=sfa, b=b.reshape(2, n, k), sfb=sfb.reshape(2, n, k // 32),
+               padded_offsets=np.array([2, 4], np.int32), alpha=np.array([0.5, 1.0], np.float32),
+               beta=np.ones(2, np.float32), prob=np.array([1.0, 0.5, 1.0, 0.25], np.float32),
+               c_in=c_in, norm_const=np.ones(1, np.float32))
+    return _problem(2, m, n, k, ab="e4m3", act="dswiglu", d=d_dtype), arr
+
+
+def test_block_scaled_dswiglu_amax_pairs_closed_form():
+    prob_, arr = _bs_dswiglu_case("bf16")
+    out = oracle.grouped_gemm(prob_, arr)
+    np.testing.assert_array_equal(out["r"], np.repeat([[0.5], [0.5], [2.0], [2.0]], 32, axis=1))
+    assert np.all(out["dc"][:, :32] == 0.0)
+    np.testing.assert_array_equal(out["dc"][:, 32], [0.5, 0.25, 2.0, 0.5])
+    np.testing.assert_array_equal(out["dprob"], 0.0)
+    # (L, 2): [max |d_input|, max |d_gate|] per expert
+    np.testing.assert_array_equal(out["amax2"], [[0.0, 0.5], [0.0, 2.0]])
+
+
+def test_block_scaled_dswiglu_fp8_dc_closed_form():
+    prob_, arr = _bs_dswiglu_case("e4m3")
+    out = oracle.grouped_gemm(prob_, arr)
+    # input blocks all zero: byte 0, codes 0.  Gate block of row 0: amax 0.5,
+    # smallest 2^e >= 0.5/448 is 2^-9 (byte 118), 0.5 / 2^-9 = 256 = E4M3 0x78;
+    # row 1 (0.25): 2^-10 (byte 117), code 0x78 again
+    np.testing.assert_array_equal(out["sfd_row"][:, 0], 0)
+    np.testing.assert_array_equal(out["sfd_row"][:, 1], [118, 117, 120, 118])
+    assert np.all(out["d_code"][:, :32] == 0) and np.all(out["d_code"][:, 32:] == 0x78)
+
+
 # ---------------------------------------------------------------------------
 # P-i: quantisation invariants
 # ---------------------------------------------------------------------------
