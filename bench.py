@@ -72,8 +72,8 @@ def algorithmic_bytes(case) -> float:
     rd += a.get("c_in", a["prob"][:0]).nbytes
     vm = p["valid_m"]
     n = p["n"]
-    no = {"none": n, "srelu": n, "swiglu": n // 2, "dswiglu": 2 * n}[p["act"]]
-    if p["act"] == "dswiglu":
+    no = {"none": n, "srelu": n, "swiglu": n // 2, "dswiglu": 2 * n, "dsrelu": n}[p["act"]]
+    if p["act"] in ("dswiglu", "dsrelu") and p["d_dtype"] == "bf16":
         wr = vm * no * 2 + vm * 4
     elif p["d_dtype"] == "e4m3":
         wr = 2 * vm * no + vm * no // 32 + no * vm // 32
@@ -112,7 +112,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fc1_swiglu_l64")
-    ap.add_argument("--also", default="fc1_swiglu_l8,fc1_swiglu_l64:discrete,dswiglu_mxfp8_l64",
+    ap.add_argument("--also", default="fc1_swiglu_l8,fc1_swiglu_l64:discrete,dswiglu_mxfp8_l64,dsrelu_mxfp8_l32",
                     help="comma list of extra workloads to time; a ':discrete' suffix passes the expert "
                          "weights as per-expert allocations (b_ptrs / sfb_ptrs)")
     ap.add_argument("--cpu-rows", type=int, default=40960, help="rows of the oracle CPU sample")

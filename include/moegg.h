@@ -47,14 +47,16 @@
  *   C       (valid_m, N) BF16                      [optional forward output]
  *   D, D_col (valid_m, N_out) BF16 or E4M3 codes   N_out = N/2 for SwiGLU,
  *                                                  2N for dSwiGLU, else N
+ *                                                  (dC for dSwiGLU / dsReLU)
  *   SFD_row (valid_m, N_out/32) E8M0; SFD_col (N_out, valid_m/32) E8M0
  *   amax    (L) fp32, written by the call (zero-filled first); for dSwiGLU
  *           with MX operands and a BF16 dC, (L, 2): max |d_input| and max
  *           |d_gate| over the group's rows (the block-scaled dGLU contract's
  *           amax of shape (L, 2, 1); which quantity each entry holds is this
  *           library's reading)
- *   C_in    (valid_m, 2N) BF16, saved forward pre-activation [dSwiGLU only]
- *   dprob   (valid_m) fp32, caller-zeroed, accumulated with atomics [dSwiGLU]
+ *   C_in    saved forward pre-activation, BF16: (valid_m, 2N) [dSwiGLU] or
+ *           (valid_m, N) [dsReLU]
+ *   dprob   (valid_m) fp32, caller-zeroed, accumulated with atomics [dSwiGLU, dsReLU]
  *
  * Ownership: every pointer is a caller-owned device pointer (except the
  * problem/args structs, which are host memory read during the call only).
@@ -101,10 +103,16 @@ typedef enum moegg_act {
                             ("Grouped GEMM + SwiGLU", Step 2)                               */
   MOEGG_ACT_SRELU = 2,   /* D = prob * relu(C)^2, optional tanh soft clamp s
                             ("Grouped GEMM + sReLU", §Equations / §Tanh soft clamp)          */
-  MOEGG_ACT_DSWIGLU = 3  /* dC = [d_input|d_gate] from R and beta*C_in, dprob += row sums
+  MOEGG_ACT_DSWIGLU = 3, /* dC = [d_input|d_gate] from R and beta*C_in, dprob += row sums
                             ("Grouped GEMM + dGLU", BF16 contract and block-scaled contract,
                             dSwiGLU): BF16 operands -> BF16 dC; MX operands -> BF16 dC + amax
                             (L, 2), or E4M3 dC as D/D_col with SFD_row/SFD_col             */
+  MOEGG_ACT_DSRELU = 4   /* sReLU backward: R = alpha_g^2 acc, C_in the saved forward C
+                            (N wide, no beta), dC = R prob f'(C), dprob += sum R f(C),
+                            f(C) = (s tanh(relu(C)/s))^2 or relu(C)^2 for s = 0 (derived
+                            from "Grouped GEMM + sReLU", §Equations / §Tanh soft clamp; its
+                            backward page is not among the sources).  Output formats as
+                            dSwiGLU, amax (L) for a BF16 dC with MX operands              */
 } moegg_act;
 
 /* Problem description (host struct). */
@@ -130,16 +138,16 @@ typedef struct moegg_args {
   const int32_t* padded_offsets;
   const float* alpha;
   const float* prob;             /* required ("prob ... Required", Quant page) */
-  const float* beta;             /* dSwiGLU only */
+  const float* beta;             /* dSwiGLU only (L) */
   const float* norm_const;       /* required iff d_dtype == E4M3 */
-  const void* c_in;              /* dSwiGLU only: saved forward C, BF16 (valid_m, 2N) */
+  const void* c_in;              /* dSwiGLU / dsReLU: saved forward C, BF16 (valid_m, 2N) / (valid_m, N) */
   void* c;                       /* optional C output (c_dtype BF16) */
   void* d;                       /* D (or dC for dSwiGLU) */
   void* d_col;                   /* E4M3 only */
   uint8_t* sfd_row;              /* E4M3 only */
   uint8_t* sfd_col;              /* E4M3 only */
   float* amax;                   /* BF16 D: (L), or (L, 2) for dSwiGLU with MX operands */
-  float* dprob;                  /* dSwiGLU only, caller-zeroed */
+  float* dprob;                  /* dSwiGLU / dsReLU, caller-zeroed */
   const void* const* b_ptrs;     /* discrete weights instead of b: (L) device array, 8-byte aligned */
   const uint8_t* const* sfb_ptrs;/* discrete weights, MX only, instead of sfb: (L) device array */
 } moegg_args;

@@ -27,7 +27,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libmoegg.so")
 
 DTYPES = {None: 0, "none": 0, "e4m3": 1, "e2m1x2": 2, "bf16": 3}
-ACTS = {"none": 0, "swiglu": 1, "srelu": 2, "dswiglu": 3}
+ACTS = {"none": 0, "swiglu": 1, "srelu": 2, "dswiglu": 3, "dsrelu": 4}
 STATUS = {0: "MOEGG_OK", 1: "MOEGG_ERROR_INVALID_VALUE", 2: "MOEGG_ERROR_MISALIGNED",
           3: "MOEGG_ERROR_NOT_SUPPORTED", 4: "MOEGG_ERROR_LAUNCH"}
 

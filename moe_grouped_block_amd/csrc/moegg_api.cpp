@@ -45,6 +45,7 @@ int64_t n_out_of(const moegg_problem& p) {
     case MOEGG_ACT_SRELU: return p.n;
     case MOEGG_ACT_SWIGLU: return p.n / 2;
     case MOEGG_ACT_DSWIGLU: return 2 * static_cast<int64_t>(p.n);
+    case MOEGG_ACT_DSRELU: return p.n;
     default: return -1;
   }
 }
@@ -74,7 +75,7 @@ moegg_status check_impl(const moegg_problem* pp, const moegg_args* ap) {
   const bool mx = p.ab_dtype == MOEGG_DT_E4M3 || p.ab_dtype == MOEGG_DT_E2M1X2;
   if (!mx && p.ab_dtype != MOEGG_DT_BF16)
     return fail(MOEGG_ERROR_INVALID_VALUE, "ab_dtype=%d must be E4M3, E2M1X2 or BF16", p.ab_dtype);
-  if (p.act < MOEGG_ACT_NONE || p.act > MOEGG_ACT_DSWIGLU)
+  if (p.act < MOEGG_ACT_NONE || p.act > MOEGG_ACT_DSRELU)
     return fail(MOEGG_ERROR_INVALID_VALUE, "act=%d unknown", p.act);
   if (p.d_dtype != MOEGG_DT_BF16 && p.d_dtype != MOEGG_DT_E4M3)
     return fail(MOEGG_ERROR_INVALID_VALUE, "d_dtype=%d must be BF16 or E4M3", p.d_dtype);
@@ -84,11 +85,12 @@ moegg_status check_impl(const moegg_problem* pp, const moegg_args* ap) {
     return fail(MOEGG_ERROR_INVALID_VALUE, "srelu_tanh_s must be finite and >= 0");
   if (p.act == MOEGG_ACT_SWIGLU && p.n % 64 != 0)
     return fail(MOEGG_ERROR_INVALID_VALUE, "SwiGLU needs n %% 64 == 0 (32-column pairs), n=%d", p.n);
-  if (p.act == MOEGG_ACT_DSWIGLU) {
-    if (p.n % 32 != 0) return fail(MOEGG_ERROR_INVALID_VALUE, "dSwiGLU needs n %% 32 == 0, n=%d", p.n);
+  const bool bwd = p.act == MOEGG_ACT_DSWIGLU || p.act == MOEGG_ACT_DSRELU;
+  if (bwd) {
+    if (p.n % 32 != 0) return fail(MOEGG_ERROR_INVALID_VALUE, "backward activations need n %% 32 == 0, n=%d", p.n);
     if (!mx && p.d_dtype != MOEGG_DT_BF16)
-      return fail(MOEGG_ERROR_NOT_SUPPORTED, "dSwiGLU with BF16 operands writes a BF16 dC only");
-    if (p.c_dtype != MOEGG_DT_NONE) return fail(MOEGG_ERROR_INVALID_VALUE, "dSwiGLU writes no C");
+      return fail(MOEGG_ERROR_NOT_SUPPORTED, "backward activations with BF16 operands write a BF16 dC only");
+    if (p.c_dtype != MOEGG_DT_NONE) return fail(MOEGG_ERROR_INVALID_VALUE, "backward activations write no C");
   }
   if (p.n % 32 != 0) return fail(MOEGG_ERROR_NOT_SUPPORTED, "n=%d: this build needs n %% 32 == 0", p.n);
   const int kstep = p.ab_dtype == MOEGG_DT_E4M3 ? 128 : p.ab_dtype == MOEGG_DT_E2M1X2 ? 256 : 64;   // 128-byte steps
@@ -124,15 +126,16 @@ moegg_status check_impl(const moegg_problem* pp, const moegg_args* ap) {
   } else {
     if (nq != 0 || a.d_col)
       return fail(MOEGG_ERROR_INVALID_VALUE, "d_col/sfd_row/sfd_col/norm_const are for E4M3 D only");
-    if ((p.act != MOEGG_ACT_DSWIGLU || mx) && !a.amax)
+    if ((!bwd || mx) && !a.amax)
       return fail(MOEGG_ERROR_INVALID_VALUE, "BF16 D needs amax");
   }
-  if (p.act == MOEGG_ACT_DSWIGLU) {
-    if (!a.beta || !a.c_in || !a.dprob)
-      return fail(MOEGG_ERROR_INVALID_VALUE, "dSwiGLU needs beta, c_in and dprob");
-    if (!mx && a.amax) return fail(MOEGG_ERROR_INVALID_VALUE, "dSwiGLU with BF16 operands writes no amax");
+  if (bwd) {
+    if (!a.c_in || !a.dprob) return fail(MOEGG_ERROR_INVALID_VALUE, "backward activations need c_in and dprob");
+    if (p.act == MOEGG_ACT_DSWIGLU && !a.beta) return fail(MOEGG_ERROR_INVALID_VALUE, "dSwiGLU needs beta");
+    if (p.act == MOEGG_ACT_DSRELU && a.beta) return fail(MOEGG_ERROR_INVALID_VALUE, "dsReLU takes no beta");
+    if (!mx && a.amax) return fail(MOEGG_ERROR_INVALID_VALUE, "backward activations with BF16 operands write no amax");
   } else if (a.beta || a.c_in || a.dprob) {
-    return fail(MOEGG_ERROR_INVALID_VALUE, "beta/c_in/dprob are for dSwiGLU only");
+    return fail(MOEGG_ERROR_INVALID_VALUE, "beta/c_in/dprob are for the backward activations only");
   }
 
   // --- alignment (16 B on the contiguous dimension, as the pages require) ------

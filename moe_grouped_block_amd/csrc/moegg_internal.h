@@ -10,7 +10,7 @@ namespace moegg {
 // Operand family of A/B.
 enum AbKind : int { AB_E4M3 = 0, AB_E2M1 = 1, AB_BF16 = 2 };
 // Epilogue activation.
-enum ActKind : int { ACT_NONE = 0, ACT_SWIGLU = 1, ACT_SRELU = 2, ACT_DSWIGLU = 3 };
+enum ActKind : int { ACT_NONE = 0, ACT_SWIGLU = 1, ACT_SRELU = 2, ACT_DSWIGLU = 3, ACT_DSRELU = 4 };
 // Output formatting of D.
 enum OutKind : int { OUT_BF16 = 0, OUT_E4M3 = 1 };
 
@@ -36,7 +36,7 @@ struct KernelArgs {
   const float* prob;       // (valid_m)
   const float* beta;       // (L) dSwiGLU
   const float* norm_const; // (1) E4M3 D
-  const uint16_t* c_in;    // (valid_m, 2n) dSwiGLU
+  const uint16_t* c_in;    // (valid_m, 2n) dSwiGLU, (valid_m, n) dsReLU
   uint16_t* c;             // (valid_m, n) optional
   uint8_t* d;              // (valid_m, n_out) bf16 or e4m3
   uint8_t* d_col;          // (valid_m, n_out) e4m3

@@ -806,6 +806,80 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           atomicMax(reinterpret_cast<unsigned int*>(p.amax + 2 * g + 1), __float_as_uint(wg));
         }
       }
+    } else if constexpr (ACT == ACT_DSRELU) {
+      // sReLU backward (derived from "Grouped GEMM + sReLU (SM100)",
+      // §Equations / §Tanh soft clamp): R = alpha^2 acc, C the saved forward
+      // C; with t = min(tanh(relu(C)/s), 1), c = s t: dC = R prob 2 c (1 - t^2),
+      // dprob += R c^2 (s = 0: c = relu(C), dC = R prob 2 c)
+      const float a2 = alpha * alpha;
+      const float sc = p.srelu_s;
+      const float rs = sc > 0.0f ? 1.0f / sc : 0.0f;
+      float amax_l = 0.0f;
+      uint32_t colw[TN];
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) colw[tn] = 0;
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int m = mbase + tm * 32 + l32;
+        float dp = 0.0f;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int ncol = nbase + tn * 32;
+          if (ncol >= p.n) continue;
+          if constexpr (OUT == OUT_E4M3) asm volatile("" ::: "memory");
+          const int64_t coff = static_cast<int64_t>(m) * p.n + ncol;
+          float cv[16];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const v2u w = *reinterpret_cast<const v2u*>(p.c_in + coff + 8 * j + 4 * hi);
+            cv[4 * j + 0] = __uint_as_float(w.x << 16);
+            cv[4 * j + 1] = __uint_as_float(w.x & 0xFFFF0000u);
+            cv[4 * j + 2] = __uint_as_float(w.y << 16);
+            cv[4 * j + 3] = __uint_as_float(w.y & 0xFFFF0000u);
+          }
+          float d[16];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float r = a2 * acc[tm][tn][v];
+            float c = fmaxf(cv[v], 0.0f), fp;
+            if (sc > 0.0f) {
+              const float t = fminf(tanh_nonneg(c * rs), 1.0f);
+              c = sc * t;
+              fp = 2.0f * c * (1.0f - t * t);
+            } else {
+              fp = 2.0f * c;
+            }
+            d[v] = r * pr[tm] * fp;
+            dp += r * (c * c);
+          }
+          if constexpr (OUT == OUT_BF16) {
+            store_bf16_tile(p.d, m, p.n_out, ncol, hi, d);
+            if constexpr (MX) {
+#pragma unroll
+              for (int v = 0; v < 16; v += 2) amax_l = max_abs2(amax_l, d[v], d[v + 1]);
+            }
+          } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) d[v] *= nc;
+            colw[tn] |= quant_tile(p, sT, sS, m, ncol, hi, l32, d) << (8 * tm);
+          }
+        }
+        dp = halves_sum(dp);
+        if (hi == 0) atomicAdd(p.dprob + m, dp);
+      }
+      if constexpr (OUT == OUT_E4M3) {
+        const int mblk0 = mbase >> 5;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int ncol = nbase + tn * 32;
+          if (ncol >= p.n || hi != 0) continue;
+          *reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(ncol + l32) * (vm >> 5) + mblk0) = colw[tn];
+        }
+      }
+      if constexpr (MX && OUT == OUT_BF16) {
+        const float w = wave_max(amax_l);
+        if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(p.amax + g), __float_as_uint(w));
+      }
     } else {
       float amax_l = 0.0f;
       const int mblk0 = mbase >> 5;
@@ -1114,6 +1188,19 @@ hipError_t launch_ab(int act, int out, const KernelArgs& a, hipStream_t s) {
 
 hipError_t launch_grouped_gemm(int ab, int act, int out, const KernelArgs& a, hipStream_t s) {
   if (a.grid <= 0) return hipErrorInvalidValue;
+  if (act == ACT_DSRELU) {
+    switch (ab) {
+      case AB_BF16:
+        return out == OUT_BF16 ? launch_one<AB_BF16, ACT_DSRELU, OUT_BF16>(a, s) : hipErrorInvalidValue;
+      case AB_E4M3:
+        return out == OUT_E4M3 ? launch_one<AB_E4M3, ACT_DSRELU, OUT_E4M3>(a, s)
+                               : launch_one<AB_E4M3, ACT_DSRELU, OUT_BF16>(a, s);
+      case AB_E2M1:
+        return out == OUT_E4M3 ? launch_one<AB_E2M1, ACT_DSRELU, OUT_E4M3>(a, s)
+                               : launch_one<AB_E2M1, ACT_DSRELU, OUT_BF16>(a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (act == ACT_DSWIGLU) {
     switch (ab) {
       case AB_BF16:

@@ -38,6 +38,10 @@ reason, in the design notes of the repository):
 * sReLU tanh clamp: t = tanh(relu(C)/s) capped at 1, c = s*t, D = prob*c^2.
 * amax is the max |D| (before any output rounding) over the group's rows and
   all output columns; an empty group reports 0.
+* sReLU backward: R = alpha_g^2 * acc as for dSwiGLU, the saved forward C is
+  read without a beta scale, and dC / dprob follow from the forward equation
+  (see dsrelu); with MX operands its dC is formatted like a forward D (bf16 +
+  per-group amax of shape (L), or FP8 rows and columns).
 * Block-scaled dSwiGLU with a BF16 dC reports amax of shape (L, 2) (the dGLU
   page's block-scaled outputs): entry 0 is max |d_input| over the group's
   rows and its input blocks, entry 1 max |d_gate| over its gate blocks.  With
@@ -146,6 +150,28 @@ def dswiglu(rmat, x_saved, prob):
     return dc, dprob
 
 
+def dsrelu(rmat, c_saved, prob, s: float):
+    """sReLU backward (the pair of "Grouped GEMM + sReLU (SM100)"; its own page
+    is not among the sources, so the derivative is taken from the forward's
+    §Equations / §Tanh soft clamp): with f(C) = (s * tanh(relu(C)/s))^2
+    (relu(C)^2 for s = 0) and the forward D = prob * f(C),
+      dC    = R * prob * f'(C),  f'(C) = 2 c (1 - t^2) for C > 0 (t = tanh(C/s),
+              c = s t), 2 relu(C) for s = 0, 0 for C <= 0
+      dprob = sum over the N columns of R * f(C)
+    """
+    r = np.maximum(c_saved, 0.0)
+    if s > 0:
+        t = np.minimum(np.tanh(r / s), 1.0)
+        c = s * t
+        fprime = 2.0 * c * (1.0 - t * t)
+    else:
+        c = r
+        fprime = 2.0 * r
+    dc = rmat * prob[:, None] * fprime
+    dprob = (rmat * (c * c)).sum(axis=1)
+    return dc, dprob
+
+
 # ---------------------------------------------------------------------------
 # step 5: FP8 quantisation with E8M0 block scales (float32 decisions)
 # ---------------------------------------------------------------------------
@@ -237,19 +263,24 @@ def grouped_gemm(problem: dict, arrays: dict, rows=None) -> dict:
     prob = np.asarray(arrays["prob"], dtype=np.float64)[rows]
     out = {"rows": rows, "group": grp, "acc": acc}
 
-    if act == "dswiglu":
+    if act in ("dswiglu", "dsrelu"):
         # "Grouped GEMM + dGLU (SM100)": R_g = alpha_g^2 A_g B_g^T (BF16 contract;
-        # block-scaled Step 1 with dequantised A, B), then Step 2
+        # block-scaled Step 1 with dequantised A, B), then Step 2; the sReLU
+        # backward takes the same R and the saved forward C as it is
         rmat = (alpha ** 2)[:, None] * acc
-        beta = np.asarray(arrays["beta"], dtype=np.float64)[grp]
-        x_saved = beta[:, None] * F.decode_bf16(arrays["c_in"][rows])
-        dc, dprob = dswiglu(rmat, x_saved, prob)
+        if act == "dswiglu":
+            beta = np.asarray(arrays["beta"], dtype=np.float64)[grp]
+            x_saved = beta[:, None] * F.decode_bf16(arrays["c_in"][rows])
+            dc, dprob = dswiglu(rmat, x_saved, prob)
+        else:
+            dc, dprob = dsrelu(rmat, F.decode_bf16(arrays["c_in"][rows]), prob,
+                               float(problem.get("srelu_tanh_s", 0.0)))
         out.update(r=rmat, dc=dc, dprob=dprob, dc_bits=F.encode_bf16(dc))
         if ab == "bf16":
             return out
         # block-scaled backend: output formatting of dC (Step 3)
         d = dc
-        if problem["d_dtype"] == "bf16":
+        if act == "dswiglu" and problem["d_dtype"] == "bf16":
             halves = np.abs(dc).reshape(len(rows), -1, 2, 32)
             amax2 = np.zeros((L, 2), dtype=np.float64)
             for g in np.unique(grp):

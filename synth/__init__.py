@@ -198,6 +198,13 @@ CONFIGS = {
     "dswiglu_mxfp8_l64": dict(L=64, K=2048, N=1408, ab="e4m3", act="dswiglu", d="e4m3", c=None,
                               routing=("topk", 16384, 6), alpha=("const", 1.0), beta=("const", 1.0),
                               prob=("softmax_picks",), a_std=0.1, b_std="1/sqrtK", seed=107),
+    # sReLU backward with the tanh soft clamp: the pair of srelu_tanh_fp4_l32's
+    # forward (same routing and shapes), MXFP8 upstream gradient and weights,
+    # saved forward C ~ N(0, 4^2) so that many positive values reach the
+    # curved part of tanh(C/8), FP8 dC
+    "dsrelu_mxfp8_l32": dict(L=32, K=4096, N=4096, ab="e4m3", act="dsrelu", d="e4m3", c=None,
+                             routing=("multinomial", 32768), alpha=("const", 1.0),
+                             prob=("uniform",), a_std=0.1, b_std="1/sqrtK", c_std=4.0, s=8.0, seed=108),
     # FC1 + SwiGLU at L=64 (the forward whose backward is dswiglu_bf16_l64)
     "fc1_swiglu_l64": dict(L=64, K=2048, N=2816, ab="e4m3", act="swiglu", d="e4m3", c=None,
                            routing=("topk", 16384, 6), alpha=("const", 1.0),
@@ -352,17 +359,21 @@ def make_case(spec_or_name, seed: int | None = None, **overrides) -> Case:
                          else np.zeros((0, K // 32), np.uint8))
         arrays["sfb"] = np.stack([p[1] for p in b_parts])
     act = spec["act"]
-    if act == "dswiglu":
-        arrays["beta"] = beta
+    if act in ("dswiglu", "dsrelu"):
+        if act == "dswiglu":
+            arrays["beta"] = beta
         cin_chunks = [(r0, min(valid_m, r0 + _A_CHUNK)) for r0 in range(0, valid_m, _A_CHUNK)]
+        cw = 2 * N if act == "dswiglu" else N
+        c_std = np.float32(spec.get("c_std", 1.0))
 
         def _c_chunk(ci):
             r0, r1 = cin_chunks[ci]
-            x = _rng(seed, _S_CIN, ci).standard_normal((r1 - r0, 2 * N), dtype=np.float32)
+            x = _rng(seed, _S_CIN, ci).standard_normal((r1 - r0, cw), dtype=np.float32)
+            x *= c_std
             return encode_bf16(x)
         with ThreadPoolExecutor(_THREADS) as ex:
             parts = list(ex.map(_c_chunk, range(len(cin_chunks))))
-        arrays["c_in"] = np.concatenate(parts) if parts else np.zeros((0, 2 * N), np.uint16)
+        arrays["c_in"] = np.concatenate(parts) if parts else np.zeros((0, cw), np.uint16)
 
     problem = dict(num_groups=L, valid_m=valid_m, n=N, k=K, m_aligned=m_al,
                    ab_dtype=ab, c_dtype=spec.get("c"), d_dtype=spec["d"], act=act,

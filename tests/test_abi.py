@@ -120,6 +120,12 @@ CASES = [
     ("dswiglu", dict(ab_dtype="e4m3", d_dtype="e4m3"),
      dict(sfa=FAKE, sfb=FAKE, d_col=FAKE + 0x40000, sfd_row=FAKE + 0x50000, sfd_col=FAKE + 0x60000), INVALID),
     ("dswiglu", {}, dict(amax=FAKE), INVALID),                                   # BF16 operands: no amax
+    # sReLU backward: c_in (N wide) and dprob, no beta
+    ("dswiglu", dict(act="dsrelu"), dict(beta=None), OK),
+    ("dswiglu", dict(act="dsrelu"), {}, INVALID),                                # beta given
+    ("dswiglu", dict(act="dsrelu"), dict(beta=None, c_in=None), INVALID),
+    ("dswiglu", dict(act="dsrelu", ab_dtype="e4m3"), dict(beta=None, sfa=FAKE, sfb=FAKE, amax=FAKE), OK),
+    ("dswiglu", dict(act="dsrelu", d_dtype="e4m3"), dict(beta=None), NOT_SUPPORTED),   # BF16 ops: bf16 dC
     ("gating_bf16", {}, dict(prob=None), INVALID),                     # prob required
     ("gating_bf16", {}, dict(amax=None), INVALID),                     # amax for bf16 D
     ("gating_bf16", {}, dict(sfa=None), INVALID),
@@ -185,7 +191,7 @@ def test_null_structs():
 
 def test_n_out():
     for act, n, expect in [("none", 512, 512), ("swiglu", 2816, 1408), ("srelu", 4096, 4096),
-                           ("dswiglu", 1408, 2816)]:
+                           ("dswiglu", 1408, 2816), ("dsrelu", 4096, 4096)]:
         p, _ = _base("gating_bf16")
         p.update(act=act, n=n)
         assert mg.moegg_n_out(mg.make_problem(p)) == expect

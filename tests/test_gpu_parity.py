@@ -45,7 +45,7 @@ def check_case(case, got, rows=None):
     r = ref["rows"]
     grp = ref["group"]
     stats = {}
-    if p["act"] == "dswiglu":
+    if p["act"] in ("dswiglu", "dsrelu"):
         stats["dprob"] = rule1(got["dprob"][r], ref["dprob"], grp, "dprob")
         if p["d_dtype"] == "e4m3":
             nc = float(case.arrays["norm_const"][0])
@@ -58,6 +58,8 @@ def check_case(case, got, rows=None):
         stats["dc"] = rule1(decode_bf16(got["d"][r]), ref["dc"], g2, "dC")
         if "amax2" in ref and rows is None:
             stats["amax2"] = amax_rule(got["amax"].reshape(-1), ref["amax2"].reshape(-1))
+        if "amax" in ref and rows is None:
+            stats["amax"] = amax_rule(got["amax"], ref["amax"])
         return stats
     if p.get("c_dtype") == "bf16":
         g2 = np.repeat(grp[:, None], ref["c"].shape[1], axis=1)
@@ -112,6 +114,16 @@ SMALL = {
     "dswiglu_mxfp4_bf16_amax": ("dswiglu_mxfp8_l64", dict(ab="e2m1x2", d="bf16", L=3, K=1024, N=288,
                                                           routing=("topk", 150, 2), a_std=1.0, b_std=1.0,
                                                           clip=6.0)),
+    # sReLU backward (tanh clamp s = 8 and plain s = 0), every operand family
+    "dsrelu_mxfp8_e4m3": ("dsrelu_mxfp8_l32", dict(L=3, K=1024, N=320, routing=("multinomial", 300),
+                                                   alpha=("uniform", 0.5, 2.0))),
+    "dsrelu_mxfp8_e4m3_odd_plain": ("dsrelu_mxfp8_l32", dict(L=2, K=640, N=256, routing=("multinomial", 200),
+                                                             s=0.0, norm_const=0.5)),
+    "dsrelu_mxfp4_bf16_amax": ("dsrelu_mxfp8_l32", dict(ab="e2m1x2", d="bf16", L=3, K=1024, N=288,
+                                                        routing=("multinomial", 300), a_std=1.0, b_std=1.0,
+                                                        clip=6.0)),
+    "dsrelu_bf16_ops": ("dsrelu_mxfp8_l32", dict(ab="bf16", d="bf16", L=2, K=192, N=256,
+                                                 routing=("multinomial", 200))),
 }
 
 
@@ -311,7 +323,7 @@ def test_check_offsets_on_device():
 # ---------------------------------------------------------------------------
 
 FULL = ["fc1_swiglu_l8", "fc2_gating_l64_zipf", "srelu_tanh_fp4_l32", "dswiglu_bf16_l64", "fc1_swiglu_l64",
-        "dswiglu_mxfp8_l64"]
+        "dswiglu_mxfp8_l64", "dsrelu_mxfp8_l32"]
 
 
 @pytest.mark.slow
@@ -335,7 +347,7 @@ def test_full_size_sampled(name):
     stats = check_case(case, got, rows)
     p = case.problem
     pad = ~case.row_valid
-    if p["act"] == "dswiglu":
+    if p["act"] in ("dswiglu", "dsrelu"):
         # padding rows have A = 0, so R = 0: dC and dprob are (signed) zeros
         dpad = F.decode_e4m3(got["d"][pad]) if p["d_dtype"] == "e4m3" else decode_bf16(got["d"][pad])
         assert np.all(dpad == 0) and np.all(got["dprob"][pad] == 0)

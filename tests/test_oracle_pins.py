@@ -296,6 +296,56 @@ def test_dswiglu_alpha_squared_and_beta_placement():
     np.testing.assert_allclose(out["dprob"], 32 * 9.0 * 0.5 * 0.5 * s, rtol=1e-14)
 
 
+@pytest.mark.parametrize("s_clamp", [0.0, 2.0])
+def test_dsrelu_matches_finite_differences(s_clamp):
+    """dC and dprob of the sReLU backward against central differences of the
+    forward loss L = sum R * prob * f(C), f from the sReLU page's equations."""
+    rng = np.random.default_rng(9)
+    rows, n = 3, 40
+    R = rng.standard_normal((rows, n))
+    C = rng.standard_normal((rows, n)) * 3
+    C[np.abs(C) < 1e-3] = 0.5                     # keep away from the kink at 0
+    p = rng.random(rows)
+
+    def loss(Cv, pv):
+        return (R * G.srelu(Cv, pv, s_clamp)).sum()
+
+    dc, dprob = G.dsrelu(R, C, p, s_clamp)
+    h = 1e-6
+    num = np.zeros_like(C)
+    for r in range(rows):
+        for j in range(n):
+            Cp, Cm = C.copy(), C.copy()
+            Cp[r, j] += h
+            Cm[r, j] -= h
+            num[r, j] = (loss(Cp, p) - loss(Cm, p)) / (2 * h)
+    np.testing.assert_allclose(dc, num, rtol=1e-6, atol=1e-8)
+    nump = np.zeros(rows)
+    for r in range(rows):
+        pp, pm = p.copy(), p.copy()
+        pp[r] += h
+        pm[r] -= h
+        nump[r] = (loss(C, pp) - loss(C, pm)) / (2 * h)
+    np.testing.assert_allclose(dprob, nump, rtol=1e-7, atol=1e-9)
+    assert np.all(dc[C <= 0] == 0.0)
+
+
+def test_dsrelu_through_the_gemm_closed_form():
+    """R = alpha^2 * acc, C read without scaling: A = 1.0 (byte 127), B = 1/32
+    (byte 122), K = 64 -> acc = 2, alpha 0.5 -> R = 0.5; C = 2.0, s = 0:
+    dC = 0.5 * prob * 4, dprob = 0.5 * 64 columns * 4 = 128 (N = 64)."""
+    m, k, n = 2, 64, 64
+    a, sfa = _const_mx(m, k, 0x38, 127)
+    b, sfb = _const_mx(n, k, 0x38, 122)
+    arr = dict(a=a, sfa=sfa, b=b.reshape(1, n, k), sfb=sfb.reshape(1, n, k // 32),
+               padded_offsets=np.array([m], np.int32), alpha=np.array([0.5], np.float32),
+               prob=np.array([1.0, 0.25], np.float32), c_in=np.full((m, n), 0x4000, np.uint16))
+    out = oracle.grouped_gemm(_problem(1, m, n, k, ab="e4m3", act="dsrelu", d="bf16"), arr)
+    np.testing.assert_array_equal(out["dc"], np.repeat([[2.0], [0.5]], n, axis=1))
+    np.testing.assert_array_equal(out["dprob"], [128.0, 128.0])
+    np.testing.assert_array_equal(out["amax"], [2.0])
+
+
 def _bs_dswiglu_case(d_dtype):
     """Two experts of 2 rows, MXFP8 A = 1.0 and B = 1/32 (scale byte 122), K = 64:
     acc = 2; alpha = (0.5, 1) -> R = (0.5, 2).  C_in: input blocks 2.0, gate
