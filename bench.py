@@ -33,7 +33,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"e4m3": 5000.0, "e2m1x2": 10100.0, "bf16": 2500.0}   # dense MFMA peaks, MI355X
 HBM_GBS = 8000.0
-KERNEL_SOURCES = ["moe_grouped_block_amd/csrc/moegg_kernels.hip", "moe_grouped_block_amd/csrc/moegg_internal.h"]
+KERNEL_SOURCES = ["moe_grouped_block_amd/csrc/grouped_gemm.h", "moe_grouped_block_amd/csrc/moegg_kernels.hip",
+                  "moe_grouped_block_amd/csrc/inst_e4m3.hip", "moe_grouped_block_amd/csrc/inst_e2m1.hip",
+                  "moe_grouped_block_amd/csrc/inst_bf16.hip", "moe_grouped_block_amd/csrc/moegg_internal.h"]
 TRAFFIC_FILE = "profiles/grouped_gemm_fc1_swiglu_l64_traffic.md"
 
 

@@ -1,0 +1,1195 @@
+// The fused kernel of libmoegg for gfx950 (CDNA4): contiguous grouped
+// block-scaled GEMM with fused epilogue.  Included by one translation unit
+// per operand family (inst_*.hip), which instantiate it.
+//
+// Method ("Grouped GEMM + Quant (SM100)", "Grouped GEMM + SwiGLU (SM100)",
+// "Grouped GEMM + sReLU (SM100)", "Grouped GEMM + dGLU (SM100)", §Equations):
+// rows m of A in [padded_offsets[g-1], padded_offsets[g]) are multiplied by
+// expert g's weight B[g] (N x K, K-major) with per-32-element E8M0 block
+// scales on both operands, scaled by alpha_g (alpha_g^2 for the dSwiGLU
+// backward), then the activation / gating / output-formatting epilogue.
+//
+// Mapping onto CDNA4:
+//  * persistent workgroups, one per CU (8 wave64s, about 140 KB of LDS),
+//    walk a list of 256 x 256 output tiles.  A tile never straddles two
+//    experts: expert g's padded rows are cut into 256-row tiles plus one
+//    128-row tile when its row count is an odd number of 128-row blocks.
+//    Each workgroup builds the per-expert tile prefix sums in LDS from
+//    padded_offsets once and maps a linear tile index to (expert, first row,
+//    first column) by binary search.  Linear tile indices are handed out so
+//    that the workgroups resident on one XCD (one L2) work on a compact patch
+//    of neighbouring tiles at any time.
+//  * the contraction runs on the block-scaled matrix cores:
+//    v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 or E2M1 operands, one E8M0 byte
+//    per lane and operand selects the scale of that lane's 32 K-elements) or
+//    v_mfma_f32_32x32x16_bf16.  The weight tile is the instruction's first
+//    operand and the token tile the second, so an accumulator lane holds one
+//    token row and 16 output columns (4 runs of 4 contiguous columns): row
+//    reductions are lane-local.
+//  * K advances in steps of 128 bytes per row (128 E4M3, 256 E2M1 or 64 BF16
+//    elements).  Two LDS stages (A, B and their scale words) are filled by
+//    direct global -> LDS loads one step ahead; the first stage of the next
+//    tile is loaded while the current tile's epilogue runs.
+//  * the epilogue works on the fp32 accumulators in registers; column
+//    blocks of the FP8 output are reduced through a per-wave LDS transpose.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "moegg_internal.h"
+
+namespace moegg {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));   // native vectors (HIP's uint4
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));   // struct defeats SROA)
+
+constexpr int kBK = 128;          // bytes of K per row and pipeline stage (one cache line)
+constexpr int kBandM = 8;         // m-tiles per raster band (L2 reuse of B)
+constexpr int kTPitch = 36;       // floats per row of the epilogue transpose (see quant_tile)
+constexpr int kScratch = 8192;    // bytes of epilogue scratch per wave
+
+// Unrolled loop whose index is a compile-time constant (instruction
+// immediates such as the MFMA scale byte selectors need one).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRcp448 = 1.0f / 448.0f;   // rcp_max of E4M3, rounded to fp32
+
+// ---------------------------------------------------------------------------
+// device codecs
+// ---------------------------------------------------------------------------
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// E8M0 byte of the smallest power of two >= sf (sf >= 0), clamped to [0, 254].
+__device__ __forceinline__ uint32_t e8m0_ceil(float sf) {
+  const uint32_t u = __float_as_uint(sf);
+  const uint32_t e = u >> 23, m = u & 0x7FFFFFu;
+  uint32_t b = (e == 0) ? (m > 0x400000u ? 1u : 0u) : e + (m != 0u ? 1u : 0u);
+  return b > 254u ? 254u : b;
+}
+
+// 2^(127 - byte), exact.
+__device__ __forceinline__ float e8m0_inverse(uint32_t byte) {
+  return byte < 254u ? __uint_as_float((254u - byte) << 23) : __uint_as_float(0x00400000u);
+}
+
+// E8M0 byte -> its value 2^(byte - 127) as fp32 (byte 0 is the subnormal
+// 2^-127), the form the scaled conversions take.
+__device__ __forceinline__ float e8m0_value(uint32_t byte) {
+  return __uint_as_float(byte ? byte << 23 : 0x00400000u);
+}
+
+// Four fp32 -> four E4M3 codes, RNE by the conversion unit, packed
+// little-endian (a is the lowest byte).  The inputs are block-scaled values,
+// |x| <= 448 (1 + 2^-22) for finite D, which the conversion rounds to +-448;
+// non-finite D gives the E4M3 NaN code.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// Same for x / 2^(byte - 127) with the block scale folded into the conversion
+// (v_cvt_scalef32_pk_fp8_f32 takes the exponent of `scale`): equal to
+// e4m3x4(x * 2^(127 - byte)) for every finite x.
+__device__ __forceinline__ uint32_t e4m3x4_scaled(float a, float b, float c, float d, float scale) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  v2s w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, a, b, scale, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, scale, true);
+  return static_cast<uint32_t>(static_cast<uint16_t>(w.x)) | (static_cast<uint32_t>(static_cast<uint16_t>(w.y)) << 16);
+}
+
+// sigmoid(x) = 1 / (1 + 2^(-x log2 e)); saturates to 0 / 1 at the extremes.
+__device__ __forceinline__ float sigmoid_f(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
+}
+
+// tanh(x) for x >= 0: odd Taylor series below 1/8 (error < 2e-10), else
+// (1 - e^-2x) / (1 + e^-2x).  Result <= 1.
+__device__ __forceinline__ float tanh_nonneg(float x) {
+  const float x2 = x * x;
+  const float series = x * (1.0f + x2 * (-1.0f / 3.0f + x2 * (2.0f / 15.0f + x2 * (-17.0f / 315.0f))));
+  const float e = __builtin_amdgcn_exp2f(-2.0f * kLog2e * x);
+  const float big = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
+  return x < 0.125f ? series : big;
+}
+
+// Cross-lane helpers on the VALU (DPP and the gfx950 permlane swaps), no LDS.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Max over the 32 lanes of each half-wave (lanes 0-31 and 32-63 separately):
+// pairs, quads, 8-lane halves of a row (mirror), 16-lane rows (mirror), then
+// rows 0/1 and 2/3 exchanged by v_permlane16_swap.
+__device__ __forceinline__ float half_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));     // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));     // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));    // row_half_mirror
+  x = fmaxf(x, dpp_f<0x140>(x));    // row_mirror
+  const v2u sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw.x), __uint_as_float(sw.y));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = half_max(v);
+  const v2u sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(sw.x), __uint_as_float(sw.y));
+}
+
+// Sum of the two halves' values (lane l and lane l ^ 32), in every lane.
+__device__ __forceinline__ float halves_sum(float v) {
+  const v2u sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(sw.x) + __uint_as_float(sw.y);
+}
+
+// Max of the two halves' values, in every lane.
+__device__ __forceinline__ float halves_max(float v) {
+  const v2u sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(sw.x), __uint_as_float(sw.y));
+}
+
+// The value lane l ^ 32 holds, in every lane.
+__device__ __forceinline__ uint32_t other_half(uint32_t v, int hi) {
+  const v2u sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return hi ? sw.x : sw.y;
+}
+
+// max(|a|, |b|, c) (one v_max3_f32 with abs modifiers).
+__device__ __forceinline__ float max_abs2(float c, float a, float b) {
+  return fmaxf(fmaxf(fabsf(a), fabsf(b)), c);
+}
+
+// Store 16 values of one row (one 32-column tile) as bf16: 4 runs of 4.
+__device__ __forceinline__ void store_bf16_tile(uint8_t* base, int64_t m, int ld, int col, int hi,
+                                                const float* v) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v2u w;
+    w.x = bf16_rne(v[4 * j + 0]) | (bf16_rne(v[4 * j + 1]) << 16);
+    w.y = bf16_rne(v[4 * j + 2]) | (bf16_rne(v[4 * j + 3]) << 16);
+    *reinterpret_cast<v2u*>(base + (m * ld + col + 8 * j + 4 * hi) * 2) = w;
+  }
+}
+
+// Store one row's 32 E4M3 codes of a 32-column tile.  This lane holds the
+// codes of columns 8j + 4*hi + [0, 4) (w[j]).  v_permlane32_swap(x, y)
+// exchanges x of lanes 32-63 with y of lanes 0-31: with x = w[j], y = w[j+2]
+// lane hi = 0 ends with (own w[j], partner's w[j]) = columns 8j + [0, 8) and
+// lane hi = 1 with (partner's w[j+2], own w[j+2]) = columns 16 + 8j + [0, 8),
+// so lane hi = 0 stores columns [0, 16) and lane hi = 1 columns [16, 32),
+// one 16-byte store each.
+__device__ __forceinline__ void store_e4m3_row(uint8_t* dst_row, int hi, const uint32_t* w) {
+  const v2u s0 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+  const v2u s1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+  *reinterpret_cast<v4u*>(dst_row + 16 * hi) = v4u{s0.x, s0.y, s1.x, s1.y};
+}
+
+// FP8 row + column quantisation of one 32 x 32 output tile ("Grouped GEMM +
+// Quant (SM100)", §Equations Step 3 and §Diagram Row/Col Quantize).
+// dn[v] = D * norm_const for row m (this lane's row) and column
+// 8*(v/4) + 4*hi + v%4 of the tile.  A row block is one row's 32 values
+// (this lane and lane ^ 32); a column block is one column over the tile's 32
+// rows, reduced through the wave's LDS scratch:
+//   T: 32 rows x kTPitch floats, row r at T + r * kTPitch (16-byte writes of
+//      4 columns; the pitch keeps every 16-lane group of writes on distinct
+//      banks),
+//   S: 32 floats, the inverse column scales.
+// Lanes 0-31 read rows 0-15 of column l, lanes 32-63 rows 24-31 then 16-23,
+// so that both halves of a 64-lane read hit complementary bank ranges.
+// Returns the E8M0 byte of this lane's column (l % 32) block.
+__device__ __forceinline__ uint32_t quant_tile(const KernelArgs& p, float* T, float* S, int m, int ocol, int hi,
+                                               int l32, const float* dn) {
+  // the previous call's cross-lane reads of T and S stay ahead of this
+  // call's writes
+  __builtin_amdgcn_wave_barrier();
+  // ---- row block ----
+  float ra = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 16; v += 2) ra = max_abs2(ra, dn[v], dn[v + 1]);
+  ra = halves_max(ra);
+  const uint32_t br = e8m0_ceil(ra * kRcp448);
+  const float sr = e8m0_value(br);
+
+  // ---- column blocks through LDS ----
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<v4f*>(T + l32 * kTPitch + 8 * j + 4 * hi) = v4f{dn[4 * j], dn[4 * j + 1], dn[4 * j + 2], dn[4 * j + 3]};
+  // lanes read what other lanes of the wave wrote: keep the compiler from
+  // moving LDS accesses across this point (the LDS executes one wave's
+  // accesses in order)
+  __builtin_amdgcn_wave_barrier();
+  float cm = 0.0f;
+  const float* c0 = T + l32 + (hi ? 24 * kTPitch : 0);      // rows [0, 8) / [24, 32)
+  const float* c1 = T + l32 + (hi ? 8 * kTPitch : 0);       // rows [8, 16) / [16, 24) at r + 8
+#pragma unroll
+  for (int r = 0; r < 8; r += 2) cm = max_abs2(cm, c0[r * kTPitch], c0[(r + 1) * kTPitch]);
+#pragma unroll
+  for (int r = 8; r < 16; r += 2) cm = max_abs2(cm, c1[r * kTPitch], c1[(r + 1) * kTPitch]);
+  cm = halves_max(cm);
+  const uint32_t bc = e8m0_ceil(cm * kRcp448);
+  if (hi == 0) S[l32] = e8m0_inverse(bc);
+  __builtin_amdgcn_wave_barrier();
+  v4f sc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sc[j] = *reinterpret_cast<const v4f*>(S + 8 * j + 4 * hi);
+
+  uint32_t wr[4], wc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    wr[j] = e4m3x4_scaled(dn[4 * j], dn[4 * j + 1], dn[4 * j + 2], dn[4 * j + 3], sr);
+    wc[j] = e4m3x4(dn[4 * j] * sc[j].x, dn[4 * j + 1] * sc[j].y, dn[4 * j + 2] * sc[j].z, dn[4 * j + 3] * sc[j].w);
+  }
+  const int64_t rowoff = static_cast<int64_t>(m) * p.n_out + ocol;
+  store_e4m3_row(p.d + rowoff, hi, wr);
+  store_e4m3_row(p.d_col + rowoff, hi, wc);
+  if (hi == 0) p.sfd_row[static_cast<int64_t>(m) * (p.n_out >> 5) + (ocol >> 5)] = static_cast<uint8_t>(br);
+  return bc;
+}
+
+// ---------------------------------------------------------------------------
+// the fused kernel
+// ---------------------------------------------------------------------------
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane i of the wave writes lds_base + 16 i.  `lds_base` must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+// Same with 4 bytes per lane (global_load_lds_dword).
+__device__ __forceinline__ void dma4(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// One output tile: rows [row0, row0 + rows) of expert g, GEMM columns
+// [n0, n0 + 256).  rows is 0 (nothing to store), 128 or 256.
+struct Tile {
+  int g, row0, rows, n0;
+  const uint8_t* bg;    // expert g's weights (row 0) and SFB words (row 0 of plane 0)
+  const uint8_t* sg;
+};
+
+template <int AB, int ACT, int OUT>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p) {
+  constexpr int BM = kBM, BN = kBN, BK = kBK;
+  constexpr int NW = kThreads / 64;  // 8 waves: 2 (m) x 4 (n), waves w and w+4 share a SIMD
+  constexpr int WM = BM / 2;         // rows per wave (128)
+  constexpr int WN = BN / 4;         // GEMM columns per wave (64)
+  constexpr int TM = WM / 32;        // 32-row MFMA tiles per wave (4)
+  constexpr int TN = WN / 32;        // 32-column MFMA tiles per wave (2)
+  constexpr bool MX = AB != AB_BF16;
+  constexpr int SW = AB == AB_E2M1 ? 2 : 1;          // scale words per row per step
+  constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
+  constexpr int AH_BYTES = A_BYTES / 2;              // one of the two A row halves
+  constexpr int SA_WORDS = MX ? SW * BM : 1, SB_WORDS = MX ? SW * BN : 1;
+  static_assert(NW == 8 && TM == 4 && TN == 2, "tile shape");
+  static_assert(2 * kScratch <= AH_BYTES && 4 * kScratch <= B_BYTES, "epilogue scratch lives in stage 1");
+
+  // Two LDS stages (about 66 KB each), one distinct array per stage, operand
+  // and A row half: the compiler can then tell them apart and adds no
+  // conservative waits for the direct-to-LDS loads (the explicit waits below
+  // order them).  A's rows are split by bit 6 of the tile row: rows with it
+  // clear (the first two 32-row MFMA tiles of each wave row) sit in sAl,
+  // the others in sAh, each half at index (r & 63) | ((r >> 1) & 64).
+  // Rows are BK = 128 bytes, a whole cache line, so every load instruction
+  // moves whole lines; the 16-byte chunk c of array row i sits at chunk slot
+  // c ^ ((i >> 1) & 7).  The LDS has 64 four-byte banks (256 bytes), so two
+  // consecutive 128-byte rows fill one bank window and a 16-lane group of
+  // 16-byte reads (16 consecutive rows, one chunk each) hits 16 distinct bank
+  // quads.  Stage 1's A and B areas double as the epilogue scratch.
+  __shared__ __attribute__((aligned(16))) uint8_t sAl0[AH_BYTES], sAh0[AH_BYTES], sAl1[AH_BYTES], sAh1[AH_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sB0[B_BYTES], sB1[B_BYTES];
+  __shared__ __attribute__((aligned(16))) uint32_t sSA0[SA_WORDS], sSA1[SA_WORDS];
+  __shared__ __attribute__((aligned(16))) uint32_t sSB0[SB_WORDS], sSB1[SB_WORDS];
+  __shared__ int32_t sTiles[1025];   // m-tiles before expert g, g = 0..L
+  __shared__ float sPr[kThreads / 64][kBM / 2];   // prob of each wave's 128 rows (epilogue)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int L = p.num_groups;
+  const int vm = static_cast<int>(p.valid_m);
+
+  // ---- per-expert tile prefix sums (once per workgroup) ----
+  // expert g owns P_g = (po[g] - po[g-1]) / 128 row blocks -> ceil(P_g / 2)
+  // m-tiles.  Counts are clamped so that inconsistent offsets can neither
+  // overflow the sums nor address rows outside [0, valid_m).
+  if (wave == 0) {
+    int base = 0;
+    for (int c0 = 0; c0 < L; c0 += 64) {
+      const int gi = c0 + lane;
+      int cnt = 0;
+      if (gi < L) {
+        const int end = p.po[gi], beg = gi ? p.po[gi - 1] : 0;
+        const int blocks = min(max(end - beg, 0) >> 7, vm >> 7);
+        cnt = (blocks + 1) >> 1;
+      }
+      int x = cnt;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+      }
+      if (gi < L) sTiles[gi + 1] = min(base + x, 1 << 30);
+      base = min(base + __shfl(x, 63), 1 << 30);
+    }
+    if (lane == 0) sTiles[0] = 0;
+  }
+  __syncthreads();
+  const int m_tiles = sTiles[L];
+  const int n_tiles = p.n_tiles;
+  // the host guarantees (valid_m / 128 + L) / 2 * n_tiles < 2^31
+  const int total = __builtin_amdgcn_readfirstlane(m_tiles * n_tiles);
+
+  // Linear tile index -> tile.  Workgroups are dispatched round-robin over
+  // the 8 XCDs (each with its own L2): workgroup w runs on XCD w % 8.  The
+  // workgroups of XCD x take the contiguous slots [x*q + min(x, r), ...) of
+  // the nwg slots, and pass i of slot s handles linear tile i * nwg + s, so
+  // the tiles in flight on one XCD are consecutive.  Linear tiles run in
+  // bands of kBandM m-tiles, m fastest, so consecutive tiles share B (same
+  // expert and columns) or A (same rows) through L2.
+  const int nwg = static_cast<int>(gridDim.x);
+  const int wg = static_cast<int>(blockIdx.x);
+  const int slot = [&] {
+    const int xcd = wg & 7, j = wg >> 3, q = nwg >> 3, r = nwg & 7;
+    return xcd * q + min(xcd, r) + j;
+  }();
+  auto tile_of = [&](int t) __attribute__((always_inline)) -> Tile {
+    const int band_size = kBandM * n_tiles;
+    const int band = t / band_size;
+    const int in_band = t - band * band_size;
+    const int band_rows = min(kBandM, m_tiles - band * kBandM);
+    const int nt = in_band / band_rows;
+    const int mt = band * kBandM + (in_band - nt * band_rows);
+    // expert: the largest g with sTiles[g] <= mt (empty experts skipped)
+    int lo = 0, up = L;
+    while (up - lo > 1) {
+      const int mid = (lo + up) >> 1;
+      if (sTiles[mid] <= mt) lo = mid; else up = mid;
+    }
+    Tile tl;
+    tl.g = __builtin_amdgcn_readfirstlane(lo);
+    // first row: a multiple of 128 in [0, valid_m - 128] whatever the offsets
+    // hold (valid_m is a positive multiple of 128 here); rows past the
+    // expert's end or valid_m are not stored
+    const int64_t beg = lo ? p.po[lo - 1] : 0, end = p.po[lo];
+    const int64_t jt = min(mt - sTiles[lo], vm >> 8);
+    const int r0 = static_cast<int>(min((max(beg, int64_t{0}) + jt * BM) & ~int64_t{127}, int64_t{vm - 128}));
+    const int64_t rows = min(min(int64_t{BM}, end - r0), int64_t{vm - r0});
+    tl.row0 = __builtin_amdgcn_readfirstlane(r0);
+    tl.rows = __builtin_amdgcn_readfirstlane(static_cast<int>(max(rows, int64_t{0})) & ~127);
+    tl.n0 = __builtin_amdgcn_readfirstlane(nt * BN);
+    // dense weights: expert g's rows follow the previous experts'; discrete
+    // weights: its own allocations (low 4 bits cleared: 16-byte aligned
+    // loads).  Resolved here, at tile set-up, so that the operand loads of
+    // the K loop need no branch.
+    if (p.b_ptrs) {
+      tl.bg = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(p.b_ptrs[tl.g]) & ~uintptr_t{15});
+      tl.sg = p.sfb_ptrs ? reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(p.sfb_ptrs[tl.g]) &
+                                                            ~uintptr_t{15})
+                         : nullptr;
+    } else {
+      tl.bg = p.b + static_cast<int64_t>(tl.g) * p.n * p.row_bytes;
+      tl.sg = p.sfb ? p.sfb + static_cast<int64_t>(tl.g) * p.n * 4 : nullptr;
+    }
+    return tl;
+  };
+
+  // ---- direct global -> LDS staging ----
+  // One wave instruction fills 8 rows (1 KB): lane i writes row 8j + i/8 of
+  // its group, chunk slot i%8, i.e. logical chunk (i%8) ^ ((row >> 1) & 7).
+  // Wave w fills B rows [32w, 32w+32) (4 instructions) and rows
+  // [16w, 16w+16) of each A half (2 + 2).  A rows past the tile's valid rows
+  // repeat its last row and B rows past N repeat row N-1 (loaded, never
+  // stored).  Scale dwords ride along, one per lane: E4M3 (one dword per row
+  // and step): waves 0-3 load A rows, waves 4-7 B rows; E2M1 (two dwords):
+  // two loads per wave; BF16 has none.
+  // A stage's loads come in two sets: the early set (B, the low A half and
+  // all scale words: everything the first operand cluster of a step reads)
+  // and the late set (the high A half, read by the second cluster).
+  constexpr int S_LOADS = AB == AB_E4M3 ? 1 : AB == AB_E2M1 ? 2 : 0;
+  constexpr int SL = S_LOADS > 0 ? S_LOADS : 1;
+  constexpr int S_HALF = AB == AB_E4M3 ? 4 : 8;      // scale jobs of A (the rest are B's)
+  constexpr int N_EA = 2 + S_LOADS, N_EB = 4, N_EARLY = N_EA + N_EB, N_LATE = 2;
+
+  struct Src {
+    const uint8_t* a;    // wave-uniform bases
+    const uint8_t* b;
+    uint32_t oa[4];      // per-lane byte offsets: low half j = 0, 1; high half 2, 3
+    uint32_t ob[4];
+    const uint8_t* s[SL];
+  };
+  auto make_src = [&](const Tile& tl) __attribute__((always_inline)) {
+    // per-lane values are rebuilt from an opaque copy of the lane id instead
+    // of being kept live (and spilled) across the K loop
+    int lid = lane;
+    asm volatile("" : "+v"(lid));
+    const int lrow = lid >> 3;
+    Src s;
+    s.a = p.a + static_cast<int64_t>(tl.row0) * p.row_bytes;
+    s.b = tl.bg + static_cast<int64_t>(tl.n0) * p.row_bytes;
+    const int alast = max(min(tl.rows, vm - tl.row0), 1) - 1;   // last loadable row of the tile
+    const int blast = p.n - 1 - tl.n0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = wave * 16 + (j & 1) * 8 + lrow;              // row within the half
+      const int r = (i & 63) | ((j >> 1) << 6) | ((i & 64) << 1);
+      s.oa[j] = static_cast<uint32_t>(min(r, alast) * p.row_bytes + (((lid & 7) ^ ((i >> 1) & 7)) * 16));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wave * 32 + j * 8 + lrow;
+      s.ob[j] = static_cast<uint32_t>(min(r, blast) * p.row_bytes + (((lid & 7) ^ ((r >> 1) & 7)) * 16));
+    }
+    if constexpr (MX) {
+#pragma unroll
+      for (int u = 0; u < S_LOADS; ++u) {
+        // job (wave * S_LOADS + u): E4M3 jobs 0-3 A rows, 4-7 B rows;
+        // E2M1 jobs 0-7 A (word, quarter), 8-15 B (word, quarter)
+        const int job = wave * S_LOADS + u;
+        const bool isA = job < S_HALF;
+        const int jj = isA ? job : job - S_HALF;
+        const int word = jj >> 2, rowsel = (jj & 3) * 64 + lid;
+        // word planes: word j of row r at 4 * (j * rows + r) (rows = valid_m for
+        // SFA, sfb_rows for SFB: L * N dense with row g * N + n, N discrete);
+        // step ks uses planes SW*ks .. SW*ks + SW-1
+        s.s[u] = isA ? p.sfa + (static_cast<int64_t>(word) * vm + tl.row0 + min(rowsel, alast)) * 4
+                     : tl.sg + (static_cast<int64_t>(word) * p.sfb_rows + tl.n0 + min(rowsel, blast)) * 4;
+      }
+    }
+    return s;
+  };
+
+  // One LDS stage: the two A halves, B, scale words.
+  struct Stage {
+    uint8_t* al;
+    uint8_t* ah;
+    uint8_t* b;
+    uint32_t* sa;
+    uint32_t* sb;
+  };
+  const Stage st0{sAl0, sAh0, sB0, sSA0, sSB0};
+  const Stage st1{sAl1, sAh1, sB1, sSA1, sSB1};
+  // early set, first part: the low A half and the scale words
+  auto issue_ea = [&](const Src& s, int ks, const Stage& d) __attribute__((always_inline)) {
+    const int kb = ks * BK;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(s.a + s.oa[j] + kb, d.al + (wave * 16 + j * 8) * BK);
+    if constexpr (MX) {
+#pragma unroll
+      for (int u = 0; u < S_LOADS; ++u) {
+        // LDS words: word w of row r at [w * rows + r], 64 rows per load
+        const int job = wave * S_LOADS + u;
+        const bool isA = job < S_HALF;
+        const int jj = isA ? job : job - S_HALF;
+        uint32_t* dst = (isA ? d.sa : d.sb) + (jj >> 2) * (isA ? BM : BN) + (jj & 3) * 64;
+        const int64_t plane = isA ? static_cast<int64_t>(vm) * 4 : p.sfb_rows * 4;
+        dma4(s.s[u] + static_cast<int64_t>(ks) * SW * plane, dst);
+      }
+    }
+  };
+  // early set, second part: B row load j (0..3)
+  auto issue_eb = [&](const Src& s, int ks, const Stage& d, int j) __attribute__((always_inline)) {
+    dma16(s.b + s.ob[j] + ks * BK, d.b + (wave * 32 + j * 8) * BK);
+  };
+  // late set: high A half load j (0..1)
+  auto issue_l = [&](const Src& s, int ks, const Stage& d, int j) __attribute__((always_inline)) {
+    dma16(s.a + s.oa[2 + j] + ks * BK, d.ah + (wave * 16 + j * 8) * BK);
+  };
+  // a whole stage, in the order early (first part, second part), late
+  auto issue = [&](const Src& s, int ks, const Stage& d) __attribute__((always_inline)) {
+    issue_ea(s, ks, d);
+#pragma unroll
+    for (int j = 0; j < N_EB; ++j) issue_eb(s, ks, d, j);
+#pragma unroll
+    for (int j = 0; j < N_LATE; ++j) issue_l(s, ks, d, j);
+  };
+
+  v16f acc[TM][TN];
+  // The K loop runs in clusters: an M cluster reads operands from LDS into
+  // registers and issues direct loads, a C cluster runs MFMAs only.  Step s
+  // is M0 (B and the A tiles 0, 1 of the wave, all scale words), C0 (those
+  // A tiles), M1 (A tiles 2, 3), C1 (those, with B still in registers).  The
+  // two waves sharing a SIMD (w and w + 4) run one cluster apart, so one of
+  // them issues MFMAs while the other reads LDS and issues loads.
+  // A lane's 16-byte pieces of a 32-row tile for one step: chunks hi + 2c,
+  // c = 0..3.  E4M3 window kk uses pieces 2kk, 2kk+1 (K [16hi, 16hi+16) and
+  // [32+16hi, 48+16hi) of the window; its scale byte covers the 32-element
+  // block hi of the window); E2M1 (32 elements) and BF16 (8 elements) window
+  // kk use piece kk.
+  typedef v4u Pieces[4];
+  auto read_tile = [&](const uint8_t* base, int l32, int hi, Pieces& x) __attribute__((always_inline)) {
+    const int sw = (l32 >> 1) & 7;      // swizzle of this lane's rows (tiles start at multiples of 32)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[c] = *reinterpret_cast<const v4u*>(base + (((hi + 2 * c) ^ sw) * 16));
+  };
+  auto settle = [&](Pieces& x) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(x[c]));
+  };
+  struct Ops0 {
+    Pieces a[2], b[TN];
+    uint32_t sa[TM][SW], sb[TN][SW];
+  };
+  struct Ops1 {
+    Pieces a[2];
+  };
+  // M0: B, A tiles 0, 1 and the scale words (fin0 waits for them and
+  // shifts the scale words so that byte 0 / 2 is this lane's block of an
+  // even / odd window)
+  auto read0 = [&](const Stage& st) __attribute__((always_inline)) {
+    int lid = lane;
+    asm volatile("" : "+v"(lid));
+    const int l32 = lid & 31, hi = lid >> 5;
+    Ops0 o;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) read_tile(st.b + (wn * WN + tn * 32 + l32) * BK, l32, hi, o.b[tn]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) read_tile(st.al + (wm * 64 + t * 32 + l32) * BK, l32, hi, o.a[t]);
+    if constexpr (MX) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int w = 0; w < SW; ++w) o.sa[tm][w] = st.sa[w * BM + wm * WM + tm * 32 + l32];
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int w = 0; w < SW; ++w) o.sb[tn][w] = st.sb[w * BN + wn * WN + tn * 32 + l32];
+    }
+    return o;
+  };
+  auto fin0 = [&](Ops0& o) __attribute__((always_inline)) {
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) settle(o.b[tn]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) settle(o.a[t]);
+    if constexpr (MX) {
+      int lid = lane;
+      asm volatile("" : "+v"(lid));
+      const int sh = 8 * (lid >> 5);
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int w = 0; w < SW; ++w) {
+          asm volatile("" : "+v"(o.sa[tm][w]));
+          o.sa[tm][w] >>= sh;
+        }
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int w = 0; w < SW; ++w) {
+          asm volatile("" : "+v"(o.sb[tn][w]));
+          o.sb[tn][w] >>= sh;
+        }
+    }
+  };
+  // M1: A tiles 2, 3
+  auto read1 = [&](const Stage& st) __attribute__((always_inline)) {
+    int lid = lane;
+    asm volatile("" : "+v"(lid));
+    const int l32 = lid & 31, hi = lid >> 5;
+    Ops1 o;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) read_tile(st.ah + (wm * 64 + t * 32 + l32) * BK, l32, hi, o.a[t]);
+    return o;
+  };
+  auto fin1 = [&](Ops1& o) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) settle(o.a[t]);
+  };
+  // C cluster: MFMA tiles tm0, tm0 + 1 (A pieces a[0], a[1]) x all tn, all
+  // windows of the step
+  // `hook(i)` runs right after the cluster's MFMA number i (0 .. NMMA-1)
+  constexpr int NWIN = AB == AB_E4M3 ? 2 : 4;
+  constexpr int NMMA = NWIN * 2 * TN;
+  auto mma = [&](int tm0, const Pieces* a, const Ops0& o0, auto&& hook) __attribute__((always_inline)) {
+    static_for<0, NWIN>([&](auto kc) {
+      constexpr int kk = decltype(kc)::value;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int mi = (kk * 2 + t) * TN + tn;
+          v16f& c = acc[tm0 + t][tn];
+          if constexpr (AB == AB_E4M3) {
+            const v4u a0 = a[t][2 * kk], a1 = a[t][2 * kk + 1], b0 = o0.b[tn][2 * kk], b1 = o0.b[tn][2 * kk + 1];
+            const v8i fa{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+            const v8i fb{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, c, 0, 0, kk * 2, (int)o0.sb[tn][0], kk * 2,
+                                                                (int)o0.sa[tm0 + t][0]);
+          } else if constexpr (AB == AB_E2M1) {
+            const v4u a0 = a[t][kk], b0 = o0.b[tn][kk];
+            const v8i fa{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
+            const v8i fb{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
+            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, c, 4, 4, (kk & 1) * 2, (int)o0.sb[tn][kk >> 1],
+                                                                (kk & 1) * 2, (int)o0.sa[tm0 + t][kk >> 1]);
+          } else {
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, o0.b[tn][kk]),
+                                                        __builtin_bit_cast(v8bf, a[t][kk]), c, 0, 0, 0);
+          }
+          hook(mi);
+        }
+    });
+  };
+
+  // ---- epilogue of one tile (accumulators -> outputs) ----
+  float nc = 1.0f;
+  if constexpr (OUT == OUT_E4M3) nc = p.norm_const[0];
+  // this wave's epilogue scratch: 8 KB of stage 1 (free once every wave has
+  // finished the tile's last K-step)
+  float* scratch = reinterpret_cast<float*>(wave < 2   ? sAl1 + wave * kScratch
+                                            : wave < 4 ? sAh1 + (wave - 2) * kScratch
+                                                       : sB1 + (wave - 4) * kScratch);
+  float* sT = scratch;
+  float* sS = scratch + 32 * kTPitch;
+
+  // Per-tile epilogue factors: alpha_g (a scalar load issued before the
+  // tile's last K-step) and prob of the wave's 128 rows, copied to LDS by two
+  // direct loads issued just before the next tile's first stage, so that no
+  // register holds them across the last K-step.
+  struct EpiIn {
+    float alpha;
+  };
+  auto epi_in = [&](const Tile& tl) __attribute__((always_inline)) {
+    EpiIn e;
+    e.alpha = p.alpha[tl.g];
+    return e;
+  };
+  auto load_prob = [&](const Tile& tl) __attribute__((always_inline)) {
+    const int mb = min(tl.row0 + wm * WM, vm - WM);      // rows of idle waves: any valid ones
+    dma4(p.prob + mb + lane, sPr[wave]);
+    dma4(p.prob + mb + 64 + lane, sPr[wave] + 64);
+  };
+
+  auto epilogue = [&](const Tile& tl, const EpiIn& ein) __attribute__((always_inline)) {
+    if (wm * WM >= tl.rows) return;     // rows of a 128-row tile (or an empty one) handled by wm = 0
+    // lane-dependent addresses are rebuilt here from an opaque copy of the
+    // lane id rather than kept live (and spilled) across the K loop
+    int lid = lane;
+    asm volatile("" : "+v"(lid));
+    const int l32 = lid & 31, hi = lid >> 5;
+    const int g = tl.g;
+    const float alpha = ein.alpha;
+    const int mbase = tl.row0 + wm * WM;
+    const int nbase = tl.n0 + wn * WN;
+    float pr[TM];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) pr[tm] = sPr[wave][tm * 32 + l32];
+
+    if constexpr (ACT == ACT_DSWIGLU) {
+      // R = alpha^2 acc; X = beta * C_in with blocks [input_b | gate_b]
+      // ("Grouped GEMM + dGLU (SM100)", BF16 contract equations and the
+      // block-scaled contract's Step 2): d_input = R prob swish(gate),
+      // d_gate = R prob input s (1 + gate (1 - s)), dprob += R input swish
+      const float a2 = alpha * alpha;
+      const float beta = p.beta[g];
+      const int ld2 = 2 * p.n;
+      // block-scaled operands with a BF16 output: amax per group of the
+      // d_input blocks and of the d_gate blocks (amax of shape (L, 2))
+      constexpr bool AMAX2 = MX && OUT == OUT_BF16;
+      float amax_in = 0.0f, amax_gt = 0.0f;
+      uint32_t colw_in[TN], colw_gt[TN];      // E4M3: column scale bytes of 4 row blocks
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) colw_in[tn] = colw_gt[tn] = 0;
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int m = mbase + tm * 32 + l32;
+        float dp = 0.0f;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int ncol = nbase + tn * 32;
+          if (ncol >= p.n) continue;
+          // keep this tile's C_in loads here (hoisting every tile's loads
+          // ahead of the FP8 quantisation would spill)
+          if constexpr (OUT == OUT_E4M3) asm volatile("" ::: "memory");
+          const int64_t xoff = static_cast<int64_t>(m) * ld2 + 2 * ncol;   // block b = ncol/32 starts at 64b
+          float xin[16], xg[16];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const v2u wi = *reinterpret_cast<const v2u*>(p.c_in + xoff + 8 * j + 4 * hi);
+            const v2u wg = *reinterpret_cast<const v2u*>(p.c_in + xoff + 32 + 8 * j + 4 * hi);
+            xin[4 * j + 0] = __uint_as_float(wi.x << 16);
+            xin[4 * j + 1] = __uint_as_float(wi.x & 0xFFFF0000u);
+            xin[4 * j + 2] = __uint_as_float(wi.y << 16);
+            xin[4 * j + 3] = __uint_as_float(wi.y & 0xFFFF0000u);
+            xg[4 * j + 0] = __uint_as_float(wg.x << 16);
+            xg[4 * j + 1] = __uint_as_float(wg.x & 0xFFFF0000u);
+            xg[4 * j + 2] = __uint_as_float(wg.y << 16);
+            xg[4 * j + 3] = __uint_as_float(wg.y & 0xFFFF0000u);
+          }
+          float din[16], dgt[16];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float r = a2 * acc[tm][tn][v];
+            const float x = beta * xin[v];
+            const float gt = beta * xg[v];
+            const float s = sigmoid_f(gt);
+            const float swish = gt * s;
+            din[v] = r * pr[tm] * swish;
+            dgt[v] = r * pr[tm] * x * s * (1.0f + gt * (1.0f - s));
+            dp += r * x * swish;
+          }
+          if constexpr (OUT == OUT_BF16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              v2u w;
+              w.x = bf16_rne(din[4 * j]) | (bf16_rne(din[4 * j + 1]) << 16);
+              w.y = bf16_rne(din[4 * j + 2]) | (bf16_rne(din[4 * j + 3]) << 16);
+              *reinterpret_cast<v2u*>(p.d + (xoff + 8 * j + 4 * hi) * 2) = w;
+              w.x = bf16_rne(dgt[4 * j]) | (bf16_rne(dgt[4 * j + 1]) << 16);
+              w.y = bf16_rne(dgt[4 * j + 2]) | (bf16_rne(dgt[4 * j + 3]) << 16);
+              *reinterpret_cast<v2u*>(p.d + (xoff + 32 + 8 * j + 4 * hi) * 2) = w;
+            }
+            if constexpr (AMAX2) {
+#pragma unroll
+              for (int v = 0; v < 16; v += 2) {
+                amax_in = max_abs2(amax_in, din[v], din[v + 1]);
+                amax_gt = max_abs2(amax_gt, dgt[v], dgt[v + 1]);
+              }
+            }
+          } else {
+            // FP8 dC: each 32-column output block quantised by rows and
+            // columns like a forward D ("Grouped GEMM + dGLU (SM100)",
+            // block-scaled Step 3)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              din[v] *= nc;
+              dgt[v] *= nc;
+            }
+            colw_in[tn] |= quant_tile(p, sT, sS, m, 2 * ncol, hi, l32, din) << (8 * tm);
+            colw_gt[tn] |= quant_tile(p, sT, sS, m, 2 * ncol + 32, hi, l32, dgt) << (8 * tm);
+          }
+        }
+        dp = halves_sum(dp);
+        if (hi == 0) atomicAdd(p.dprob + m, dp);
+      }
+      if constexpr (OUT == OUT_E4M3) {
+        // column l32's scale bytes of the wave's 4 consecutive 32-row blocks
+        const int mblk0 = mbase >> 5;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int ncol = nbase + tn * 32;
+          if (ncol >= p.n || hi != 0) continue;
+          *reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(2 * ncol + l32) * (vm >> 5) + mblk0) =
+              colw_in[tn];
+          *reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(2 * ncol + 32 + l32) * (vm >> 5) + mblk0) =
+              colw_gt[tn];
+        }
+      }
+      if constexpr (AMAX2) {
+        const float wi = wave_max(amax_in), wg = wave_max(amax_gt);
+        if (lane == 0) {
+          atomicMax(reinterpret_cast<unsigned int*>(p.amax + 2 * g), __float_as_uint(wi));
+          atomicMax(reinterpret_cast<unsigned int*>(p.amax + 2 * g + 1), __float_as_uint(wg));
+        }
+      }
+    } else if constexpr (ACT == ACT_DSRELU) {
+      // sReLU backward (derived from "Grouped GEMM + sReLU (SM100)",
+      // §Equations / §Tanh soft clamp): R = alpha^2 acc, C the saved forward
+      // C; with t = min(tanh(relu(C)/s), 1), c = s t: dC = R prob 2 c (1 - t^2),
+      // dprob += R c^2 (s = 0: c = relu(C), dC = R prob 2 c)
+      const float a2 = alpha * alpha;
+      const float sc = p.srelu_s;
+      const float rs = sc > 0.0f ? 1.0f / sc : 0.0f;
+      float amax_l = 0.0f;
+      uint32_t colw[TN];
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) colw[tn] = 0;
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int m = mbase + tm * 32 + l32;
+        float dp = 0.0f;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int ncol = nbase + tn * 32;
+          if (ncol >= p.n) continue;
+          if constexpr (OUT == OUT_E4M3) asm volatile("" ::: "memory");
+          const int64_t coff = static_cast<int64_t>(m) * p.n + ncol;
+          float cv[16];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const v2u w = *reinterpret_cast<const v2u*>(p.c_in + coff + 8 * j + 4 * hi);
+            cv[4 * j + 0] = __uint_as_float(w.x << 16);
+            cv[4 * j + 1] = __uint_as_float(w.x & 0xFFFF0000u);
+            cv[4 * j + 2] = __uint_as_float(w.y << 16);
+            cv[4 * j + 3] = __uint_as_float(w.y & 0xFFFF0000u);
+          }
+          float d[16];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float r = a2 * acc[tm][tn][v];
+            float c = fmaxf(cv[v], 0.0f), fp;
+            if (sc > 0.0f) {
+              const float t = fminf(tanh_nonneg(c * rs), 1.0f);
+              c = sc * t;
+              fp = 2.0f * c * (1.0f - t * t);
+            } else {
+              fp = 2.0f * c;
+            }
+            d[v] = r * pr[tm] * fp;
+            dp += r * (c * c);
+          }
+          if constexpr (OUT == OUT_BF16) {
+            store_bf16_tile(p.d, m, p.n_out, ncol, hi, d);
+            if constexpr (MX) {
+#pragma unroll
+              for (int v = 0; v < 16; v += 2) amax_l = max_abs2(amax_l, d[v], d[v + 1]);
+            }
+          } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) d[v] *= nc;
+            colw[tn] |= quant_tile(p, sT, sS, m, ncol, hi, l32, d) << (8 * tm);
+          }
+        }
+        dp = halves_sum(dp);
+        if (hi == 0) atomicAdd(p.dprob + m, dp);
+      }
+      if constexpr (OUT == OUT_E4M3) {
+        const int mblk0 = mbase >> 5;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int ncol = nbase + tn * 32;
+          if (ncol >= p.n || hi != 0) continue;
+          *reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(ncol + l32) * (vm >> 5) + mblk0) = colw[tn];
+        }
+      }
+      if constexpr (MX && OUT == OUT_BF16) {
+        const float w = wave_max(amax_l);
+        if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(p.amax + g), __float_as_uint(w));
+      }
+    } else {
+      float amax_l = 0.0f;
+      const int mblk0 = mbase >> 5;
+      // output column tiles of this wave: SwiGLU turns a [X_b | G_b] pair of
+      // 32-column MFMA tiles into one
+      constexpr int TO = ACT == ACT_SWIGLU ? TN / 2 : TN;
+#pragma unroll
+      for (int to = 0; to < TO; ++to) {
+        const int gcol = nbase + (ACT == ACT_SWIGLU ? 64 : 32) * to;   // first GEMM column
+        if (gcol >= p.n) continue;
+        const int ocol = ACT == ACT_SWIGLU ? gcol >> 1 : gcol;
+        uint32_t colw = 0;                                             // E8M0 bytes of 4 column blocks
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          const int m = mbase + tm * 32 + l32;
+          float d[16];
+          if constexpr (ACT == ACT_SWIGLU) {
+            // pairs [X_b | G_b] of 32 columns ("Grouped GEMM + SwiGLU (SM100)",
+            // Step 2): D = prob * (alpha X) * silu(alpha G), times norm_const
+            // for FP8 output, evaluated as (X G) (prob nc alpha^2) sigmoid(alpha G)
+            const v16f& ax = acc[tm][2 * to];
+            const v16f& ag = acc[tm][2 * to + 1];
+            if (p.c) {
+              float cx[16], cg[16];
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                cx[v] = alpha * ax[v];
+                cg[v] = alpha * ag[v];
+              }
+              store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, gcol, hi, cx);
+              store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, gcol + 32, hi, cg);
+            }
+            const float f = pr[tm] * nc * (alpha * alpha);
+            const float nal = -alpha * kLog2e;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(ag[v] * nal));
+              d[v] = (ax[v] * ag[v]) * (f * s);
+            }
+          } else {
+            float c[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) c[v] = alpha * acc[tm][to][v];
+            if (p.c) store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, gcol, hi, c);
+            const float f = pr[tm] * nc;
+            if constexpr (ACT == ACT_SRELU) {
+              // D = prob * (s * min(tanh(relu(C)/s), 1))^2, or prob * relu(C)^2 for s = 0
+              // ("Grouped GEMM + sReLU (SM100)", §Equations, §Tanh soft clamp)
+              const float s = p.srelu_s;
+              const float rs = s > 0.0f ? 1.0f / s : 0.0f;
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                float r = fmaxf(c[v], 0.0f);
+                if (s > 0.0f) r = s * fminf(tanh_nonneg(r * rs), 1.0f);
+                d[v] = f * (r * r);
+              }
+            } else {
+#pragma unroll
+              for (int v = 0; v < 16; ++v) d[v] = f * c[v];
+            }
+          }
+          if constexpr (OUT == OUT_BF16) {
+            store_bf16_tile(p.d, m, p.n_out, ocol, hi, d);
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) amax_l = max_abs2(amax_l, d[v], d[v + 1]);
+          } else {
+            const uint32_t bc = quant_tile(p, sT, sS, m, ocol, hi, l32, d);
+            colw |= bc << (8 * tm);
+          }
+        }
+        if constexpr (OUT == OUT_E4M3) {
+          // column l32's scale bytes of the wave's 4 consecutive 32-row blocks
+          if (hi == 0)
+            *reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(ocol + l32) * (vm >> 5) + mblk0) = colw;
+        }
+      }
+      if constexpr (OUT == OUT_BF16) {
+        const float w = wave_max(amax_l);
+        if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(p.amax + g), __float_as_uint(w));
+      }
+    }
+  };
+
+  // ---- persistent tile loop ----
+  // Two LDS stages.  Every cluster ends at a workgroup barrier; waves 4-7
+  // pass one extra barrier at the start of a tile and waves 0-3 one at its
+  // end, so between two barriers one wave of each SIMD is in a C cluster and
+  // the other in an M cluster.  A stage's early set (read in M0) is free once
+  // both wave groups have passed M0, its late set once both have passed M1.
+  //
+  // Even step counts >= 4: stage s+2's early set is issued in M1(s) into the
+  // buffer of stage s, its late set in M0(s+1); M1(s) waits for stage s+1's
+  // early set and M0(s+1) for its late set, so every load has about four
+  // clusters to arrive and the barrier after the wait publishes it before
+  // any wave reads it.  A tile's last two steps load the next tile's first
+  // stage into buffer 0 (the current tile's again when there is none), so
+  // every tile starts in buffer 0; the tile's first M0 loads stage 1 whole
+  // into buffer 1, which the previous epilogue used as scratch.
+  // Other step counts: stage s+1 is loaded whole in M0(s) and waited for in
+  // M1(s); the next tile's first stage is loaded during the epilogue.
+  // The K loop is unrolled by two (no exits inside) so every buffer is named
+  // statically.
+  const int nks = p.k_steps;
+  int t = __builtin_amdgcn_readfirstlane(slot);
+  if (t >= total) return;
+  Tile cur = tile_of(t);
+  Src src = make_src(cur);
+  issue(src, 0, st0);
+
+  auto sync = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // pin the accumulators after each MFMA cluster (the MFMAs are pure
+  // operations that the compiler would otherwise sink past the barriers,
+  // out of their cluster and into the code after the K loop)
+  auto pin_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) asm volatile("" : "+v"(acc[tm][tn]));
+  };
+  using NoWait = std::integral_constant<int, -1>;
+  using WaitAll = std::integral_constant<int, 0>;
+  // steady state: M0(s) waits for stage s's late set, M1(s) for stage s+1's
+  // early set (see the issue order in the loop below)
+  using WaitM0 = std::integral_constant<int, N_EARLY>;
+  using WaitM1 = std::integral_constant<int, N_LATE + N_EA>;
+  auto no_loads = []() __attribute__((always_inline)) {};
+  auto no_hook = [](int) __attribute__((always_inline)) {};
+  // hook issuing N loads spread evenly over a C cluster's MFMAs
+  auto spread = [&](auto nc, auto&& f) __attribute__((always_inline)) {
+    constexpr int N = decltype(nc)::value;
+    return [f](int i) __attribute__((always_inline)) {
+      constexpr int gap = NMMA / N;
+      if (i % gap == 0 && i / gap < N) f(i / gap);
+    };
+  };
+  // one K-step out of stage `st`: m0 / m1 issue loads in the M clusters
+  // after the LDS reads, c0 / c1 are hooks run between the MFMAs of the C
+  // clusters; the M clusters then wait until at most W0 / W1 of this wave's
+  // loads are outstanding (no wait for -1)
+  auto step = [&](const Stage& st, auto&& m0, auto&& c0, auto&& m1, auto&& c1, auto w0c, auto w1c)
+      __attribute__((always_inline)) {
+    constexpr int W0 = decltype(w0c)::value, W1 = decltype(w1c)::value;
+    Ops0 o0 = read0(st);
+    m0();
+    fin0(o0);
+    if constexpr (W0 >= 0) wait_vmcnt<W0>();
+    sync();
+    mma(0, o0.a, o0, c0);
+    pin_acc();
+    sync();
+    Ops1 o1 = read1(st);
+    m1();
+    fin1(o1);
+    if constexpr (W1 >= 0) wait_vmcnt<W1>();
+    sync();
+    mma(2, o1.a, o0, c1);
+    pin_acc();
+    sync();
+  };
+  auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
+  };
+
+  // Stage s+2 is loaded during step s: its early first part in M1(s), its
+  // B rows in C1(s), its late set in C0(s+1).  Hooks and waits of a
+  // steady-state pair of steps (s even in buffer 0, s+1 in buffer 1):
+  using I2 = std::integral_constant<int, N_LATE>;
+  using I4 = std::integral_constant<int, N_EB>;
+  auto lhook = [&](int ks, Stage d) __attribute__((always_inline)) {
+    return spread(I2{}, [&, ks, d](int j) __attribute__((always_inline)) { issue_l(src, ks, d, j); });
+  };
+  auto ehook = [&](int ks, Stage d) __attribute__((always_inline)) {
+    return spread(I4{}, [&, ks, d](int j) __attribute__((always_inline)) { issue_eb(src, ks, d, j); });
+  };
+  // steps 0 and 1 of a tile (stage 0 resident): stage 1 whole in M0(0)
+  auto first_pair = [&]() __attribute__((always_inline)) {
+    step(st0, [&]() __attribute__((always_inline)) { issue(src, 1, st1); }, no_hook,
+         [&]() __attribute__((always_inline)) { issue_ea(src, 2, st0); }, ehook(2, st0), NoWait{}, WaitM1{});
+    step(st1, no_loads, lhook(2, st0), [&]() __attribute__((always_inline)) { issue_ea(src, 3, st1); }, ehook(3, st1),
+         WaitM0{}, WaitM1{});
+  };
+  // steps ks (buffer 0) and ks+1 (buffer 1), loading stages up to ks+3
+  auto mid_pair = [&](int ks) __attribute__((always_inline)) {
+    step(st0, no_loads, lhook(ks + 1, st1), [&]() __attribute__((always_inline)) { issue_ea(src, ks + 2, st0); },
+         ehook(ks + 2, st0), WaitM0{}, WaitM1{});
+    step(st1, no_loads, lhook(ks + 2, st0), [&]() __attribute__((always_inline)) { issue_ea(src, ks + 3, st1); },
+         ehook(ks + 3, st1), WaitM0{}, WaitM1{});
+  };
+
+  // MODE 0: even step counts >= 4, the next tile's first stage loaded
+  // during the last two steps; MODE 1: odd step counts >= 5, MODE 3: three
+  // steps and MODE 2: one or two steps, the next tile's first stage loaded
+  // during the epilogue.  (No mode branches on the step count between
+  // different step bodies: such branches make the register allocator spill.)
+  auto run = [&](auto mode_c) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_c)::value;
+    while (true) {
+      zero_acc();
+      const int t_next = t + nwg;
+      const bool has_next = t_next < total;
+      const Tile nxt = tile_of(has_next ? t_next : t);
+      // stage 0 (and whatever the previous epilogue left in flight) complete
+      // and visible, the previous epilogue's scratch free
+      wait_vmcnt<0>();
+      sync();
+      if (wm) sync();
+      if constexpr (MODE == 0) {
+        first_pair();
+        for (int ks = 2; ks < nks - 2; ks += 2) mid_pair(ks);
+        const EpiIn ein = epi_in(cur);
+        step(st0, no_loads, lhook(nks - 1, st1),
+             [&]() __attribute__((always_inline)) {
+               src = make_src(nxt);
+               issue_ea(src, 0, st0);
+             },
+             ehook(0, st0), WaitM0{}, WaitM1{});
+        step(st1, no_loads,
+             spread(I2{}, [&](int j) __attribute__((always_inline)) {
+               if (j == 0) load_prob(cur);
+               issue_l(src, 0, st0, j);
+             }),
+             no_loads, no_hook, WaitM0{}, NoWait{});
+        if (!wm) sync();
+        wait_vmcnt<N_LATE>();      // prob (issued before the next tile's late set)
+        epilogue(cur, ein);
+      } else {
+        if constexpr (MODE == 1 || MODE == 3) {
+          // steps 0 .. nks-4 in pairs, then nks-3 (buffer 0), nks-2 (buffer 1)
+          // and nks-1 (buffer 0), which load nothing beyond stage nks-1
+          // (MODE 1: odd nks >= 5; MODE 3: nks == 3, whose step 0 loads
+          // stage 1 whole)
+          if constexpr (MODE == 1) {
+            first_pair();
+            for (int ks = 2; ks < nks - 3; ks += 2) mid_pair(ks);
+            step(st0, no_loads, lhook(nks - 2, st1),
+                 [&]() __attribute__((always_inline)) { issue_ea(src, nks - 1, st0); }, ehook(nks - 1, st0), WaitM0{},
+                 WaitM1{});
+          } else {
+            step(st0, [&]() __attribute__((always_inline)) { issue(src, 1, st1); }, no_hook,
+                 [&]() __attribute__((always_inline)) { issue_ea(src, 2, st0); }, ehook(2, st0), NoWait{}, WaitM1{});
+          }
+          step(st1, no_loads, lhook(nks - 1, st0), no_loads, no_hook, WaitM0{},
+               std::integral_constant<int, N_LATE>{});
+          step(st0, no_loads, no_hook, no_loads, no_hook, WaitAll{}, NoWait{});
+        } else {
+          if (nks == 2) {
+            step(st0, [&]() __attribute__((always_inline)) { issue(src, 1, st1); }, no_hook, no_loads, no_hook,
+                 NoWait{}, WaitAll{});
+            step(st1, no_loads, no_hook, no_loads, no_hook, NoWait{}, NoWait{});
+          } else {
+            step(st0, no_loads, no_hook, no_loads, no_hook, NoWait{}, NoWait{});
+          }
+        }
+        const EpiIn ein = epi_in(cur);
+        if (!wm) sync();
+        src = make_src(nxt);
+        load_prob(cur);
+        issue(src, 0, st0);
+        wait_vmcnt<N_EARLY + N_LATE>();   // prob (issued before the next tile's first stage)
+        epilogue(cur, ein);
+      }
+      if (!has_next) break;
+      t = t_next;
+      cur = nxt;
+    }
+  };
+  if ((nks & 1) == 0 && nks >= 4) run(std::integral_constant<int, 0>{});
+  else if (nks >= 5) run(std::integral_constant<int, 1>{});
+  else if (nks == 3) run(std::integral_constant<int, 3>{});
+  else run(std::integral_constant<int, 2>{});
+  // no direct-to-LDS write may still be in flight when the workgroup ends
+  wait_vmcnt<0>();
+}
+
+template <int AB, int ACT, int OUT>
+hipError_t launch_one(const KernelArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((grouped_gemm_kernel<AB, ACT, OUT>), dim3(static_cast<unsigned>(a.grid)), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// Every instance of one operand family.  Backward activations with BF16
+// operands write a BF16 dC only.
+template <int AB>
+hipError_t launch_family(int act, int out, const KernelArgs& a, hipStream_t s) {
+  const bool e4 = out == OUT_E4M3;
+  switch (act) {
+    case ACT_NONE: return e4 ? launch_one<AB, ACT_NONE, OUT_E4M3>(a, s) : launch_one<AB, ACT_NONE, OUT_BF16>(a, s);
+    case ACT_SWIGLU: return e4 ? launch_one<AB, ACT_SWIGLU, OUT_E4M3>(a, s) : launch_one<AB, ACT_SWIGLU, OUT_BF16>(a, s);
+    case ACT_SRELU: return e4 ? launch_one<AB, ACT_SRELU, OUT_E4M3>(a, s) : launch_one<AB, ACT_SRELU, OUT_BF16>(a, s);
+    case ACT_DSWIGLU:
+      if constexpr (AB == AB_BF16) return e4 ? hipErrorInvalidValue : launch_one<AB, ACT_DSWIGLU, OUT_BF16>(a, s);
+      else return e4 ? launch_one<AB, ACT_DSWIGLU, OUT_E4M3>(a, s) : launch_one<AB, ACT_DSWIGLU, OUT_BF16>(a, s);
+    case ACT_DSRELU:
+      if constexpr (AB == AB_BF16) return e4 ? hipErrorInvalidValue : launch_one<AB, ACT_DSRELU, OUT_BF16>(a, s);
+      else return e4 ? launch_one<AB, ACT_DSRELU, OUT_E4M3>(a, s) : launch_one<AB, ACT_DSRELU, OUT_BF16>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+}  // namespace moegg

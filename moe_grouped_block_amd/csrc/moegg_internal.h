@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI front (moegg_api.cpp) and the HIP
-// kernels (moegg_kernels.hip).  Not installed, not part of the ABI.
+// kernels (grouped_gemm.h, instantiated by inst_*.hip; dispatch and the
+// amax fill in moegg_kernels.hip).  Not installed, not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -56,6 +57,11 @@ struct KernelArgs {
   int32_t grid;            // persistent workgroups launched (>= 1)
   float srelu_s;
 };
+
+// Instances of one operand family (inst_*.hip).
+hipError_t launch_e4m3(int act, int out, const KernelArgs& args, hipStream_t stream);
+hipError_t launch_e2m1(int act, int out, const KernelArgs& args, hipStream_t stream);
+hipError_t launch_bf16(int act, int out, const KernelArgs& args, hipStream_t stream);
 
 // Launch the grouped GEMM kernel instance for (ab, act, out).  Returns the
 // HIP error of the launch (hipSuccess if enqueued).
