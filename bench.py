@@ -35,7 +35,8 @@ PEAK_TFLOPS = {"e4m3": 5000.0, "e2m1x2": 10100.0, "bf16": 2500.0}   # dense MFMA
 HBM_GBS = 8000.0
 KERNEL_SOURCES = ["moe_grouped_block_amd/csrc/grouped_gemm.h", "moe_grouped_block_amd/csrc/moegg_kernels.hip",
                   "moe_grouped_block_amd/csrc/inst_e4m3.hip", "moe_grouped_block_amd/csrc/inst_e2m1.hip",
-                  "moe_grouped_block_amd/csrc/inst_bf16.hip", "moe_grouped_block_amd/csrc/moegg_internal.h"]
+                  "moe_grouped_block_amd/csrc/inst_bf16.hip", "moe_grouped_block_amd/csrc/inst_e5m2.hip",
+                  "moe_grouped_block_amd/csrc/moegg_internal.h"]
 TRAFFIC_FILE = "profiles/grouped_gemm_fc1_swiglu_l64_traffic.md"
 
 
@@ -74,13 +75,14 @@ def algorithmic_bytes(case) -> float:
     rd += a.get("c_in", a["prob"][:0]).nbytes
     vm = p["valid_m"]
     n = p["n"]
-    no = {"none": n, "srelu": n, "swiglu": n // 2, "dswiglu": 2 * n, "dsrelu": n}[p["act"]]
-    if p["act"] in ("dswiglu", "dsrelu") and p["d_dtype"] == "bf16":
-        wr = vm * no * 2 + vm * 4
-    elif p["d_dtype"] == "e4m3":
+    no = {"none": n, "srelu": n, "swiglu": n // 2, "geglu": n // 2, "dswiglu": 2 * n, "dgeglu": 2 * n,
+          "dsrelu": n}[p["act"]]
+    if p["d_dtype"] == "e4m3":
         wr = 2 * vm * no + vm * no // 32 + no * vm // 32
     else:
         wr = vm * no * 2
+    if p["act"] in ("dswiglu", "dsrelu", "dgeglu"):
+        wr += vm * 4                      # dprob
     if p.get("c_dtype") == "bf16":
         wr += vm * n * 2
     return float(rd + wr)
@@ -114,7 +116,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fc1_swiglu_l64")
-    ap.add_argument("--also", default="fc1_swiglu_l8,fc1_swiglu_l64:discrete,dswiglu_mxfp8_l64,dsrelu_mxfp8_l32",
+    ap.add_argument("--also", default="fc1_swiglu_l8,fc1_swiglu_l64:discrete,dswiglu_mxfp8_l64,dsrelu_mxfp8_l32,"
+                    "fc1_geglu_e5m2_l8,dgeglu_mxfp8_l64",
                     help="comma list of extra workloads to time; a ':discrete' suffix passes the expert "
                          "weights as per-expert allocations (b_ptrs / sfb_ptrs)")
     ap.add_argument("--cpu-rows", type=int, default=40960, help="rows of the oracle CPU sample")

@@ -22,7 +22,7 @@
  *
  * Layouts ("logical" layouts defined by this library; every tensor is dense,
  * row-major, with no padding between rows):
- *   A       (valid_m, K)   E4M3 codes, or (valid_m, K/2) packed E2M1 pairs
+ *   A       (valid_m, K)   E4M3 or E5M2 codes, or (valid_m, K/2) packed E2M1 pairs
  *                          (the even K element in the low nibble), or BF16
  *   B       (L, N, K)      same encoding as A, K contiguous ("K-major")
  *   SFA     E8M0 bytes, one per 32 K-elements of each row of A (MX formats
@@ -45,17 +45,18 @@
  *                          nondecreasing (empty groups repeat the previous end)
  *   alpha, beta (L) fp32; prob (valid_m) fp32; norm_const (1) fp32
  *   C       (valid_m, N) BF16                      [optional forward output]
- *   D, D_col (valid_m, N_out) BF16 or E4M3 codes   N_out = N/2 for SwiGLU,
- *                                                  2N for dSwiGLU, else N
+ *   D, D_col (valid_m, N_out) BF16 or E4M3 codes   N_out = N/2 for SwiGLU and
+ *                                                  GeGLU, 2N for dSwiGLU and
+ *                                                  dGeGLU, else N
  *                                                  (dC for dSwiGLU / dsReLU)
  *   SFD_row (valid_m, N_out/32) E8M0; SFD_col (N_out, valid_m/32) E8M0
- *   amax    (L) fp32, written by the call (zero-filled first); for dSwiGLU
- *           with MX operands and a BF16 dC, (L, 2): max |d_input| and max
- *           |d_gate| over the group's rows (the block-scaled dGLU contract's
- *           amax of shape (L, 2, 1); which quantity each entry holds is this
- *           library's reading)
- *   C_in    saved forward pre-activation, BF16: (valid_m, 2N) [dSwiGLU] or
- *           (valid_m, N) [dsReLU]
+ *   amax    (L) fp32, written by the call (zero-filled first); for dSwiGLU /
+ *           dGeGLU with MX operands and a BF16 dC, (L, 2): the max |dC| of
+ *           the first and of the second blocks of the pairs over the group's
+ *           rows (the block-scaled dGLU contract's amax of shape (L, 2, 1);
+ *           which quantity each entry holds is this library's reading)
+ *   C_in    saved forward pre-activation, BF16: (valid_m, 2N) [dSwiGLU, dGeGLU]
+ *           or (valid_m, N) [dsReLU]
  *   dprob   (valid_m) fp32, caller-zeroed, accumulated with atomics [dSwiGLU, dsReLU]
  *
  * Ownership: every pointer is a caller-owned device pointer (except the
@@ -80,7 +81,7 @@
 extern "C" {
 #endif
 
-#define MOEGG_ABI_VERSION 3
+#define MOEGG_ABI_VERSION 4
 
 typedef enum moegg_status {
   MOEGG_OK = 0,
@@ -94,7 +95,8 @@ typedef enum moegg_dtype {
   MOEGG_DT_NONE = 0,
   MOEGG_DT_E4M3 = 1,   /* OCP E4M3FN: A/B operands (MXFP8) or D/D_col outputs */
   MOEGG_DT_E2M1X2 = 2, /* packed OCP E2M1 pairs: A/B operands (MXFP4) */
-  MOEGG_DT_BF16 = 3    /* A/B operands (dense BF16 backend) or C / D outputs */
+  MOEGG_DT_BF16 = 3,   /* A/B operands (dense BF16 backend) or C / D outputs */
+  MOEGG_DT_E5M2 = 4    /* OCP E5M2: A/B operands (MXFP8, "Grouped GEMM + Quant", §Data Types) */
 } moegg_dtype;
 
 typedef enum moegg_act {
@@ -107,12 +109,21 @@ typedef enum moegg_act {
                             ("Grouped GEMM + dGLU", BF16 contract and block-scaled contract,
                             dSwiGLU): BF16 operands -> BF16 dC; MX operands -> BF16 dC + amax
                             (L, 2), or E4M3 dC as D/D_col with SFD_row/SFD_col             */
-  MOEGG_ACT_DSRELU = 4   /* sReLU backward: R = alpha_g^2 acc, C_in the saved forward C
+  MOEGG_ACT_DSRELU = 4,  /* sReLU backward: R = alpha_g^2 acc, C_in the saved forward C
                             (N wide, no beta), dC = R prob f'(C), dprob += sum R f(C),
                             f(C) = (s tanh(relu(C)/s))^2 or relu(C)^2 for s = 0 (derived
                             from "Grouped GEMM + sReLU", §Equations / §Tanh soft clamp; its
                             backward page is not among the sources).  Output formats as
                             dSwiGLU, amax (L) for a BF16 dC with MX operands              */
+  MOEGG_ACT_GEGLU = 5,   /* D = gamma prob (U_b + offset) G_b sigmoid(a G_b), pairs [G_b|U_b]
+                            of 32 columns, gate first, both clamped to [clamp_min, clamp_max]
+                            ("Grouped GEMM + GLU + Hadamard", §Equations, GeGLU; the page's
+                            constants are a = 1.702, offset = 1)                          */
+  MOEGG_ACT_DGEGLU = 6   /* dGeGLU backward: C_in pairs [gate_b|up_b], dC = [dgate_b|dup_b],
+                            gate clamped above at clamp_max, up to [clamp_min, clamp_max],
+                            dprob += row sums ("Grouped GEMM + dGLU", dGeGLU equations; the
+                            page's defaults a = 1.702, offset = 1, clamps -7 / 7).  Output
+                            formats as dSwiGLU (amax (L, 2) = [dgate, dup] blocks)        */
 } moegg_act;
 
 /* Problem description (host struct). */
@@ -127,6 +138,14 @@ typedef struct moegg_problem {
   int32_t d_dtype;      /* BF16 (needs amax) | E4M3 (needs SFD_row, SFD_col, norm_const)  */
   int32_t act;          /* moegg_act                                                      */
   float srelu_tanh_s;   /* sReLU soft clamp s; 0 = plain relu^2                           */
+  /* GeGLU / dGeGLU constants (read for those activations only; no implicit
+   * defaults: the pages' values are gamma 1, geglu_alpha 1.702, linear_offset 1,
+   * dGeGLU clamps -7 / 7; +-INFINITY disables a clamp) */
+  float glu_gamma;      /* GeGLU output scale                                             */
+  float geglu_alpha;    /* sigmoid input scale                                            */
+  float linear_offset;  /* offset added to the (clamped) up branch                       */
+  float glu_clamp_min;  /* lower clamp (GeGLU: both halves; dGeGLU: up)                   */
+  float glu_clamp_max;  /* upper clamp (both halves, both directions)                     */
 } moegg_problem;
 
 /* Tensor pointers (device memory, caller-owned).  NULL where not used. */
@@ -140,14 +159,14 @@ typedef struct moegg_args {
   const float* prob;             /* required ("prob ... Required", Quant page) */
   const float* beta;             /* dSwiGLU only (L) */
   const float* norm_const;       /* required iff d_dtype == E4M3 */
-  const void* c_in;              /* dSwiGLU / dsReLU: saved forward C, BF16 (valid_m, 2N) / (valid_m, N) */
+  const void* c_in;              /* backward: saved forward C, BF16 (valid_m, 2N) or (valid_m, N) dsReLU */
   void* c;                       /* optional C output (c_dtype BF16) */
   void* d;                       /* D (or dC for dSwiGLU) */
   void* d_col;                   /* E4M3 only */
   uint8_t* sfd_row;              /* E4M3 only */
   uint8_t* sfd_col;              /* E4M3 only */
-  float* amax;                   /* BF16 D: (L), or (L, 2) for dSwiGLU with MX operands */
-  float* dprob;                  /* dSwiGLU / dsReLU, caller-zeroed */
+  float* amax;                   /* BF16 D: (L), or (L, 2) for dSwiGLU / dGeGLU with MX operands */
+  float* dprob;                  /* backward activations, caller-zeroed */
   const void* const* b_ptrs;     /* discrete weights instead of b: (L) device array, 8-byte aligned */
   const uint8_t* const* sfb_ptrs;/* discrete weights, MX only, instead of sfb: (L) device array */
 } moegg_args;
@@ -167,7 +186,8 @@ moegg_status moegg_run(const moegg_problem* problem, const moegg_args* args, voi
 moegg_status moegg_check_offsets(const moegg_problem* problem, const int32_t* padded_offsets,
                                  void* stream);
 
-/* Output width N_out for a problem (N/2 SwiGLU, 2N dSwiGLU, else N); -1 if invalid act. */
+/* Output width N_out for a problem (N/2 SwiGLU / GeGLU, 2N dSwiGLU / dGeGLU, else N);
+ * -1 if invalid act. */
 int64_t moegg_n_out(const moegg_problem* problem);
 
 const char* moegg_status_string(moegg_status status);

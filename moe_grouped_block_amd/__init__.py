@@ -21,13 +21,14 @@ import os
 
 __all__ = ["MoeggError", "moegg_check", "moegg_run", "moegg_check_offsets", "moegg_n_out",
            "moegg_status_string", "moegg_last_error", "moegg_abi_version", "make_problem",
-           "make_args", "run", "check", "lib_path", "DTYPES", "ACTS", "STATUS"]
+           "make_args", "run", "check", "lib_path", "ABI_VERSION", "DTYPES", "ACTS", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libmoegg.so")
 
-DTYPES = {None: 0, "none": 0, "e4m3": 1, "e2m1x2": 2, "bf16": 3}
-ACTS = {"none": 0, "swiglu": 1, "srelu": 2, "dswiglu": 3, "dsrelu": 4}
+ABI_VERSION = 4   # MOEGG_ABI_VERSION of the structs below
+DTYPES = {None: 0, "none": 0, "e4m3": 1, "e2m1x2": 2, "bf16": 3, "e5m2": 4}
+ACTS = {"none": 0, "swiglu": 1, "srelu": 2, "dswiglu": 3, "dsrelu": 4, "geglu": 5, "dgeglu": 6}
 STATUS = {0: "MOEGG_OK", 1: "MOEGG_ERROR_INVALID_VALUE", 2: "MOEGG_ERROR_MISALIGNED",
           3: "MOEGG_ERROR_NOT_SUPPORTED", 4: "MOEGG_ERROR_LAUNCH"}
 
@@ -40,7 +41,9 @@ class moegg_problem(ctypes.Structure):
                 ("valid_m", ctypes.c_int64), ("n", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("ab_dtype", ctypes.c_int32), ("c_dtype", ctypes.c_int32),
                 ("d_dtype", ctypes.c_int32), ("act", ctypes.c_int32),
-                ("srelu_tanh_s", ctypes.c_float)]
+                ("srelu_tanh_s", ctypes.c_float), ("glu_gamma", ctypes.c_float),
+                ("geglu_alpha", ctypes.c_float), ("linear_offset", ctypes.c_float),
+                ("glu_clamp_min", ctypes.c_float), ("glu_clamp_max", ctypes.c_float)]
 
 
 class moegg_args(ctypes.Structure):
@@ -73,6 +76,9 @@ def _load():
         lib.moegg_status_string.argtypes, lib.moegg_status_string.restype = [ctypes.c_int], ctypes.c_char_p
         lib.moegg_last_error.argtypes, lib.moegg_last_error.restype = [], ctypes.c_char_p
         lib.moegg_abi_version.argtypes, lib.moegg_abi_version.restype = [], ctypes.c_int
+        if lib.moegg_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{lib_path} has ABI {lib.moegg_abi_version()}, these bindings "
+                               f"expect {ABI_VERSION}: rebuild it with __graft_entry__.build()")
         _lib = lib
     return _lib
 
@@ -109,13 +115,23 @@ def moegg_abi_version() -> int:
 
 # ---- marshalling helpers ---------------------------------------------------------
 
+def _code(table: dict, v) -> int:
+    return v if isinstance(v, int) else table[v]
+
+
 def make_problem(p: dict) -> moegg_problem:
-    """Problem dict (keys as in the C struct; dtypes/act as strings) -> struct."""
+    """Problem dict (keys as in the C struct; dtypes/act as names or raw enum
+    values) -> struct."""
     return moegg_problem(num_groups=int(p["num_groups"]), m_aligned=int(p.get("m_aligned", 128)),
                          valid_m=int(p["valid_m"]), n=int(p["n"]), k=int(p["k"]),
-                         ab_dtype=DTYPES[p["ab_dtype"]], c_dtype=DTYPES[p.get("c_dtype")],
-                         d_dtype=DTYPES[p["d_dtype"]], act=ACTS[p["act"]],
-                         srelu_tanh_s=float(p.get("srelu_tanh_s", 0.0) or 0.0))
+                         ab_dtype=_code(DTYPES, p["ab_dtype"]), c_dtype=_code(DTYPES, p.get("c_dtype")),
+                         d_dtype=_code(DTYPES, p["d_dtype"]), act=_code(ACTS, p["act"]),
+                         srelu_tanh_s=float(p.get("srelu_tanh_s", 0.0) or 0.0),
+                         glu_gamma=float(p.get("glu_gamma", 1.0)),
+                         geglu_alpha=float(p.get("geglu_alpha", 1.702)),
+                         linear_offset=float(p.get("linear_offset", 1.0)),
+                         glu_clamp_min=float(p.get("glu_clamp_min", float("-inf"))),
+                         glu_clamp_max=float(p.get("glu_clamp_max", float("inf"))))
 
 
 def _ptr(t) -> int | None:

@@ -32,7 +32,7 @@ COMMON = [
     "-Wno-unused-command-line-argument",
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]
-SOURCES = ["moegg_api.cpp", "moegg_kernels.hip", "inst_e4m3.hip", "inst_e2m1.hip", "inst_bf16.hip"]
+SOURCES = ["moegg_api.cpp", "moegg_kernels.hip", "inst_e4m3.hip", "inst_e2m1.hip", "inst_bf16.hip", "inst_e5m2.hip"]
 
 
 def _compile(src: str) -> str:

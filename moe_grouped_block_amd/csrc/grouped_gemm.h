@@ -20,7 +20,7 @@
 //    that the workgroups resident on one XCD (one L2) work on a compact patch
 //    of neighbouring tiles at any time.
 //  * the contraction runs on the block-scaled matrix cores:
-//    v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 or E2M1 operands, one E8M0 byte
+//    v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3, E5M2 or E2M1 operands, one E8M0 byte
 //    per lane and operand selects the scale of that lane's 32 K-elements) or
 //    v_mfma_f32_32x32x16_bf16.  The weight tile is the instruction's first
 //    operand and the token tile the second, so an accumulator lane holds one
@@ -303,6 +303,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   constexpr int TM = WM / 32;        // 32-row MFMA tiles per wave (4)
   constexpr int TN = WN / 32;        // 32-column MFMA tiles per wave (2)
   constexpr bool MX = AB != AB_BF16;
+  constexpr bool F8 = AB == AB_E4M3 || AB == AB_E5M2;   // 8-bit operands (one layout, two MFMA formats)
+  constexpr int FMT8 = AB == AB_E5M2 ? 1 : 0;           // MFMA operand format: E4M3 0, E5M2 1
   constexpr int SW = AB == AB_E2M1 ? 2 : 1;          // scale words per row per step
   constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
   constexpr int AH_BYTES = A_BYTES / 2;              // one of the two A row halves
@@ -427,15 +429,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   // Wave w fills B rows [32w, 32w+32) (4 instructions) and rows
   // [16w, 16w+16) of each A half (2 + 2).  A rows past the tile's valid rows
   // repeat its last row and B rows past N repeat row N-1 (loaded, never
-  // stored).  Scale dwords ride along, one per lane: E4M3 (one dword per row
+  // stored).  Scale dwords ride along, one per lane: 8-bit operands (one dword per row
   // and step): waves 0-3 load A rows, waves 4-7 B rows; E2M1 (two dwords):
   // two loads per wave; BF16 has none.
   // A stage's loads come in two sets: the early set (B, the low A half and
   // all scale words: everything the first operand cluster of a step reads)
   // and the late set (the high A half, read by the second cluster).
-  constexpr int S_LOADS = AB == AB_E4M3 ? 1 : AB == AB_E2M1 ? 2 : 0;
+  constexpr int S_LOADS = F8 ? 1 : AB == AB_E2M1 ? 2 : 0;
   constexpr int SL = S_LOADS > 0 ? S_LOADS : 1;
-  constexpr int S_HALF = AB == AB_E4M3 ? 4 : 8;      // scale jobs of A (the rest are B's)
+  constexpr int S_HALF = F8 ? 4 : 8;                 // scale jobs of A (the rest are B's)
   constexpr int N_EA = 2 + S_LOADS, N_EB = 4, N_EARLY = N_EA + N_EB, N_LATE = 2;
 
   struct Src {
@@ -470,7 +472,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
     if constexpr (MX) {
 #pragma unroll
       for (int u = 0; u < S_LOADS; ++u) {
-        // job (wave * S_LOADS + u): E4M3 jobs 0-3 A rows, 4-7 B rows;
+        // job (wave * S_LOADS + u): 8-bit operands: jobs 0-3 A rows, 4-7 B rows;
         // E2M1 jobs 0-7 A (word, quarter), 8-15 B (word, quarter)
         const int job = wave * S_LOADS + u;
         const bool isA = job < S_HALF;
@@ -626,7 +628,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   // C cluster: MFMA tiles tm0, tm0 + 1 (A pieces a[0], a[1]) x all tn, all
   // windows of the step
   // `hook(i)` runs right after the cluster's MFMA number i (0 .. NMMA-1)
-  constexpr int NWIN = AB == AB_E4M3 ? 2 : 4;
+  constexpr int NWIN = F8 ? 2 : 4;
   constexpr int NMMA = NWIN * 2 * TN;
   auto mma = [&](int tm0, const Pieces* a, const Ops0& o0, auto&& hook) __attribute__((always_inline)) {
     static_for<0, NWIN>([&](auto kc) {
@@ -637,12 +639,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         for (int tn = 0; tn < TN; ++tn) {
           const int mi = (kk * 2 + t) * TN + tn;
           v16f& c = acc[tm0 + t][tn];
-          if constexpr (AB == AB_E4M3) {
+          if constexpr (F8) {
             const v4u a0 = a[t][2 * kk], a1 = a[t][2 * kk + 1], b0 = o0.b[tn][2 * kk], b1 = o0.b[tn][2 * kk + 1];
             const v8i fa{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
             const v8i fb{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, c, 0, 0, kk * 2, (int)o0.sb[tn][0], kk * 2,
-                                                                (int)o0.sa[tm0 + t][0]);
+            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, c, FMT8, FMT8, kk * 2, (int)o0.sb[tn][0],
+                                                                kk * 2, (int)o0.sa[tm0 + t][0]);
           } else if constexpr (AB == AB_E2M1) {
             const v4u a0 = a[t][kk], b0 = o0.b[tn][kk];
             const v8i fa{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
@@ -702,21 +704,29 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) pr[tm] = sPr[wave][tm * 32 + l32];
 
-    if constexpr (ACT == ACT_DSWIGLU) {
-      // R = alpha^2 acc; X = beta * C_in with blocks [input_b | gate_b]
-      // ("Grouped GEMM + dGLU (SM100)", BF16 contract equations and the
-      // block-scaled contract's Step 2): d_input = R prob swish(gate),
-      // d_gate = R prob input s (1 + gate (1 - s)), dprob += R input swish
+    if constexpr (ACT == ACT_DSWIGLU || ACT == ACT_DGEGLU) {
+      // GLU backwards over pairs of 32-column blocks of the saved C_in, R =
+      // alpha^2 acc ("Grouped GEMM + dGLU (SM100)", BF16 contract equations
+      // and the block-scaled contract's Step 2).
+      // dSwiGLU: X = beta * C_in, blocks [input_b | gate_b], s = sigmoid(gate):
+      //   d_input = R prob swish(gate), d_gate = R prob input s (1 + gate (1 - s)),
+      //   dprob += R input swish(gate)
+      // dGeGLU: C_in as stored, blocks [gate_b | up_b], gate_c = min(gate, cmax),
+      //   up_c = clamp(up, cmin, cmax), s = sigmoid(a gate_c):
+      //   d_gate = R prob (up_c + off) s (1 + a gate_c (1 - s)) [gate <= cmax],
+      //   d_up = R prob gate_c s [cmin <= up <= cmax], dprob += R gate_c s (up_c + off)
+      // The outputs keep the pair order of the input blocks.
       const float a2 = alpha * alpha;
-      const float beta = p.beta[g];
+      float beta = 1.0f;
+      if constexpr (ACT == ACT_DSWIGLU) beta = p.beta[g];
       const int ld2 = 2 * p.n;
-      // block-scaled operands with a BF16 output: amax per group of the
-      // d_input blocks and of the d_gate blocks (amax of shape (L, 2))
+      // block-scaled operands with a BF16 output: amax per group of the first
+      // and of the second blocks of the pairs (amax of shape (L, 2))
       constexpr bool AMAX2 = MX && OUT == OUT_BF16;
-      float amax_in = 0.0f, amax_gt = 0.0f;
-      uint32_t colw_in[TN], colw_gt[TN];      // E4M3: column scale bytes of 4 row blocks
+      float amax0 = 0.0f, amax1 = 0.0f;
+      uint32_t colw0[TN], colw1[TN];          // E4M3: column scale bytes of 4 row blocks
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) colw_in[tn] = colw_gt[tn] = 0;
+      for (int tn = 0; tn < TN; ++tn) colw0[tn] = colw1[tn] = 0;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
         const int m = mbase + tm * 32 + l32;
@@ -729,48 +739,59 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           // ahead of the FP8 quantisation would spill)
           if constexpr (OUT == OUT_E4M3) asm volatile("" ::: "memory");
           const int64_t xoff = static_cast<int64_t>(m) * ld2 + 2 * ncol;   // block b = ncol/32 starts at 64b
-          float xin[16], xg[16];
+          float x0[16], x1[16];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const v2u wi = *reinterpret_cast<const v2u*>(p.c_in + xoff + 8 * j + 4 * hi);
             const v2u wg = *reinterpret_cast<const v2u*>(p.c_in + xoff + 32 + 8 * j + 4 * hi);
-            xin[4 * j + 0] = __uint_as_float(wi.x << 16);
-            xin[4 * j + 1] = __uint_as_float(wi.x & 0xFFFF0000u);
-            xin[4 * j + 2] = __uint_as_float(wi.y << 16);
-            xin[4 * j + 3] = __uint_as_float(wi.y & 0xFFFF0000u);
-            xg[4 * j + 0] = __uint_as_float(wg.x << 16);
-            xg[4 * j + 1] = __uint_as_float(wg.x & 0xFFFF0000u);
-            xg[4 * j + 2] = __uint_as_float(wg.y << 16);
-            xg[4 * j + 3] = __uint_as_float(wg.y & 0xFFFF0000u);
+            x0[4 * j + 0] = __uint_as_float(wi.x << 16);
+            x0[4 * j + 1] = __uint_as_float(wi.x & 0xFFFF0000u);
+            x0[4 * j + 2] = __uint_as_float(wi.y << 16);
+            x0[4 * j + 3] = __uint_as_float(wi.y & 0xFFFF0000u);
+            x1[4 * j + 0] = __uint_as_float(wg.x << 16);
+            x1[4 * j + 1] = __uint_as_float(wg.x & 0xFFFF0000u);
+            x1[4 * j + 2] = __uint_as_float(wg.y << 16);
+            x1[4 * j + 3] = __uint_as_float(wg.y & 0xFFFF0000u);
           }
-          float din[16], dgt[16];
+          float d0[16], d1[16];
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const float r = a2 * acc[tm][tn][v];
-            const float x = beta * xin[v];
-            const float gt = beta * xg[v];
-            const float s = sigmoid_f(gt);
-            const float swish = gt * s;
-            din[v] = r * pr[tm] * swish;
-            dgt[v] = r * pr[tm] * x * s * (1.0f + gt * (1.0f - s));
-            dp += r * x * swish;
+            if constexpr (ACT == ACT_DSWIGLU) {
+              const float x = beta * x0[v];
+              const float gt = beta * x1[v];
+              const float s = sigmoid_f(gt);
+              const float swish = gt * s;
+              d0[v] = r * pr[tm] * swish;
+              d1[v] = r * pr[tm] * x * s * (1.0f + gt * (1.0f - s));
+              dp += r * x * swish;
+            } else {
+              const float gate = x0[v], up = x1[v];
+              const float gc = fminf(gate, p.glu_clamp_max);
+              const float uc = fminf(fmaxf(up, p.glu_clamp_min), p.glu_clamp_max);
+              const float s = sigmoid_f(p.geglu_alpha * gc);
+              const float uo = uc + p.linear_offset;
+              d0[v] = gate <= p.glu_clamp_max ? r * pr[tm] * uo * s * (1.0f + p.geglu_alpha * gc * (1.0f - s)) : 0.0f;
+              d1[v] = (up >= p.glu_clamp_min && up <= p.glu_clamp_max) ? r * pr[tm] * gc * s : 0.0f;
+              dp += r * gc * s * uo;
+            }
           }
           if constexpr (OUT == OUT_BF16) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               v2u w;
-              w.x = bf16_rne(din[4 * j]) | (bf16_rne(din[4 * j + 1]) << 16);
-              w.y = bf16_rne(din[4 * j + 2]) | (bf16_rne(din[4 * j + 3]) << 16);
+              w.x = bf16_rne(d0[4 * j]) | (bf16_rne(d0[4 * j + 1]) << 16);
+              w.y = bf16_rne(d0[4 * j + 2]) | (bf16_rne(d0[4 * j + 3]) << 16);
               *reinterpret_cast<v2u*>(p.d + (xoff + 8 * j + 4 * hi) * 2) = w;
-              w.x = bf16_rne(dgt[4 * j]) | (bf16_rne(dgt[4 * j + 1]) << 16);
-              w.y = bf16_rne(dgt[4 * j + 2]) | (bf16_rne(dgt[4 * j + 3]) << 16);
+              w.x = bf16_rne(d1[4 * j]) | (bf16_rne(d1[4 * j + 1]) << 16);
+              w.y = bf16_rne(d1[4 * j + 2]) | (bf16_rne(d1[4 * j + 3]) << 16);
               *reinterpret_cast<v2u*>(p.d + (xoff + 32 + 8 * j + 4 * hi) * 2) = w;
             }
             if constexpr (AMAX2) {
 #pragma unroll
               for (int v = 0; v < 16; v += 2) {
-                amax_in = max_abs2(amax_in, din[v], din[v + 1]);
-                amax_gt = max_abs2(amax_gt, dgt[v], dgt[v + 1]);
+                amax0 = max_abs2(amax0, d0[v], d0[v + 1]);
+                amax1 = max_abs2(amax1, d1[v], d1[v + 1]);
               }
             }
           } else {
@@ -779,11 +800,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             // block-scaled Step 3)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              din[v] *= nc;
-              dgt[v] *= nc;
+              d0[v] *= nc;
+              d1[v] *= nc;
             }
-            colw_in[tn] |= quant_tile(p, sT, sS, m, 2 * ncol, hi, l32, din) << (8 * tm);
-            colw_gt[tn] |= quant_tile(p, sT, sS, m, 2 * ncol + 32, hi, l32, dgt) << (8 * tm);
+            colw0[tn] |= quant_tile(p, sT, sS, m, 2 * ncol, hi, l32, d0) << (8 * tm);
+            colw1[tn] |= quant_tile(p, sT, sS, m, 2 * ncol + 32, hi, l32, d1) << (8 * tm);
           }
         }
         dp = halves_sum(dp);
@@ -797,13 +818,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           const int ncol = nbase + tn * 32;
           if (ncol >= p.n || hi != 0) continue;
           *reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(2 * ncol + l32) * (vm >> 5) + mblk0) =
-              colw_in[tn];
+              colw0[tn];
           *reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(2 * ncol + 32 + l32) * (vm >> 5) + mblk0) =
-              colw_gt[tn];
+              colw1[tn];
         }
       }
       if constexpr (AMAX2) {
-        const float wi = wave_max(amax_in), wg = wave_max(amax_gt);
+        const float wi = wave_max(amax0), wg = wave_max(amax1);
         if (lane == 0) {
           atomicMax(reinterpret_cast<unsigned int*>(p.amax + 2 * g), __float_as_uint(wi));
           atomicMax(reinterpret_cast<unsigned int*>(p.amax + 2 * g + 1), __float_as_uint(wg));
@@ -887,13 +908,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       float amax_l = 0.0f;
       const int mblk0 = mbase >> 5;
       // output column tiles of this wave: SwiGLU turns a [X_b | G_b] pair of
-      // 32-column MFMA tiles into one
-      constexpr int TO = ACT == ACT_SWIGLU ? TN / 2 : TN;
+      // 32-column MFMA tiles into one, GeGLU a [G_b | U_b] pair
+      constexpr bool PAIR = ACT == ACT_SWIGLU || ACT == ACT_GEGLU;
+      constexpr int TO = PAIR ? TN / 2 : TN;
 #pragma unroll
       for (int to = 0; to < TO; ++to) {
-        const int gcol = nbase + (ACT == ACT_SWIGLU ? 64 : 32) * to;   // first GEMM column
+        const int gcol = nbase + (PAIR ? 64 : 32) * to;   // first GEMM column
         if (gcol >= p.n) continue;
-        const int ocol = ACT == ACT_SWIGLU ? gcol >> 1 : gcol;
+        const int ocol = PAIR ? gcol >> 1 : gcol;
         uint32_t colw = 0;                                             // E8M0 bytes of 4 column blocks
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
@@ -921,6 +943,32 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             for (int v = 0; v < 16; ++v) {
               const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(ag[v] * nal));
               d[v] = (ax[v] * ag[v]) * (f * s);
+            }
+          } else if constexpr (ACT == ACT_GEGLU) {
+            // pairs [G_b | U_b] of 32 columns, gate first ("Grouped GEMM + GLU +
+            // Hadamard", §Equations, GeGLU): both halves of C = alpha acc
+            // clamped to [glu_clamp_min, glu_clamp_max], then
+            // D = gamma prob (U + offset) G sigmoid(geglu_alpha G), times norm_const
+            const v16f& ag = acc[tm][2 * to];
+            const v16f& au = acc[tm][2 * to + 1];
+            float cg[16], cu[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              cg[v] = alpha * ag[v];
+              cu[v] = alpha * au[v];
+            }
+            if (p.c) {
+              store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, gcol, hi, cg);
+              store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, gcol + 32, hi, cu);
+            }
+            const float f = pr[tm] * nc * p.glu_gamma;
+            const float nga = -p.geglu_alpha * kLog2e;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const float g = fminf(fmaxf(cg[v], p.glu_clamp_min), p.glu_clamp_max);
+              const float u = fminf(fmaxf(cu[v], p.glu_clamp_min), p.glu_clamp_max);
+              const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * nga));
+              d[v] = ((u + p.linear_offset) * g) * (f * s);
             }
           } else {
             float c[16];
@@ -1187,6 +1235,10 @@ hipError_t launch_family(int act, int out, const KernelArgs& a, hipStream_t s) {
     case ACT_DSRELU:
       if constexpr (AB == AB_BF16) return e4 ? hipErrorInvalidValue : launch_one<AB, ACT_DSRELU, OUT_BF16>(a, s);
       else return e4 ? launch_one<AB, ACT_DSRELU, OUT_E4M3>(a, s) : launch_one<AB, ACT_DSRELU, OUT_BF16>(a, s);
+    case ACT_GEGLU: return e4 ? launch_one<AB, ACT_GEGLU, OUT_E4M3>(a, s) : launch_one<AB, ACT_GEGLU, OUT_BF16>(a, s);
+    case ACT_DGEGLU:
+      if constexpr (AB == AB_BF16) return e4 ? hipErrorInvalidValue : launch_one<AB, ACT_DGEGLU, OUT_BF16>(a, s);
+      else return e4 ? launch_one<AB, ACT_DGEGLU, OUT_E4M3>(a, s) : launch_one<AB, ACT_DGEGLU, OUT_BF16>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -46,6 +46,8 @@ int64_t n_out_of(const moegg_problem& p) {
     case MOEGG_ACT_SWIGLU: return p.n / 2;
     case MOEGG_ACT_DSWIGLU: return 2 * static_cast<int64_t>(p.n);
     case MOEGG_ACT_DSRELU: return p.n;
+    case MOEGG_ACT_GEGLU: return p.n / 2;
+    case MOEGG_ACT_DGEGLU: return 2 * static_cast<int64_t>(p.n);
     default: return -1;
   }
 }
@@ -72,10 +74,10 @@ moegg_status check_impl(const moegg_problem* pp, const moegg_args* ap) {
   if (p.k % 32 != 0) return fail(MOEGG_ERROR_INVALID_VALUE, "k=%d not a multiple of 32 (sf_vec_size 32)", p.k);
 
   // --- dtypes / activation ------------------------------------------------
-  const bool mx = p.ab_dtype == MOEGG_DT_E4M3 || p.ab_dtype == MOEGG_DT_E2M1X2;
+  const bool mx = p.ab_dtype == MOEGG_DT_E4M3 || p.ab_dtype == MOEGG_DT_E5M2 || p.ab_dtype == MOEGG_DT_E2M1X2;
   if (!mx && p.ab_dtype != MOEGG_DT_BF16)
-    return fail(MOEGG_ERROR_INVALID_VALUE, "ab_dtype=%d must be E4M3, E2M1X2 or BF16", p.ab_dtype);
-  if (p.act < MOEGG_ACT_NONE || p.act > MOEGG_ACT_DSRELU)
+    return fail(MOEGG_ERROR_INVALID_VALUE, "ab_dtype=%d must be E4M3, E5M2, E2M1X2 or BF16", p.ab_dtype);
+  if (p.act < MOEGG_ACT_NONE || p.act > MOEGG_ACT_DGEGLU)
     return fail(MOEGG_ERROR_INVALID_VALUE, "act=%d unknown", p.act);
   if (p.d_dtype != MOEGG_DT_BF16 && p.d_dtype != MOEGG_DT_E4M3)
     return fail(MOEGG_ERROR_INVALID_VALUE, "d_dtype=%d must be BF16 or E4M3", p.d_dtype);
@@ -83,9 +85,15 @@ moegg_status check_impl(const moegg_problem* pp, const moegg_args* ap) {
     return fail(MOEGG_ERROR_INVALID_VALUE, "c_dtype=%d must be NONE or BF16", p.c_dtype);
   if (!(p.srelu_tanh_s >= 0.0f) || !std::isfinite(p.srelu_tanh_s))
     return fail(MOEGG_ERROR_INVALID_VALUE, "srelu_tanh_s must be finite and >= 0");
-  if (p.act == MOEGG_ACT_SWIGLU && p.n % 64 != 0)
-    return fail(MOEGG_ERROR_INVALID_VALUE, "SwiGLU needs n %% 64 == 0 (32-column pairs), n=%d", p.n);
-  const bool bwd = p.act == MOEGG_ACT_DSWIGLU || p.act == MOEGG_ACT_DSRELU;
+  if ((p.act == MOEGG_ACT_SWIGLU || p.act == MOEGG_ACT_GEGLU) && p.n % 64 != 0)
+    return fail(MOEGG_ERROR_INVALID_VALUE, "SwiGLU / GeGLU need n %% 64 == 0 (32-column pairs), n=%d", p.n);
+  if (p.act == MOEGG_ACT_GEGLU || p.act == MOEGG_ACT_DGEGLU) {
+    if (!std::isfinite(p.glu_gamma) || !std::isfinite(p.geglu_alpha) || !std::isfinite(p.linear_offset))
+      return fail(MOEGG_ERROR_INVALID_VALUE, "glu_gamma, geglu_alpha and linear_offset must be finite");
+    if (!(p.glu_clamp_min <= p.glu_clamp_max))
+      return fail(MOEGG_ERROR_INVALID_VALUE, "glu_clamp_min must not exceed glu_clamp_max (NaN rejected)");
+  }
+  const bool bwd = p.act == MOEGG_ACT_DSWIGLU || p.act == MOEGG_ACT_DSRELU || p.act == MOEGG_ACT_DGEGLU;
   if (bwd) {
     if (p.n % 32 != 0) return fail(MOEGG_ERROR_INVALID_VALUE, "backward activations need n %% 32 == 0, n=%d", p.n);
     if (!mx && p.d_dtype != MOEGG_DT_BF16)
@@ -93,7 +101,7 @@ moegg_status check_impl(const moegg_problem* pp, const moegg_args* ap) {
     if (p.c_dtype != MOEGG_DT_NONE) return fail(MOEGG_ERROR_INVALID_VALUE, "backward activations write no C");
   }
   if (p.n % 32 != 0) return fail(MOEGG_ERROR_NOT_SUPPORTED, "n=%d: this build needs n %% 32 == 0", p.n);
-  const int kstep = p.ab_dtype == MOEGG_DT_E4M3 ? 128 : p.ab_dtype == MOEGG_DT_E2M1X2 ? 256 : 64;   // 128-byte steps
+  const int kstep = p.ab_dtype == MOEGG_DT_E2M1X2 ? 256 : p.ab_dtype == MOEGG_DT_BF16 ? 64 : 128;   // 128-byte steps
   if (p.k % kstep != 0)
     return fail(MOEGG_ERROR_NOT_SUPPORTED, "k=%d: this build needs k %% %d == 0 for this operand type", p.k, kstep);
   if (p.k > (1 << 20)) return fail(MOEGG_ERROR_NOT_SUPPORTED, "k=%d too large", p.k);
@@ -132,7 +140,8 @@ moegg_status check_impl(const moegg_problem* pp, const moegg_args* ap) {
   if (bwd) {
     if (!a.c_in || !a.dprob) return fail(MOEGG_ERROR_INVALID_VALUE, "backward activations need c_in and dprob");
     if (p.act == MOEGG_ACT_DSWIGLU && !a.beta) return fail(MOEGG_ERROR_INVALID_VALUE, "dSwiGLU needs beta");
-    if (p.act == MOEGG_ACT_DSRELU && a.beta) return fail(MOEGG_ERROR_INVALID_VALUE, "dsReLU takes no beta");
+    if (p.act != MOEGG_ACT_DSWIGLU && a.beta)
+      return fail(MOEGG_ERROR_INVALID_VALUE, "beta is for dSwiGLU only (dsReLU / dGeGLU read C_in as stored)");
     if (!mx && a.amax) return fail(MOEGG_ERROR_INVALID_VALUE, "backward activations with BF16 operands write no amax");
   } else if (a.beta || a.c_in || a.dprob) {
     return fail(MOEGG_ERROR_INVALID_VALUE, "beta/c_in/dprob are for the backward activations only");
@@ -171,7 +180,7 @@ moegg_status moegg_run(const moegg_problem* problem, const moegg_args* args, voi
 
   if (a.amax) {
     // (L) per group, or (L, 2) for dSwiGLU: [d_input blocks, d_gate blocks]
-    const int count = p.act == MOEGG_ACT_DSWIGLU ? 2 * p.num_groups : p.num_groups;
+    const int count = p.act == MOEGG_ACT_DSWIGLU || p.act == MOEGG_ACT_DGEGLU ? 2 * p.num_groups : p.num_groups;
     hipError_t e = moegg::launch_fill_zero(a.amax, count, stream);
     if (e != hipSuccess) return fail(MOEGG_ERROR_LAUNCH, "amax fill: %s", hipGetErrorString(e));
   }
@@ -203,8 +212,15 @@ moegg_status moegg_run(const moegg_problem* problem, const moegg_args* args, voi
   k.n = p.n;
   k.k = p.k;
   k.n_out = static_cast<int32_t>(n_out_of(p));
-  const int ab = p.ab_dtype == MOEGG_DT_E4M3 ? moegg::AB_E4M3 : p.ab_dtype == MOEGG_DT_E2M1X2 ? moegg::AB_E2M1 : moegg::AB_BF16;
-  k.row_bytes = ab == moegg::AB_E4M3 ? p.k : ab == moegg::AB_E2M1 ? p.k / 2 : 2 * p.k;
+  const int ab = p.ab_dtype == MOEGG_DT_E4M3   ? moegg::AB_E4M3
+                 : p.ab_dtype == MOEGG_DT_E5M2 ? moegg::AB_E5M2
+                 : p.ab_dtype == MOEGG_DT_E2M1X2 ? moegg::AB_E2M1 : moegg::AB_BF16;
+  k.row_bytes = ab == moegg::AB_E2M1 ? p.k / 2 : ab == moegg::AB_BF16 ? 2 * p.k : p.k;
+  k.glu_gamma = p.glu_gamma;
+  k.geglu_alpha = p.geglu_alpha;
+  k.linear_offset = p.linear_offset;
+  k.glu_clamp_min = p.glu_clamp_min;
+  k.glu_clamp_max = p.glu_clamp_max;
   k.ksf = p.k / 32;
   k.k_steps = k.row_bytes / 128;
   k.n_tiles = (p.n + moegg::kBN - 1) / moegg::kBN;

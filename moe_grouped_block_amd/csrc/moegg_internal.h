@@ -9,9 +9,11 @@
 namespace moegg {
 
 // Operand family of A/B.
-enum AbKind : int { AB_E4M3 = 0, AB_E2M1 = 1, AB_BF16 = 2 };
+enum AbKind : int { AB_E4M3 = 0, AB_E2M1 = 1, AB_BF16 = 2, AB_E5M2 = 3 };
 // Epilogue activation.
-enum ActKind : int { ACT_NONE = 0, ACT_SWIGLU = 1, ACT_SRELU = 2, ACT_DSWIGLU = 3, ACT_DSRELU = 4 };
+enum ActKind : int {
+  ACT_NONE = 0, ACT_SWIGLU = 1, ACT_SRELU = 2, ACT_DSWIGLU = 3, ACT_DSRELU = 4, ACT_GEGLU = 5, ACT_DGEGLU = 6
+};
 // Output formatting of D.
 enum OutKind : int { OUT_BF16 = 0, OUT_E4M3 = 1 };
 
@@ -56,12 +58,18 @@ struct KernelArgs {
   int32_t k_steps;         // row bytes / 128 (one 128-byte step per row)
   int32_t grid;            // persistent workgroups launched (>= 1)
   float srelu_s;
+  float glu_gamma;         // GeGLU forward output scale
+  float geglu_alpha;       // GeGLU / dGeGLU sigmoid input scale
+  float linear_offset;     // GeGLU / dGeGLU offset of the up branch
+  float glu_clamp_min;     // GeGLU: both halves; dGeGLU: up only
+  float glu_clamp_max;     // GeGLU: both halves; dGeGLU: gate and up
 };
 
 // Instances of one operand family (inst_*.hip).
 hipError_t launch_e4m3(int act, int out, const KernelArgs& args, hipStream_t stream);
 hipError_t launch_e2m1(int act, int out, const KernelArgs& args, hipStream_t stream);
 hipError_t launch_bf16(int act, int out, const KernelArgs& args, hipStream_t stream);
+hipError_t launch_e5m2(int act, int out, const KernelArgs& args, hipStream_t stream);
 
 // Launch the grouped GEMM kernel instance for (ab, act, out).  Returns the
 // HIP error of the launch (hipSuccess if enqueued).

@@ -20,6 +20,7 @@ hipError_t launch_grouped_gemm(int ab, int act, int out, const KernelArgs& a, hi
     case AB_E4M3: return launch_e4m3(act, out, a, s);
     case AB_E2M1: return launch_e2m1(act, out, a, s);
     case AB_BF16: return launch_bf16(act, out, a, s);
+    case AB_E5M2: return launch_e5m2(act, out, a, s);
     default: return hipErrorInvalidValue;
   }
 }

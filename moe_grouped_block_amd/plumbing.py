@@ -72,7 +72,8 @@ def discrete_weights(problem: dict, arrays: dict, device="cuda", seed: int = 0, 
 
 def n_out(problem: dict) -> int:
     n = int(problem["n"])
-    return {"none": n, "srelu": n, "swiglu": n // 2, "dswiglu": 2 * n, "dsrelu": n}[problem["act"]]
+    return {"none": n, "srelu": n, "swiglu": n // 2, "geglu": n // 2, "dswiglu": 2 * n, "dgeglu": 2 * n,
+            "dsrelu": n}[problem["act"]]
 
 
 def empty_outputs(problem: dict, device="cuda", fill: int | None = None) -> dict:
@@ -88,7 +89,7 @@ def empty_outputs(problem: dict, device="cuda", fill: int | None = None) -> dict
         if fill is not None:
             t.view(torch.uint8).fill_(fill)
         return t
-    if problem["act"] in ("dswiglu", "dsrelu"):
+    if problem["act"] in ("dswiglu", "dsrelu", "dgeglu"):
         out["dprob"] = torch.zeros(m, dtype=torch.float32, device=device)
         if problem["d_dtype"] == "e4m3":
             out["d"] = mk((m, no), torch.uint8)
@@ -98,7 +99,7 @@ def empty_outputs(problem: dict, device="cuda", fill: int | None = None) -> dict
         else:
             out["d"] = mk((m, no), torch.int16)
             if problem["ab_dtype"] != "bf16":
-                out["amax"] = mk((L, 2) if problem["act"] == "dswiglu" else (L,), torch.float32)
+                out["amax"] = mk((L, 2) if problem["act"] in ("dswiglu", "dgeglu") else (L,), torch.float32)
         return out
     if problem.get("c_dtype") == "bf16":
         out["c"] = mk((m, n), torch.int16)
@@ -119,17 +120,15 @@ def inputs_for(problem: dict, dev_arrays: dict, discrete: dict | None = None) ->
     keys = ["a", "b", "padded_offsets", "alpha", "prob"]
     if problem["ab_dtype"] != "bf16":
         keys += ["sfa", "sfb"]
-    if discrete is not None:
-        keys = [k for k in keys if k not in ("b", "sfb")]
-        return {**{k: dev_arrays[k] for k in keys + [k for k in ("norm_const",) if problem["d_dtype"] == "e4m3"]
-                   + (["beta", "c_in"] if problem["act"] == "dswiglu" else [])
-                   + (["c_in"] if problem["act"] == "dsrelu" else [])}, **discrete}
     if problem["d_dtype"] == "e4m3":
         keys += ["norm_const"]
     if problem["act"] == "dswiglu":
         keys += ["beta", "c_in"]
-    if problem["act"] == "dsrelu":
+    if problem["act"] in ("dsrelu", "dgeglu"):
         keys += ["c_in"]
+    if discrete is not None:
+        keys = [k for k in keys if k not in ("b", "sfb")]
+        return {**{k: dev_arrays[k] for k in keys}, **discrete}
     return {k: dev_arrays[k] for k in keys}
 
 

@@ -9,6 +9,9 @@ Formats (the element and scale types the pages' support tables name:
   Exponent field 0 holds subnormals m/8 * 2^-6; S.1111.111 is NaN; there is
   no infinity; the largest finite magnitude is 448 (the q_max the
   quantisation step of the same page names for E4M3).
+* E5M2 ("float8_e5m2"): sign, 5 exponent bits (bias 15), 2 mantissa bits,
+  the upper byte of an IEEE binary16: exponent field 0 holds subnormals
+  m/4 * 2^-14, field 31 is infinity (m = 0) or NaN; largest finite 57344.
 * E2M1 ("float4_e2m1fn_x2", two per byte): sign, 2 exponent bits (bias 1),
   1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
 * E8M0 ("float8_e8m0fnu"): a bare biased exponent, value 2^(x-127); 0xFF is NaN.
@@ -32,6 +35,16 @@ def decode_e4m3(codes) -> np.ndarray:
     m = (c & 0x7).astype(np.float64)
     val = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
     val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return sign * val
+
+
+def decode_e5m2(codes) -> np.ndarray:
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 2) & 0x1F
+    m = (c & 0x3).astype(np.float64)
+    val = np.where(e == 0, (m / 4.0) * 2.0 ** -14, (1.0 + m / 4.0) * np.exp2(e.astype(np.float64) - 15.0))
+    val = np.where(e == 31, np.where(m == 0, np.inf, np.nan), val)
     return sign * val
 
 

@@ -42,6 +42,10 @@ reason, in the design notes of the repository):
   read without a beta scale, and dC / dprob follow from the forward equation
   (see dsrelu); with MX operands its dC is formatted like a forward D (bf16 +
   per-group amax of shape (L), or FP8 rows and columns).
+* GeGLU (forward) and dGeGLU (backward): blocks in the order the pages give
+  for them, gate first ([G_b | U_b], [dgate_b | dup_b]); the forward's clamp
+  applies [glu_clamp_min, glu_clamp_max] to both halves, the backward's to the
+  gate from above and to up on both sides, as the dGLU page states.
 * Block-scaled dSwiGLU with a BF16 dC reports amax of shape (L, 2) (the dGLU
   page's block-scaled outputs): entry 0 is max |d_input| over the group's
   rows and its input blocks, entry 1 max |d_gate| over its gate blocks.  With
@@ -69,6 +73,8 @@ def dequantize(codes, scales, ab_dtype: str) -> np.ndarray:
         return F.decode_bf16(codes)
     if ab_dtype == "e4m3":
         elem = F.decode_e4m3(codes)
+    elif ab_dtype == "e5m2":
+        elem = F.decode_e5m2(codes)
     elif ab_dtype == "e2m1x2":
         elem = F.decode_e2m1(F.unpack_e2m1x2(codes))
     else:
@@ -147,6 +153,53 @@ def dswiglu(rmat, x_saved, prob):
     d_gate = rr * p * inp * s * (1.0 + gate * (1.0 - s))
     dc = np.stack([d_in, d_gate], axis=2).reshape(r, 2 * n)
     dprob = (rr * inp * gate * s).reshape(r, n).sum(axis=1)
+    return dc, dprob
+
+
+def glu_params(problem: dict):
+    """GeGLU / dGeGLU constants of a problem: (gamma, alpha, offset, clamp_min,
+    clamp_max); the pages' defaults are gamma 1, alpha 1.702, offset 1 and, for
+    the backward, clamps -7 / 7."""
+    return (float(problem.get("glu_gamma", 1.0)), float(problem.get("geglu_alpha", 1.702)),
+            float(problem.get("linear_offset", 1.0)), float(problem.get("glu_clamp_min", -np.inf)),
+            float(problem.get("glu_clamp_max", np.inf)))
+
+
+def geglu(c, prob, gamma, alpha, offset, cmin, cmax):
+    """GeGLU over pairs [G_b | U_b] of 32 columns, gate first ("Grouped GEMM +
+    GLU + Hadamard", §Equations, GeGLU): both halves clamped to [cmin, cmax]
+    (the page's glu_limit) before the activation,
+      D_b = gamma * prob * (U_b + offset) * G_b * sigmoid(alpha * G_b)
+    (the page's constants: alpha 1.702, offset 1)."""
+    r, n = c.shape
+    cs = c.reshape(r, n // 64, 2, 32)
+    g = np.clip(cs[:, :, 0, :], cmin, cmax)
+    u = np.clip(cs[:, :, 1, :], cmin, cmax)
+    d = gamma * prob[:, None, None] * (u + offset) * g * sigmoid(alpha * g)
+    return d.reshape(r, n // 2)
+
+
+def dgeglu(rmat, c_saved, prob, alpha, offset, cmin, cmax):
+    """dGeGLU backward ("Grouped GEMM + dGLU (SM100)", dGeGLU equations of the
+    BF16 and block-scaled contracts): saved C in pairs [gate_b | up_b] (the
+    page's [dgate, dup] output order), gate clamped above only, up on both
+    sides, masks from the unclamped values (gradient kept at equality):
+      dgate = R prob (up_c + offset) s (1 + alpha gate_c (1 - s)) [gate <= cmax]
+      dup   = R prob gate_c s [cmin <= up <= cmax]
+      dprob = sum R gate_c s (up_c + offset),  s = sigmoid(alpha gate_c)
+    """
+    r, n = rmat.shape
+    xs = c_saved.reshape(r, n // 32, 2, 32)
+    gate, up = xs[:, :, 0, :], xs[:, :, 1, :]
+    gc = np.minimum(gate, cmax)
+    uc = np.clip(up, cmin, cmax)
+    s = sigmoid(alpha * gc)
+    rr = rmat.reshape(r, n // 32, 32)
+    p = prob[:, None, None]
+    dgate = rr * p * (uc + offset) * s * (1.0 + alpha * gc * (1.0 - s)) * (gate <= cmax)
+    dup = rr * p * gc * s * ((cmin <= up) & (up <= cmax))
+    dc = np.stack([dgate, dup], axis=2).reshape(r, 2 * n)
+    dprob = (rr * gc * s * (uc + offset)).reshape(r, n).sum(axis=1)
     return dc, dprob
 
 
@@ -263,7 +316,7 @@ def grouped_gemm(problem: dict, arrays: dict, rows=None) -> dict:
     prob = np.asarray(arrays["prob"], dtype=np.float64)[rows]
     out = {"rows": rows, "group": grp, "acc": acc}
 
-    if act in ("dswiglu", "dsrelu"):
+    if act in ("dswiglu", "dsrelu", "dgeglu"):
         # "Grouped GEMM + dGLU (SM100)": R_g = alpha_g^2 A_g B_g^T (BF16 contract;
         # block-scaled Step 1 with dequantised A, B), then Step 2; the sReLU
         # backward takes the same R and the saved forward C as it is
@@ -272,15 +325,18 @@ def grouped_gemm(problem: dict, arrays: dict, rows=None) -> dict:
             beta = np.asarray(arrays["beta"], dtype=np.float64)[grp]
             x_saved = beta[:, None] * F.decode_bf16(arrays["c_in"][rows])
             dc, dprob = dswiglu(rmat, x_saved, prob)
-        else:
+        elif act == "dsrelu":
             dc, dprob = dsrelu(rmat, F.decode_bf16(arrays["c_in"][rows]), prob,
                                float(problem.get("srelu_tanh_s", 0.0)))
+        else:
+            _, ga, off, cmin, cmax = glu_params(problem)
+            dc, dprob = dgeglu(rmat, F.decode_bf16(arrays["c_in"][rows]), prob, ga, off, cmin, cmax)
         out.update(r=rmat, dc=dc, dprob=dprob, dc_bits=F.encode_bf16(dc))
         if ab == "bf16":
             return out
         # block-scaled backend: output formatting of dC (Step 3)
         d = dc
-        if act == "dswiglu" and problem["d_dtype"] == "bf16":
+        if act in ("dswiglu", "dgeglu") and problem["d_dtype"] == "bf16":
             halves = np.abs(dc).reshape(len(rows), -1, 2, 32)
             amax2 = np.zeros((L, 2), dtype=np.float64)
             for g in np.unique(grp):
@@ -301,6 +357,9 @@ def grouped_gemm(problem: dict, arrays: dict, rows=None) -> dict:
             d = swiglu(c, prob)
         elif act == "srelu":
             d = srelu(c, prob, float(problem.get("srelu_tanh_s", 0.0)))
+        elif act == "geglu":
+            gm, ga, off, cmin, cmax = glu_params(problem)
+            d = geglu(c, prob, gm, ga, off, cmin, cmax)
         else:
             raise ValueError(act)
         out["d"] = d

@@ -66,6 +66,22 @@ def encode_e4m3(v: np.ndarray) -> np.ndarray:
     return code.astype(np.uint8)
 
 
+def encode_e5m2(v: np.ndarray) -> np.ndarray:
+    """float32 values with |v| <= 57344 -> OCP E5M2 codes (uint8), RNE."""
+    v = np.asarray(v, dtype=np.float32)
+    mag = np.abs(v)
+    bits = mag.view(np.uint32).astype(np.int64)
+    # normal range: keep 2 mantissa bits with round-half-even on the 21 dropped bits
+    rounded = bits + 0xFFFFF + ((bits >> 21) & 1)
+    normal = (rounded >> 21) - (112 << 2)
+    # subnormal range (|v| < 2^-14): integer multiples of 2^-16, RNE via rint
+    sub = np.rint(mag.astype(np.float64) * 65536.0).astype(np.int64)
+    code = np.where(mag < 2.0 ** -14, sub, normal)
+    code = np.clip(code, 0, 0x7B)
+    code = code | np.where((v < 0) & (code != 0), 0x80, 0)
+    return code.astype(np.uint8)
+
+
 _E2M1_EDGES_GT = np.array([0.25, 1.25, 2.5, 5.0], dtype=np.float32)   # tie stays (even code below)
 _E2M1_EDGES_GE = np.array([0.75, 1.75, 3.5], dtype=np.float32)        # tie advances (even code above)
 
@@ -103,7 +119,7 @@ def mx_quantize(x: np.ndarray, fmt: str):
     rounded to nearest even in the element format.  E2M1 codes are packed two
     per byte, the even K element in the low nibble.
     """
-    fmt_max = {"e4m3": 448.0, "e2m1x2": 6.0}[fmt]
+    fmt_max = {"e4m3": 448.0, "e5m2": 57344.0, "e2m1x2": 6.0}[fmt]
     shp = x.shape
     k = shp[-1]
     assert k % 32 == 0
@@ -117,6 +133,8 @@ def mx_quantize(x: np.ndarray, fmt: str):
     scaled = np.clip(scaled, -fmt_max, fmt_max)
     if fmt == "e4m3":
         codes = encode_e4m3(scaled).reshape(shp)
+    elif fmt == "e5m2":
+        codes = encode_e5m2(scaled).reshape(shp)
     else:
         nib = encode_e2m1(scaled).reshape(shp)
         codes = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
@@ -205,6 +223,19 @@ CONFIGS = {
     "dsrelu_mxfp8_l32": dict(L=32, K=4096, N=4096, ab="e4m3", act="dsrelu", d="e4m3", c=None,
                              routing=("multinomial", 32768), alpha=("const", 1.0),
                              prob=("uniform",), a_std=0.1, b_std="1/sqrtK", c_std=4.0, s=8.0, seed=108),
+    # GeGLU forward over the FC1 L=8 shapes, MXFP8 E5M2 operands, clamp +-7
+    # (the backward's default bounds), FP8 D
+    "fc1_geglu_e5m2_l8": dict(L=8, K=2048, N=2816, ab="e5m2", act="geglu", d="e4m3", c=None,
+                              routing=("topk", 4096, 2), alpha=("const", 1.0), prob=("softmax_all",),
+                              a_std=1.0, b_std="1/sqrtK", glu_gamma=1.0, geglu_alpha=1.702, linear_offset=1.0,
+                              glu_clamp_min=-7.0, glu_clamp_max=7.0, seed=109),
+    # dGeGLU backward over the dSwiGLU L=64 shapes, MXFP8 operands, FP8 dC,
+    # the pages' default constants (alpha 1.702, offset 1, clamps -7 / 7); the
+    # saved C ~ N(0, 4^2) so that the clamps are active on some elements
+    "dgeglu_mxfp8_l64": dict(L=64, K=2048, N=1408, ab="e4m3", act="dgeglu", d="e4m3", c=None,
+                             routing=("topk", 16384, 6), alpha=("const", 1.0), prob=("softmax_picks",),
+                             a_std=0.1, b_std="1/sqrtK", c_std=4.0, geglu_alpha=1.702, linear_offset=1.0,
+                             glu_clamp_min=-7.0, glu_clamp_max=7.0, seed=110),
     # FC1 + SwiGLU at L=64 (the forward whose backward is dswiglu_bf16_l64)
     "fc1_swiglu_l64": dict(L=64, K=2048, N=2816, ab="e4m3", act="swiglu", d="e4m3", c=None,
                            routing=("topk", 16384, 6), alpha=("const", 1.0),
@@ -359,11 +390,11 @@ def make_case(spec_or_name, seed: int | None = None, **overrides) -> Case:
                          else np.zeros((0, K // 32), np.uint8))
         arrays["sfb"] = np.stack([p[1] for p in b_parts])
     act = spec["act"]
-    if act in ("dswiglu", "dsrelu"):
+    if act in ("dswiglu", "dsrelu", "dgeglu"):
         if act == "dswiglu":
             arrays["beta"] = beta
         cin_chunks = [(r0, min(valid_m, r0 + _A_CHUNK)) for r0 in range(0, valid_m, _A_CHUNK)]
-        cw = 2 * N if act == "dswiglu" else N
+        cw = N if act == "dsrelu" else 2 * N
         c_std = np.float32(spec.get("c_std", 1.0))
 
         def _c_chunk(ci):
@@ -378,5 +409,8 @@ def make_case(spec_or_name, seed: int | None = None, **overrides) -> Case:
     problem = dict(num_groups=L, valid_m=valid_m, n=N, k=K, m_aligned=m_al,
                    ab_dtype=ab, c_dtype=spec.get("c"), d_dtype=spec["d"], act=act,
                    srelu_tanh_s=float(spec.get("s", 0.0) or 0.0))
+    for key in ("glu_gamma", "geglu_alpha", "linear_offset", "glu_clamp_min", "glu_clamp_max"):
+        if key in spec:
+            problem[key] = float(spec[key])
     return Case(name=spec.get("name", "custom"), seed=seed, problem=problem, arrays=arrays,
                 counts=np.asarray(counts), row_valid=row_valid, spec=spec)

@@ -42,7 +42,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_strings():
-    assert mg.moegg_abi_version() == 3
+    assert mg.moegg_abi_version() == 4 == mg.ABI_VERSION
     for code, name in mg.STATUS.items():
         assert mg.moegg_status_string(code) == name
     assert mg.moegg_status_string(99) == "MOEGG_UNKNOWN_STATUS"
@@ -50,7 +50,7 @@ def test_version_and_strings():
 
 def test_struct_layout_matches_header():
     # problem: 2 x int32, int64, 6 x int32, float -> 44 bytes, padded to 48
-    assert ctypes.sizeof(mg.moegg_problem) == 48
+    assert ctypes.sizeof(mg.moegg_problem) == 64
     assert mg.moegg_problem.valid_m.offset == 8
     assert ctypes.sizeof(mg.moegg_args) == 19 * 8
     assert mg.moegg_args.b_ptrs.offset == 17 * 8 and mg.moegg_args.sfb_ptrs.offset == 18 * 8
@@ -159,6 +159,34 @@ CASES = [
     ("gating_bf16", {}, dict(sfb_ptrs=FAKE + 0x21000), INVALID),             # sfb_ptrs with dense b
     ("dswiglu", {}, dict(b=None, b_ptrs=FAKE + 0x20000, sfb_ptrs=FAKE + 0x21000), INVALID),   # BF16 + sfb_ptrs
     ("gating_bf16", {}, dict(b=None, sfb=None, b_ptrs=FAKE + 0x20004, sfb_ptrs=FAKE + 0x21000), MISALIGNED),
+    # E5M2 operands: the E4M3 layout and K step
+    ("swiglu_e4m3", dict(ab_dtype="e5m2"), {}, OK),
+    ("swiglu_e4m3", dict(ab_dtype="e5m2", k=2048 + 64), {}, NOT_SUPPORTED),
+    ("swiglu_e4m3", dict(ab_dtype="e5m2"), dict(sfb=None), INVALID),
+    # GeGLU forward: pairs of 32 columns, finite constants, ordered clamps
+    ("swiglu_e4m3", dict(act="geglu", glu_clamp_min=-7.0, glu_clamp_max=7.0), {}, OK),
+    ("swiglu_e4m3", dict(act="geglu", ab_dtype="e5m2"), {}, OK),
+    ("swiglu_e4m3", dict(act="geglu", n=2816 + 32), {}, INVALID),
+    ("swiglu_e4m3", dict(act="geglu", glu_clamp_min=1.0, glu_clamp_max=-1.0), {}, INVALID),
+    ("swiglu_e4m3", dict(act="geglu", glu_clamp_min=float("nan")), {}, INVALID),
+    ("swiglu_e4m3", dict(act="geglu", geglu_alpha=float("inf")), {}, INVALID),
+    ("swiglu_e4m3", dict(act="geglu", linear_offset=float("nan")), {}, INVALID),
+    ("swiglu_e4m3", dict(act="geglu", glu_gamma=float("-inf")), {}, INVALID),
+    ("gating_bf16", dict(act="geglu"), {}, OK),                               # bf16 D + amax
+    # dGeGLU backward: c_in 2N wide, dprob, no beta; amax (L, 2) for MX operands and a bf16 dC
+    ("dswiglu", dict(act="dgeglu"), dict(beta=None), OK),
+    ("dswiglu", dict(act="dgeglu"), {}, INVALID),                                # beta given
+    ("dswiglu", dict(act="dgeglu"), dict(beta=None, c_in=None), INVALID),
+    ("dswiglu", dict(act="dgeglu"), dict(beta=None, dprob=None), INVALID),
+    ("dswiglu", dict(act="dgeglu", glu_clamp_min=7.0, glu_clamp_max=-7.0), dict(beta=None), INVALID),
+    ("dswiglu", dict(act="dgeglu", ab_dtype="e4m3"), dict(beta=None, sfa=FAKE, sfb=FAKE, amax=FAKE), OK),
+    ("dswiglu", dict(act="dgeglu", ab_dtype="e5m2"), dict(beta=None, sfa=FAKE, sfb=FAKE, amax=FAKE), OK),
+    ("dswiglu", dict(act="dgeglu", ab_dtype="e4m3"), dict(beta=None, sfa=FAKE, sfb=FAKE), INVALID),
+    ("dswiglu", dict(act="dgeglu", ab_dtype="e4m3", d_dtype="e4m3"),
+     dict(beta=None, sfa=FAKE, sfb=FAKE, d_col=FAKE + 0x40000, sfd_row=FAKE + 0x50000,
+          sfd_col=FAKE + 0x60000, norm_const=FAKE + 0x70000), OK),
+    ("dswiglu", dict(act="dgeglu", d_dtype="e4m3"), dict(beta=None), NOT_SUPPORTED),   # BF16 ops: bf16 dC
+    ("dswiglu", dict(act=7), {}, INVALID),
 ]
 
 
@@ -191,7 +219,8 @@ def test_null_structs():
 
 def test_n_out():
     for act, n, expect in [("none", 512, 512), ("swiglu", 2816, 1408), ("srelu", 4096, 4096),
-                           ("dswiglu", 1408, 2816), ("dsrelu", 4096, 4096)]:
+                           ("dswiglu", 1408, 2816), ("dsrelu", 4096, 4096), ("geglu", 2816, 1408),
+                           ("dgeglu", 1408, 2816)]:
         p, _ = _base("gating_bf16")
         p.update(act=act, n=n)
         assert mg.moegg_n_out(mg.make_problem(p)) == expect

@@ -45,7 +45,7 @@ def check_case(case, got, rows=None):
     r = ref["rows"]
     grp = ref["group"]
     stats = {}
-    if p["act"] in ("dswiglu", "dsrelu"):
+    if p["act"] in ("dswiglu", "dsrelu", "dgeglu"):
         stats["dprob"] = rule1(got["dprob"][r], ref["dprob"], grp, "dprob")
         if p["d_dtype"] == "e4m3":
             nc = float(case.arrays["norm_const"][0])
@@ -124,6 +124,34 @@ SMALL = {
                                                         clip=6.0)),
     "dsrelu_bf16_ops": ("dsrelu_mxfp8_l32", dict(ab="bf16", d="bf16", L=2, K=192, N=256,
                                                  routing=("multinomial", 200))),
+    # E5M2 operands ("Grouped GEMM + Quant", §Data Types) through the other epilogues
+    "e5m2_gating_bf16": ("quant_gating_l4", dict(ab="e5m2", L=3, K=384, N=288, routing=("multinomial", 300))),
+    "e5m2_swiglu_e4m3": ("fc1_swiglu_l8", dict(ab="e5m2", L=3, K=640, N=320, routing=("topk", 300, 2))),
+    # GeGLU forward: clamps that bite (|C| ~ 1 against bounds -1.5 / 1), other
+    # constants, every operand family, both output formats
+    "geglu_e5m2_e4m3_clamped": ("fc1_geglu_e5m2_l8", dict(L=3, K=1024, N=320, routing=("topk", 300, 2),
+                                                          glu_clamp_min=-1.5, glu_clamp_max=1.0)),
+    "geglu_fp8_bf16_consts": ("fc1_geglu_e5m2_l8", dict(ab="e4m3", d="bf16", L=3, K=384, N=256,
+                                                        routing=("topk", 200, 2), glu_gamma=0.75,
+                                                        geglu_alpha=1.25, linear_offset=0.5,
+                                                        glu_clamp_min=float("-inf"), glu_clamp_max=float("inf"),
+                                                        alpha=("uniform", 0.5, 2.0))),
+    "geglu_fp4_e4m3_c": ("fc1_geglu_e5m2_l8", dict(ab="e2m1x2", L=2, K=512, N=320, routing=("topk", 160, 2),
+                                                   b_std=1.0, clip=6.0, c="bf16", glu_clamp_min=-4.0,
+                                                   glu_clamp_max=3.0)),
+    "geglu_bf16_ops": ("fc1_geglu_e5m2_l8", dict(ab="bf16", L=2, K=192, N=256, routing=("topk", 200, 2),
+                                                 glu_clamp_min=-0.75, glu_clamp_max=0.75)),
+    # dGeGLU backward ("Grouped GEMM + dGLU (SM100)", dGeGLU): C ~ N(0, 4^2)
+    # against clamps -7 / 7, so both masks and the sigmoid tails are exercised
+    "dgeglu_mxfp8_e4m3": ("dgeglu_mxfp8_l64", dict(L=5, K=1024, N=288, routing=("topk", 200, 3),
+                                                   alpha=("uniform", 0.5, 2.0))),
+    "dgeglu_e5m2_bf16_amax": ("dgeglu_mxfp8_l64", dict(ab="e5m2", d="bf16", L=3, K=640, N=256,
+                                                       routing=("topk", 150, 2), linear_offset=0.25,
+                                                       glu_clamp_min=-3.0, glu_clamp_max=5.0)),
+    "dgeglu_mxfp4_e4m3": ("dgeglu_mxfp8_l64", dict(ab="e2m1x2", L=3, K=512, N=256, routing=("topk", 150, 2),
+                                                   a_std=1.0, b_std=1.0, clip=6.0, norm_const=2.0)),
+    "dgeglu_bf16_ops": ("dgeglu_mxfp8_l64", dict(ab="bf16", d="bf16", L=2, K=192, N=288,
+                                                 routing=("topk", 150, 2), geglu_alpha=1.0)),
 }
 
 
@@ -172,6 +200,7 @@ DISCRETE = {
                                                                 routing=("topk_zipf", 400, 3, 1.1, 2))),
     "discrete_dswiglu_bf16": ("dswiglu_bf16_l64", dict(L=4, K=256, N=288, routing=("topk", 200, 3))),
     "discrete_empty_groups": ("quant_gating_l4", dict(L=7, K=512, N=256, force_counts=[0, 1, 0, 128, 129, 0, 1])),
+    "discrete_dgeglu_e5m2_e4m3": ("dgeglu_mxfp8_l64", dict(ab="e5m2", L=4, K=512, N=256, routing=("topk", 200, 3))),
 }
 
 
@@ -323,7 +352,7 @@ def test_check_offsets_on_device():
 # ---------------------------------------------------------------------------
 
 FULL = ["fc1_swiglu_l8", "fc2_gating_l64_zipf", "srelu_tanh_fp4_l32", "dswiglu_bf16_l64", "fc1_swiglu_l64",
-        "dswiglu_mxfp8_l64", "dsrelu_mxfp8_l32"]
+        "dswiglu_mxfp8_l64", "dsrelu_mxfp8_l32", "fc1_geglu_e5m2_l8", "dgeglu_mxfp8_l64"]
 
 
 @pytest.mark.slow
@@ -347,7 +376,7 @@ def test_full_size_sampled(name):
     stats = check_case(case, got, rows)
     p = case.problem
     pad = ~case.row_valid
-    if p["act"] in ("dswiglu", "dsrelu"):
+    if p["act"] in ("dswiglu", "dsrelu", "dgeglu"):
         # padding rows have A = 0, so R = 0: dC and dprob are (signed) zeros
         dpad = F.decode_e4m3(got["d"][pad]) if p["d_dtype"] == "e4m3" else decode_bf16(got["d"][pad])
         assert np.all(dpad == 0) and np.all(got["dprob"][pad] == 0)

@@ -346,6 +346,81 @@ def test_dsrelu_through_the_gemm_closed_form():
     np.testing.assert_array_equal(out["amax"], [2.0])
 
 
+def test_e5m2_is_the_upper_byte_of_binary16():
+    """Every E5M2 code decodes to the IEEE binary16 value whose upper byte it
+    is (numpy's float16 is the reference)."""
+    c = np.arange(256)
+    ref = (c.astype(np.uint16) << 8).view(np.float16).astype(np.float64)
+    got = F.decode_e5m2(c)
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    assert got[0x3C] == 1.0 and got[0x7B] == 57344.0 and got[0x01] == 2.0 ** -16 and got[0x7C] == np.inf
+
+
+def test_dgeglu_matches_finite_differences_of_geglu():
+    """Without clamps the dGeGLU backward is the derivative of the GeGLU forward:
+    with L = sum R * D(C) over the GeGLU outputs, dC = dL/dC and dprob = dL/dprob
+    (R indexed by output column, the pairs [gate | up] gate first)."""
+    rng = np.random.default_rng(10)
+    rows, nb = 3, 2                      # 2 pairs -> C width 128, output width 64
+    R = rng.standard_normal((rows, 32 * nb))
+    C = rng.standard_normal((rows, 64 * nb)) * 2
+    p = rng.random(rows)
+    a, off = 1.3, 0.75
+
+    def loss(Cv, pv):
+        return (R * G.geglu(Cv, pv, 1.0, a, off, -np.inf, np.inf)).sum()
+
+    dc, dprob = G.dgeglu(R, C, p, a, off, -np.inf, np.inf)
+    h = 1e-6
+    num = np.zeros_like(C)
+    for r in range(rows):
+        for j in range(C.shape[1]):
+            Cp, Cm = C.copy(), C.copy()
+            Cp[r, j] += h
+            Cm[r, j] -= h
+            num[r, j] = (loss(Cp, p) - loss(Cm, p)) / (2 * h)
+    np.testing.assert_allclose(dc, num, rtol=1e-6, atol=1e-8)
+    nump = np.array([(loss(C, p + h * (np.arange(rows) == r)) - loss(C, p - h * (np.arange(rows) == r))) / (2 * h)
+                     for r in range(rows)])
+    np.testing.assert_allclose(dprob, nump, rtol=1e-7, atol=1e-9)
+
+
+def test_dgeglu_clamp_masks_closed_form():
+    """Gate above clamp_max: dgate = 0, dup uses the clamped gate; up outside
+    [min, max]: dup = 0, dgate uses the clamped up; equality keeps the gradient."""
+    R = np.ones((1, 32))
+    c = np.zeros((1, 64))
+    c[0, :32] = [9.0, 7.0, 1.0, 1.0] + [0.0] * 28          # gate
+    c[0, 32:] = [2.0, 2.0, -9.0, 7.0] + [0.0] * 28         # up
+    dc, dprob = G.dgeglu(R, c, np.ones(1), 1.702, 1.0, -7.0, 7.0)
+    s7 = 1 / (1 + np.exp(-1.702 * 7.0))
+    s1 = 1 / (1 + np.exp(-1.702))
+    assert dc[0, 0] == 0.0                                  # gate 9 > 7
+    np.testing.assert_allclose(dc[0, 32], 7.0 * s7, rtol=1e-15)            # dup with gate_c = 7
+    np.testing.assert_allclose(dc[0, 1], 3.0 * s7 * (1 + 1.702 * 7 * (1 - s7)), rtol=1e-15)   # gate == 7 kept
+    assert dc[0, 34] == 0.0                                 # up -9 < -7
+    np.testing.assert_allclose(dc[0, 2], (-7.0 + 1.0) * s1 * (1 + 1.702 * (1 - s1)), rtol=1e-15)
+    np.testing.assert_allclose(dc[0, 35], 1.0 * s1, rtol=1e-15)             # up == 7 kept
+    np.testing.assert_allclose(dprob[0], 7 * s7 * 3 + 7 * s7 * 3 + s1 * (-6) + s1 * 8, rtol=1e-14)
+
+
+def test_geglu_is_sigmoid_gelu_times_up():
+    """GeGLU with offset 1, gamma 1 and no clamp: D = (U + 1) * G * sigmoid(1.702 G),
+    checked against scipy's logistic function; the clamp bounds both halves."""
+    from scipy.special import expit
+    rng = np.random.default_rng(11)
+    c = rng.standard_normal((4, 128)) * 3
+    p = rng.random(4)
+    d = G.geglu(c, p, 1.0, 1.702, 1.0, -np.inf, np.inf)
+    g, u = c[:, :32], c[:, 32:64]
+    np.testing.assert_allclose(d[:, :32], p[:, None] * (u + 1) * g * expit(1.702 * g), rtol=1e-13)
+    dcl = G.geglu(c, p, 2.0, 1.702, 1.0, -1.0, 1.0)
+    gc, uc = np.clip(g, -1, 1), np.clip(u, -1, 1)
+    np.testing.assert_allclose(dcl[:, :32], 2 * p[:, None] * (uc + 1) * gc * expit(1.702 * gc), rtol=1e-13)
+
+
 def _bs_dswiglu_case(d_dtype):
     """Two experts of 2 rows, MXFP8 A = 1.0 and B = 1/32 (scale byte 122), K = 64:
     acc = 2; alpha = (0.5, 1) -> R = (0.5, 2).  C_in: input blocks 2.0, gate
