@@ -31,7 +31,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"e4m3": 5000.0, "e2m1x2": 10100.0, "bf16": 2500.0}   # dense MFMA peaks, MI355X
+PEAK_TFLOPS = {"e4m3": 5000.0, "e5m2": 5000.0, "e2m1x2": 10100.0, "bf16": 2500.0}   # dense MFMA peaks, MI355X
 HBM_GBS = 8000.0
 KERNEL_SOURCES = ["moe_grouped_block_amd/csrc/grouped_gemm.h", "moe_grouped_block_amd/csrc/moegg_kernels.hip",
                   "moe_grouped_block_amd/csrc/inst_e4m3.hip", "moe_grouped_block_amd/csrc/inst_e2m1.hip",
@@ -219,7 +219,7 @@ def main():
         r = measure(name, max(args.steps, 20), args.warmup, args.cold)
         c = r["case"]
         also[name] = {"ms_per_step": round(r["ms"], 5), "tflops_routed": round(r["tflops"], 2),
-                      "frac_mxfp8_peak": round(r["tflops"] / PEAK_TFLOPS[c.problem["ab_dtype"]], 4),
+                      "frac_mfma_peak": round(r["tflops"] / PEAK_TFLOPS[c.problem["ab_dtype"]], 4),
                       "valid_m": c.problem["valid_m"], "routed_rows": c.routed_rows,
                       "experts": c.problem["num_groups"]}
         if "cold_ms" in r:
