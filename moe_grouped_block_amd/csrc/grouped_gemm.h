@@ -179,15 +179,26 @@ __device__ __forceinline__ float max_abs2(float c, float a, float b) {
   return fmaxf(fmaxf(fabsf(a), fabsf(b)), c);
 }
 
+// Epilogue addressing: every output address is a wave-uniform base (the
+// wave's first row and the block's first column, scalar registers) plus a
+// 32-bit per-lane byte offset, so that an address costs one vector register
+// and the loads and stores take their scalar-base form.  Offsets stay below
+// 2^32: 128 rows of at most 2^21 two-byte elements.
+template <typename T>
+__device__ __forceinline__ T* at(T* base, uint32_t byte_off) {
+  return reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(base) + static_cast<uint64_t>(byte_off));
+}
+
 // Store 16 values of one row (one 32-column tile) as bf16: 4 runs of 4.
-__device__ __forceinline__ void store_bf16_tile(uint8_t* base, int64_t m, int ld, int col, int hi,
-                                                const float* v) {
+// `base` is the tile's first column in the wave's first row; `roff` the
+// lane's row offset in bytes.
+__device__ __forceinline__ void store_bf16_tile(uint8_t* base, uint32_t roff, int hi, const float* v) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     v2u w;
     w.x = bf16_rne(v[4 * j + 0]) | (bf16_rne(v[4 * j + 1]) << 16);
     w.y = bf16_rne(v[4 * j + 2]) | (bf16_rne(v[4 * j + 3]) << 16);
-    *reinterpret_cast<v2u*>(base + (m * ld + col + 8 * j + 4 * hi) * 2) = w;
+    *at(reinterpret_cast<v2u*>(base + 16 * j), roff + 8 * hi) = w;
   }
 }
 
@@ -198,10 +209,10 @@ __device__ __forceinline__ void store_bf16_tile(uint8_t* base, int64_t m, int ld
 // lane hi = 1 with (partner's w[j+2], own w[j+2]) = columns 16 + 8j + [0, 8),
 // so lane hi = 0 stores columns [0, 16) and lane hi = 1 columns [16, 32),
 // one 16-byte store each.
-__device__ __forceinline__ void store_e4m3_row(uint8_t* dst_row, int hi, const uint32_t* w) {
+__device__ __forceinline__ void store_e4m3_row(uint8_t* base, uint32_t roff, int hi, const uint32_t* w) {
   const v2u s0 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
   const v2u s1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
-  *reinterpret_cast<v4u*>(dst_row + 16 * hi) = v4u{s0.x, s0.y, s1.x, s1.y};
+  *at(reinterpret_cast<v4u*>(base), roff + 16 * hi) = v4u{s0.x, s0.y, s1.x, s1.y};
 }
 
 // FP8 row + column quantisation of one 32 x 32 output tile ("Grouped GEMM +
@@ -216,9 +227,12 @@ __device__ __forceinline__ void store_e4m3_row(uint8_t* dst_row, int hi, const u
 //   S: 32 floats, the inverse column scales.
 // Lanes 0-31 read rows 0-15 of column l, lanes 32-63 rows 24-31 then 16-23,
 // so that both halves of a 64-lane read hit complementary bank ranges.
+// Outputs: D at dW + roff, D_col at dcW + roff (dW, dcW: the block's first
+// column in the wave's first row; roff: the lane's row offset), the row
+// block's scale byte at sfW + sfoff.
 // Returns the E8M0 byte of this lane's column (l % 32) block.
-__device__ __forceinline__ uint32_t quant_tile(const KernelArgs& p, float* T, float* S, int m, int ocol, int hi,
-                                               int l32, const float* dn) {
+__device__ __forceinline__ uint32_t quant_tile(float* T, float* S, uint8_t* dW, uint8_t* dcW, uint8_t* sfW,
+                                               uint32_t roff, uint32_t sfoff, int hi, int l32, const float* dn) {
   // the previous call's cross-lane reads of T and S stay ahead of this
   // call's writes
   __builtin_amdgcn_wave_barrier();
@@ -259,10 +273,9 @@ __device__ __forceinline__ uint32_t quant_tile(const KernelArgs& p, float* T, fl
     wr[j] = e4m3x4_scaled(dn[4 * j], dn[4 * j + 1], dn[4 * j + 2], dn[4 * j + 3], sr);
     wc[j] = e4m3x4(dn[4 * j] * sc[j].x, dn[4 * j + 1] * sc[j].y, dn[4 * j + 2] * sc[j].z, dn[4 * j + 3] * sc[j].w);
   }
-  const int64_t rowoff = static_cast<int64_t>(m) * p.n_out + ocol;
-  store_e4m3_row(p.d + rowoff, hi, wr);
-  store_e4m3_row(p.d_col + rowoff, hi, wc);
-  if (hi == 0) p.sfd_row[static_cast<int64_t>(m) * (p.n_out >> 5) + (ocol >> 5)] = static_cast<uint8_t>(br);
+  store_e4m3_row(dW, roff, hi, wr);
+  store_e4m3_row(dcW, roff, hi, wc);
+  if (hi == 0) *at(sfW, sfoff) = static_cast<uint8_t>(br);
   return bc;
 }
 
@@ -445,7 +458,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
     const uint8_t* b;
     uint32_t oa[4];      // per-lane byte offsets: low half j = 0, 1; high half 2, 3
     uint32_t ob[4];
-    const uint8_t* s[SL];
+    const uint8_t* s[SL];   // scale words: wave-uniform bases ...
+    uint32_t so[SL];         // ... and per-lane byte offsets
   };
   auto make_src = [&](const Tile& tl) __attribute__((always_inline)) {
     // per-lane values are rebuilt from an opaque copy of the lane id instead
@@ -481,8 +495,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         // word planes: word j of row r at 4 * (j * rows + r) (rows = valid_m for
         // SFA, sfb_rows for SFB: L * N dense with row g * N + n, N discrete);
         // step ks uses planes SW*ks .. SW*ks + SW-1
-        s.s[u] = isA ? p.sfa + (static_cast<int64_t>(word) * vm + tl.row0 + min(rowsel, alast)) * 4
-                     : tl.sg + (static_cast<int64_t>(word) * p.sfb_rows + tl.n0 + min(rowsel, blast)) * 4;
+        s.s[u] = isA ? p.sfa + (static_cast<int64_t>(word) * vm + tl.row0) * 4
+                     : tl.sg + (static_cast<int64_t>(word) * p.sfb_rows + tl.n0) * 4;
+        s.so[u] = static_cast<uint32_t>(min(rowsel, isA ? alast : blast)) * 4;
       }
     }
     return s;
@@ -502,7 +517,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   auto issue_ea = [&](const Src& s, int ks, const Stage& d) __attribute__((always_inline)) {
     const int kb = ks * BK;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dma16(s.a + s.oa[j] + kb, d.al + (wave * 16 + j * 8) * BK);
+    for (int j = 0; j < 2; ++j) dma16(at(s.a + kb, s.oa[j]), d.al + (wave * 16 + j * 8) * BK);
     if constexpr (MX) {
 #pragma unroll
       for (int u = 0; u < S_LOADS; ++u) {
@@ -512,17 +527,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         const int jj = isA ? job : job - S_HALF;
         uint32_t* dst = (isA ? d.sa : d.sb) + (jj >> 2) * (isA ? BM : BN) + (jj & 3) * 64;
         const int64_t plane = isA ? static_cast<int64_t>(vm) * 4 : p.sfb_rows * 4;
-        dma4(s.s[u] + static_cast<int64_t>(ks) * SW * plane, dst);
+        dma4(at(s.s[u] + static_cast<int64_t>(ks) * SW * plane, s.so[u]), dst);
       }
     }
   };
   // early set, second part: B row load j (0..3)
   auto issue_eb = [&](const Src& s, int ks, const Stage& d, int j) __attribute__((always_inline)) {
-    dma16(s.b + s.ob[j] + ks * BK, d.b + (wave * 32 + j * 8) * BK);
+    dma16(at(s.b + ks * BK, s.ob[j]), d.b + (wave * 32 + j * 8) * BK);
   };
   // late set: high A half load j (0..1)
   auto issue_l = [&](const Src& s, int ks, const Stage& d, int j) __attribute__((always_inline)) {
-    dma16(s.a + s.oa[2 + j] + ks * BK, d.ah + (wave * 16 + j * 8) * BK);
+    dma16(at(s.a + ks * BK, s.oa[2 + j]), d.ah + (wave * 16 + j * 8) * BK);
   };
   // a whole stage, in the order early (first part, second part), late
   auto issue = [&](const Src& s, int ks, const Stage& d) __attribute__((always_inline)) {
@@ -700,6 +715,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
     const float alpha = ein.alpha;
     const int mbase = tl.row0 + wm * WM;
     const int nbase = tl.n0 + wn * WN;
+    const int64_t mb = mbase;
+    // FP8 outputs: the wave's first row of D, D_col and SFD_row (uniform)
+    uint8_t* const dW0 = OUT == OUT_E4M3 ? p.d + mb * p.n_out : nullptr;
+    uint8_t* const dcW0 = OUT == OUT_E4M3 ? p.d_col + mb * p.n_out : nullptr;
+    uint8_t* const sfW0 = OUT == OUT_E4M3 ? p.sfd_row + mb * (p.n_out >> 5) : nullptr;
+    const uint32_t sfc_pitch = static_cast<uint32_t>(vm >> 5);     // bytes per SFD_col row
     float pr[TM];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) pr[tm] = sPr[wave][tm * 32 + l32];
@@ -720,6 +741,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       float beta = 1.0f;
       if constexpr (ACT == ACT_DSWIGLU) beta = p.beta[g];
       const int ld2 = 2 * p.n;
+      const uint16_t* const cinW = p.c_in + mb * ld2 + 2 * nbase;   // wave's first row, block pair 0
+      uint8_t* const dbW = p.d + (mb * ld2 + 2 * nbase) * 2;          // BF16 dC, same layout
       // block-scaled operands with a BF16 output: amax per group of the first
       // and of the second blocks of the pairs (amax of shape (L, 2))
       constexpr bool AMAX2 = MX && OUT == OUT_BF16;
@@ -729,7 +752,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       for (int tn = 0; tn < TN; ++tn) colw0[tn] = colw1[tn] = 0;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
-        const int m = mbase + tm * 32 + l32;
+        const uint32_t ml = tm * 32 + l32;                 // row within the wave's 128
+        const uint32_t xr = ml * static_cast<uint32_t>(ld2) * 2;   // its C_in / BF16 dC row, bytes
         float dp = 0.0f;
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
@@ -738,55 +762,56 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           // keep this tile's C_in loads here (hoisting every tile's loads
           // ahead of the FP8 quantisation would spill)
           if constexpr (OUT == OUT_E4M3) asm volatile("" ::: "memory");
-          const int64_t xoff = static_cast<int64_t>(m) * ld2 + 2 * ncol;   // block b = ncol/32 starts at 64b
-          float x0[16], x1[16];
+          // block b = ncol/32 of R pairs with C_in columns [64b, 64b + 64)
+          const uint16_t* const xb = cinW + 64 * tn;
+          v2u wi[4], wg[4];          // packed bf16 of the first and second blocks of the pair
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const v2u wi = *reinterpret_cast<const v2u*>(p.c_in + xoff + 8 * j + 4 * hi);
-            const v2u wg = *reinterpret_cast<const v2u*>(p.c_in + xoff + 32 + 8 * j + 4 * hi);
-            x0[4 * j + 0] = __uint_as_float(wi.x << 16);
-            x0[4 * j + 1] = __uint_as_float(wi.x & 0xFFFF0000u);
-            x0[4 * j + 2] = __uint_as_float(wi.y << 16);
-            x0[4 * j + 3] = __uint_as_float(wi.y & 0xFFFF0000u);
-            x1[4 * j + 0] = __uint_as_float(wg.x << 16);
-            x1[4 * j + 1] = __uint_as_float(wg.x & 0xFFFF0000u);
-            x1[4 * j + 2] = __uint_as_float(wg.y << 16);
-            x1[4 * j + 3] = __uint_as_float(wg.y & 0xFFFF0000u);
+            wi[j] = *at(reinterpret_cast<const v2u*>(xb + 8 * j), xr + 8 * hi);
+            wg[j] = *at(reinterpret_cast<const v2u*>(xb + 32 + 8 * j), xr + 8 * hi);
           }
-          float d0[16], d1[16];
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
+          // element v of a packed block (columns 8(v/4) + 4 hi + v%4)
+          auto bf = [](const v2u* w, int v) __attribute__((always_inline)) {
+            const uint32_t u = (v & 2) ? w[v >> 2].y : w[v >> 2].x;
+            return __uint_as_float((v & 1) ? (u & 0xFFFF0000u) : (u << 16));
+          };
+          // dC of element v in the first (part 0) or second (part 1) block;
+          // part 0 also accumulates the dprob term
+          auto dglu = [&](int v, int part, float& dpv) __attribute__((always_inline)) -> float {
             const float r = a2 * acc[tm][tn][v];
             if constexpr (ACT == ACT_DSWIGLU) {
-              const float x = beta * x0[v];
-              const float gt = beta * x1[v];
-              const float s = sigmoid_f(gt);
-              const float swish = gt * s;
-              d0[v] = r * pr[tm] * swish;
-              d1[v] = r * pr[tm] * x * s * (1.0f + gt * (1.0f - s));
-              dp += r * x * swish;
+              const float x = beta * bf(wi, v);
+              const float gt = beta * bf(wg, v);
+              const float sg = sigmoid_f(gt);
+              const float swish = gt * sg;
+              if (part == 0) {
+                dpv += r * x * swish;
+                return r * pr[tm] * swish;
+              }
+              return r * pr[tm] * x * sg * (1.0f + gt * (1.0f - sg));
             } else {
-              const float gate = x0[v], up = x1[v];
+              const float gate = bf(wi, v), up = bf(wg, v);
               const float gc = fminf(gate, p.glu_clamp_max);
               const float uc = fminf(fmaxf(up, p.glu_clamp_min), p.glu_clamp_max);
-              const float s = sigmoid_f(p.geglu_alpha * gc);
+              const float sg = sigmoid_f(p.geglu_alpha * gc);
               const float uo = uc + p.linear_offset;
-              d0[v] = gate <= p.glu_clamp_max ? r * pr[tm] * uo * s * (1.0f + p.geglu_alpha * gc * (1.0f - s)) : 0.0f;
-              d1[v] = (up >= p.glu_clamp_min && up <= p.glu_clamp_max) ? r * pr[tm] * gc * s : 0.0f;
-              dp += r * gc * s * uo;
+              if (part == 0) {
+                dpv += r * gc * sg * uo;
+                return gate <= p.glu_clamp_max ? r * pr[tm] * uo * sg * (1.0f + p.geglu_alpha * gc * (1.0f - sg))
+                                               : 0.0f;
+              }
+              return (up >= p.glu_clamp_min && up <= p.glu_clamp_max) ? r * pr[tm] * gc * sg : 0.0f;
             }
-          }
+          };
           if constexpr (OUT == OUT_BF16) {
+            float d0[16], d1[16], unused = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              v2u w;
-              w.x = bf16_rne(d0[4 * j]) | (bf16_rne(d0[4 * j + 1]) << 16);
-              w.y = bf16_rne(d0[4 * j + 2]) | (bf16_rne(d0[4 * j + 3]) << 16);
-              *reinterpret_cast<v2u*>(p.d + (xoff + 8 * j + 4 * hi) * 2) = w;
-              w.x = bf16_rne(d1[4 * j]) | (bf16_rne(d1[4 * j + 1]) << 16);
-              w.y = bf16_rne(d1[4 * j + 2]) | (bf16_rne(d1[4 * j + 3]) << 16);
-              *reinterpret_cast<v2u*>(p.d + (xoff + 32 + 8 * j + 4 * hi) * 2) = w;
+            for (int v = 0; v < 16; ++v) {
+              d0[v] = dglu(v, 0, dp);
+              d1[v] = dglu(v, 1, unused);
             }
+            store_bf16_tile(dbW + 128 * tn, xr, hi, d0);
+            store_bf16_tile(dbW + 128 * tn + 64, xr, hi, d1);
             if constexpr (AMAX2) {
 #pragma unroll
               for (int v = 0; v < 16; v += 2) {
@@ -797,18 +822,29 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           } else {
             // FP8 dC: each 32-column output block quantised by rows and
             // columns like a forward D ("Grouped GEMM + dGLU (SM100)",
-            // block-scaled Step 3)
+            // block-scaled Step 3).  One block at a time, the shared terms
+            // recomputed for the second, so that a single block of values is
+            // live during a quantisation.
+            const int oc = 2 * ncol;
+            const uint32_t ro = ml * static_cast<uint32_t>(p.n_out), so = ml * static_cast<uint32_t>(p.n_out >> 5);
+            float d[16], unused = 0.0f;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              d0[v] *= nc;
-              d1[v] *= nc;
+            for (int v = 0; v < 16; ++v) d[v] = dglu(v, 0, dp) * nc;
+            colw0[tn] |= quant_tile(sT, sS, dW0 + oc, dcW0 + oc, sfW0 + (oc >> 5), ro, so, hi, l32, d) << (8 * tm);
+            // opaque copies: the second block's terms are recomputed, not kept
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              asm volatile("" : "+v"(wi[j]));
+              asm volatile("" : "+v"(wg[j]));
             }
-            colw0[tn] |= quant_tile(p, sT, sS, m, 2 * ncol, hi, l32, d0) << (8 * tm);
-            colw1[tn] |= quant_tile(p, sT, sS, m, 2 * ncol + 32, hi, l32, d1) << (8 * tm);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) d[v] = dglu(v, 1, unused) * nc;
+            colw1[tn] |= quant_tile(sT, sS, dW0 + oc + 32, dcW0 + oc + 32, sfW0 + (oc >> 5) + 1, ro, so, hi, l32, d)
+                         << (8 * tm);
           }
         }
         dp = halves_sum(dp);
-        if (hi == 0) atomicAdd(p.dprob + m, dp);
+        if (hi == 0) atomicAdd(at(p.dprob + mb, 4 * ml), dp);
       }
       if constexpr (OUT == OUT_E4M3) {
         // column l32's scale bytes of the wave's 4 consecutive 32-row blocks
@@ -817,10 +853,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         for (int tn = 0; tn < TN; ++tn) {
           const int ncol = nbase + tn * 32;
           if (ncol >= p.n || hi != 0) continue;
-          *reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(2 * ncol + l32) * (vm >> 5) + mblk0) =
-              colw0[tn];
-          *reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(2 * ncol + 32 + l32) * (vm >> 5) + mblk0) =
-              colw1[tn];
+          uint8_t* const c0 = p.sfd_col + static_cast<int64_t>(2 * ncol) * (vm >> 5) + mblk0;
+          *at(reinterpret_cast<uint32_t*>(c0), l32 * sfc_pitch) = colw0[tn];
+          *at(reinterpret_cast<uint32_t*>(c0 + 32 * (vm >> 5)), l32 * sfc_pitch) = colw1[tn];
         }
       }
       if constexpr (AMAX2) {
@@ -842,20 +877,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       uint32_t colw[TN];
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) colw[tn] = 0;
+      const uint16_t* const cinW = p.c_in + mb * p.n + nbase;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
-        const int m = mbase + tm * 32 + l32;
+        const uint32_t ml = tm * 32 + l32;
+        const uint32_t cr = ml * static_cast<uint32_t>(p.n) * 2;      // C_in row, bytes
         float dp = 0.0f;
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           const int ncol = nbase + tn * 32;
           if (ncol >= p.n) continue;
           if constexpr (OUT == OUT_E4M3) asm volatile("" ::: "memory");
-          const int64_t coff = static_cast<int64_t>(m) * p.n + ncol;
           float cv[16];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const v2u w = *reinterpret_cast<const v2u*>(p.c_in + coff + 8 * j + 4 * hi);
+            const v2u w = *at(reinterpret_cast<const v2u*>(cinW + 32 * tn + 8 * j), cr + 8 * hi);
             cv[4 * j + 0] = __uint_as_float(w.x << 16);
             cv[4 * j + 1] = __uint_as_float(w.x & 0xFFFF0000u);
             cv[4 * j + 2] = __uint_as_float(w.y << 16);
@@ -877,7 +913,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             dp += r * (c * c);
           }
           if constexpr (OUT == OUT_BF16) {
-            store_bf16_tile(p.d, m, p.n_out, ncol, hi, d);
+            store_bf16_tile(p.d + (mb * p.n_out + ncol) * 2, ml * static_cast<uint32_t>(p.n_out) * 2, hi, d);
             if constexpr (MX) {
 #pragma unroll
               for (int v = 0; v < 16; v += 2) amax_l = max_abs2(amax_l, d[v], d[v + 1]);
@@ -885,11 +921,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           } else {
 #pragma unroll
             for (int v = 0; v < 16; ++v) d[v] *= nc;
-            colw[tn] |= quant_tile(p, sT, sS, m, ncol, hi, l32, d) << (8 * tm);
+            colw[tn] |= quant_tile(sT, sS, dW0 + ncol, dcW0 + ncol, sfW0 + (ncol >> 5), ml * static_cast<uint32_t>(p.n_out),
+                                   ml * static_cast<uint32_t>(p.n_out >> 5), hi, l32, d)
+                        << (8 * tm);
           }
         }
         dp = halves_sum(dp);
-        if (hi == 0) atomicAdd(p.dprob + m, dp);
+        if (hi == 0) atomicAdd(at(p.dprob + mb, 4 * ml), dp);
       }
       if constexpr (OUT == OUT_E4M3) {
         const int mblk0 = mbase >> 5;
@@ -897,7 +935,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         for (int tn = 0; tn < TN; ++tn) {
           const int ncol = nbase + tn * 32;
           if (ncol >= p.n || hi != 0) continue;
-          *reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(ncol + l32) * (vm >> 5) + mblk0) = colw[tn];
+          *at(reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(ncol) * (vm >> 5) + mblk0), l32 * sfc_pitch) =
+              colw[tn];
         }
       }
       if constexpr (MX && OUT == OUT_BF16) {
@@ -917,9 +956,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         if (gcol >= p.n) continue;
         const int ocol = PAIR ? gcol >> 1 : gcol;
         uint32_t colw = 0;                                             // E8M0 bytes of 4 column blocks
+        uint8_t* const cW = reinterpret_cast<uint8_t*>(p.c + mb * p.n + gcol);        // C store, block 0
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
-          const int m = mbase + tm * 32 + l32;
+          const uint32_t ml = tm * 32 + l32;
+          const uint32_t cr = ml * static_cast<uint32_t>(p.n) * 2;       // C row, bytes
           float d[16];
           if constexpr (ACT == ACT_SWIGLU) {
             // pairs [X_b | G_b] of 32 columns ("Grouped GEMM + SwiGLU (SM100)",
@@ -934,8 +975,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
                 cx[v] = alpha * ax[v];
                 cg[v] = alpha * ag[v];
               }
-              store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, gcol, hi, cx);
-              store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, gcol + 32, hi, cg);
+              store_bf16_tile(cW, cr, hi, cx);
+              store_bf16_tile(cW + 64, cr, hi, cg);
             }
             const float f = pr[tm] * nc * (alpha * alpha);
             const float nal = -alpha * kLog2e;
@@ -958,8 +999,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
               cu[v] = alpha * au[v];
             }
             if (p.c) {
-              store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, gcol, hi, cg);
-              store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, gcol + 32, hi, cu);
+              store_bf16_tile(cW, cr, hi, cg);
+              store_bf16_tile(cW + 64, cr, hi, cu);
             }
             const float f = pr[tm] * nc * p.glu_gamma;
             const float nga = -p.geglu_alpha * kLog2e;
@@ -974,7 +1015,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             float c[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) c[v] = alpha * acc[tm][to][v];
-            if (p.c) store_bf16_tile(reinterpret_cast<uint8_t*>(p.c), m, p.n, gcol, hi, c);
+            if (p.c) store_bf16_tile(cW, cr, hi, c);
             const float f = pr[tm] * nc;
             if constexpr (ACT == ACT_SRELU) {
               // D = prob * (s * min(tanh(relu(C)/s), 1))^2, or prob * relu(C)^2 for s = 0
@@ -993,18 +1034,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             }
           }
           if constexpr (OUT == OUT_BF16) {
-            store_bf16_tile(p.d, m, p.n_out, ocol, hi, d);
+            store_bf16_tile(p.d + (mb * p.n_out + ocol) * 2, ml * static_cast<uint32_t>(p.n_out) * 2, hi, d);
 #pragma unroll
             for (int v = 0; v < 16; v += 2) amax_l = max_abs2(amax_l, d[v], d[v + 1]);
           } else {
-            const uint32_t bc = quant_tile(p, sT, sS, m, ocol, hi, l32, d);
+            const uint32_t bc = quant_tile(sT, sS, dW0 + ocol, dcW0 + ocol, sfW0 + (ocol >> 5),
+                                           ml * static_cast<uint32_t>(p.n_out), ml * static_cast<uint32_t>(p.n_out >> 5),
+                                           hi, l32, d);
             colw |= bc << (8 * tm);
           }
         }
         if constexpr (OUT == OUT_E4M3) {
           // column l32's scale bytes of the wave's 4 consecutive 32-row blocks
           if (hi == 0)
-            *reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(ocol + l32) * (vm >> 5) + mblk0) = colw;
+            *at(reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(ocol) * (vm >> 5) + mblk0), l32 * sfc_pitch) =
+                colw;
         }
       }
       if constexpr (OUT == OUT_BF16) {
@@ -1204,6 +1248,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       if (!has_next) break;
       t = t_next;
       cur = nxt;
+      // the new tile's per-lane source offsets are rebuilt here (from a fresh
+      // opaque lane id) instead of being kept live through the epilogue
+      src = make_src(cur);
     }
   };
   if ((nks & 1) == 0 && nks >= 4) run(std::integral_constant<int, 0>{});

@@ -105,6 +105,7 @@ moegg_status check_impl(const moegg_problem* pp, const moegg_args* ap) {
   if (p.k % kstep != 0)
     return fail(MOEGG_ERROR_NOT_SUPPORTED, "k=%d: this build needs k %% %d == 0 for this operand type", p.k, kstep);
   if (p.k > (1 << 20)) return fail(MOEGG_ERROR_NOT_SUPPORTED, "k=%d too large", p.k);
+  if (p.n > (1 << 20)) return fail(MOEGG_ERROR_NOT_SUPPORTED, "n=%d above 2^20", p.n);
   const int64_t n_out = n_out_of(p);
   if (p.d_dtype == MOEGG_DT_E4M3 && n_out % 32 != 0)
     return fail(MOEGG_ERROR_INVALID_VALUE, "E4M3 D needs N_out %% 32 == 0 (row blocks), N_out=%lld", (long long)n_out);
