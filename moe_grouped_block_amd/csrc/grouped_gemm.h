@@ -750,6 +750,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       uint32_t colw0[TN], colw1[TN];          // E4M3: column scale bytes of 4 row blocks
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) colw0[tn] = colw1[tn] = 0;
+      // C_in of sub-tile (tm, tn): packed bf16 of the pair's two blocks
+      // (block b = ncol/32 of R pairs with C_in columns [64b, 64b + 64))
+      auto load_x = [&](int tm, int tn, v2u* wi, v2u* wg) __attribute__((always_inline)) {
+        const uint32_t xr = (tm * 32 + l32) * static_cast<uint32_t>(ld2) * 2;
+        const uint16_t* const xb = cinW + 64 * tn;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          wi[j] = *at(reinterpret_cast<const v2u*>(xb + 8 * j), xr + 8 * hi);
+          wg[j] = *at(reinterpret_cast<const v2u*>(xb + 32 + 8 * j), xr + 8 * hi);
+        }
+      };
+      auto has_cols = [&](int tn) __attribute__((always_inline)) { return nbase + tn * 32 < p.n; };
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
         const uint32_t ml = tm * 32 + l32;                 // row within the wave's 128
@@ -757,19 +769,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         float dp = 0.0f;
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
+          if (!has_cols(tn)) continue;
           const int ncol = nbase + tn * 32;
-          if (ncol >= p.n) continue;
-          // keep this tile's C_in loads here (hoisting every tile's loads
-          // ahead of the FP8 quantisation would spill)
-          if constexpr (OUT == OUT_E4M3) asm volatile("" ::: "memory");
-          // block b = ncol/32 of R pairs with C_in columns [64b, 64b + 64)
-          const uint16_t* const xb = cinW + 64 * tn;
+          // keep this sub-tile's C_in loads here (hoisting every sub-tile's
+          // loads ahead of the FP8 quantisation would spill)
           v2u wi[4], wg[4];          // packed bf16 of the first and second blocks of the pair
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            wi[j] = *at(reinterpret_cast<const v2u*>(xb + 8 * j), xr + 8 * hi);
-            wg[j] = *at(reinterpret_cast<const v2u*>(xb + 32 + 8 * j), xr + 8 * hi);
-          }
+          if constexpr (OUT == OUT_E4M3) asm volatile("" ::: "memory");
+          load_x(tm, tn, wi, wg);
           // element v of a packed block (columns 8(v/4) + 4 hi + v%4)
           auto bf = [](const v2u* w, int v) __attribute__((always_inline)) {
             const uint32_t u = (v & 2) ? w[v >> 2].y : w[v >> 2].x;
@@ -827,9 +833,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             // live during a quantisation.
             const int oc = 2 * ncol;
             const uint32_t ro = ml * static_cast<uint32_t>(p.n_out), so = ml * static_cast<uint32_t>(p.n_out >> 5);
+            // (the elements in groups of eight, pinned after each group, so
+            // that the scheduler does not keep sixteen sigmoid chains in
+            // flight at once and spill)
             float d[16], unused = 0.0f;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) d[v] = dglu(v, 0, dp) * nc;
+            for (int v = 0; v < 16; ++v) {
+              d[v] = dglu(v, 0, dp) * nc;
+              if ((v & 7) == 7) asm volatile("" : "+v"(d[v - 7]), "+v"(d[v - 6]), "+v"(d[v - 5]), "+v"(d[v - 4]), "+v"(d[v - 3]), "+v"(d[v - 2]), "+v"(d[v - 1]), "+v"(d[v]), "+v"(dp));
+            }
             colw0[tn] |= quant_tile(sT, sS, dW0 + oc, dcW0 + oc, sfW0 + (oc >> 5), ro, so, hi, l32, d) << (8 * tm);
             // opaque copies: the second block's terms are recomputed, not kept
 #pragma unroll
@@ -838,7 +850,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
               asm volatile("" : "+v"(wg[j]));
             }
 #pragma unroll
-            for (int v = 0; v < 16; ++v) d[v] = dglu(v, 1, unused) * nc;
+            for (int v = 0; v < 16; ++v) {
+              d[v] = dglu(v, 1, unused) * nc;
+              if ((v & 7) == 7) asm volatile("" : "+v"(d[v - 7]), "+v"(d[v - 6]), "+v"(d[v - 5]), "+v"(d[v - 4]), "+v"(d[v - 3]), "+v"(d[v - 2]), "+v"(d[v - 1]), "+v"(d[v]));
+            }
             colw1[tn] |= quant_tile(sT, sS, dW0 + oc + 32, dcW0 + oc + 32, sfW0 + (oc >> 5) + 1, ro, so, hi, l32, d)
                          << (8 * tm);
           }
