@@ -116,7 +116,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fc1_swiglu_l64")
-    ap.add_argument("--also", default="fc1_swiglu_l8,fc1_swiglu_l64:discrete,dswiglu_mxfp8_l64,dsrelu_mxfp8_l32,"
+    ap.add_argument("--also", default="fc1_swiglu_l8,quant_gating_l4,fc2_gating_l64_zipf,srelu_tanh_fp4_l32,"
+                    "dswiglu_bf16_l64,fc1_swiglu_l64:discrete,dswiglu_mxfp8_l64,dsrelu_mxfp8_l32,"
                     "fc1_geglu_e5m2_l8,dgeglu_mxfp8_l64",
                     help="comma list of extra workloads to time; a ':discrete' suffix passes the expert "
                          "weights as per-expert allocations (b_ptrs / sfb_ptrs)")
@@ -218,8 +219,12 @@ def main():
     for name in [x for x in args.also.split(",") if x]:
         r = measure(name, max(args.steps, 20), args.warmup, args.cold)
         c = r["case"]
+        t_m = c.flops / (PEAK_TFLOPS[c.problem["ab_dtype"]] * 1e12)
+        t_h = algorithmic_bytes(c) / (HBM_GBS * 1e9)
         also[name] = {"ms_per_step": round(r["ms"], 5), "tflops_routed": round(r["tflops"], 2),
                       "frac_mfma_peak": round(r["tflops"] / PEAK_TFLOPS[c.problem["ab_dtype"]], 4),
+                      "bound": "mfma" if t_m >= t_h else "hbm",
+                      "frac_roofline": round(max(t_m, t_h) / (r["ms"] * 1e-3), 4),
                       "valid_m": c.problem["valid_m"], "routed_rows": c.routed_rows,
                       "experts": c.problem["num_groups"]}
         if "cold_ms" in r:

@@ -893,20 +893,32 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) colw[tn] = 0;
       const uint16_t* const cinW = p.c_in + mb * p.n + nbase;
+      // C_in of one row of sub-tiles (TN blocks of 32 rows), loaded one row
+      // ahead so that its latency overlaps the previous row's work
+      auto load_row = [&](int tm, v2u (*w)[4]) __attribute__((always_inline)) {
+        const uint32_t cr = (tm * 32 + l32) * static_cast<uint32_t>(p.n) * 2;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          if (nbase + tn * 32 >= p.n) continue;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w[tn][j] = *at(reinterpret_cast<const v2u*>(cinW + 32 * tn + 8 * j), cr + 8 * hi);
+        }
+      };
+      v2u cw[TN][4], nw[TN][4];
+      load_row(0, cw);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
         const uint32_t ml = tm * 32 + l32;
-        const uint32_t cr = ml * static_cast<uint32_t>(p.n) * 2;      // C_in row, bytes
         float dp = 0.0f;
+        if (tm + 1 < TM) load_row(tm + 1, nw);
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           const int ncol = nbase + tn * 32;
           if (ncol >= p.n) continue;
-          if constexpr (OUT == OUT_E4M3) asm volatile("" ::: "memory");
           float cv[16];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const v2u w = *at(reinterpret_cast<const v2u*>(cinW + 32 * tn + 8 * j), cr + 8 * hi);
+            const v2u w = cw[tn][j];
             cv[4 * j + 0] = __uint_as_float(w.x << 16);
             cv[4 * j + 1] = __uint_as_float(w.x & 0xFFFF0000u);
             cv[4 * j + 2] = __uint_as_float(w.y << 16);
@@ -943,6 +955,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         }
         dp = halves_sum(dp);
         if (hi == 0) atomicAdd(at(p.dprob + mb, 4 * ml), dp);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cw[tn][j] = nw[tn][j];
       }
       if constexpr (OUT == OUT_E4M3) {
         const int mblk0 = mbase >> 5;

@@ -149,6 +149,8 @@ CASES = [
     ("gating_bf16", {}, dict(beta=FAKE), INVALID),                     # dSwiGLU-only input
     ("gating_bf16", dict(ab_dtype="bf16"), {}, INVALID),               # sfa/sfb with BF16 operands
     ("gating_bf16", dict(valid_m=2 ** 31), {}, NOT_SUPPORTED),
+    ("gating_bf16", dict(n=(1 << 20) + 32), {}, NOT_SUPPORTED),            # epilogue offsets are 32-bit
+    ("gating_bf16", dict(n=1 << 20), {}, OK),
     # discrete weights (b_ptrs / sfb_ptrs instead of b / sfb)
     ("gating_bf16", {}, dict(b=None, sfb=None, b_ptrs=FAKE + 0x20000, sfb_ptrs=FAKE + 0x21000), OK),
     ("dswiglu", {}, dict(b=None, b_ptrs=FAKE + 0x20000), OK),
