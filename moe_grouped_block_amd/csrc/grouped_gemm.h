@@ -72,10 +72,12 @@ constexpr float kRcp448 = 1.0f / 448.0f;   // rcp_max of E4M3, rounded to fp32
 // device codecs
 // ---------------------------------------------------------------------------
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two fp32 -> two bf16 (a in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, bf2));
 }
 
 // E8M0 byte of the smallest power of two >= sf (sf >= 0), clamped to [0, 254].
@@ -196,8 +198,8 @@ __device__ __forceinline__ void store_bf16_tile(uint8_t* base, uint32_t roff, in
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     v2u w;
-    w.x = bf16_rne(v[4 * j + 0]) | (bf16_rne(v[4 * j + 1]) << 16);
-    w.y = bf16_rne(v[4 * j + 2]) | (bf16_rne(v[4 * j + 3]) << 16);
+    w.x = bf16x2(v[4 * j + 0], v[4 * j + 1]);
+    w.y = bf16x2(v[4 * j + 2], v[4 * j + 3]);
     *at(reinterpret_cast<v2u*>(base + 16 * j), roff + 8 * hi) = w;
   }
 }

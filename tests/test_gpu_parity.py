@@ -307,6 +307,35 @@ def test_e4m3_rounding_through_epilogue_bit_exact():
     assert np.array_equal(got["d_col"], ref["d_col_code"])
 
 
+def test_bf16_rounding_through_epilogue_bit_exact():
+    """BF16 D = prob[m] * 2^-e(n) exactly (one nonzero product per dot), with
+    prob on BF16 rounding ties (both parities) and one fp32 ulp either side
+    of them: every BF16 code and the amax must match the oracle bit for bit
+    (round to nearest, ties to even)."""
+    rows, n, k = 1024, 256, 128
+    case = synth.make_case("quant_gating_l4", seed=6, name="bf16_rounding", L=1, K=k, N=n, d="bf16",
+                           force_counts=[rows])
+    a = case.arrays
+    a["a"][:] = 0
+    a["a"][:, 0] = 0x38                                       # A[m, 0] = 1, rest 0
+    a["sfa"][:] = 127
+    a["b"][:] = 0
+    e = (np.arange(n) % 32) // 2                              # 0..15 per 32-column block
+    a["b"][0, :, 0] = 0x38
+    a["sfb"][0, :, 0] = (127 - e).astype(np.uint8)            # B[n, 0] = 2^-e(n)
+    a["sfb"][0, :, 1:] = 127
+    a["alpha"][:] = 1.0
+    rng = np.random.default_rng(66)
+    hi16 = rng.integers(0x3F00, 0x3F80, rows).astype(np.uint32)   # values in [0.5, 1)
+    lo16 = np.array([0x8000, 0x7FFF, 0x8001, 0x0000], dtype=np.uint32)[np.arange(rows) % 4]
+    lo16[rows // 2:] = rng.integers(0, 1 << 16, rows - rows // 2).astype(np.uint32)
+    a["prob"][:] = ((hi16 << 16) | lo16).view(np.float32)
+    got = run_gpu(case)
+    ref = oracle.grouped_gemm(case.problem, a)
+    assert np.array_equal(got["d"].view(np.uint16), ref["d_bits"])
+    assert np.array_equal(got["amax"].view(np.uint32), np.float32(ref["amax"]).view(np.uint32))
+
+
 def test_deterministic_repeat():
     case = synth.make_case("fc1_swiglu_l8", seed=6, name="determinism", L=3, K=256, N=256,
                            routing=("topk", 300, 2))
