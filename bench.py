@@ -40,11 +40,17 @@ KERNEL_SOURCES = ["moe_grouped_block_amd/csrc/grouped_gemm.h", "moe_grouped_bloc
 TRAFFIC_FILE = "profiles/grouped_gemm_fc1_swiglu_l64_traffic.md"
 
 
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code (comments and whitespace removed), so
+    that a counter summary stays valid across comment-only edits."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            code = _COMMENT.sub(" ", fh.read())
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

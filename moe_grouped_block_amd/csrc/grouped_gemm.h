@@ -26,10 +26,12 @@
 //    operand and the token tile the second, so an accumulator lane holds one
 //    token row and 16 output columns (4 runs of 4 contiguous columns): row
 //    reductions are lane-local.
-//  * K advances in steps of 128 bytes per row (128 E4M3, 256 E2M1 or 64 BF16
-//    elements).  Two LDS stages (A, B and their scale words) are filled by
-//    direct global -> LDS loads one step ahead; the first stage of the next
-//    tile is loaded while the current tile's epilogue runs.
+//  * K advances in steps of 128 bytes per row (128 E4M3 or E5M2, 256 E2M1 or
+//    64 BF16 elements).  Two LDS stages (A, B and their scale words) are
+//    filled by direct global -> LDS loads issued up to two steps ahead,
+//    spread over the clusters of the ping-pong schedule (see the tile loop).
+//    With an even step count the next tile's first stage is loaded during
+//    the tile's last two steps, otherwise while its epilogue runs.
 //  * the epilogue works on the fp32 accumulators in registers; column
 //    blocks of the FP8 output are reduced through a per-wave LDS transpose.
 #pragma once
