@@ -184,10 +184,14 @@ __device__ __forceinline__ float max_abs2(float c, float a, float b) {
 }
 
 // Epilogue addressing: every output address is a wave-uniform base (the
-// wave's first row and the block's first column, scalar registers) plus a
-// 32-bit per-lane byte offset, so that an address costs one vector register
-// and the loads and stores take their scalar-base form.  Offsets stay below
-// 2^32: 128 rows of at most 2^21 two-byte elements.
+// wave's first row and the block's first column) plus a 32-bit per-lane byte
+// offset.  Offsets stay below 2^32: 128 rows of at most 2^21 two-byte
+// elements.
+// The integer round trip hides the address space, so these accesses compile
+// to flat_* instructions with 64-bit lane addresses.  Byte-pointer arithmetic
+// would keep them global_* with a scalar base, but measured 2-7 % slower on
+// every workload (more scalar registers live through the epilogue, more
+// spills).
 template <typename T>
 __device__ __forceinline__ T* at(T* base, uint32_t byte_off) {
   return reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(base) + static_cast<uint64_t>(byte_off));
