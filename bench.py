@@ -120,7 +120,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed launches first; the GPU's power management throttles hard a few "
+                         "launches into sustained load and settles after about 40 launches (25 ms)")
     ap.add_argument("--workload", default="fc1_swiglu_l64")
     ap.add_argument("--also", default="fc1_swiglu_l8,quant_gating_l4,fc2_gating_l64_zipf,srelu_tanh_fp4_l32,"
                     "dswiglu_bf16_l64,fc1_swiglu_l64:discrete,dswiglu_mxfp8_l64,dsrelu_mxfp8_l32,"
