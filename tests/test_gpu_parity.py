@@ -176,6 +176,13 @@ EDGE = {
     "edge_n64_swiglu": ("fc1_swiglu_l8", dict(L=2, K=128, N=64, routing=("topk", 100, 1))),
     "edge_k_one_step_fp4": ("srelu_tanh_fp4_l32", dict(L=2, K=256, N=64, routing=("multinomial", 70))),
     "edge_k_one_step_bf16": ("dswiglu_bf16_l64", dict(L=2, K=64, N=32, routing=("topk", 50, 1))),
+    # the maximum expert count: 1024 groups, most of them empty, the first and
+    # the last one populated (the whole tile prefix and its search)
+    "edge_l1024_sparse": ("quant_gating_l4", dict(L=1024, K=128, N=64,
+                                                  force_counts=[3] + [0] * 200 + [130] + [0] * 300 + [1]
+                                                  + [0] * 400 + [257] + [0] * 119 + [2])),
+    # groups aligned to 256 rows (the pages' default padding)
+    "edge_m_aligned_256": ("fc1_swiglu_l8", dict(L=3, K=256, N=128, m_aligned=256, routing=("topk", 300, 2))),
 }
 
 
