@@ -130,10 +130,13 @@ typedef enum moegg_act {
 typedef struct moegg_problem {
   int32_t num_groups;   /* L, 1..1024 ("Shapes and Divisibility": expert count <= 1024) */
   int32_t m_aligned;    /* group row alignment; multiple of 128 here                     */
-  int64_t valid_m;      /* rows of A == padded_offsets[L-1]; multiple of m_aligned       */
-  int32_t n;            /* GEMM N (rows of each expert's B)                               */
-  int32_t k;            /* reduction length K                                             */
-  int32_t ab_dtype;     /* moegg_dtype of A and B: E4M3 | E2M1X2 | BF16                   */
+  int64_t valid_m;      /* rows of A == padded_offsets[L-1]; multiple of m_aligned,
+                           < 2^31 here                                                    */
+  int32_t n;            /* GEMM N (rows of each expert's B); multiple of 32, <= 2^20 here
+                           (64 for SwiGLU / GeGLU)                                        */
+  int32_t k;            /* reduction length K; multiple of 128 bytes per row here (128
+                           E4M3 / E5M2, 256 E2M1, 64 BF16 elements), <= 2^20             */
+  int32_t ab_dtype;     /* moegg_dtype of A and B: E4M3 | E5M2 | E2M1X2 | BF16            */
   int32_t c_dtype;      /* NONE (C not written) | BF16                                    */
   int32_t d_dtype;      /* BF16 (needs amax) | E4M3 (needs SFD_row, SFD_col, norm_const)  */
   int32_t act;          /* moegg_act                                                      */

@@ -901,7 +901,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) colw[tn] = 0;
       const uint16_t* const cinW = p.c_in + mb * p.n + nbase;
-      // C_in of one row of sub-tiles (TN blocks of 32 rows), loaded one row
+      // C_in of one row of sub-tiles (32 rows, TN blocks of 32 columns), loaded one row
       // ahead so that its latency overlaps the previous row's work
       auto load_row = [&](int tm, v2u (*w)[4]) __attribute__((always_inline)) {
         const uint32_t cr = (tm * 32 + l32) * static_cast<uint32_t>(p.n) * 2;
