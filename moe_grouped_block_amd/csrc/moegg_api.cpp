@@ -5,6 +5,7 @@
 // allocation or compilation": "Grouped GEMM + dGLU (SM100)", §Backend dispatch).
 #include "moegg.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -25,15 +26,19 @@ moegg_status fail(moegg_status st, const char* fmt, ...) {
   return st;
 }
 
-// Compute units of the current device (cached per device id), 0 on error.
+// Compute units of the current device (cached per device id; calls from
+// several host threads may fill the cache concurrently), 0 on error.
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (dev < 64) cache[dev] = cus;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
@@ -180,7 +185,7 @@ moegg_status moegg_run(const moegg_problem* problem, const moegg_args* args, voi
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
 
   if (a.amax) {
-    // (L) per group, or (L, 2) for dSwiGLU: [d_input blocks, d_gate blocks]
+    // (L) per group, or (L, 2) for dSwiGLU / dGeGLU: [first blocks, second blocks] of the pairs
     const int count = p.act == MOEGG_ACT_DSWIGLU || p.act == MOEGG_ACT_DGEGLU ? 2 * p.num_groups : p.num_groups;
     hipError_t e = moegg::launch_fill_zero(a.amax, count, stream);
     if (e != hipSuccess) return fail(MOEGG_ERROR_LAUNCH, "amax fill: %s", hipGetErrorString(e));
