@@ -197,16 +197,21 @@ __device__ __forceinline__ T* at(T* base, uint32_t byte_off) {
   return reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(base) + static_cast<uint64_t>(byte_off));
 }
 
-// Store 16 values of one row (one 32-column tile) as bf16: 4 runs of 4.
-// `base` is the tile's first column in the wave's first row; `roff` the
-// lane's row offset in bytes.
+// Store 16 values of one row (one 32-column tile) as bf16.  This lane holds
+// columns 8j + 4*hi + [0, 4) (8 bytes each); v_permlane32_swap(x, y)
+// exchanges x of lanes 32-63 with y of lanes 0-31, so swapping the runs of
+// j = 2i and 2i + 1 leaves lane hi = 0 with columns 16i + [0, 8) and lane
+// hi = 1 with 16i + [8, 16): two 16-byte stores per lane, each instruction
+// writing 32 contiguous bytes of every row.  `base` is the tile's first
+// column in the wave's first row; `roff` the lane's row offset in bytes.
 __device__ __forceinline__ void store_bf16_tile(uint8_t* base, uint32_t roff, int hi, const float* v) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    v2u w;
-    w.x = bf16x2(v[4 * j + 0], v[4 * j + 1]);
-    w.y = bf16x2(v[4 * j + 2], v[4 * j + 3]);
-    *at(reinterpret_cast<v2u*>(base + 16 * j), roff + 8 * hi) = w;
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t a0 = bf16x2(v[8 * i + 0], v[8 * i + 1]), a1 = bf16x2(v[8 * i + 2], v[8 * i + 3]);
+    const uint32_t b0 = bf16x2(v[8 * i + 4], v[8 * i + 5]), b1 = bf16x2(v[8 * i + 6], v[8 * i + 7]);
+    const v2u s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+    const v2u s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+    *at(reinterpret_cast<v4u*>(base + 32 * i), roff + 16 * hi) = v4u{s0.x, s1.x, s0.y, s1.y};
   }
 }
 
