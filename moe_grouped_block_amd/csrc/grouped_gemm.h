@@ -215,6 +215,21 @@ __device__ __forceinline__ void store_bf16_tile(uint8_t* base, uint32_t roff, in
   }
 }
 
+// Load one row's 32 bf16 of a 32-column tile into this lane's layout, runs
+// of 4 at columns 8j + 4*hi (w[j], 8 bytes each): the inverse of
+// store_bf16_tile (two 16-byte loads per lane, 32 contiguous bytes of every
+// row per instruction, then the runs exchanged with lane ^ 32).
+__device__ __forceinline__ void load_bf16_tile(const uint16_t* base, uint32_t roff, int hi, v2u* w) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const v4u q = *at(reinterpret_cast<const v4u*>(base + 16 * i), roff + 16 * hi);
+    const v2u s0 = __builtin_amdgcn_permlane32_swap(q.x, q.z, false, false);
+    const v2u s1 = __builtin_amdgcn_permlane32_swap(q.y, q.w, false, false);
+    w[2 * i] = v2u{s0.x, s1.x};
+    w[2 * i + 1] = v2u{s0.y, s1.y};
+  }
+}
+
 // Store one row's 32 E4M3 codes of a 32-column tile.  This lane holds the
 // codes of columns 8j + 4*hi + [0, 4) (w[j]).  v_permlane32_swap(x, y)
 // exchanges x of lanes 32-63 with y of lanes 0-31: with x = w[j], y = w[j+2]
@@ -768,11 +783,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       auto load_x = [&](int tm, int tn, v2u* wi, v2u* wg) __attribute__((always_inline)) {
         const uint32_t xr = (tm * 32 + l32) * static_cast<uint32_t>(ld2) * 2;
         const uint16_t* const xb = cinW + 64 * tn;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          wi[j] = *at(reinterpret_cast<const v2u*>(xb + 8 * j), xr + 8 * hi);
-          wg[j] = *at(reinterpret_cast<const v2u*>(xb + 32 + 8 * j), xr + 8 * hi);
-        }
+        load_bf16_tile(xb, xr, hi, wi);
+        load_bf16_tile(xb + 32, xr, hi, wg);
       };
       auto has_cols = [&](int tn) __attribute__((always_inline)) { return nbase + tn * 32 < p.n; };
 #pragma unroll
@@ -913,8 +925,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           if (nbase + tn * 32 >= p.n) continue;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) w[tn][j] = *at(reinterpret_cast<const v2u*>(cinW + 32 * tn + 8 * j), cr + 8 * hi);
+          load_bf16_tile(cinW + 32 * tn, cr, hi, w[tn]);
         }
       };
       v2u cw[TN][4], nw[TN][4];
