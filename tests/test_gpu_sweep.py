@@ -1,0 +1,61 @@
+"""Seeded sweep over the configuration space, every output against the
+oracle: operand family x activation x output format x K-step count x ragged
+N x expert count x group alignment.  The cases are drawn once from a fixed
+seed (the same list on every run), each small enough for the oracle."""
+import numpy as np
+import pytest
+
+import synth
+from test_gpu_parity import check_case, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+BASE = {"none": "quant_gating_l4", "swiglu": "fc1_swiglu_l8", "srelu": "srelu_tanh_fp4_l32",
+        "geglu": "fc1_geglu_e5m2_l8", "dswiglu": "dswiglu_mxfp8_l64", "dsrelu": "dsrelu_mxfp8_l32",
+        "dgeglu": "dgeglu_mxfp8_l64"}
+KSTEP = {"e4m3": 128, "e5m2": 128, "e2m1x2": 256, "bf16": 64}
+
+
+def draw_cases(n=24, seed=20261202):
+    rng = np.random.default_rng(seed)
+    cases = []
+    acts = list(BASE)
+    abs_ = list(KSTEP)
+    for i in range(n):
+        act = acts[i % len(acts)]
+        ab = abs_[int(rng.integers(len(abs_)))]
+        bwd = act.startswith("d")
+        d = "bf16" if (ab == "bf16" and bwd) else ("e4m3" if rng.random() < 0.5 else "bf16")
+        c = "bf16" if (not bwd and rng.random() < 0.3) else None
+        pair = act in ("swiglu", "geglu")
+        n_cols = int(rng.integers(1, 12)) * (64 if pair else 32)
+        if d == "e4m3" and act in ("swiglu", "geglu"):
+            n_cols = max(n_cols, 64)
+        k = int(rng.integers(1, 8)) * KSTEP[ab]
+        L = int(rng.integers(1, 10))
+        rows = int(rng.integers(1, 500))
+        m_al = 256 if rng.random() < 0.25 else 128
+        if L >= 2 and rng.random() < 0.5:
+            route = dict(routing=("topk", rows, 2), prob=("softmax_picks",))
+        else:
+            route = dict(routing=("multinomial", rows), prob=("uniform",))
+        over = dict(ab=ab, d=d, c=c, L=L, K=k, N=n_cols, m_aligned=m_al, alpha=("uniform", 0.5, 2.0), **route)
+        if act == "dswiglu":
+            over["beta"] = ("uniform", 0.5, 2.0)
+        if ab == "e2m1x2":
+            over.update(a_std=1.0, b_std=1.0, clip=6.0)
+        if act in ("geglu", "dgeglu"):
+            over.update(glu_clamp_min=-2.5, glu_clamp_max=2.0)
+        cases.append((f"sweep{i:02d}_{act}_{ab}_{d}", BASE[act], over))
+    return cases
+
+
+CASES = draw_cases()
+
+
+@pytest.mark.parametrize("name,base,over", CASES, ids=[c[0] for c in CASES])
+def test_sweep_parity(name, base, over):
+    case = synth.make_case(base, seed=5000 + CASES.index((name, base, over)), name=name, **over)
+    got = run_gpu(case)
+    stats = check_case(case, got)
+    print(f"[gpu-case] {name} stats {stats}", flush=True)
