@@ -673,7 +673,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   // `hook(i)` runs right after the cluster's MFMA number i (0 .. NMMA-1)
   constexpr int NWIN = F8 ? 2 : 4;
   constexpr int NMMA = NWIN * 2 * TN;
-  auto mma = [&](int tm0, const Pieces* a, const Ops0& o0, auto&& hook) __attribute__((always_inline)) {
+  // zc: std::integral_constant<bool, Z>; with Z the first window starts from
+  // a zero accumulator (the MFMA's inline constant 0), as a tile's first step
+  // does instead of clearing the accumulators
+  auto mma = [&](int tm0, const Pieces* a, const Ops0& o0, auto&& hook, auto zc) __attribute__((always_inline)) {
+    constexpr bool ZERO = decltype(zc)::value;
     static_for<0, NWIN>([&](auto kc) {
       constexpr int kk = decltype(kc)::value;
 #pragma unroll
@@ -682,21 +686,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         for (int tn = 0; tn < TN; ++tn) {
           const int mi = (kk * 2 + t) * TN + tn;
           v16f& c = acc[tm0 + t][tn];
+          const v16f cin = ZERO && kk == 0 ? v16f{} : c;
           if constexpr (F8) {
             const v4u a0 = a[t][2 * kk], a1 = a[t][2 * kk + 1], b0 = o0.b[tn][2 * kk], b1 = o0.b[tn][2 * kk + 1];
             const v8i fa{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
             const v8i fb{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, c, FMT8, FMT8, kk * 2, (int)o0.sb[tn][0],
+            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, cin, FMT8, FMT8, kk * 2, (int)o0.sb[tn][0],
                                                                 kk * 2, (int)o0.sa[tm0 + t][0]);
           } else if constexpr (AB == AB_E2M1) {
             const v4u a0 = a[t][kk], b0 = o0.b[tn][kk];
             const v8i fa{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
             const v8i fb{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
-            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, c, 4, 4, (kk & 1) * 2, (int)o0.sb[tn][kk >> 1],
+            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, cin, 4, 4, (kk & 1) * 2, (int)o0.sb[tn][kk >> 1],
                                                                 (kk & 1) * 2, (int)o0.sa[tm0 + t][kk >> 1]);
           } else {
             c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, o0.b[tn][kk]),
-                                                        __builtin_bit_cast(v8bf, a[t][kk]), c, 0, 0, 0);
+                                                        __builtin_bit_cast(v8bf, a[t][kk]), cin, 0, 0, 0);
           }
           hook(mi);
         }
@@ -1147,11 +1152,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   // pin the accumulators after each MFMA cluster (the MFMAs are pure
   // operations that the compiler would otherwise sink past the barriers,
   // out of their cluster and into the code after the K loop)
-  auto pin_acc = [&]() __attribute__((always_inline)) {
+  // (rows [0, tm_end): a tile's first step pins after its first cluster only
+  // the rows that cluster wrote, so the previous tile's values of the other
+  // rows are not kept alive through the epilogue)
+  auto pin_acc = [&](int tm_end = TM) __attribute__((always_inline)) {
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) asm volatile("" : "+v"(acc[tm][tn]));
+      for (int tn = 0; tn < TN; ++tn)
+        if (tm < tm_end) asm volatile("" : "+v"(acc[tm][tn]));
   };
   using NoWait = std::integral_constant<int, -1>;
   using WaitAll = std::integral_constant<int, 0>;
@@ -1173,7 +1182,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   // after the LDS reads, c0 / c1 are hooks run between the MFMAs of the C
   // clusters; the M clusters then wait until at most W0 / W1 of this wave's
   // loads are outstanding (no wait for -1)
-  auto step = [&](const Stage& st, auto&& m0, auto&& c0, auto&& m1, auto&& c1, auto w0c, auto w1c)
+  auto step_impl = [&](auto zc, const Stage& st, auto&& m0, auto&& c0, auto&& m1, auto&& c1, auto w0c, auto w1c)
       __attribute__((always_inline)) {
     constexpr int W0 = decltype(w0c)::value, W1 = decltype(w1c)::value;
     Ops0 o0 = read0(st);
@@ -1181,25 +1190,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
     fin0(o0);
     if constexpr (W0 >= 0) wait_vmcnt<W0>();
     sync();
-    mma(0, o0.a, o0, c0);
-    pin_acc();
+    mma(0, o0.a, o0, c0, zc);
+    pin_acc(decltype(zc)::value ? 2 : TM);
     sync();
     Ops1 o1 = read1(st);
     m1();
     fin1(o1);
     if constexpr (W1 >= 0) wait_vmcnt<W1>();
     sync();
-    mma(2, o1.a, o0, c1);
+    mma(2, o1.a, o0, c1, zc);
     pin_acc();
     sync();
   };
-  auto zero_acc = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
+  // a K-step accumulating onto the tile's sums, and a tile's first K-step,
+  // which starts them from zero
+  auto step = [&](auto&&... args) __attribute__((always_inline)) {
+    step_impl(std::false_type{}, static_cast<decltype(args)&&>(args)...);
+  };
+  auto step_z = [&](auto&&... args) __attribute__((always_inline)) {
+    step_impl(std::true_type{}, static_cast<decltype(args)&&>(args)...);
   };
 
   // Stage s+2 is loaded during step s: its early first part in M1(s), its
@@ -1215,7 +1224,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   };
   // steps 0 and 1 of a tile (stage 0 resident): stage 1 whole in M0(0)
   auto first_pair = [&]() __attribute__((always_inline)) {
-    step(st0, [&]() __attribute__((always_inline)) { issue(src, 1, st1); }, no_hook,
+    step_z(st0, [&]() __attribute__((always_inline)) { issue(src, 1, st1); }, no_hook,
          [&]() __attribute__((always_inline)) { issue_ea(src, 2, st0); }, ehook(2, st0), NoWait{}, WaitM1{});
     step(st1, no_loads, lhook(2, st0), [&]() __attribute__((always_inline)) { issue_ea(src, 3, st1); }, ehook(3, st1),
          WaitM0{}, WaitM1{});
@@ -1236,7 +1245,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   auto run = [&](auto mode_c) __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode_c)::value;
     while (true) {
-      zero_acc();
       const int t_next = t + nwg;
       const bool has_next = t_next < total;
       const Tile nxt = tile_of(has_next ? t_next : t);
@@ -1277,19 +1285,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
                  [&]() __attribute__((always_inline)) { issue_ea(src, nks - 1, st0); }, ehook(nks - 1, st0), WaitM0{},
                  WaitM1{});
           } else {
-            step(st0, [&]() __attribute__((always_inline)) { issue(src, 1, st1); }, no_hook,
-                 [&]() __attribute__((always_inline)) { issue_ea(src, 2, st0); }, ehook(2, st0), NoWait{}, WaitM1{});
+            step_z(st0, [&]() __attribute__((always_inline)) { issue(src, 1, st1); }, no_hook,
+                   [&]() __attribute__((always_inline)) { issue_ea(src, 2, st0); }, ehook(2, st0), NoWait{}, WaitM1{});
           }
           step(st1, no_loads, lhook(nks - 1, st0), no_loads, no_hook, WaitM0{},
                std::integral_constant<int, N_LATE>{});
           step(st0, no_loads, no_hook, no_loads, no_hook, WaitAll{}, NoWait{});
         } else {
           if (nks == 2) {
-            step(st0, [&]() __attribute__((always_inline)) { issue(src, 1, st1); }, no_hook, no_loads, no_hook,
-                 NoWait{}, WaitAll{});
+            step_z(st0, [&]() __attribute__((always_inline)) { issue(src, 1, st1); }, no_hook, no_loads, no_hook,
+                   NoWait{}, WaitAll{});
             step(st1, no_loads, no_hook, no_loads, no_hook, NoWait{}, NoWait{});
           } else {
-            step(st0, no_loads, no_hook, no_loads, no_hook, NoWait{}, NoWait{});
+            step_z(st0, no_loads, no_hook, no_loads, no_hook, NoWait{}, NoWait{});
           }
         }
         const EpiIn ein = epi_in(cur);
