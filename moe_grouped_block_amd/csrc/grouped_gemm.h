@@ -863,14 +863,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             // live during a quantisation.
             const int oc = 2 * ncol;
             const uint32_t ro = ml * static_cast<uint32_t>(p.n_out), so = ml * static_cast<uint32_t>(p.n_out >> 5);
-            // (the elements in groups of eight, pinned after each group, so
-            // that the scheduler does not keep sixteen sigmoid chains in
-            // flight at once and spill)
+            // (dGeGLU: the elements in groups of eight, pinned after each
+            // group, so that the scheduler does not keep sixteen sigmoid
+            // chains in flight at once and spill; dSwiGLU does not need it)
             float d[16], unused = 0.0f;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
               d[v] = dglu(v, 0, dp) * nc;
-              if ((v & 7) == 7) asm volatile("" : "+v"(d[v - 7]), "+v"(d[v - 6]), "+v"(d[v - 5]), "+v"(d[v - 4]), "+v"(d[v - 3]), "+v"(d[v - 2]), "+v"(d[v - 1]), "+v"(d[v]), "+v"(dp));
+              if (ACT == ACT_DGEGLU && (v & 7) == 7) asm volatile("" : "+v"(d[v - 7]), "+v"(d[v - 6]), "+v"(d[v - 5]), "+v"(d[v - 4]), "+v"(d[v - 3]), "+v"(d[v - 2]), "+v"(d[v - 1]), "+v"(d[v]), "+v"(dp));
             }
             colw0[tn] |= quant_tile(sT, sS, dW0 + oc, dcW0 + oc, sfW0 + (oc >> 5), ro, so, hi, l32, d) << (8 * tm);
             // opaque copies: the second block's terms are recomputed, not kept
@@ -882,7 +882,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
               d[v] = dglu(v, 1, unused) * nc;
-              if ((v & 7) == 7) asm volatile("" : "+v"(d[v - 7]), "+v"(d[v - 6]), "+v"(d[v - 5]), "+v"(d[v - 4]), "+v"(d[v - 3]), "+v"(d[v - 2]), "+v"(d[v - 1]), "+v"(d[v]));
+              if (ACT == ACT_DGEGLU && (v & 7) == 7) asm volatile("" : "+v"(d[v - 7]), "+v"(d[v - 6]), "+v"(d[v - 5]), "+v"(d[v - 4]), "+v"(d[v - 3]), "+v"(d[v - 2]), "+v"(d[v - 1]), "+v"(d[v]));
             }
             colw1[tn] |= quant_tile(sT, sS, dW0 + oc + 32, dcW0 + oc + 32, sfW0 + (oc >> 5) + 1, ro, so, hi, l32, d)
                          << (8 * tm);
