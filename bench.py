@@ -229,7 +229,10 @@ def main():
         c = r["case"]
         t_m = c.flops / (PEAK_TFLOPS[c.problem["ab_dtype"]] * 1e12)
         t_h = algorithmic_bytes(c) / (HBM_GBS * 1e9)
+        padded_flops = 2.0 * c.problem["valid_m"] * c.problem["n"] * c.problem["k"]
         also[name] = {"ms_per_step": round(r["ms"], 5), "tflops_routed": round(r["tflops"], 2),
+                      "tflops_padded": round(padded_flops / (r["ms"] * 1e-3) / 1e12, 2),
+                      "hbm_gbs_algorithmic": round(algorithmic_bytes(c) / (r["ms"] * 1e-3) / 1e9, 1),
                       "frac_mfma_peak": round(r["tflops"] / PEAK_TFLOPS[c.problem["ab_dtype"]], 4),
                       "bound": "mfma" if t_m >= t_h else "hbm",
                       "frac_roofline": round(max(t_m, t_h) / (r["ms"] * 1e-3), 4),
@@ -262,6 +265,8 @@ def main():
                    "d_dtype": p["d_dtype"], "parallelism": "single-gpu"},
         "roofline": roof,
         "pct_mxfp8_peak": round(100.0 * value / PEAK_TFLOPS["e4m3"], 2),
+        "tflops_padded": round(2.0 * p["valid_m"] * p["n"] * p["k"] / (ms * 1e-3) / 1e12, 2),
+        "hbm_gbs_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
         "wall_s_timed": round(wall, 4),
     }
     line.update(extra)
