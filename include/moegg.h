@@ -87,7 +87,7 @@ typedef enum moegg_status {
   MOEGG_OK = 0,
   MOEGG_ERROR_INVALID_VALUE = 1, /* bad shape, dtype combination, NULL where required */
   MOEGG_ERROR_MISALIGNED = 2,    /* pointer not 16-byte aligned */
-  MOEGG_ERROR_NOT_SUPPORTED = 3, /* valid per the pages but not built here (e.g. K % 128 != 0) */
+  MOEGG_ERROR_NOT_SUPPORTED = 3, /* valid per the pages, not supported by this library (e.g. K % 128 != 0) */
   MOEGG_ERROR_LAUNCH = 4         /* a HIP runtime call failed */
 } moegg_status;
 

@@ -70,7 +70,7 @@ moegg_status check_impl(const moegg_problem* pp, const moegg_args* ap) {
   if (p.m_aligned <= 0 || p.m_aligned % 32 != 0)
     return fail(MOEGG_ERROR_INVALID_VALUE, "m_aligned=%d must be a positive multiple of 32", p.m_aligned);
   if (p.m_aligned % moegg::kRowBlock != 0)
-    return fail(MOEGG_ERROR_NOT_SUPPORTED, "m_aligned=%d: this build needs a multiple of %d", p.m_aligned,
+    return fail(MOEGG_ERROR_NOT_SUPPORTED, "m_aligned=%d: libmoegg needs a multiple of %d", p.m_aligned,
                 moegg::kRowBlock);
   if (p.valid_m % p.m_aligned != 0)
     return fail(MOEGG_ERROR_INVALID_VALUE, "valid_m=%lld not a multiple of m_aligned=%d", (long long)p.valid_m, p.m_aligned);
@@ -105,10 +105,10 @@ moegg_status check_impl(const moegg_problem* pp, const moegg_args* ap) {
       return fail(MOEGG_ERROR_NOT_SUPPORTED, "backward activations with BF16 operands write a BF16 dC only");
     if (p.c_dtype != MOEGG_DT_NONE) return fail(MOEGG_ERROR_INVALID_VALUE, "backward activations write no C");
   }
-  if (p.n % 32 != 0) return fail(MOEGG_ERROR_NOT_SUPPORTED, "n=%d: this build needs n %% 32 == 0", p.n);
+  if (p.n % 32 != 0) return fail(MOEGG_ERROR_NOT_SUPPORTED, "n=%d: libmoegg needs n %% 32 == 0", p.n);
   const int kstep = p.ab_dtype == MOEGG_DT_E2M1X2 ? 256 : p.ab_dtype == MOEGG_DT_BF16 ? 64 : 128;   // 128-byte steps
   if (p.k % kstep != 0)
-    return fail(MOEGG_ERROR_NOT_SUPPORTED, "k=%d: this build needs k %% %d == 0 for this operand type", p.k, kstep);
+    return fail(MOEGG_ERROR_NOT_SUPPORTED, "k=%d: libmoegg needs k %% %d == 0 for this operand type", p.k, kstep);
   if (p.k > (1 << 20)) return fail(MOEGG_ERROR_NOT_SUPPORTED, "k=%d too large", p.k);
   if (p.n > (1 << 20)) return fail(MOEGG_ERROR_NOT_SUPPORTED, "n=%d above 2^20", p.n);
   const int64_t n_out = n_out_of(p);
