@@ -226,3 +226,20 @@ def test_n_out():
         p, _ = _base("gating_bf16")
         p.update(act=act, n=n)
         assert mg.moegg_n_out(mg.make_problem(p)) == expect
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):
+    # no fallback path: a missing library is an error, not a silent CPU run
+    monkeypatch.setattr(mg, "lib_path", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(mg, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        mg.moegg_abi_version()
+
+
+def test_binding_rejects_a_library_of_another_abi(tmp_path, monkeypatch):
+    # a stale build (an older struct layout) must not be called with these structs
+    monkeypatch.setattr(mg, "_lib", None)
+    monkeypatch.setattr(mg, "ABI_VERSION", mg.ABI_VERSION + 1)
+    with pytest.raises(RuntimeError, match="rebuild"):
+        mg.moegg_abi_version()
+    monkeypatch.setattr(mg, "_lib", None)
