@@ -542,15 +542,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   const Stage st0{sAl0, sAh0, sB0, sSA0, sSB0};
   const Stage st1{sAl1, sAh1, sB1, sSA1, sSB1};
   // early set, first part: the low A half and the scale words
+  // the per-wave LDS destinations are rebuilt from an opaque copy of the
+  // wave id (two scalar operations) instead of being kept in scalar registers
+  auto owave = [&]() __attribute__((always_inline)) {
+    int w = wave;
+    asm volatile("" : "+s"(w));
+    return w;
+  };
   auto issue_ea = [&](const Src& s, int ks, const Stage& d) __attribute__((always_inline)) {
     const int kb = ks * BK;
+    const int wo = owave();
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dma16(at(s.a + kb, s.oa[j]), d.al + (wave * 16 + j * 8) * BK);
+    for (int j = 0; j < 2; ++j) dma16(at(s.a + kb, s.oa[j]), d.al + (wo * 16 + j * 8) * BK);
     if constexpr (MX) {
 #pragma unroll
       for (int u = 0; u < S_LOADS; ++u) {
         // LDS words: word w of row r at [w * rows + r], 64 rows per load
-        const int job = wave * S_LOADS + u;
+        const int job = wo * S_LOADS + u;
         const bool isA = job < S_HALF;
         const int jj = isA ? job : job - S_HALF;
         uint32_t* dst = (isA ? d.sa : d.sb) + (jj >> 2) * (isA ? BM : BN) + (jj & 3) * 64;
@@ -561,11 +569,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   };
   // early set, second part: B row load j (0..3)
   auto issue_eb = [&](const Src& s, int ks, const Stage& d, int j) __attribute__((always_inline)) {
-    dma16(at(s.b + ks * BK, s.ob[j]), d.b + (wave * 32 + j * 8) * BK);
+    dma16(at(s.b + ks * BK, s.ob[j]), d.b + (owave() * 32 + j * 8) * BK);
   };
   // late set: high A half load j (0..1)
   auto issue_l = [&](const Src& s, int ks, const Stage& d, int j) __attribute__((always_inline)) {
-    dma16(at(s.a + ks * BK, s.oa[2 + j]), d.ah + (wave * 16 + j * 8) * BK);
+    dma16(at(s.a + ks * BK, s.oa[2 + j]), d.ah + (owave() * 16 + j * 8) * BK);
   };
   // a whole stage, in the order early (first part, second part), late
   auto issue = [&](const Src& s, int ks, const Stage& d) __attribute__((always_inline)) {
