@@ -197,6 +197,14 @@ __device__ __forceinline__ T* at(T* base, uint32_t byte_off) {
   return reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(base) + static_cast<uint64_t>(byte_off));
 }
 
+// Element i of read-only kernel data at a wave-uniform index, read through
+// the scalar cache (s_load): it waits on the scalar-memory counter only, not
+// behind vector stores still in flight.
+template <typename T>
+__device__ __forceinline__ T sload(const T* base, int i) {
+  return ((const __attribute__((address_space(4))) T*)base)[i];
+}
+
 // Store 16 values of one row (one 32-column tile) as bf16.  This lane holds
 // columns 8j + 4*hi + [0, 4) (8 bytes each); v_permlane32_swap(x, y)
 // exchanges x of lanes 32-63 with y of lanes 0-31, so swapping the runs of
@@ -430,18 +438,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
     const int band_rows = min(kBandM, m_tiles - band * kBandM);
     const int nt = in_band / band_rows;
     const int mt = band * kBandM + (in_band - nt * band_rows);
-    // expert: the largest g with sTiles[g] <= mt (empty experts skipped)
-    int lo = 0, up = L;
-    while (up - lo > 1) {
-      const int mid = (lo + up) >> 1;
-      if (sTiles[mid] <= mt) lo = mid; else up = mid;
+    // expert: the largest g < L with sTiles[g] <= mt (empty experts
+    // skipped).  sTiles is non-decreasing, so that is the number of entries
+    // <= mt less one: counted 64 entries per LDS read with a ballot, up to
+    // the first chunk holding an entry above mt.
+    int cnt = 0;
+    for (int c0 = 0; c0 < L; c0 += 64) {
+      const int i = c0 + lane;
+      const int v = i < L ? sTiles[i] : 0x7FFFFFFF;
+      cnt += __popcll(__ballot(v <= mt));
+      if (cnt < c0 + 64) break;
     }
+    const int lo = cnt - 1;
     Tile tl;
     tl.g = __builtin_amdgcn_readfirstlane(lo);
     // first row: a multiple of 128 in [0, valid_m - 128] whatever the offsets
     // hold (valid_m is a positive multiple of 128 here); rows past the
     // expert's end or valid_m are not stored
-    const int64_t beg = lo ? p.po[lo - 1] : 0, end = p.po[lo];
+    const int64_t beg = tl.g ? sload(p.po, tl.g - 1) : 0, end = sload(p.po, tl.g);
     const int64_t jt = min(mt - sTiles[lo], vm >> 8);
     const int r0 = static_cast<int>(min((max(beg, int64_t{0}) + jt * BM) & ~int64_t{127}, int64_t{vm - 128}));
     const int64_t rows = min(min(int64_t{BM}, end - r0), int64_t{vm - r0});
@@ -453,8 +467,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
     // loads).  Resolved here, at tile set-up, so that the operand loads of
     // the K loop need no branch.
     if (p.b_ptrs) {
-      tl.bg = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(p.b_ptrs[tl.g]) & ~uintptr_t{15});
-      tl.sg = p.sfb_ptrs ? reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(p.sfb_ptrs[tl.g]) &
+      tl.bg = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(sload(p.b_ptrs, tl.g)) & ~uintptr_t{15});
+      tl.sg = p.sfb_ptrs ? reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(sload(p.sfb_ptrs, tl.g)) &
                                                             ~uintptr_t{15})
                          : nullptr;
     } else {
