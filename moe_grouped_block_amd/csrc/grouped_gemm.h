@@ -227,15 +227,25 @@ __device__ __forceinline__ void store_bf16_tile(uint8_t* base, uint32_t roff, in
 // of 4 at columns 8j + 4*hi (w[j], 8 bytes each): the inverse of
 // store_bf16_tile (two 16-byte loads per lane, 32 contiguous bytes of every
 // row per instruction, then the runs exchanged with lane ^ 32).
-__device__ __forceinline__ void load_bf16_tile(const uint16_t* base, uint32_t roff, int hi, v2u* w) {
+// Split in two so that the loads can be issued ahead of the exchange:
+// load_bf16_raw issues them (q[0], q[1]), unpack_bf16 exchanges the runs.
+__device__ __forceinline__ void load_bf16_raw(const uint16_t* base, uint32_t roff, int hi, v4u* q) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) q[i] = *at(reinterpret_cast<const v4u*>(base + 16 * i), roff + 16 * hi);
+}
+__device__ __forceinline__ void unpack_bf16(const v4u* q, v2u* w) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const v4u q = *at(reinterpret_cast<const v4u*>(base + 16 * i), roff + 16 * hi);
-    const v2u s0 = __builtin_amdgcn_permlane32_swap(q.x, q.z, false, false);
-    const v2u s1 = __builtin_amdgcn_permlane32_swap(q.y, q.w, false, false);
+    const v2u s0 = __builtin_amdgcn_permlane32_swap(q[i].x, q[i].z, false, false);
+    const v2u s1 = __builtin_amdgcn_permlane32_swap(q[i].y, q[i].w, false, false);
     w[2 * i] = v2u{s0.x, s1.x};
     w[2 * i + 1] = v2u{s0.y, s1.y};
   }
+}
+__device__ __forceinline__ void load_bf16_tile(const uint16_t* base, uint32_t roff, int hi, v2u* w) {
+  v4u q[2];
+  load_bf16_raw(base, roff, hi, q);
+  unpack_bf16(q, w);
 }
 
 // Store one row's 32 E4M3 codes of a 32-column tile.  This lane holds the
@@ -807,13 +817,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       for (int tn = 0; tn < TN; ++tn) colw0[tn] = colw1[tn] = 0;
       // C_in of sub-tile (tm, tn): packed bf16 of the pair's two blocks
       // (block b = ncol/32 of R pairs with C_in columns [64b, 64b + 64))
-      auto load_x = [&](int tm, int tn, v2u* wi, v2u* wg) __attribute__((always_inline)) {
+      // (raw loads q[0, 2) of the first block, q[2, 4) of the second)
+      auto load_x = [&](int tm, int tn, v4u* q) __attribute__((always_inline)) {
         const uint32_t xr = (tm * 32 + l32) * static_cast<uint32_t>(ld2) * 2;
         const uint16_t* const xb = cinW + 64 * tn;
-        load_bf16_tile(xb, xr, hi, wi);
-        load_bf16_tile(xb + 32, xr, hi, wg);
+        load_bf16_raw(xb, xr, hi, q);
+        load_bf16_raw(xb + 32, xr, hi, q + 2);
       };
       auto has_cols = [&](int tn) __attribute__((always_inline)) { return nbase + tn * 32 < p.n; };
+      // dGeGLU loads C_in one sub-tile ahead of its use, so that its latency
+      // overlaps the previous sub-tile's arithmetic and stores (dSwiGLU
+      // loads it where it is used: ahead, its registers spill)
+      constexpr bool PREFETCH = ACT == ACT_DGEGLU;
+      v4u nq[4];
+      if constexpr (PREFETCH) {
+        if (has_cols(0)) load_x(0, 0, nq);
+      }
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
         const uint32_t ml = tm * 32 + l32;                 // row within the wave's 128
@@ -823,11 +842,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         for (int tn = 0; tn < TN; ++tn) {
           if (!has_cols(tn)) continue;
           const int ncol = nbase + tn * 32;
-          // keep this sub-tile's C_in loads here (hoisting every sub-tile's
-          // loads ahead of the FP8 quantisation would spill)
+          // (loads of later sub-tiles are not hoisted above this point:
+          // holding more of them would spill)
           v2u wi[4], wg[4];          // packed bf16 of the first and second blocks of the pair
           if constexpr (OUT == OUT_E4M3) asm volatile("" ::: "memory");
-          load_x(tm, tn, wi, wg);
+          if constexpr (!PREFETCH) load_x(tm, tn, nq);
+          unpack_bf16(nq, wi);
+          unpack_bf16(nq + 2, wg);
+          if constexpr (PREFETCH) {
+            if (tn + 1 < TN && has_cols(tn + 1)) load_x(tm, tn + 1, nq);
+            else if (tm + 1 < TM) load_x(tm + 1, 0, nq);
+          }
           // element v of a packed block (columns 8(v/4) + 4 hi + v%4)
           auto bf = [](const v2u* w, int v) __attribute__((always_inline)) {
             const uint32_t u = (v & 2) ? w[v >> 2].y : w[v >> 2].x;
