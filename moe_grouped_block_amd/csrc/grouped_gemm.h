@@ -389,6 +389,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   __shared__ __attribute__((aligned(16))) uint32_t sSB0[SB_WORDS], sSB1[SB_WORDS];
   __shared__ int32_t sTiles[1025];   // m-tiles before expert g, g = 0..L
   __shared__ float sPr[kThreads / 64][kBM / 2];   // prob of each wave's 128 rows (epilogue)
+  // dSwiGLU: the second block of a sub-tile's C_in, staged (2 KB per wave)
+  __shared__ __attribute__((aligned(16))) uint8_t sCin[kThreads / 64][2048];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -825,13 +827,40 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         load_bf16_raw(xb + 32, xr, hi, q + 2);
       };
       auto has_cols = [&](int tn) __attribute__((always_inline)) { return nbase + tn * 32 < p.n; };
-      // dGeGLU loads C_in one sub-tile ahead of its use, so that its latency
-      // overlaps the previous sub-tile's arithmetic and stores (dSwiGLU
-      // loads it where it is used: ahead, its registers spill)
+      // C_in is loaded one sub-tile ahead of its use, so that its latency
+      // overlaps the previous sub-tile's arithmetic and stores: dGeGLU into
+      // registers, dSwiGLU (whose registers would spill) by direct loads into
+      // LDS, the first block behind the wave's transpose scratch, the second
+      // in sCin, 32 rows of 64 bytes each
       constexpr bool PREFETCH = ACT == ACT_DGEGLU;
+      constexpr bool STAGE = ACT == ACT_DSWIGLU && AB != AB_E2M1;   // (E2M1 has no LDS left for it)
+      uint8_t* const stg0 = reinterpret_cast<uint8_t*>(sS + 32);
+      uint8_t* const stg1 = sCin[wave];
+      auto stage_x = [&](int tm, int tn) __attribute__((always_inline)) {
+        int lid2 = lane;
+        asm volatile("" : "+v"(lid2));
+        const uint16_t* const xb = cinW + 64 * tn;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          // lane i of load k: row 16 k + i / 4, 16-byte chunk i % 4
+          const uint32_t off = (tm * 32 + 16 * k + (lid2 >> 2)) * static_cast<uint32_t>(ld2) * 2 + 16 * (lid2 & 3);
+          dma16(at(xb, off), stg0 + 1024 * k);
+          dma16(at(xb + 32, off), stg1 + 1024 * k);
+        }
+      };
+      auto read_x = [&](v4u* q) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          q[i] = *reinterpret_cast<const v4u*>(stg0 + l32 * 64 + 32 * i + 16 * hi);
+          q[2 + i] = *reinterpret_cast<const v4u*>(stg1 + l32 * 64 + 32 * i + 16 * hi);
+        }
+      };
       v4u nq[4];
       if constexpr (PREFETCH) {
         if (has_cols(0)) load_x(0, 0, nq);
+      }
+      if constexpr (STAGE) {
+        if (has_cols(0)) stage_x(0, 0);
       }
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
@@ -846,9 +875,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           // holding more of them would spill)
           v2u wi[4], wg[4];          // packed bf16 of the first and second blocks of the pair
           if constexpr (OUT == OUT_E4M3) asm volatile("" ::: "memory");
-          if constexpr (!PREFETCH) load_x(tm, tn, nq);
+          if constexpr (STAGE) {
+            // this sub-tile's staged C_in has landed (every direct load of
+            // this wave complete) before the LDS reads
+            wait_vmcnt<0>();
+            read_x(nq);
+          } else if constexpr (!PREFETCH) {
+            load_x(tm, tn, nq);
+          }
           unpack_bf16(nq, wi);
           unpack_bf16(nq + 2, wg);
+          if constexpr (STAGE) {
+            // the reads above have returned before the next sub-tile's loads
+            // overwrite the staging
+            __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
+            __builtin_amdgcn_sched_barrier(0);
+            if (tn + 1 < TN && has_cols(tn + 1)) stage_x(tm, tn + 1);
+            else if (tm + 1 < TM) stage_x(tm + 1, 0);
+          }
           if constexpr (PREFETCH) {
             if (tn + 1 < TN && has_cols(tn + 1)) load_x(tm, tn + 1, nq);
             else if (tm + 1 < TM) load_x(tm + 1, 0, nq);
