@@ -832,8 +832,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       // registers, dSwiGLU (whose registers would spill) by direct loads into
       // LDS, the first block behind the wave's transpose scratch, the second
       // in sCin, 32 rows of 64 bytes each
-      constexpr bool PREFETCH = ACT == ACT_DGEGLU;
-      constexpr bool STAGE = ACT == ACT_DSWIGLU && AB != AB_E2M1;   // (E2M1 has no LDS left for it)
+      constexpr bool STAGE = (ACT == ACT_DSWIGLU || ACT == ACT_DGEGLU) && AB != AB_E2M1;   // (E2M1 has no LDS left for it)
+      constexpr bool PREFETCH = ACT == ACT_DGEGLU && !STAGE;
       uint8_t* const stg0 = reinterpret_cast<uint8_t*>(sS + 32);
       uint8_t* const stg1 = sCin[wave];
       auto stage_x = [&](int tm, int tn) __attribute__((always_inline)) {
@@ -1024,13 +1024,51 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           load_bf16_tile(cinW + 32 * tn, cr, hi, w[tn]);
         }
       };
+      // operands other than E2M1 stage the next row in LDS by direct loads
+      // (block tn behind the wave's transpose scratch or in sCin, 32 rows of
+      // 64 bytes), E2M1 (no LDS left) holds it in registers
+      constexpr bool STAGE = AB != AB_E2M1;
+      uint8_t* const stg[2] = {reinterpret_cast<uint8_t*>(sS + 32), sCin[wave]};
+      static_assert(TN == 2, "one staging block per column block");
+      auto stage_row = [&](int tm) __attribute__((always_inline)) {
+        int lid2 = lane;
+        asm volatile("" : "+v"(lid2));
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          if (nbase + tn * 32 >= p.n) continue;
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            // lane i of load k: row 16 k + i / 4, 16-byte chunk i % 4
+            const uint32_t off = (tm * 32 + 16 * k + (lid2 >> 2)) * static_cast<uint32_t>(p.n) * 2 + 16 * (lid2 & 3);
+            dma16(at(cinW + 32 * tn, off), stg[tn] + 1024 * k);
+          }
+        }
+      };
       v2u cw[TN][4], nw[TN][4];
-      load_row(0, cw);
+      if constexpr (STAGE) stage_row(0);
+      else load_row(0, cw);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
         const uint32_t ml = tm * 32 + l32;
         float dp = 0.0f;
-        if (tm + 1 < TM) load_row(tm + 1, nw);
+        if constexpr (STAGE) {
+          // this row's staged C_in has landed before the LDS reads, and the
+          // reads have returned before the next row's loads overwrite it
+          wait_vmcnt<0>();
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) {
+            if (nbase + tn * 32 >= p.n) continue;
+            v4u q[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) q[i] = *reinterpret_cast<const v4u*>(stg[tn] + l32 * 64 + 32 * i + 16 * hi);
+            unpack_bf16(q, cw[tn]);
+          }
+          __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
+          __builtin_amdgcn_sched_barrier(0);
+          if (tm + 1 < TM) stage_row(tm + 1);
+        } else {
+          if (tm + 1 < TM) load_row(tm + 1, nw);
+        }
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           const int ncol = nbase + tn * 32;
@@ -1075,10 +1113,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         }
         dp = halves_sum(dp);
         if (hi == 0) atomicAdd(at(p.dprob + mb, 4 * ml), dp);
+        if constexpr (!STAGE) {
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
+          for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) cw[tn][j] = nw[tn][j];
+            for (int j = 0; j < 4; ++j) cw[tn][j] = nw[tn][j];
+        }
       }
       if constexpr (OUT == OUT_E4M3) {
         const int mblk0 = mbase >> 5;
