@@ -223,16 +223,11 @@ __device__ __forceinline__ void store_bf16_tile(uint8_t* base, uint32_t roff, in
   }
 }
 
-// Load one row's 32 bf16 of a 32-column tile into this lane's layout, runs
-// of 4 at columns 8j + 4*hi (w[j], 8 bytes each): the inverse of
-// store_bf16_tile (two 16-byte loads per lane, 32 contiguous bytes of every
-// row per instruction, then the runs exchanged with lane ^ 32).
-// Split in two so that the loads can be issued ahead of the exchange:
-// load_bf16_raw issues them (q[0], q[1]), unpack_bf16 exchanges the runs.
-__device__ __forceinline__ void load_bf16_raw(const uint16_t* base, uint32_t roff, int hi, v4u* q) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) q[i] = *at(reinterpret_cast<const v4u*>(base + 16 * i), roff + 16 * hi);
-}
+// One row's 32 bf16 of a 32-column tile into this lane's layout, runs of 4
+// at columns 8j + 4*hi (w[j], 8 bytes each): the inverse of store_bf16_tile.
+// q[i] holds the row's bytes [32 i + 16 hi, + 16) (two 16-byte reads per
+// lane cover 32 contiguous bytes of every row); the runs are exchanged with
+// lane ^ 32.
 __device__ __forceinline__ void unpack_bf16(const v4u* q, v2u* w) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -241,11 +236,6 @@ __device__ __forceinline__ void unpack_bf16(const v4u* q, v2u* w) {
     w[2 * i] = v2u{s0.x, s1.x};
     w[2 * i + 1] = v2u{s0.y, s1.y};
   }
-}
-__device__ __forceinline__ void load_bf16_tile(const uint16_t* base, uint32_t roff, int hi, v2u* w) {
-  v4u q[2];
-  load_bf16_raw(base, roff, hi, q);
-  unpack_bf16(q, w);
 }
 
 // Store one row's 32 E4M3 codes of a 32-column tile.  This lane holds the
@@ -389,8 +379,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   __shared__ __attribute__((aligned(16))) uint32_t sSB0[SB_WORDS], sSB1[SB_WORDS];
   __shared__ int32_t sTiles[1025];   // m-tiles before expert g, g = 0..L
   __shared__ float sPr[kThreads / 64][kBM / 2];   // prob of each wave's 128 rows (epilogue)
-  // dSwiGLU: the second block of a sub-tile's C_in, staged (2 KB per wave)
-  __shared__ __attribute__((aligned(16))) uint8_t sCin[kThreads / 64][2048];
+  // backward epilogues: rows 16-31 of the second staged C_in block (1 KB per wave)
+  __shared__ __attribute__((aligned(16))) uint8_t sCin[kThreads / 64][1024];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -752,6 +742,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
                                                        : sB1 + (wave - 4) * kScratch);
   float* sT = scratch;
   float* sS = scratch + 32 * kTPitch;
+  // C_in staging of the backward epilogues: two blocks of 32 rows x 64 bytes;
+  // block 0 and rows [0, 16) of block 1 in the 3 KB behind the wave's
+  // transpose scratch, rows [16, 32) of block 1 in sCin
+  static_assert(32 * kTPitch * 4 + 32 * 4 + 3072 <= kScratch, "C_in staging fits the wave's scratch");
+  uint8_t* const stgA = reinterpret_cast<uint8_t*>(sS + 32);
+  uint8_t* const stgB = sCin[wave];
+  // destination of direct load k (rows [16 k, 16 k + 16)) of block b
+  auto stg_dst = [&](int b, int k) __attribute__((always_inline)) {
+    return b == 0 ? stgA + 1024 * k : k == 0 ? stgA + 2048 : stgB;
+  };
+  // row r of block b
+  auto stg_row = [&](int b, int r) __attribute__((always_inline)) {
+    return b == 0 ? stgA + 64 * r : r < 16 ? stgA + 2048 + 64 * r : stgB + 64 * (r - 16);
+  };
 
   // Per-tile epilogue factors: alpha_g (a scalar load issued before the
   // tile's last K-step) and prob of the wave's 128 rows, copied to LDS by two
@@ -819,23 +823,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       for (int tn = 0; tn < TN; ++tn) colw0[tn] = colw1[tn] = 0;
       // C_in of sub-tile (tm, tn): packed bf16 of the pair's two blocks
       // (block b = ncol/32 of R pairs with C_in columns [64b, 64b + 64))
-      // (raw loads q[0, 2) of the first block, q[2, 4) of the second)
-      auto load_x = [&](int tm, int tn, v4u* q) __attribute__((always_inline)) {
-        const uint32_t xr = (tm * 32 + l32) * static_cast<uint32_t>(ld2) * 2;
-        const uint16_t* const xb = cinW + 64 * tn;
-        load_bf16_raw(xb, xr, hi, q);
-        load_bf16_raw(xb + 32, xr, hi, q + 2);
-      };
       auto has_cols = [&](int tn) __attribute__((always_inline)) { return nbase + tn * 32 < p.n; };
       // C_in is loaded one sub-tile ahead of its use, so that its latency
-      // overlaps the previous sub-tile's arithmetic and stores: dGeGLU into
-      // registers, dSwiGLU (whose registers would spill) by direct loads into
-      // LDS, the first block behind the wave's transpose scratch, the second
-      // in sCin, 32 rows of 64 bytes each
-      constexpr bool STAGE = (ACT == ACT_DSWIGLU || ACT == ACT_DGEGLU) && AB != AB_E2M1;   // (E2M1 has no LDS left for it)
-      constexpr bool PREFETCH = ACT == ACT_DGEGLU && !STAGE;
-      uint8_t* const stg0 = reinterpret_cast<uint8_t*>(sS + 32);
-      uint8_t* const stg1 = sCin[wave];
+      // overlaps the previous sub-tile's arithmetic and stores (in
+      // registers it would spill): by direct loads into the LDS staging,
+      // the first block of the pair as block 0, the second as block 1
       auto stage_x = [&](int tm, int tn) __attribute__((always_inline)) {
         int lid2 = lane;
         asm volatile("" : "+v"(lid2));
@@ -844,24 +836,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         for (int k = 0; k < 2; ++k) {
           // lane i of load k: row 16 k + i / 4, 16-byte chunk i % 4
           const uint32_t off = (tm * 32 + 16 * k + (lid2 >> 2)) * static_cast<uint32_t>(ld2) * 2 + 16 * (lid2 & 3);
-          dma16(at(xb, off), stg0 + 1024 * k);
-          dma16(at(xb + 32, off), stg1 + 1024 * k);
+          dma16(at(xb, off), stg_dst(0, k));
+          dma16(at(xb + 32, off), stg_dst(1, k));
         }
       };
       auto read_x = [&](v4u* q) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          q[i] = *reinterpret_cast<const v4u*>(stg0 + l32 * 64 + 32 * i + 16 * hi);
-          q[2 + i] = *reinterpret_cast<const v4u*>(stg1 + l32 * 64 + 32 * i + 16 * hi);
+          q[i] = *reinterpret_cast<const v4u*>(stg_row(0, l32) + 32 * i + 16 * hi);
+          q[2 + i] = *reinterpret_cast<const v4u*>(stg_row(1, l32) + 32 * i + 16 * hi);
         }
       };
+      // (raw reads q[0, 2) of the first block, q[2, 4) of the second)
       v4u nq[4];
-      if constexpr (PREFETCH) {
-        if (has_cols(0)) load_x(0, 0, nq);
-      }
-      if constexpr (STAGE) {
-        if (has_cols(0)) stage_x(0, 0);
-      }
+      if (has_cols(0)) stage_x(0, 0);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
         const uint32_t ml = tm * 32 + l32;                 // row within the wave's 128
@@ -875,28 +863,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           // holding more of them would spill)
           v2u wi[4], wg[4];          // packed bf16 of the first and second blocks of the pair
           if constexpr (OUT == OUT_E4M3) asm volatile("" ::: "memory");
-          if constexpr (STAGE) {
-            // this sub-tile's staged C_in has landed (every direct load of
-            // this wave complete) before the LDS reads
-            wait_vmcnt<0>();
-            read_x(nq);
-          } else if constexpr (!PREFETCH) {
-            load_x(tm, tn, nq);
-          }
+          // this sub-tile's staged C_in has landed (every direct load of this
+          // wave complete) before the LDS reads
+          wait_vmcnt<0>();
+          read_x(nq);
           unpack_bf16(nq, wi);
           unpack_bf16(nq + 2, wg);
-          if constexpr (STAGE) {
-            // the reads above have returned before the next sub-tile's loads
-            // overwrite the staging
-            __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
-            __builtin_amdgcn_sched_barrier(0);
-            if (tn + 1 < TN && has_cols(tn + 1)) stage_x(tm, tn + 1);
-            else if (tm + 1 < TM) stage_x(tm + 1, 0);
-          }
-          if constexpr (PREFETCH) {
-            if (tn + 1 < TN && has_cols(tn + 1)) load_x(tm, tn + 1, nq);
-            else if (tm + 1 < TM) load_x(tm + 1, 0, nq);
-          }
+          // the reads above have returned before the next sub-tile's loads
+          // overwrite the staging
+          __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
+          __builtin_amdgcn_sched_barrier(0);
+          if (tn + 1 < TN && has_cols(tn + 1)) stage_x(tm, tn + 1);
+          else if (tm + 1 < TM) stage_x(tm + 1, 0);
           // element v of a packed block (columns 8(v/4) + 4 hi + v%4)
           auto bf = [](const v2u* w, int v) __attribute__((always_inline)) {
             const uint32_t u = (v & 2) ? w[v >> 2].y : w[v >> 2].x;
@@ -1014,21 +992,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) colw[tn] = 0;
       const uint16_t* const cinW = p.c_in + mb * p.n + nbase;
-      // C_in of one row of sub-tiles (32 rows, TN blocks of 32 columns), loaded one row
-      // ahead so that its latency overlaps the previous row's work
-      auto load_row = [&](int tm, v2u (*w)[4]) __attribute__((always_inline)) {
-        const uint32_t cr = (tm * 32 + l32) * static_cast<uint32_t>(p.n) * 2;
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          if (nbase + tn * 32 >= p.n) continue;
-          load_bf16_tile(cinW + 32 * tn, cr, hi, w[tn]);
-        }
-      };
-      // operands other than E2M1 stage the next row in LDS by direct loads
-      // (block tn behind the wave's transpose scratch or in sCin, 32 rows of
-      // 64 bytes), E2M1 (no LDS left) holds it in registers
-      constexpr bool STAGE = AB != AB_E2M1;
-      uint8_t* const stg[2] = {reinterpret_cast<uint8_t*>(sS + 32), sCin[wave]};
+      // C_in of one row of sub-tiles (32 rows, TN blocks of 32 columns),
+      // loaded one row ahead so that its latency overlaps the previous row's
+      // work: by direct loads into the LDS staging, column block tn as
+      // staging block tn
       static_assert(TN == 2, "one staging block per column block");
       auto stage_row = [&](int tm) __attribute__((always_inline)) {
         int lid2 = lane;
@@ -1040,35 +1007,30 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           for (int k = 0; k < 2; ++k) {
             // lane i of load k: row 16 k + i / 4, 16-byte chunk i % 4
             const uint32_t off = (tm * 32 + 16 * k + (lid2 >> 2)) * static_cast<uint32_t>(p.n) * 2 + 16 * (lid2 & 3);
-            dma16(at(cinW + 32 * tn, off), stg[tn] + 1024 * k);
+            dma16(at(cinW + 32 * tn, off), stg_dst(tn, k));
           }
         }
       };
-      v2u cw[TN][4], nw[TN][4];
-      if constexpr (STAGE) stage_row(0);
-      else load_row(0, cw);
+      v2u cw[TN][4];
+      stage_row(0);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
         const uint32_t ml = tm * 32 + l32;
         float dp = 0.0f;
-        if constexpr (STAGE) {
-          // this row's staged C_in has landed before the LDS reads, and the
-          // reads have returned before the next row's loads overwrite it
-          wait_vmcnt<0>();
+        // this row's staged C_in has landed before the LDS reads, and the
+        // reads have returned before the next row's loads overwrite it
+        wait_vmcnt<0>();
 #pragma unroll
-          for (int tn = 0; tn < TN; ++tn) {
-            if (nbase + tn * 32 >= p.n) continue;
-            v4u q[2];
+        for (int tn = 0; tn < TN; ++tn) {
+          if (nbase + tn * 32 >= p.n) continue;
+          v4u q[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) q[i] = *reinterpret_cast<const v4u*>(stg[tn] + l32 * 64 + 32 * i + 16 * hi);
-            unpack_bf16(q, cw[tn]);
-          }
-          __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
-          __builtin_amdgcn_sched_barrier(0);
-          if (tm + 1 < TM) stage_row(tm + 1);
-        } else {
-          if (tm + 1 < TM) load_row(tm + 1, nw);
+          for (int i = 0; i < 2; ++i) q[i] = *reinterpret_cast<const v4u*>(stg_row(tn, l32) + 32 * i + 16 * hi);
+          unpack_bf16(q, cw[tn]);
         }
+        __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        if (tm + 1 < TM) stage_row(tm + 1);
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           const int ncol = nbase + tn * 32;
@@ -1113,12 +1075,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         }
         dp = halves_sum(dp);
         if (hi == 0) atomicAdd(at(p.dprob + mb, 4 * ml), dp);
-        if constexpr (!STAGE) {
-#pragma unroll
-          for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) cw[tn][j] = nw[tn][j];
-        }
       }
       if constexpr (OUT == OUT_E4M3) {
         const int mblk0 = mbase >> 5;
