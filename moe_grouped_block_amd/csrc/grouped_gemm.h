@@ -187,14 +187,17 @@ __device__ __forceinline__ float max_abs2(float c, float a, float b) {
 // wave's first row and the block's first column) plus a 32-bit per-lane byte
 // offset.  Offsets stay below 2^32: 128 rows of at most 2^21 two-byte
 // elements.
-// The integer round trip hides the address space, so these accesses compile
-// to flat_* instructions with 64-bit lane addresses.  Byte-pointer arithmetic
-// would keep them global_* with a scalar base, but measured 2-7 % slower on
-// every workload (more scalar registers live through the epilogue, more
-// spills).
+// The integer round trip keeps the compiler from carrying extra 64-bit
+// pointers through the epilogue (plain byte-pointer arithmetic measured
+// 2-7 % slower: more scalar registers live, more spills); the cast to the
+// global address space then makes the accesses global_* rather than flat_*:
+// a flat store also counts on the LDS counter, so the LDS waits of the next
+// output block would wait for it (measured 1-3 % faster on every workload).
 template <typename T>
 __device__ __forceinline__ T* at(T* base, uint32_t byte_off) {
-  return reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(base) + static_cast<uint64_t>(byte_off));
+  typedef __attribute__((address_space(1))) T GT;
+  GT* const g = (GT*)(reinterpret_cast<uintptr_t>(base) + static_cast<uint64_t>(byte_off));
+  return (T*)g;
 }
 
 // Element i of read-only kernel data at a wave-uniform index, read through
