@@ -294,10 +294,17 @@ __device__ __forceinline__ uint32_t quant_tile(float* T, float* S, uint8_t* dW, 
   float cm = 0.0f;
   const float* c0 = T + l32 + (hi ? 24 * kTPitch : 0);      // rows [0, 8) / [24, 32)
   const float* c1 = T + l32 + (hi ? 8 * kTPitch : 0);       // rows [8, 16) / [16, 24) at r + 8
+  // all sixteen reads in flight together, then one wait
+  float cv[16];
 #pragma unroll
-  for (int r = 0; r < 8; r += 2) cm = max_abs2(cm, c0[r * kTPitch], c0[(r + 1) * kTPitch]);
+  for (int r = 0; r < 8; ++r) cv[r] = c0[r * kTPitch];
 #pragma unroll
-  for (int r = 8; r < 16; r += 2) cm = max_abs2(cm, c1[r * kTPitch], c1[(r + 1) * kTPitch]);
+  for (int r = 8; r < 16; ++r) cv[r] = c1[r * kTPitch];
+  asm volatile("" : "+v"(cv[0]), "+v"(cv[1]), "+v"(cv[2]), "+v"(cv[3]), "+v"(cv[4]), "+v"(cv[5]), "+v"(cv[6]),
+               "+v"(cv[7]), "+v"(cv[8]), "+v"(cv[9]), "+v"(cv[10]), "+v"(cv[11]), "+v"(cv[12]), "+v"(cv[13]),
+               "+v"(cv[14]), "+v"(cv[15]));
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) cm = max_abs2(cm, cv[r], cv[r + 1]);
   cm = halves_max(cm);
   const uint32_t bc = e8m0_ceil(cm * kRcp448);
   if (hi == 0) S[l32] = e8m0_inverse(bc);
