@@ -124,6 +124,11 @@ SMALL = {
                                                         clip=6.0)),
     "dsrelu_bf16_ops": ("dsrelu_mxfp8_l32", dict(ab="bf16", d="bf16", L=2, K=192, N=256,
                                                  routing=("multinomial", 200))),
+    # E2M1 operands with FP8 dC and a last wave column holding one 32-column
+    # block (N % 64 == 32): the C_in staging's half-empty row
+    "dsrelu_mxfp4_e4m3_n288": ("dsrelu_mxfp8_l32", dict(ab="e2m1x2", L=3, K=512, N=288,
+                                                        routing=("multinomial", 300), a_std=1.0, b_std=1.0,
+                                                        clip=6.0)),
     # E5M2 operands ("Grouped GEMM + Quant", §Data Types) through the other epilogues
     "e5m2_gating_bf16": ("quant_gating_l4", dict(ab="e5m2", L=3, K=384, N=288, routing=("multinomial", 300))),
     "e5m2_swiglu_e4m3": ("fc1_swiglu_l8", dict(ab="e5m2", L=3, K=640, N=320, routing=("topk", 300, 2))),
@@ -152,6 +157,9 @@ SMALL = {
                                                    a_std=1.0, b_std=1.0, clip=6.0, norm_const=2.0)),
     "dgeglu_bf16_ops": ("dgeglu_mxfp8_l64", dict(ab="bf16", d="bf16", L=2, K=192, N=288,
                                                  routing=("topk", 150, 2), geglu_alpha=1.0)),
+    "dgeglu_mxfp4_bf16_amax_n288": ("dgeglu_mxfp8_l64", dict(ab="e2m1x2", d="bf16", L=3, K=512, N=288,
+                                                             routing=("topk", 150, 2), a_std=1.0, b_std=1.0,
+                                                             clip=6.0)),
 }
 
 
