@@ -10,7 +10,7 @@ import pytest
 import oracle
 import synth
 from oracle import formats as F
-from parity_util import amax_rule, decode_bf16, pick_row_blocks, rule1, rule2
+from parity_util import acc_error_bound, amax_rule, decode_bf16, pick_row_blocks, rule1, rule2
 
 pytestmark = pytest.mark.gpu
 
@@ -49,10 +49,11 @@ def check_case(case, got, rows=None):
         stats["dprob"] = rule1(got["dprob"][r], ref["dprob"], grp, "dprob")
         if p["d_dtype"] == "e4m3":
             nc = float(case.arrays["norm_const"][0])
-            stats["d_row"] = rule2(got["d"][r], got["sfd_row"][r], ref["dc"], nc, "row", "dC/SFD_row")
+            rb = acc_error_bound(case, ref)
+            stats["d_row"] = rule2(got["d"][r], got["sfd_row"][r], ref["dc"], nc, "row", "dC/SFD_row", rb)
             blocks = np.unique(r // 32)
             stats["d_col"] = rule2(got["d_col"][r], got["sfd_col"][:, blocks], ref["dc"], nc, "col",
-                                   "dC_col/SFD_col")
+                                   "dC_col/SFD_col", rb)
             return stats
         g2 = np.repeat(grp[:, None], ref["dc"].shape[1], axis=1)
         stats["dc"] = rule1(decode_bf16(got["d"][r]), ref["dc"], g2, "dC")
@@ -71,9 +72,10 @@ def check_case(case, got, rows=None):
             stats["amax"] = amax_rule(got["amax"], ref["amax"])
     else:
         nc = float(case.arrays["norm_const"][0])
-        stats["d_row"] = rule2(got["d"][r], got["sfd_row"][r], ref["d"], nc, "row", "D/SFD_row")
+        rb = acc_error_bound(case, ref)
+        stats["d_row"] = rule2(got["d"][r], got["sfd_row"][r], ref["d"], nc, "row", "D/SFD_row", rb)
         blocks = np.unique(r // 32)
-        stats["d_col"] = rule2(got["d_col"][r], got["sfd_col"][:, blocks], ref["d"], nc, "col", "D_col/SFD_col")
+        stats["d_col"] = rule2(got["d_col"][r], got["sfd_col"][:, blocks], ref["d"], nc, "col", "D_col/SFD_col", rb)
     return stats
 
 
