@@ -1,7 +1,7 @@
 """Throughput of the grouped block-scaled GEMM + fused epilogue on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--cold]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--also LIST]
+                    [--no-cpu-baseline] [--no-cold] [--no-clock]
 
 A step is one launch of the whole hot path (grouped MXFP8 GEMM, SwiGLU over
 32-column pairs, gating, FP8 row + column quantisation with E8M0 scales) over
@@ -9,8 +9,13 @@ the FC1 + SwiGLU workload at L = 64 experts: 16384 tokens routed top-6
 uniformly (98304 routed rows, each expert padded to a multiple of 128 rows),
 K = 2048, N = 2816 (44 linear/gate pairs of 32 columns), MXFP8 E4M3 operands
 with E8M0 scales per 32 K-elements.  The same line also reports the 8-expert
-FC1 + SwiGLU workload (4096 tokens top-2).  Inputs are synthetic and already
-resident in HBM.  Rank 0 prints one JSON line.
+FC1 + SwiGLU workload (4096 tokens top-2) and the other workloads of
+`--also`, which run first.  Inputs are synthetic and already resident in HBM.
+Rank 0 prints one JSON line.  Per workload: the mean per launch over the
+timed window (HIP events on the launch stream around every launch) with its
+median, min and max; the mean after a 1 GiB cache flush (cold); the core
+clock sampled during a further window of launches, and the roofline fraction
+at that clock.
 
 `value` is TFLOP/s over routed rows (2 * routed * N * K per step, padding
 excluded).  `roofline` compares the kernel's achieved rate (HIP events on the
@@ -33,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"e4m3": 5000.0, "e5m2": 5000.0, "e2m1x2": 10100.0, "bf16": 2500.0}   # dense MFMA peaks, MI355X
 HBM_GBS = 8000.0
+NOMINAL_SCLK_MHZ = 2400.0     # the clock at which the MFMA peaks are quoted
 KERNEL_SOURCES = ["moe_grouped_block_amd/csrc/grouped_gemm.h", "moe_grouped_block_amd/csrc/moegg_kernels.hip",
                   "moe_grouped_block_amd/csrc/inst_e4m3.hip", "moe_grouped_block_amd/csrc/inst_e2m1.hip",
                   "moe_grouped_block_amd/csrc/inst_bf16.hip", "moe_grouped_block_amd/csrc/inst_e5m2.hip",
@@ -116,22 +122,79 @@ def cpu_baseline(case, rows_n):
                       f"oracle pass incl. dequantise, GEMM, SwiGLU and FP8 quantisation: {dt:.1f} s"}
 
 
+class ClockSampler:
+    """Median core clock (MHz) of the GPU while a launch window runs, read
+    from the driver's metrics through amdsmi in a background thread; None
+    where amdsmi is unavailable.  Sampling only reads: it launches nothing."""
+
+    def __init__(self):
+        self.h = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            hs = amdsmi.amdsmi_get_processor_handles()
+            vis = os.environ.get("HIP_VISIBLE_DEVICES") or os.environ.get("ROCR_VISIBLE_DEVICES")
+            idx = int(vis.split(",")[0]) if vis and vis.split(",")[0].isdigit() and len(hs) > 1 else 0
+            self.amdsmi, self.h = amdsmi, hs[min(idx, len(hs) - 1)]
+            self.read()
+        except Exception as e:   # no driver access: report no clock
+            self.h, self.err = None, repr(e)[:200]
+
+    def read(self):
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
+        v = m.get("current_gfxclks")
+        if isinstance(v, (list, tuple)):
+            v = [x for x in v if isinstance(x, (int, float)) and 0 < x < 10000]
+            if v:
+                return float(sum(v)) / len(v)
+        for key in ("current_gfxclk", "average_gfxclk_frequency"):
+            x = m.get(key)
+            if isinstance(x, (int, float)) and 0 < x < 10000:
+                return float(x)
+        return None
+
+    def during(self, fn):
+        """Run fn() while sampling; return (fn's result, median MHz or None, samples)."""
+        if self.h is None:
+            return fn(), None, 0
+        import threading
+        vals, stop = [], threading.Event()
+
+        def loop():
+            while not stop.is_set():
+                try:
+                    x = self.read()
+                    if x:
+                        vals.append(x)
+                except Exception:
+                    pass
+                time.sleep(0.002)
+        th = threading.Thread(target=loop, daemon=True)
+        th.start()
+        try:
+            r = fn()
+        finally:
+            stop.set()
+            th.join()
+        return r, (float(sorted(vals)[len(vals) // 2]) if vals else None), len(vals)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50,
-                    help="untimed launches first; the GPU's power management throttles hard a few "
-                         "launches into sustained load and settles after about 40 launches (25 ms)")
+                    help="untimed launches of the headline before its timed window")
     ap.add_argument("--workload", default="fc1_swiglu_l64")
     ap.add_argument("--also", default="fc1_swiglu_l8,quant_gating_l4,fc2_gating_l64_zipf,srelu_tanh_fp4_l32,"
                     "dswiglu_bf16_l64,fc1_swiglu_l64:discrete,dswiglu_mxfp8_l64,dsrelu_mxfp8_l32,"
                     "fc1_geglu_e5m2_l8,dgeglu_mxfp8_l64",
-                    help="comma list of extra workloads to time; a ':discrete' suffix passes the expert "
-                         "weights as per-expert allocations (b_ptrs / sfb_ptrs)")
+                    help="comma list of extra workloads to time (before the headline); a ':discrete' suffix "
+                         "passes the expert weights as per-expert allocations (b_ptrs / sfb_ptrs)")
     ap.add_argument("--cpu-rows", type=int, default=40960, help="rows of the oracle CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold", action="store_true", help="also time launches after an L2/MALL flush")
+    ap.add_argument("--no-cold", action="store_true", help="skip the launches after an L2/MALL flush")
+    ap.add_argument("--no-clock", action="store_true", help="skip the clock-sampling window")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (reference for HBM counters)")
     args = ap.parse_args()
@@ -160,6 +223,8 @@ def main():
     if not os.path.exists(mg.lib_path):
         from moe_grouped_block_amd import build
         build.build()
+    clock = None if args.no_clock else ClockSampler()
+
     def measure(name, steps, warmup, cold):
         base, _, mode = name.partition(":")
         case = synth.make_case(base)
@@ -188,20 +253,33 @@ def main():
         for _ in range(warmup):
             step()
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        # one event before every launch and one after the last, all on the
+        # launch stream: launch i takes ev[i] -> ev[i + 1]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         t0 = time.perf_counter()
-        e0.record(stream)
-        for _ in range(steps):
+        for i in range(steps):
+            ev[i].record(stream)
             step()
-        e1.record(stream)
+        ev[steps].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        ms = e0.elapsed_time(e1) / steps
-        res = {"case": case, "ms": ms, "wall": wall, "tflops": case.flops / (ms * 1e-3) / 1e12}
+        per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        ms = ev[0].elapsed_time(ev[steps]) / steps
+        res = {"case": case, "ms": ms, "wall": wall, "tflops": case.flops / (ms * 1e-3) / 1e12,
+               "ms_median": per[len(per) // 2], "ms_min": per[0], "ms_max": per[-1]}
+        if clock is not None:
+            # a window of back-to-back launches (at least 30 ms) with the clock sampled
+            nclk = max(steps, int(30.0 / max(ms, 1e-3)) + 1)
+
+            def window():
+                for _ in range(nclk):
+                    step()
+                torch.cuda.synchronize()
+            _, mhz, nsamp = clock.during(window)
+            res["sclk_mhz"], res["sclk_samples"] = mhz, nsamp
         if cold:
             flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB > L2 + MALL
-            tot = 0.0
+            cl = []
             for _ in range(10):
                 flush.zero_()
                 a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -209,39 +287,53 @@ def main():
                 step()
                 a1.record(stream)
                 torch.cuda.synchronize()
-                tot += a0.elapsed_time(a1)
-            res["cold_ms"] = tot / 10
+                cl.append(a0.elapsed_time(a1))
+            res["cold_ms"] = sum(cl) / len(cl)
+            res["cold_ms_median"] = sorted(cl)[len(cl) // 2]
             del flush
         del dev, outs, tensors, keep
         torch.cuda.empty_cache()
         return res
 
-    main_res = measure(args.workload, args.steps, args.warmup, args.cold)
-    case, ms, wall, value = main_res["case"], main_res["ms"], main_res["wall"], main_res["tflops"]
-    p = case.problem
-    extra = {}
-    if args.cold:
-        extra["cold_ms_per_launch"] = round(main_res["cold_ms"], 5)
-        extra["cold_tflops"] = round(case.flops / (main_res["cold_ms"] * 1e-3) / 1e12, 2)
-    also = {}
-    for name in [x for x in args.also.split(",") if x]:
-        r = measure(name, max(args.steps, 20), args.warmup, args.cold)
+    def summary(r):
         c = r["case"]
-        t_m = c.flops / (PEAK_TFLOPS[c.problem["ab_dtype"]] * 1e12)
+        peak = PEAK_TFLOPS[c.problem["ab_dtype"]]
+        t_m = c.flops / (peak * 1e12)
         t_h = algorithmic_bytes(c) / (HBM_GBS * 1e9)
         padded_flops = 2.0 * c.problem["valid_m"] * c.problem["n"] * c.problem["k"]
-        also[name] = {"ms_per_step": round(r["ms"], 5), "tflops_routed": round(r["tflops"], 2),
-                      "tflops_padded": round(padded_flops / (r["ms"] * 1e-3) / 1e12, 2),
-                      "hbm_gbs_algorithmic": round(algorithmic_bytes(c) / (r["ms"] * 1e-3) / 1e9, 1),
-                      "frac_mfma_peak": round(r["tflops"] / PEAK_TFLOPS[c.problem["ab_dtype"]], 4),
-                      "bound": "mfma" if t_m >= t_h else "hbm",
-                      "frac_roofline": round(max(t_m, t_h) / (r["ms"] * 1e-3), 4),
-                      "valid_m": c.problem["valid_m"], "routed_rows": c.routed_rows,
-                      "experts": c.problem["num_groups"]}
+        d = {"ms_per_step": round(r["ms"], 5), "ms_median": round(r["ms_median"], 5),
+             "ms_min": round(r["ms_min"], 5), "ms_max": round(r["ms_max"], 5),
+             "tflops_routed": round(r["tflops"], 2),
+             "tflops_padded": round(padded_flops / (r["ms"] * 1e-3) / 1e12, 2),
+             "hbm_gbs_algorithmic": round(algorithmic_bytes(c) / (r["ms"] * 1e-3) / 1e9, 1),
+             "frac_mfma_peak": round(r["tflops"] / peak, 4),
+             "bound": "mfma" if t_m >= t_h else "hbm",
+             "frac_roofline": round(max(t_m, t_h) / (r["ms"] * 1e-3), 4),
+             "valid_m": c.problem["valid_m"], "routed_rows": c.routed_rows,
+             "experts": c.problem["num_groups"]}
+        if r.get("sclk_mhz"):
+            # the MFMA roofline scaled to the measured clock (the HBM one does not move)
+            t_m_clk = t_m * NOMINAL_SCLK_MHZ / r["sclk_mhz"]
+            d["sclk_mhz"] = round(r["sclk_mhz"], 1)
+            d["frac_roofline_at_sclk"] = round(max(t_m_clk, t_h) / (r["ms"] * 1e-3), 4)
         if "cold_ms" in r:
-            also[name]["cold_ms_per_launch"] = round(r["cold_ms"], 5)
-    if also:
-        extra["also"] = also
+            d["cold_ms_per_launch"] = round(r["cold_ms"], 5)
+            d["cold_ms_median"] = round(r["cold_ms_median"], 5)
+            d["cold_frac_roofline"] = round(max(t_m, t_h) / (r["cold_ms"] * 1e-3), 4)
+        return d
+
+    # The extra workloads run first: the GPU's power management throttles hard
+    # a few launches into sustained load after idle and settles within about
+    # 40 launches (25 ms), so the headline's window then measures the
+    # sustained state that a long training run sees.
+    also = {}
+    for name in [x for x in args.also.split(",") if x]:
+        r = measure(name, max(args.steps, 20), max(args.warmup, 10), not args.no_cold)
+        also[name] = summary(r)
+    main_res = measure(args.workload, args.steps, args.warmup, not args.no_cold)
+    case, ms, wall, value = main_res["case"], main_res["ms"], main_res["wall"], main_res["tflops"]
+    p = case.problem
+    hs = summary(main_res)
 
     peak = PEAK_TFLOPS[p["ab_dtype"]]
     alg_bytes = algorithmic_bytes(case)
@@ -255,6 +347,9 @@ def main():
     roof = {"bound": bound, "achieved": round(achieved, 2), "peak": pk, "unit": unit,
             "frac": round(achieved / pk, 4), "traffic": read_traffic(args.workload),
             "algorithmic_bytes": alg_bytes, "algorithmic_flops": case.flops}
+    if "frac_roofline_at_sclk" in hs:
+        roof["sclk_mhz"] = hs["sclk_mhz"]
+        roof["frac_at_sclk"] = hs["frac_roofline_at_sclk"]
     line = {
         "metric": "grouped-GEMM TFLOP/s (valid rows) + % MXFP8 MFMA peak, FC1+SwiGLU L=64",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -265,11 +360,18 @@ def main():
                    "d_dtype": p["d_dtype"], "parallelism": "single-gpu"},
         "roofline": roof,
         "pct_mxfp8_peak": round(100.0 * value / PEAK_TFLOPS["e4m3"], 2),
-        "tflops_padded": round(2.0 * p["valid_m"] * p["n"] * p["k"] / (ms * 1e-3) / 1e12, 2),
-        "hbm_gbs_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+        "ms_per_step_median": hs["ms_median"], "ms_per_step_min": hs["ms_min"], "ms_per_step_max": hs["ms_max"],
+        "tflops_padded": hs["tflops_padded"],
+        "hbm_gbs_algorithmic": hs["hbm_gbs_algorithmic"],
         "wall_s_timed": round(wall, 4),
     }
-    line.update(extra)
+    for k in ("sclk_mhz", "cold_ms_per_launch", "cold_ms_median", "cold_frac_roofline"):
+        if k in hs:
+            line[k] = hs[k]
+    if clock is not None and clock.h is None:
+        line["sclk_unavailable"] = getattr(clock, "err", "")
+    if also:
+        line["also"] = also
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_rows)
     print(json.dumps(line), flush=True)

@@ -25,21 +25,18 @@
  *   A       (valid_m, K)   E4M3 or E5M2 codes, or (valid_m, K/2) packed E2M1 pairs
  *                          (the even K element in the low nibble), or BF16
  *   B       (L, N, K)      same encoding as A, K contiguous ("K-major")
- *   SFA     E8M0 bytes, one per 32 K-elements of each row of A (MX formats
- *           only), stored as K/128 planes of 32-bit words: the byte of row r
- *           and K-block kb (kb = k / 32) is at byte offset
- *           4 * ((kb / 4) * valid_m + r) + kb % 4, i.e. a (K/128, valid_m, 4)
- *           array.  One plane holds the scales of 128 consecutive K elements
- *           of every row, so the scales a row tile needs for one K-step are
- *           contiguous.  (The logical view is the pages' (valid_m, K/32).)
- *   SFB     the same for the rows of B: (K/128, L*N, 4), row index g*N + n
+ *   SFA     (valid_m, K/32) E8M0 bytes, row-major: byte kb of row r (the
+ *           scale of A[r, 32 kb .. 32 kb + 31]) at r * K/32 + kb (MX formats
+ *           only; "Grouped GEMM + Quant (SM100)", §Shapes, SFA)
+ *   SFB     (L, N, K/32) E8M0 bytes, row-major: expert g's row n at
+ *           (g * N + n) * K/32 ("Grouped GEMM + Quant (SM100)", §Shapes, SFB)
  *   Discrete weights (the pages' b_ptrs / sfb_ptrs mode, "Grouped GEMM +
  *   sReLU (SM100)", §Discrete-weight wrapper): instead of B and SFB the
  *   caller passes device arrays of L device pointers; b_ptrs[g] points to
  *   expert g's (N, K) weights in B's encoding and sfb_ptrs[g] (MX only) to
- *   its scales as (K/128, N, 4) word planes.  Each pointer must be 16-byte
- *   aligned (the kernel ignores its low 4 bits); entries of experts with no
- *   rows are never read.
+ *   its (N, K/32) row-major scales.  Each pointer must be 16-byte aligned
+ *   (the kernel ignores its low 4 bits); entries of experts with no rows are
+ *   never read.
  *   padded_offsets (L) int32, cumulative group ends; padded_offsets[L-1] ==
  *                          valid_m; every entry a multiple of m_aligned and
  *                          nondecreasing (empty groups repeat the previous end)
@@ -57,7 +54,8 @@
  *           which quantity each entry holds is this library's reading)
  *   C_in    saved forward pre-activation, BF16: (valid_m, 2N) [dSwiGLU, dGeGLU]
  *           or (valid_m, N) [dsReLU]
- *   dprob   (valid_m) fp32, caller-zeroed, accumulated with atomics [dSwiGLU, dsReLU]
+ *   dprob   (valid_m) fp32, caller-zeroed, accumulated with atomics [dSwiGLU, dsReLU,
+ *           dGeGLU]
  *
  * Ownership: every pointer is a caller-owned device pointer (except the
  * problem/args structs, which are host memory read during the call only).
@@ -81,7 +79,7 @@
 extern "C" {
 #endif
 
-#define MOEGG_ABI_VERSION 4
+#define MOEGG_ABI_VERSION 5
 
 typedef enum moegg_status {
   MOEGG_OK = 0,
@@ -155,8 +153,8 @@ typedef struct moegg_problem {
 typedef struct moegg_args {
   const void* a;
   const void* b;
-  const uint8_t* sfa;            /* MX operands only; (K/128, valid_m, 4) word planes */
-  const uint8_t* sfb;            /* MX operands only; (K/128, L*N, 4) word planes */
+  const uint8_t* sfa;            /* MX operands only; (valid_m, K/32) E8M0, row-major */
+  const uint8_t* sfb;            /* MX operands only; (L, N, K/32) E8M0, row-major */
   const int32_t* padded_offsets;
   const float* alpha;
   const float* prob;             /* required ("prob ... Required", Quant page) */
@@ -175,17 +173,31 @@ typedef struct moegg_args {
 } moegg_args;
 
 /* Validate problem + pointers on the host.  No HIP call.  MOEGG_OK if
- * moegg_run would launch (or, for valid_m == 0, do nothing). */
+ * moegg_run would launch (or, for valid_m == 0, only zero-fill amax).
+ * The rules are the pages' ("Grouped GEMM + Quant (SM100)", §Support Surface
+ * and Constraints: §Layouts and Strides (16-byte alignment), §Data Types and
+ * §Additional Type Constraints (A and B of one dtype, the SFD trio together),
+ * §Scale Factor Output Requirements (amax with a BF16 D), §Shapes and
+ * Divisibility (L <= 1024, groups aligned to m_aligned, valid_m =
+ * padded_offsets[L-1]); "Grouped GEMM + dGLU (SM100)", §Support Surface and
+ * Constraints for the backward tensors), plus this library's own limits,
+ * reported as MOEGG_ERROR_NOT_SUPPORTED (K a multiple of 128 bytes per row,
+ * N a multiple of 32, m_aligned a multiple of 128). */
 moegg_status moegg_check(const moegg_problem* problem, const moegg_args* args);
 
-/* Validate, then enqueue the whole path on `stream` (hipStream_t).  Zero-fills
- * amax (when used) on the same stream.  valid_m == 0: returns MOEGG_OK and
- * enqueues nothing. */
+/* Validate (as moegg_check), then enqueue the whole path on `stream`
+ * (hipStream_t): the amax zero-fill (when amax is used) and the grouped GEMM
+ * with its epilogue ("Grouped GEMM + Quant (SM100)", §Equations, Steps 1-3, and
+ * the other pages' §Equations).  valid_m == 0: returns MOEGG_OK after
+ * enqueuing only the amax zero-fill. */
 moegg_status moegg_run(const moegg_problem* problem, const moegg_args* args, void* stream);
 
-/* Opt-in validator of device padded_offsets (synchronises `stream`): entries
- * nondecreasing, multiples of m_aligned, last == valid_m.  MOEGG_OK or
- * MOEGG_ERROR_INVALID_VALUE. */
+/* Opt-in validator of device padded_offsets (synchronises `stream`) against
+ * the pages' offset rules ("Grouped GEMM + Quant (SM100)", §Shapes: the
+ * cumulative sum of aligned group sizes with valid_m its last entry; §Shapes
+ * and Divisibility: every group aligned to m_aligned): entries nondecreasing,
+ * multiples of m_aligned, last == valid_m.  MOEGG_OK or
+ * MOEGG_ERROR_INVALID_VALUE (MOEGG_ERROR_LAUNCH if the copy fails). */
 moegg_status moegg_check_offsets(const moegg_problem* problem, const int32_t* padded_offsets,
                                  void* stream);
 
@@ -196,6 +208,14 @@ int64_t moegg_n_out(const moegg_problem* problem);
 const char* moegg_status_string(moegg_status status);
 const char* moegg_last_error(void);   /* thread-local detail of the last failure */
 int moegg_abi_version(void);
+
+/* Testing hook; no passage defines it and it changes no result.  Caps the
+ * persistent workgroups that later moegg_run calls launch, from any thread
+ * (0 or a negative value: no cap, the default of one workgroup per compute
+ * unit).  With a small cap every workgroup walks many output tiles, so that a
+ * problem small enough for a CPU reference still passes through every
+ * tile-to-tile hand-off of the kernel.  Returns the previous cap. */
+int moegg_set_grid_limit(int max_workgroups);
 
 #ifdef __cplusplus
 }

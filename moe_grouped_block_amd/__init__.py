@@ -6,7 +6,7 @@ The C ABI (include/moegg.h) is mirrored name for name:
     moegg_run(problem, args, stream) -> status
     moegg_check_offsets(problem, padded_offsets_ptr, stream) -> status
     moegg_n_out(problem), moegg_status_string(status), moegg_last_error(),
-    moegg_abi_version()
+    moegg_abi_version(), moegg_set_grid_limit(max_workgroups)
 
 plus ``make_problem`` / ``make_args`` (fill the C structs from a problem dict
 and torch tensors' device pointers) and ``run`` / ``check`` (build the structs,
@@ -20,13 +20,13 @@ import ctypes
 import os
 
 __all__ = ["MoeggError", "moegg_check", "moegg_run", "moegg_check_offsets", "moegg_n_out",
-           "moegg_status_string", "moegg_last_error", "moegg_abi_version", "make_problem",
+           "moegg_status_string", "moegg_last_error", "moegg_abi_version", "moegg_set_grid_limit", "make_problem",
            "make_args", "run", "check", "lib_path", "ABI_VERSION", "DTYPES", "ACTS", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libmoegg.so")
 
-ABI_VERSION = 4   # MOEGG_ABI_VERSION of the structs below
+ABI_VERSION = 5   # MOEGG_ABI_VERSION of the structs below
 DTYPES = {None: 0, "none": 0, "e4m3": 1, "e2m1x2": 2, "bf16": 3, "e5m2": 4}
 ACTS = {"none": 0, "swiglu": 1, "srelu": 2, "dswiglu": 3, "dsrelu": 4, "geglu": 5, "dgeglu": 6}
 STATUS = {0: "MOEGG_OK", 1: "MOEGG_ERROR_INVALID_VALUE", 2: "MOEGG_ERROR_MISALIGNED",
@@ -76,6 +76,7 @@ def _load():
         lib.moegg_status_string.argtypes, lib.moegg_status_string.restype = [ctypes.c_int], ctypes.c_char_p
         lib.moegg_last_error.argtypes, lib.moegg_last_error.restype = [], ctypes.c_char_p
         lib.moegg_abi_version.argtypes, lib.moegg_abi_version.restype = [], ctypes.c_int
+        lib.moegg_set_grid_limit.argtypes, lib.moegg_set_grid_limit.restype = [ctypes.c_int], ctypes.c_int
         if lib.moegg_abi_version() != ABI_VERSION:
             raise RuntimeError(f"{lib_path} has ABI {lib.moegg_abi_version()}, these bindings "
                                f"expect {ABI_VERSION}: rebuild it with __graft_entry__.build()")
@@ -111,6 +112,10 @@ def moegg_last_error() -> str:
 
 def moegg_abi_version() -> int:
     return _load().moegg_abi_version()
+
+
+def moegg_set_grid_limit(max_workgroups: int) -> int:
+    return _load().moegg_set_grid_limit(int(max_workgroups))
 
 
 # ---- marshalling helpers ---------------------------------------------------------

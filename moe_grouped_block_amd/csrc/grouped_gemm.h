@@ -349,7 +349,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // [n0, n0 + 256).  rows is 0 (nothing to store), 128 or 256.
 struct Tile {
   int g, row0, rows, n0;
-  const uint8_t* bg;    // expert g's weights (row 0) and SFB words (row 0 of plane 0)
+  const uint8_t* bg;    // expert g's weights (row 0) and SFB bytes (row 0)
   const uint8_t* sg;
 };
 
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
                          : nullptr;
     } else {
       tl.bg = p.b + static_cast<int64_t>(tl.g) * p.n * p.row_bytes;
-      tl.sg = p.sfb ? p.sfb + static_cast<int64_t>(tl.g) * p.n * 4 : nullptr;
+      tl.sg = p.sfb ? p.sfb + static_cast<int64_t>(tl.g) * p.n * p.ksf : nullptr;
     }
     return tl;
   };
@@ -546,12 +546,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         const bool isA = job < S_HALF;
         const int jj = isA ? job : job - S_HALF;
         const int word = jj >> 2, rowsel = (jj & 3) * 64 + lid;
-        // word planes: word j of row r at 4 * (j * rows + r) (rows = valid_m for
-        // SFA, sfb_rows for SFB: L * N dense with row g * N + n, N discrete);
-        // step ks uses planes SW*ks .. SW*ks + SW-1
-        s.s[u] = isA ? p.sfa + (static_cast<int64_t>(word) * vm + tl.row0) * 4
-                     : tl.sg + (static_cast<int64_t>(word) * p.sfb_rows + tl.n0) * 4;
-        s.so[u] = static_cast<uint32_t>(min(rowsel, isA ? alast : blast)) * 4;
+        // row-major (rows, K/32) scale bytes: step ks takes the SW words at
+        // bytes 4 * (SW * ks + word) of each row (4-byte aligned: K/32 is a
+        // multiple of 4 * SW), rows ksf bytes apart (SFB: L * N rows dense,
+        // row g * N + n; N rows per expert discrete)
+        s.s[u] = isA ? p.sfa + static_cast<int64_t>(tl.row0) * p.ksf + 4 * word
+                     : tl.sg + static_cast<int64_t>(tl.n0) * p.ksf + 4 * word;
+        s.so[u] = static_cast<uint32_t>(min(rowsel, isA ? alast : blast)) * static_cast<uint32_t>(p.ksf);
       }
     }
     return s;
@@ -588,8 +589,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         const bool isA = job < S_HALF;
         const int jj = isA ? job : job - S_HALF;
         uint32_t* dst = (isA ? d.sa : d.sb) + (jj >> 2) * (isA ? BM : BN) + (jj & 3) * 64;
-        const int64_t plane = isA ? static_cast<int64_t>(vm) * 4 : p.sfb_rows * 4;
-        dma4(at(s.s[u] + static_cast<int64_t>(ks) * SW * plane, s.so[u]), dst);
+        dma4(at(s.s[u] + 4 * SW * ks, s.so[u]), dst);
       }
     }
   };

@@ -18,6 +18,10 @@ namespace {
 
 thread_local char g_last_error[512] = "";
 
+// Cap on the persistent workgroups of a launch (0 = none), set by
+// moegg_set_grid_limit.
+std::atomic<int> g_grid_limit{0};
+
 moegg_status fail(moegg_status st, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -199,7 +203,6 @@ moegg_status moegg_run(const moegg_problem* problem, const moegg_args* args, voi
   k.sfb = a.sfb;
   k.b_ptrs = reinterpret_cast<const uint8_t* const*>(a.b_ptrs);
   k.sfb_ptrs = a.sfb_ptrs;
-  k.sfb_rows = a.b_ptrs ? p.n : static_cast<int64_t>(p.num_groups) * p.n;
   k.po = a.padded_offsets;
   k.alpha = a.alpha;
   k.prob = a.prob;
@@ -238,7 +241,10 @@ moegg_status moegg_run(const moegg_problem* problem, const moegg_args* args, voi
                 (long long)p.valid_m, p.n);
   const int cus = device_cus();
   if (cus <= 0) return fail(MOEGG_ERROR_LAUNCH, "cannot query the device's compute units");
-  k.grid = static_cast<int32_t>(max_tiles < cus ? max_tiles : cus);
+  int64_t grid = max_tiles < cus ? max_tiles : cus;
+  const int limit = g_grid_limit.load(std::memory_order_relaxed);
+  if (limit > 0 && grid > limit) grid = limit;
+  k.grid = static_cast<int32_t>(grid);
   k.srelu_s = p.srelu_tanh_s;
   const int out = p.d_dtype == MOEGG_DT_E4M3 ? moegg::OUT_E4M3 : moegg::OUT_BF16;
   hipError_t e = moegg::launch_grouped_gemm(ab, p.act, out, k, stream);
@@ -285,5 +291,9 @@ const char* moegg_status_string(moegg_status s) {
 const char* moegg_last_error(void) { return g_last_error; }
 
 int moegg_abi_version(void) { return MOEGG_ABI_VERSION; }
+
+int moegg_set_grid_limit(int max_workgroups) {
+  return g_grid_limit.exchange(max_workgroups > 0 ? max_workgroups : 0, std::memory_order_relaxed);
+}
 
 }  // extern "C"

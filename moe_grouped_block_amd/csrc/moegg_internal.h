@@ -29,11 +29,10 @@ constexpr int kThreads = 512;
 struct KernelArgs {
   const uint8_t* a;        // (valid_m, row_bytes)
   const uint8_t* b;        // (L, n, row_bytes)
-  const uint8_t* sfa;      // (K/128, valid_m, 4): 32-bit word planes
-  const uint8_t* sfb;      // (K/128, L*n, 4)
+  const uint8_t* sfa;      // (valid_m, K/32) E8M0, row-major
+  const uint8_t* sfb;      // (L*n, K/32)
   const uint8_t* const* b_ptrs;     // discrete weights: (L) per-expert (n, row_bytes), or null
-  const uint8_t* const* sfb_ptrs;   // discrete weights: (L) per-expert (K/128, n, 4), or null
-  int64_t sfb_rows;                 // rows of one SFB word plane: L*n dense, n discrete
+  const uint8_t* const* sfb_ptrs;   // discrete weights: (L) per-expert (n, K/32), or null
   const int32_t* po;       // (L)
   const float* alpha;      // (L)
   const float* prob;       // (valid_m)
@@ -53,7 +52,7 @@ struct KernelArgs {
   int32_t k;
   int32_t n_out;
   int32_t row_bytes;       // bytes per row of A and B
-  int32_t ksf;             // scale bytes per row (K/32)
+  int32_t ksf;             // scale bytes per row (K/32, a multiple of 4 per scale word of a step)
   int32_t n_tiles;         // ceil(n / kBN)
   int32_t k_steps;         // row bytes / 128 (one 128-byte step per row)
   int32_t grid;            // persistent workgroups launched (>= 1)

@@ -1,7 +1,7 @@
 """Device-memory plumbing around the binding (torch used for allocation only).
 
 ``to_device`` uploads host arrays in the library's ABI layouts (the
-generator's logical (rows, K/32) scale arrays become word planes);
+generator's arrays already are: row-major, scales (rows, K/32));
 ``empty_outputs`` allocates the output tensors a problem writes.  Neither
 computes anything of the method.
 """
@@ -14,24 +14,10 @@ _NP2TORCH = {np.dtype(np.uint8): torch.uint8, np.dtype(np.uint16): torch.int16,
              np.dtype(np.int32): torch.int32, np.dtype(np.float32): torch.float32}
 
 
-def scale_planes(sf: np.ndarray) -> np.ndarray:
-    """Logical E8M0 scales (..., rows, K/32) -> the ABI's word planes
-    (K/128, rows_total, 4): byte kb of row r moves to [kb // 4, r, kb % 4]."""
-    kb = sf.shape[-1]
-    rows = int(np.prod(sf.shape[:-1]))
-    if kb % 4:
-        raise ValueError("K/32 must be a multiple of 4")
-    return np.ascontiguousarray(sf.reshape(rows, kb // 4, 4).transpose(1, 0, 2))
-
-
 def to_device(arrays: dict, device="cuda") -> dict:
-    """numpy arrays -> contiguous device tensors in the ABI's layouts: scale
-    arrays (sfa, sfb) are rearranged into word planes, bf16 bits travel as
-    int16."""
+    """numpy arrays -> contiguous device tensors (bf16 bits travel as int16)."""
     out = {}
     for k, v in arrays.items():
-        if k in ("sfa", "sfb") and v.size:
-            v = scale_planes(v)
         v = np.ascontiguousarray(v)
         t = torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v)
         out[k] = t.to(device, non_blocking=False)
@@ -41,8 +27,8 @@ def to_device(arrays: dict, device="cuda") -> dict:
 def discrete_weights(problem: dict, arrays: dict, device="cuda", seed: int = 0, null_empty=None):
     """Per-expert allocations for the discrete-weight mode.
 
-    Expert g's weights (N, row units) and, for MX operands, its scales as
-    (K/128, N, 4) word planes get allocations of their own, made in a
+    Expert g's weights (N, row units) and, for MX operands, its (N, K/32)
+    scales get allocations of their own, made in a
     shuffled expert order with spacers between them, so their addresses are
     neither contiguous nor ascending.  Returns (pointer tensors {"b_ptrs",
     "sfb_ptrs"}, list of tensors to keep alive).  Experts listed in
@@ -61,7 +47,7 @@ def discrete_weights(problem: dict, arrays: dict, device="cuda", seed: int = 0, 
         keep.append(tb)
         bptr[g] = tb.data_ptr()
         if mx:
-            ts = torch.from_numpy(scale_planes(arrays["sfb"][g])).to(device)
+            ts = torch.from_numpy(np.ascontiguousarray(arrays["sfb"][g])).to(device)
             keep.append(ts)
             sptr[g] = ts.data_ptr()
     ptrs = {"b_ptrs": torch.tensor(bptr, dtype=torch.int64, device=device)}

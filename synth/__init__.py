@@ -7,8 +7,7 @@ none of the method's own arithmetic (no GEMM, activation, gating or output
 quantisation), and it imports neither the oracle nor the GPU library; both of
 those take their inputs from here.
 
-Storage conventions (logical layouts; the C ABI stores the scale arrays as
-K-block word planes, which the device plumbing builds on upload):
+Storage conventions (the C ABI's layouts, every array row-major):
 
 * ``a``      (valid_m, K) uint8 E4M3 codes, (valid_m, K/2) uint8 packed E2M1
              pairs (low nibble = even K element), or (valid_m, K) uint16 BF16 bits

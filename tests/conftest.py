@@ -29,3 +29,26 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Totals of the rule-2 (FP8) comparisons of the run: scale bytes checked,
+    those that differ within the 1e-5 power-of-two window, and those accepted
+    only under the FP32-accumulation allowance (capped per tensor)."""
+    try:
+        from parity_util import RULE2_LOG
+    except ImportError:
+        return
+    if not RULE2_LOG:
+        return
+    blocks = sum(s["scale_blocks"] for _, s in RULE2_LOG)
+    mism = sum(s["scale_boundary_mismatch"] for _, s in RULE2_LOG)
+    widened = sum(s["scale_acc_allowance"] for _, s in RULE2_LOG)
+    beyond = sum(s["beyond_1ulp"] for _, s in RULE2_LOG)
+    elems = sum(s["elements"] for _, s in RULE2_LOG)
+    worst = max(RULE2_LOG, key=lambda x: x[1]["scale_acc_allowance"] / max(x[1]["scale_blocks"], 1))
+    terminalreporter.write_line(
+        f"rule 2 over {len(RULE2_LOG)} FP8 tensors: {blocks} E8M0 scale bytes, {mism} differ by one at a "
+        f"power-of-two boundary, {widened} of them only inside the FP32-accumulation allowance "
+        f"(largest share {worst[1]['scale_acc_allowance']}/{worst[1]['scale_blocks']} in {worst[0]}); "
+        f"{beyond} of {elems} codes beyond one E4M3 ULP")

@@ -5,7 +5,12 @@ Rule 1 (BF16 C / D / dC, amax, dprob): per expert group,
 Rule 2 (E4M3 D / D_col): >= 99.9 % of elements within 1 E4M3 ULP of the
 oracle's code; E8M0 scale bytes bit-exact except for blocks whose
 norm_const * amax / 448 (float32) lies within 1e-5 relative of a power of two,
-where the two sides may round to neighbouring exponents.
+where the two sides may round to neighbouring exponents.  Where a caller
+passes the accumulation bound (acc_error_bound), that window is widened per
+block by the relative error the FP32 accumulation can put into the block's
+amax; the scale bytes that differ only inside the widened part are counted
+(`scale_acc_allowance` in the returned stats) and may not exceed
+ACC_ALLOW_FRAC of the blocks (at least one block).
 """
 from __future__ import annotations
 
@@ -15,8 +20,12 @@ from oracle import formats as F
 from oracle import grouped as G
 
 RULE1_TOL = 1e-2
+# every rule-2 comparison of this process: (what, stats), summarised at the
+# end of a pytest run (conftest.py)
+RULE2_LOG = []
 RULE2_FRAC = 1e-3
 BOUNDARY_REL = 1e-5
+ACC_ALLOW_FRAC = 5e-4      # cap on scale bytes accepted only by the accumulation allowance
 
 
 def rule1(gpu, ref, grp, what=""):
@@ -154,10 +163,16 @@ def rule2(gpu_codes, gpu_sf, ref_d64, nc, axis, what="", rel_bound=None):
             tol = BOUNDARY_REL + np.where(amax > 0, err / amax, 0.0)
     gpu_sf = np.asarray(gpu_sf)
     mism = gpu_sf != ref_sf
-    allowed = near_power_of_two(sf32, tol) & (np.abs(gpu_sf.astype(int) - ref_sf.astype(int)) == 1)
+    one_apart = np.abs(gpu_sf.astype(int) - ref_sf.astype(int)) == 1
+    allowed = near_power_of_two(sf32, tol) & one_apart
     bad_sf = mism & ~allowed
     assert not bad_sf.any(), (f"{what}: {int(bad_sf.sum())} scale bytes differ away from a "
                               f"power-of-two boundary, e.g. at {np.argwhere(bad_sf)[:5].tolist()}")
+    # accepted only because of the accumulation allowance (outside the 1e-5 window)
+    widened = int((mism & allowed & ~near_power_of_two(sf32, BOUNDARY_REL)).sum())
+    cap = max(1, int(ACC_ALLOW_FRAC * mism.size))
+    assert widened <= cap, (f"{what}: {widened} of {mism.size} scale bytes pass only under the FP32 "
+                            f"accumulation allowance (cap {cap})")
     same = ~sf_bcast(mism)
     ulp = np.abs(_ordinal(gpu_codes) - _ordinal(ref_codes))
     over = (ulp > 1) & same
@@ -174,8 +189,10 @@ def rule2(gpu_codes, gpu_sf, ref_d64, nc, axis, what="", rel_bound=None):
     frac = n_over / over.size if over.size else 0.0
     assert frac <= RULE2_FRAC, (f"{what}: {n_over}/{over.size} elements beyond 1 E4M3 ULP "
                                 f"(e.g. {np.argwhere(over)[:5].tolist()})")
-    return dict(elements=int(over.size), beyond_1ulp=n_over, exact=int((ulp == 0).sum()),
-                scale_boundary_mismatch=int(mism.sum()))
+    st = dict(elements=int(over.size), beyond_1ulp=n_over, exact=int((ulp == 0).sum()),
+              scale_boundary_mismatch=int(mism.sum()), scale_acc_allowance=widened, scale_blocks=int(mism.size))
+    RULE2_LOG.append((what, st))
+    return st
 
 
 def decode_bf16(bits):

@@ -32,7 +32,7 @@ def _declared_functions():
 def test_exports_every_declared_function():
     names = _declared_functions()
     assert {"moegg_check", "moegg_run", "moegg_check_offsets", "moegg_n_out", "moegg_status_string",
-            "moegg_last_error", "moegg_abi_version"} <= set(names)
+            "moegg_last_error", "moegg_abi_version", "moegg_set_grid_limit"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", mg.lib_path], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (moegg_[a-z_]+)\b", out))
     assert set(names) <= exported, set(names) - exported
@@ -42,7 +42,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_strings():
-    assert mg.moegg_abi_version() == 4 == mg.ABI_VERSION
+    assert mg.moegg_abi_version() == 5 == mg.ABI_VERSION
     for code, name in mg.STATUS.items():
         assert mg.moegg_status_string(code) == name
     assert mg.moegg_status_string(99) == "MOEGG_UNKNOWN_STATUS"
@@ -243,3 +243,14 @@ def test_binding_rejects_a_library_of_another_abi(tmp_path, monkeypatch):
     with pytest.raises(RuntimeError, match="rebuild"):
         mg.moegg_abi_version()
     monkeypatch.setattr(mg, "_lib", None)
+
+
+def test_grid_limit_hook_round_trips():
+    """The testing hook returns the previous cap; 0 and negative values clear it."""
+    prev = mg.moegg_set_grid_limit(3)
+    try:
+        assert mg.moegg_set_grid_limit(7) == 3
+        assert mg.moegg_set_grid_limit(-5) == 7
+        assert mg.moegg_set_grid_limit(0) == 0
+    finally:
+        mg.moegg_set_grid_limit(prev)

@@ -23,7 +23,7 @@ def test_more_than_one_gpu_is_refused():
 
 def test_algorithmic_bytes_by_hand_fc1():
     # each input read once (B and SFB of non-empty experts only), each output
-    # written once: E4M3 D and D_col (valid_m x N/2) plus both scale planes
+    # written once: E4M3 D and D_col (valid_m x N/2) plus both scale arrays
     case = synth.make_case("fc1_swiglu_l8", L=3, K=256, N=128, routing=("topk", 200, 2))
     p, a = case.problem, case.arrays
     vm, n, k, L = p["valid_m"], p["n"], p["k"], p["num_groups"]

@@ -429,18 +429,20 @@ def test_full_size_sampled(name):
     elif p["d_dtype"] == "bf16":
         d = decode_bf16(got["d"])
         assert np.all(d[pad] == 0)
-        grp = oracle.group_of_rows(case.arrays["padded_offsets"], np.arange(p["valid_m"]))
-        ref_rows = oracle.grouped_gemm(p, case.arrays, rows)
+        # every group against the oracle, one group's rows at a time: rule 1
+        # on all of D and on each group's amax (0 for an empty group)
+        po = np.asarray(case.arrays["padded_offsets"], np.int64)
+        starts = np.concatenate([[0], po[:-1]])
+        worst_d, ref_amax = 0.0, np.zeros(p["num_groups"])
         for g in range(p["num_groups"]):
-            sel = grp == g
-            if not sel.any():
-                assert got["amax"][g] == 0.0
+            if po[g] == starts[g]:
                 continue
-            mx = np.abs(d[sel]).max()           # bf16-rounded max vs fp32 amax
-            assert abs(got["amax"][g] - mx) <= mx * 2.0 ** -8, (g, got["amax"][g], mx)
-            sub = ref_rows["group"] == g
-            if sub.any():
-                assert got["amax"][g] >= np.abs(ref_rows["d"][sub]).max() * (1 - 1e-2)
+            grows = np.arange(starts[g], po[g])
+            ref_g = oracle.grouped_gemm(p, case.arrays, grows)
+            worst_d = max(worst_d, rule1(d[grows], ref_g["d"], np.full(ref_g["d"].shape, g), f"D group {g}"))
+            ref_amax[g] = ref_g["amax"][g]
+        stats["d_all_rows"] = worst_d
+        stats["amax_all_groups"] = amax_rule(got["amax"], ref_amax)
     else:
         assert np.all(F.decode_e4m3(got["d"][pad]) == 0) and np.all(got["sfd_row"][pad] == 0)
     print(f"[gpu-case] {name} stats {stats}", flush=True)

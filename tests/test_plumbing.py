@@ -1,24 +1,23 @@
-"""Host-side layout plumbing (no GPU): the word-plane scale layout the C ABI
-documents for SFA/SFB -- the byte of row r and K-block kb sits at byte offset
-4 * ((kb // 4) * rows + r) + kb % 4."""
+"""Host-side plumbing (no GPU): the generator's scale arrays are already the
+C ABI's row-major (rows, K/32) layout, so uploads keep every byte in place,
+and a discrete-weight expert's scales are its (N, K/32) slice of SFB."""
 import numpy as np
 import pytest
 
+torch = pytest.importorskip("torch")
 pl = pytest.importorskip("moe_grouped_block_amd.plumbing")
+synth = pytest.importorskip("synth")
 
 
-@pytest.mark.parametrize("shape", [(7, 16), (3, 5, 8), (1, 4)])
-def test_scale_planes_offsets(shape):
-    rng = np.random.default_rng(1)
-    sf = rng.integers(0, 255, shape, dtype=np.uint8)
-    planes = pl.scale_planes(sf).reshape(-1)
-    rows = int(np.prod(shape[:-1]))
-    logical = sf.reshape(rows, shape[-1])
-    for r in range(rows):
-        for kb in range(shape[-1]):
-            assert planes[4 * ((kb // 4) * rows + r) + kb % 4] == logical[r, kb]
-
-
-def test_scale_planes_rejects_partial_words():
-    with pytest.raises(ValueError):
-        pl.scale_planes(np.zeros((4, 6), np.uint8))
+def test_scales_upload_row_major():
+    case = synth.make_case("fc1_swiglu_l8", seed=3, name="plumb", L=3, K=512, N=128, routing=("topk", 100, 2))
+    dev = pl.to_device(case.arrays, device="cpu")
+    for k in ("sfa", "sfb"):
+        src = case.arrays[k]
+        got = dev[k].numpy()
+        assert got.shape == src.shape and np.array_equal(got, src)
+        # byte kb of row r at r * K/32 + kb
+        flat = got.reshape(-1)
+        kb = src.shape[-1]
+        r, c = 5, 7
+        assert flat[r * kb + c] == src.reshape(-1, kb)[r, c]
