@@ -1,27 +1,29 @@
 """Throughput of the grouped block-scaled GEMM + fused epilogue on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--also LIST]
-                    [--no-cpu-baseline] [--no-cold] [--no-clock]
+                    [--no-cpu-baseline] [--no-cold] [--profile-launches N]
 
 A step is one launch of the whole hot path (grouped MXFP8 GEMM, SwiGLU over
 32-column pairs, gating, FP8 row + column quantisation with E8M0 scales) over
 the FC1 + SwiGLU workload at L = 64 experts: 16384 tokens routed top-6
 uniformly (98304 routed rows, each expert padded to a multiple of 128 rows),
 K = 2048, N = 2816 (44 linear/gate pairs of 32 columns), MXFP8 E4M3 operands
-with E8M0 scales per 32 K-elements.  The same line also reports the 8-expert
-FC1 + SwiGLU workload (4096 tokens top-2) and the other workloads of
-`--also`, which run first.  Inputs are synthetic and already resident in HBM.
-Rank 0 prints one JSON line.  Per workload: the mean per launch over the
-timed window (HIP events on the launch stream around every launch) with its
-median, min and max; the mean after a 1 GiB cache flush (cold); the core
-clock sampled during a further window of launches, and the roofline fraction
-at that clock.
+with E8M0 scales per 32 K-elements, passed in the library's K-block plane
+layout (laid out on the device before the timed region).  The same line also
+reports the other workloads of `--also` (the 8-expert FC1 + SwiGLU workload,
+the other configurations, the row-major scale layout, discrete weights),
+which run first.  Inputs are synthetic and already resident in HBM.  Rank 0
+prints one JSON line.  Per workload: the mean per launch over the timed
+window (HIP events on the launch stream around every launch) with its
+median, min and max, and the mean after a 1 GiB cache flush (cold).
 
 `value` is TFLOP/s over routed rows (2 * routed * N * K per step, padding
 excluded).  `roofline` compares the kernel's achieved rate (HIP events on the
-launch stream) with the dense MXFP8 MFMA peak; `traffic` is read from the
-committed rocprofv3 counter summary when it was taken on the current kernel
-source, else null.  `cpu_baseline` is the float64 oracle on the host cores.
+launch stream) with the dense MXFP8 MFMA peak; `traffic`, the core clock
+under the kernel (and the roofline fraction at that clock) and the MFMA-busy
+fraction come from the committed rocprofv3 counter summary when it was taken
+on the current kernel source, else they are left out (traffic null).
+`cpu_baseline` is the float64 oracle on the host cores.
 """
 from __future__ import annotations
 
@@ -43,7 +45,7 @@ KERNEL_SOURCES = ["moe_grouped_block_amd/csrc/grouped_gemm.h", "moe_grouped_bloc
                   "moe_grouped_block_amd/csrc/inst_e4m3.hip", "moe_grouped_block_amd/csrc/inst_e2m1.hip",
                   "moe_grouped_block_amd/csrc/inst_bf16.hip", "moe_grouped_block_amd/csrc/inst_e5m2.hip",
                   "moe_grouped_block_amd/csrc/moegg_internal.h"]
-TRAFFIC_FILE = "profiles/grouped_gemm_fc1_swiglu_l64_traffic.md"
+PROFILE_FILE = "profiles/grouped_gemm_counters_bench_workloads.md"
 
 
 _COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
@@ -60,21 +62,22 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per launch from the committed counter summary, if it matches
-    the current kernel source and workload."""
-    path = os.path.join(ROOT, TRAFFIC_FILE)
+def read_profile(workload: str):
+    """Counter-derived figures of one workload from the committed rocprofv3
+    summary (HBM bytes per launch, the core clock while its kernel ran, the
+    MFMA-busy fraction), if that summary was taken on the current kernel
+    source; else None."""
+    path = os.path.join(ROOT, PROFILE_FILE)
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    m_work = re.search(r"workload:\s*(\S+)", text)
-    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not (m_hash and m_work and m_bytes):
+    if not m_hash or m_hash.group(1) != kernel_source_hash():
         return None
-    if m_hash.group(1) != kernel_source_hash() or m_work.group(1) != workload:
-        return None
-    return float(m_bytes.group(1))
+    for m in re.finditer(r"^workload=(\S+)((?: [a-z_]+=\S+)*)\s*$", text, re.M):
+        if m.group(1) == workload:
+            return {k: float(v) for k, v in (kv.split("=") for kv in m.group(2).split())}
+    return None
 
 
 def algorithmic_bytes(case) -> float:
@@ -122,63 +125,6 @@ def cpu_baseline(case, rows_n):
                       f"oracle pass incl. dequantise, GEMM, SwiGLU and FP8 quantisation: {dt:.1f} s"}
 
 
-class ClockSampler:
-    """Median core clock (MHz) of the GPU while a launch window runs, read
-    from the driver's metrics through amdsmi in a background thread; None
-    where amdsmi is unavailable.  Sampling only reads: it launches nothing."""
-
-    def __init__(self):
-        self.h = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            hs = amdsmi.amdsmi_get_processor_handles()
-            vis = os.environ.get("HIP_VISIBLE_DEVICES") or os.environ.get("ROCR_VISIBLE_DEVICES")
-            idx = int(vis.split(",")[0]) if vis and vis.split(",")[0].isdigit() and len(hs) > 1 else 0
-            self.amdsmi, self.h = amdsmi, hs[min(idx, len(hs) - 1)]
-            self.read()
-        except Exception as e:   # no driver access: report no clock
-            self.h, self.err = None, repr(e)[:200]
-
-    def read(self):
-        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
-        v = m.get("current_gfxclks")
-        if isinstance(v, (list, tuple)):
-            v = [x for x in v if isinstance(x, (int, float)) and 0 < x < 10000]
-            if v:
-                return float(sum(v)) / len(v)
-        for key in ("current_gfxclk", "average_gfxclk_frequency"):
-            x = m.get(key)
-            if isinstance(x, (int, float)) and 0 < x < 10000:
-                return float(x)
-        return None
-
-    def during(self, fn):
-        """Run fn() while sampling; return (fn's result, median MHz or None, samples)."""
-        if self.h is None:
-            return fn(), None, 0
-        import threading
-        vals, stop = [], threading.Event()
-
-        def loop():
-            while not stop.is_set():
-                try:
-                    x = self.read()
-                    if x:
-                        vals.append(x)
-                except Exception:
-                    pass
-                time.sleep(0.002)
-        th = threading.Thread(target=loop, daemon=True)
-        th.start()
-        try:
-            r = fn()
-        finally:
-            stop.set()
-            th.join()
-        return r, (float(sorted(vals)[len(vals) // 2]) if vals else None), len(vals)
-
-
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,14 +133,18 @@ def main():
                     help="untimed launches of the headline before its timed window")
     ap.add_argument("--workload", default="fc1_swiglu_l64")
     ap.add_argument("--also", default="fc1_swiglu_l8,quant_gating_l4,fc2_gating_l64_zipf,srelu_tanh_fp4_l32,"
-                    "dswiglu_bf16_l64,fc1_swiglu_l64:discrete,dswiglu_mxfp8_l64,dsrelu_mxfp8_l32,"
-                    "fc1_geglu_e5m2_l8,dgeglu_mxfp8_l64",
-                    help="comma list of extra workloads to time (before the headline); a ':discrete' suffix "
-                         "passes the expert weights as per-expert allocations (b_ptrs / sfb_ptrs)")
+                    "dswiglu_bf16_l64,fc1_swiglu_l64:discrete,fc1_swiglu_l64:rowmajor,dswiglu_mxfp8_l64,"
+                    "dsrelu_mxfp8_l32,fc1_geglu_e5m2_l8,dgeglu_mxfp8_l64",
+                    help="comma list of extra workloads to time (before the headline).  Scales are passed as "
+                         "K-block planes (sf_layout KPLANES) unless a ':rowmajor' suffix asks for the row-major "
+                         "(rows, K/32) layout; a ':discrete' suffix passes the expert weights as per-expert "
+                         "allocations (b_ptrs / sfb_ptrs)")
     ap.add_argument("--cpu-rows", type=int, default=40960, help="rows of the oracle CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true", help="skip the launches after an L2/MALL flush")
-    ap.add_argument("--no-clock", action="store_true", help="skip the clock-sampling window")
+    ap.add_argument("--profile-launches", type=int, default=0,
+                    help="profiling mode: launch every workload (the --also list, then --workload) this "
+                         "many times back to back, untimed, and print the order (for rocprofv3 passes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (reference for HBM counters)")
     args = ap.parse_args()
@@ -223,22 +173,24 @@ def main():
     if not os.path.exists(mg.lib_path):
         from moe_grouped_block_amd import build
         build.build()
-    clock = None if args.no_clock else ClockSampler()
 
-    def measure(name, steps, warmup, cold):
-        base, _, mode = name.partition(":")
+    def prepare(name):
+        """Upload one workload (inputs resident in HBM, scales laid out as the
+        workload's mode asks) and return (case, launch function, tensors)."""
+        base, *modes = name.split(":")
+        if set(modes) - {"discrete", "rowmajor"}:
+            raise SystemExit(f"unknown workload mode in {name!r}")
         case = synth.make_case(base)
-        p = case.problem
-        dev = pl.to_device(case.arrays)
+        layout = "row_major" if "rowmajor" in modes else "kplanes"
+        p = dict(case.problem, sf_layout=layout)
+        dev = pl.to_device(case.arrays, sf_layout=layout, k=p["k"])
         outs = pl.empty_outputs(p)
         keep = None
-        if mode == "discrete":
-            ptrs, keep = pl.discrete_weights(p, case.arrays, seed=case.seed)
+        if "discrete" in modes:
+            ptrs, keep = pl.discrete_weights(p, case.arrays, seed=case.seed, sf_layout=layout)
             del dev["b"]
             dev.pop("sfb", None)
             tensors = {**pl.inputs_for(p, dev, discrete=ptrs), **outs}
-        elif mode:
-            raise SystemExit(f"unknown workload mode {mode!r}")
         else:
             tensors = {**pl.inputs_for(p, dev), **outs}
         stream = torch.cuda.current_stream()
@@ -249,7 +201,24 @@ def main():
             st = mg.moegg_run(prob_s, args_s, handle)
             if st != 0:
                 raise mg.MoeggError(st, mg.moegg_last_error())
+        torch.cuda.synchronize()
+        return case, step, (dev, outs, tensors, keep)
 
+    names = [x for x in args.also.split(",") if x] + [args.workload]
+    if args.profile_launches > 0:
+        for name in names:
+            _, step, held = prepare(name)
+            for _ in range(args.profile_launches):
+                step()
+            torch.cuda.synchronize()
+            del held
+            torch.cuda.empty_cache()
+        print(json.dumps({"profile_order": names, "launches": args.profile_launches}), flush=True)
+        return
+
+    def measure(name, steps, warmup, cold):
+        case, step, held = prepare(name)
+        stream = torch.cuda.current_stream()
         for _ in range(warmup):
             step()
         torch.cuda.synchronize()
@@ -265,18 +234,8 @@ def main():
         wall = time.perf_counter() - t0
         per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
         ms = ev[0].elapsed_time(ev[steps]) / steps
-        res = {"case": case, "ms": ms, "wall": wall, "tflops": case.flops / (ms * 1e-3) / 1e12,
+        res = {"case": case, "name": name, "ms": ms, "wall": wall, "tflops": case.flops / (ms * 1e-3) / 1e12,
                "ms_median": per[len(per) // 2], "ms_min": per[0], "ms_max": per[-1]}
-        if clock is not None:
-            # a window of back-to-back launches (at least 30 ms) with the clock sampled
-            nclk = max(steps, int(30.0 / max(ms, 1e-3)) + 1)
-
-            def window():
-                for _ in range(nclk):
-                    step()
-                torch.cuda.synchronize()
-            _, mhz, nsamp = clock.during(window)
-            res["sclk_mhz"], res["sclk_samples"] = mhz, nsamp
         if cold:
             flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB > L2 + MALL
             cl = []
@@ -291,7 +250,7 @@ def main():
             res["cold_ms"] = sum(cl) / len(cl)
             res["cold_ms_median"] = sorted(cl)[len(cl) // 2]
             del flush
-        del dev, outs, tensors, keep
+        del held
         torch.cuda.empty_cache()
         return res
 
@@ -311,11 +270,18 @@ def main():
              "frac_roofline": round(max(t_m, t_h) / (r["ms"] * 1e-3), 4),
              "valid_m": c.problem["valid_m"], "routed_rows": c.routed_rows,
              "experts": c.problem["num_groups"]}
-        if r.get("sclk_mhz"):
-            # the MFMA roofline scaled to the measured clock (the HBM one does not move)
-            t_m_clk = t_m * NOMINAL_SCLK_MHZ / r["sclk_mhz"]
-            d["sclk_mhz"] = round(r["sclk_mhz"], 1)
+        prof = read_profile(r["name"])
+        if prof and prof.get("sclk_mhz"):
+            # the core clock under this kernel (rocprofv3 counters: GPU cycles per
+            # XCD over the dispatch time) and the MFMA roofline scaled to it (the
+            # HBM roofline does not move with the core clock)
+            t_m_clk = t_m * NOMINAL_SCLK_MHZ / prof["sclk_mhz"]
+            d["sclk_mhz"] = round(prof["sclk_mhz"], 1)
             d["frac_roofline_at_sclk"] = round(max(t_m_clk, t_h) / (r["ms"] * 1e-3), 4)
+        if prof and prof.get("mfma_busy_frac"):
+            d["mfma_busy_frac"] = prof["mfma_busy_frac"]
+        if prof and prof.get("hbm_bytes_per_launch"):
+            d["traffic"] = prof["hbm_bytes_per_launch"]
         if "cold_ms" in r:
             d["cold_ms_per_launch"] = round(r["cold_ms"], 5)
             d["cold_ms_median"] = round(r["cold_ms_median"], 5)
@@ -327,7 +293,7 @@ def main():
     # 40 launches (25 ms), so the headline's window then measures the
     # sustained state that a long training run sees.
     also = {}
-    for name in [x for x in args.also.split(",") if x]:
+    for name in names[:-1]:
         r = measure(name, max(args.steps, 20), max(args.warmup, 10), not args.no_cold)
         also[name] = summary(r)
     main_res = measure(args.workload, args.steps, args.warmup, not args.no_cold)
@@ -345,7 +311,7 @@ def main():
     else:
         achieved, pk, unit = alg_bytes / (ms * 1e-3) / 1e9, HBM_GBS, "GB/s"
     roof = {"bound": bound, "achieved": round(achieved, 2), "peak": pk, "unit": unit,
-            "frac": round(achieved / pk, 4), "traffic": read_traffic(args.workload),
+            "frac": round(achieved / pk, 4), "traffic": hs.get("traffic"),
             "algorithmic_bytes": alg_bytes, "algorithmic_flops": case.flops}
     if "frac_roofline_at_sclk" in hs:
         roof["sclk_mhz"] = hs["sclk_mhz"]
@@ -365,11 +331,10 @@ def main():
         "hbm_gbs_algorithmic": hs["hbm_gbs_algorithmic"],
         "wall_s_timed": round(wall, 4),
     }
-    for k in ("sclk_mhz", "cold_ms_per_launch", "cold_ms_median", "cold_frac_roofline"):
+    line["config"]["sf_layout"] = "kplanes"
+    for k in ("sclk_mhz", "mfma_busy_frac", "cold_ms_per_launch", "cold_ms_median", "cold_frac_roofline"):
         if k in hs:
             line[k] = hs[k]
-    if clock is not None and clock.h is None:
-        line["sclk_unavailable"] = getattr(clock, "err", "")
     if also:
         line["also"] = also
     if not args.no_cpu_baseline:

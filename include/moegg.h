@@ -30,11 +30,20 @@
  *           only; "Grouped GEMM + Quant (SM100)", §Shapes, SFA)
  *   SFB     (L, N, K/32) E8M0 bytes, row-major: expert g's row n at
  *           (g * N + n) * K/32 ("Grouped GEMM + Quant (SM100)", §Shapes, SFB)
+ *   With sf_layout = MOEGG_SF_KPLANES the same bytes come instead as K-block
+ *   planes of 32-bit words, (K/128, rows, 4): byte kb of row r at
+ *   4 * ((kb / 4) * rows + r) + kb % 4 (rows = valid_m for SFA, L * N for a
+ *   dense SFB, N for one expert's discrete SFB).  A plane holds the scales of
+ *   128 consecutive K elements of every row, so those of a row tile for one
+ *   K-step are contiguous and the kernel fetches them in whole cache lines
+ *   (the pages' own kernels likewise take scale factors in a tiled layout of
+ *   their own, §Shapes and Divisibility).  moegg_sf_to_kplanes converts.
  *   Discrete weights (the pages' b_ptrs / sfb_ptrs mode, "Grouped GEMM +
  *   sReLU (SM100)", §Discrete-weight wrapper): instead of B and SFB the
  *   caller passes device arrays of L device pointers; b_ptrs[g] points to
  *   expert g's (N, K) weights in B's encoding and sfb_ptrs[g] (MX only) to
- *   its (N, K/32) row-major scales.  Each pointer must be 16-byte aligned
+ *   its (N, K/32) row-major scales (or (K/128, N, 4) planes with
+ *   MOEGG_SF_KPLANES).  Each pointer must be 16-byte aligned
  *   (the kernel ignores its low 4 bits); entries of experts with no rows are
  *   never read.
  *   padded_offsets (L) int32, cumulative group ends; padded_offsets[L-1] ==
@@ -97,6 +106,11 @@ typedef enum moegg_dtype {
   MOEGG_DT_E5M2 = 4    /* OCP E5M2: A/B operands (MXFP8, "Grouped GEMM + Quant", §Data Types) */
 } moegg_dtype;
 
+typedef enum moegg_sf_layout {
+  MOEGG_SF_ROW_MAJOR = 0, /* SFA (valid_m, K/32), SFB (L, N, K/32): the default */
+  MOEGG_SF_KPLANES = 1    /* SFA (K/128, valid_m, 4), SFB (K/128, L*N, 4) 32-bit word planes */
+} moegg_sf_layout;
+
 typedef enum moegg_act {
   MOEGG_ACT_NONE = 0,    /* D = prob * C            ("Grouped GEMM + Quant", Step 2)        */
   MOEGG_ACT_SWIGLU = 1,  /* D = prob * X_b * swish(G_b), pairs [X_b|G_b] of 32 columns
@@ -147,14 +161,15 @@ typedef struct moegg_problem {
   float linear_offset;  /* offset added to the (clamped) up branch                       */
   float glu_clamp_min;  /* lower clamp (GeGLU: both halves; dGeGLU: up)                   */
   float glu_clamp_max;  /* upper clamp (both halves, both directions)                     */
+  int32_t sf_layout;    /* moegg_sf_layout of SFA / SFB (MX operands; 0 = row-major)       */
 } moegg_problem;
 
 /* Tensor pointers (device memory, caller-owned).  NULL where not used. */
 typedef struct moegg_args {
   const void* a;
   const void* b;
-  const uint8_t* sfa;            /* MX operands only; (valid_m, K/32) E8M0, row-major */
-  const uint8_t* sfb;            /* MX operands only; (L, N, K/32) E8M0, row-major */
+  const uint8_t* sfa;            /* MX operands only; (valid_m, K/32) E8M0 (or planes, sf_layout) */
+  const uint8_t* sfb;            /* MX operands only; (L, N, K/32) E8M0 (or planes, sf_layout) */
   const int32_t* padded_offsets;
   const float* alpha;
   const float* prob;             /* required ("prob ... Required", Quant page) */
@@ -200,6 +215,19 @@ moegg_status moegg_run(const moegg_problem* problem, const moegg_args* args, voi
  * MOEGG_ERROR_INVALID_VALUE (MOEGG_ERROR_LAUNCH if the copy fails). */
 moegg_status moegg_check_offsets(const moegg_problem* problem, const int32_t* padded_offsets,
                                  void* stream);
+
+/* Lay out E8M0 scale bytes given row-major as (rows, K/32) (SFA with rows =
+ * valid_m, a dense SFB with rows = L * N, one expert's SFB with rows = N)
+ * as the K-block word planes (K/128, rows, 4) that MOEGG_SF_KPLANES reads:
+ * dst[4 * ((kb / 4) * rows + r) + kb % 4] = src[r * K/32 + kb].  The layout is
+ * this library's; the scale values follow "Grouped GEMM + Quant (SM100)",
+ * §Shapes (SFA, SFB: one E8M0 byte per 32 K elements).  Enqueued on `stream`
+ * with no allocation and no synchronisation (capturable).  k must be a
+ * positive multiple of 128, rows >= 0 (0: nothing enqueued); src and dst are
+ * caller-owned device buffers of rows * K/32 bytes, 16-byte aligned, not
+ * overlapping.  Returns MOEGG_OK, MOEGG_ERROR_INVALID_VALUE,
+ * MOEGG_ERROR_MISALIGNED or MOEGG_ERROR_LAUNCH. */
+moegg_status moegg_sf_to_kplanes(const uint8_t* src, uint8_t* dst, int64_t rows, int32_t k, void* stream);
 
 /* Output width N_out for a problem (N/2 SwiGLU / GeGLU, 2N dSwiGLU / dGeGLU, else N);
  * -1 if invalid act. */

@@ -6,7 +6,8 @@ The C ABI (include/moegg.h) is mirrored name for name:
     moegg_run(problem, args, stream) -> status
     moegg_check_offsets(problem, padded_offsets_ptr, stream) -> status
     moegg_n_out(problem), moegg_status_string(status), moegg_last_error(),
-    moegg_abi_version(), moegg_set_grid_limit(max_workgroups)
+    moegg_abi_version(), moegg_set_grid_limit(max_workgroups),
+    moegg_sf_to_kplanes(src, dst, rows, k, stream)
 
 plus ``make_problem`` / ``make_args`` (fill the C structs from a problem dict
 and torch tensors' device pointers) and ``run`` / ``check`` (build the structs,
@@ -21,7 +22,8 @@ import os
 
 __all__ = ["MoeggError", "moegg_check", "moegg_run", "moegg_check_offsets", "moegg_n_out",
            "moegg_status_string", "moegg_last_error", "moegg_abi_version", "moegg_set_grid_limit", "make_problem",
-           "make_args", "run", "check", "lib_path", "ABI_VERSION", "DTYPES", "ACTS", "STATUS"]
+           "make_args", "run", "check", "lib_path", "ABI_VERSION", "DTYPES", "ACTS", "STATUS", "SF_LAYOUTS",
+           "moegg_sf_to_kplanes", "sf_to_kplanes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libmoegg.so")
@@ -29,6 +31,7 @@ lib_path = os.path.join(_HERE, "libmoegg.so")
 ABI_VERSION = 5   # MOEGG_ABI_VERSION of the structs below
 DTYPES = {None: 0, "none": 0, "e4m3": 1, "e2m1x2": 2, "bf16": 3, "e5m2": 4}
 ACTS = {"none": 0, "swiglu": 1, "srelu": 2, "dswiglu": 3, "dsrelu": 4, "geglu": 5, "dgeglu": 6}
+SF_LAYOUTS = {"row_major": 0, "kplanes": 1}
 STATUS = {0: "MOEGG_OK", 1: "MOEGG_ERROR_INVALID_VALUE", 2: "MOEGG_ERROR_MISALIGNED",
           3: "MOEGG_ERROR_NOT_SUPPORTED", 4: "MOEGG_ERROR_LAUNCH"}
 
@@ -43,7 +46,8 @@ class moegg_problem(ctypes.Structure):
                 ("d_dtype", ctypes.c_int32), ("act", ctypes.c_int32),
                 ("srelu_tanh_s", ctypes.c_float), ("glu_gamma", ctypes.c_float),
                 ("geglu_alpha", ctypes.c_float), ("linear_offset", ctypes.c_float),
-                ("glu_clamp_min", ctypes.c_float), ("glu_clamp_max", ctypes.c_float)]
+                ("glu_clamp_min", ctypes.c_float), ("glu_clamp_max", ctypes.c_float),
+                ("sf_layout", ctypes.c_int32)]
 
 
 class moegg_args(ctypes.Structure):
@@ -77,6 +81,9 @@ def _load():
         lib.moegg_last_error.argtypes, lib.moegg_last_error.restype = [], ctypes.c_char_p
         lib.moegg_abi_version.argtypes, lib.moegg_abi_version.restype = [], ctypes.c_int
         lib.moegg_set_grid_limit.argtypes, lib.moegg_set_grid_limit.restype = [ctypes.c_int], ctypes.c_int
+        lib.moegg_sf_to_kplanes.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                            ctypes.c_void_p]
+        lib.moegg_sf_to_kplanes.restype = ctypes.c_int
         if lib.moegg_abi_version() != ABI_VERSION:
             raise RuntimeError(f"{lib_path} has ABI {lib.moegg_abi_version()}, these bindings "
                                f"expect {ABI_VERSION}: rebuild it with __graft_entry__.build()")
@@ -118,6 +125,10 @@ def moegg_set_grid_limit(max_workgroups: int) -> int:
     return _load().moegg_set_grid_limit(int(max_workgroups))
 
 
+def moegg_sf_to_kplanes(src_ptr: int, dst_ptr: int, rows: int, k: int, stream: int | None) -> int:
+    return _load().moegg_sf_to_kplanes(src_ptr, dst_ptr, int(rows), int(k), stream or None)
+
+
 # ---- marshalling helpers ---------------------------------------------------------
 
 def _code(table: dict, v) -> int:
@@ -136,7 +147,8 @@ def make_problem(p: dict) -> moegg_problem:
                          geglu_alpha=float(p.get("geglu_alpha", 1.702)),
                          linear_offset=float(p.get("linear_offset", 1.0)),
                          glu_clamp_min=float(p.get("glu_clamp_min", float("-inf"))),
-                         glu_clamp_max=float(p.get("glu_clamp_max", float("inf"))))
+                         glu_clamp_max=float(p.get("glu_clamp_max", float("inf"))),
+                         sf_layout=_code(SF_LAYOUTS, p.get("sf_layout", 0)))
 
 
 def _ptr(t) -> int | None:
@@ -166,6 +178,13 @@ def _stream_handle(stream):
 
 def check(problem: dict, tensors: dict) -> None:
     st = moegg_check(make_problem(problem), make_args(tensors))
+    if st != 0:
+        raise MoeggError(st, moegg_last_error())
+
+
+def sf_to_kplanes(src, dst, rows: int, k: int, stream=None) -> None:
+    """Enqueue the row-major -> K-block-plane scale conversion (device tensors or pointers)."""
+    st = moegg_sf_to_kplanes(_ptr(src), _ptr(dst), rows, k, _stream_handle(stream))
     if st != 0:
         raise MoeggError(st, moegg_last_error())
 

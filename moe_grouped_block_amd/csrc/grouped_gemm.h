@@ -485,7 +485,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
                          : nullptr;
     } else {
       tl.bg = p.b + static_cast<int64_t>(tl.g) * p.n * p.row_bytes;
-      tl.sg = p.sfb ? p.sfb + static_cast<int64_t>(tl.g) * p.n * p.ksf : nullptr;
+      tl.sg = p.sfb ? p.sfb + static_cast<int64_t>(tl.g) * p.n * p.sf_row_b : nullptr;
     }
     return tl;
   };
@@ -546,13 +546,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         const bool isA = job < S_HALF;
         const int jj = isA ? job : job - S_HALF;
         const int word = jj >> 2, rowsel = (jj & 3) * 64 + lid;
-        // row-major (rows, K/32) scale bytes: step ks takes the SW words at
-        // bytes 4 * (SW * ks + word) of each row (4-byte aligned: K/32 is a
-        // multiple of 4 * SW), rows ksf bytes apart (SFB: L * N rows dense,
-        // row g * N + n; N rows per expert discrete)
-        s.s[u] = isA ? p.sfa + static_cast<int64_t>(tl.row0) * p.ksf + 4 * word
-                     : tl.sg + static_cast<int64_t>(tl.n0) * p.ksf + 4 * word;
-        s.so[u] = static_cast<uint32_t>(min(rowsel, isA ? alast : blast)) * static_cast<uint32_t>(p.ksf);
+        // scale word `word` of K-step ks for row r sits at
+        //   r * sf_row + (SW * ks + word) * sf_word
+        // (row-major (rows, K/32): sf_row = K/32, sf_word = 4; K-block planes
+        // (K/128, rows, 4): sf_row = 4, sf_word = 4 * rows; SFB rows: L * N
+        // dense with row g * N + n, N per expert discrete)
+        s.s[u] = isA ? p.sfa + static_cast<int64_t>(tl.row0) * p.sf_row_a + static_cast<int64_t>(word) * p.sf_word_a
+                     : tl.sg + static_cast<int64_t>(tl.n0) * p.sf_row_b + static_cast<int64_t>(word) * p.sf_word_b;
+        s.so[u] = static_cast<uint32_t>(min(rowsel, isA ? alast : blast)) * static_cast<uint32_t>(isA ? p.sf_row_a : p.sf_row_b);
       }
     }
     return s;
@@ -589,7 +590,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         const bool isA = job < S_HALF;
         const int jj = isA ? job : job - S_HALF;
         uint32_t* dst = (isA ? d.sa : d.sb) + (jj >> 2) * (isA ? BM : BN) + (jj & 3) * 64;
-        dma4(at(s.s[u] + 4 * SW * ks, s.so[u]), dst);
+        dma4(at(s.s[u] + static_cast<int64_t>(SW * ks) * (isA ? p.sf_word_a : p.sf_word_b), s.so[u]), dst);
       }
     }
   };

@@ -92,6 +92,8 @@ moegg_status check_impl(const moegg_problem* pp, const moegg_args* ap) {
     return fail(MOEGG_ERROR_INVALID_VALUE, "d_dtype=%d must be BF16 or E4M3", p.d_dtype);
   if (p.c_dtype != MOEGG_DT_NONE && p.c_dtype != MOEGG_DT_BF16)
     return fail(MOEGG_ERROR_INVALID_VALUE, "c_dtype=%d must be NONE or BF16", p.c_dtype);
+  if (p.sf_layout != MOEGG_SF_ROW_MAJOR && p.sf_layout != MOEGG_SF_KPLANES)
+    return fail(MOEGG_ERROR_INVALID_VALUE, "sf_layout=%d must be ROW_MAJOR or KPLANES", p.sf_layout);
   if (!(p.srelu_tanh_s >= 0.0f) || !std::isfinite(p.srelu_tanh_s))
     return fail(MOEGG_ERROR_INVALID_VALUE, "srelu_tanh_s must be finite and >= 0");
   if ((p.act == MOEGG_ACT_SWIGLU || p.act == MOEGG_ACT_GEGLU) && p.n % 64 != 0)
@@ -231,6 +233,14 @@ moegg_status moegg_run(const moegg_problem* problem, const moegg_args* args, voi
   k.glu_clamp_min = p.glu_clamp_min;
   k.glu_clamp_max = p.glu_clamp_max;
   k.ksf = p.k / 32;
+  if (p.sf_layout == MOEGG_SF_KPLANES) {
+    k.sf_row_a = k.sf_row_b = 4;
+    k.sf_word_a = 4 * p.valid_m;
+    k.sf_word_b = 4 * (a.b_ptrs ? static_cast<int64_t>(p.n) : static_cast<int64_t>(p.num_groups) * p.n);
+  } else {
+    k.sf_row_a = k.sf_row_b = k.ksf;
+    k.sf_word_a = k.sf_word_b = 4;
+  }
   k.k_steps = k.row_bytes / 128;
   k.n_tiles = (p.n + moegg::kBN - 1) / moegg::kBN;
   // persistent grid: one workgroup per CU, never more than there are tiles
@@ -271,6 +281,26 @@ moegg_status moegg_check_offsets(const moegg_problem* problem, const int32_t* po
   }
   if (prev != p.valid_m)
     return fail(MOEGG_ERROR_INVALID_VALUE, "padded_offsets[L-1]=%lld != valid_m=%lld", (long long)prev, (long long)p.valid_m);
+  g_last_error[0] = '\0';
+  return MOEGG_OK;
+}
+
+moegg_status moegg_sf_to_kplanes(const uint8_t* src, uint8_t* dst, int64_t rows, int32_t k, void* stream_) {
+  if (rows < 0 || k <= 0 || k % 128 != 0)
+    return fail(MOEGG_ERROR_INVALID_VALUE, "rows=%lld k=%d: rows >= 0 and k a positive multiple of 128 needed",
+                (long long)rows, k);
+  if (k / 128 > 65535) return fail(MOEGG_ERROR_INVALID_VALUE, "k=%d too large", k);
+  if (rows == 0) {
+    g_last_error[0] = '\0';
+    return MOEGG_OK;
+  }
+  if (!src || !dst) return fail(MOEGG_ERROR_INVALID_VALUE, "src and dst must be non-NULL");
+  if (!aligned(src, 16) || !aligned(dst, 16)) return fail(MOEGG_ERROR_MISALIGNED, "src/dst not 16-byte aligned");
+  const uintptr_t bytes = static_cast<uintptr_t>(rows) * (k / 32);
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(MOEGG_ERROR_INVALID_VALUE, "src and dst overlap");
+  hipError_t e = moegg::launch_sf_kplanes(src, dst, rows, k / 128, reinterpret_cast<hipStream_t>(stream_));
+  if (e != hipSuccess) return fail(MOEGG_ERROR_LAUNCH, "scale layout kernel: %s", hipGetErrorString(e));
   g_last_error[0] = '\0';
   return MOEGG_OK;
 }

@@ -29,10 +29,13 @@ constexpr int kThreads = 512;
 struct KernelArgs {
   const uint8_t* a;        // (valid_m, row_bytes)
   const uint8_t* b;        // (L, n, row_bytes)
-  const uint8_t* sfa;      // (valid_m, K/32) E8M0, row-major
-  const uint8_t* sfb;      // (L*n, K/32)
+  const uint8_t* sfa;      // E8M0: (valid_m, K/32) row-major or (K/128, valid_m, 4) planes
+  const uint8_t* sfb;      // (L*n, K/32) or (K/128, L*n, 4)
   const uint8_t* const* b_ptrs;     // discrete weights: (L) per-expert (n, row_bytes), or null
-  const uint8_t* const* sfb_ptrs;   // discrete weights: (L) per-expert (n, K/32), or null
+  const uint8_t* const* sfb_ptrs;   // discrete weights: (L) per-expert (n, K/32) or (K/128, n, 4), or null
+  // scale word w (4 bytes: 128 K elements) of row r at r * sf_row + w * sf_word
+  int64_t sf_word_a, sf_word_b;
+  int32_t sf_row_a, sf_row_b;
   const int32_t* po;       // (L)
   const float* alpha;      // (L)
   const float* prob;       // (valid_m)
@@ -73,6 +76,9 @@ hipError_t launch_e5m2(int act, int out, const KernelArgs& args, hipStream_t str
 // Launch the grouped GEMM kernel instance for (ab, act, out).  Returns the
 // HIP error of the launch (hipSuccess if enqueued).
 hipError_t launch_grouped_gemm(int ab, int act, int out, const KernelArgs& args, hipStream_t stream);
+
+// Row-major (rows, words) 32-bit scale words -> (words, rows) planes.
+hipError_t launch_sf_kplanes(const uint8_t* src, uint8_t* dst, int64_t rows, int words, hipStream_t stream);
 
 // Zero `count` floats with a fill kernel (usable under stream capture).
 hipError_t launch_fill_zero(float* ptr, int count, hipStream_t stream);

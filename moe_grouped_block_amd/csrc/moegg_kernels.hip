@@ -1,5 +1,6 @@
 // Kernel dispatch of libmoegg: routes a call to the instances of its operand
-// family (inst_*.hip, one translation unit each) and the amax fill kernel.
+// family (inst_*.hip, one translation unit each), the amax fill kernel and
+// the scale-layout conversion.
 #include <hip/hip_runtime.h>
 
 #include "moegg_internal.h"
@@ -12,7 +13,26 @@ __global__ void fill_zero_kernel(float* ptr, int count) {
   if (i < count) ptr[i] = 0.0f;
 }
 
+// One 32-bit scale word per thread: word w (128 K elements) of row r moves
+// from r * words + w (row-major) to w * rows + r (K-block planes).  Threads
+// run along the rows of one plane (blockIdx.y), so the writes are contiguous.
+__global__ void sf_kplanes_kernel(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst, int64_t rows,
+                                  int words) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int w = static_cast<int>(blockIdx.y);
+  if (r < rows) dst[static_cast<int64_t>(w) * rows + r] = src[r * words + w];
+}
+
 }  // namespace
+
+hipError_t launch_sf_kplanes(const uint8_t* src, uint8_t* dst, int64_t rows, int words, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t bx = (rows + 255) / 256;
+  if (bx > 0x7FFFFFFF || words <= 0 || words > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sf_kplanes_kernel, dim3(static_cast<unsigned>(bx), static_cast<unsigned>(words)), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(src), reinterpret_cast<uint32_t*>(dst), rows, words);
+  return hipGetLastError();
+}
 
 hipError_t launch_grouped_gemm(int ab, int act, int out, const KernelArgs& a, hipStream_t s) {
   if (a.grid <= 0) return hipErrorInvalidValue;

@@ -14,21 +14,37 @@ _NP2TORCH = {np.dtype(np.uint8): torch.uint8, np.dtype(np.uint16): torch.int16,
              np.dtype(np.int32): torch.int32, np.dtype(np.float32): torch.float32}
 
 
-def to_device(arrays: dict, device="cuda") -> dict:
-    """numpy arrays -> contiguous device tensors (bf16 bits travel as int16)."""
+def _kplanes(t: torch.Tensor, k: int) -> torch.Tensor:
+    """Device (..., rows, K/32) scale tensor -> its K-block planes, laid out by
+    the library's moegg_sf_to_kplanes on the current stream."""
+    import moe_grouped_block_amd as mg
+    rows = int(t.numel() // (k // 32))
+    dst = torch.empty(t.numel(), dtype=torch.uint8, device=t.device)
+    mg.sf_to_kplanes(t, dst, rows, k)
+    return dst
+
+
+def to_device(arrays: dict, device="cuda", sf_layout: str = "row_major", k: int | None = None) -> dict:
+    """numpy arrays -> contiguous device tensors (bf16 bits travel as int16).
+    With sf_layout "kplanes" the scale arrays (sfa, sfb) are uploaded
+    row-major and laid out as K-block planes on the device (K = `k`)."""
     out = {}
-    for k, v in arrays.items():
+    for key, v in arrays.items():
         v = np.ascontiguousarray(v)
         t = torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v)
-        out[k] = t.to(device, non_blocking=False)
+        out[key] = t.to(device, non_blocking=False)
+        if sf_layout == "kplanes" and key in ("sfa", "sfb") and v.size:
+            out[key] = _kplanes(out[key], int(k))
     return out
 
 
-def discrete_weights(problem: dict, arrays: dict, device="cuda", seed: int = 0, null_empty=None):
+def discrete_weights(problem: dict, arrays: dict, device="cuda", seed: int = 0, null_empty=None,
+                     sf_layout: str = "row_major"):
     """Per-expert allocations for the discrete-weight mode.
 
     Expert g's weights (N, row units) and, for MX operands, its (N, K/32)
-    scales get allocations of their own, made in a
+    scales (as K-block planes with sf_layout "kplanes") get allocations of
+    their own, made in a
     shuffled expert order with spacers between them, so their addresses are
     neither contiguous nor ascending.  Returns (pointer tensors {"b_ptrs",
     "sfb_ptrs"}, list of tensors to keep alive).  Experts listed in
@@ -48,6 +64,8 @@ def discrete_weights(problem: dict, arrays: dict, device="cuda", seed: int = 0, 
         bptr[g] = tb.data_ptr()
         if mx:
             ts = torch.from_numpy(np.ascontiguousarray(arrays["sfb"][g])).to(device)
+            if sf_layout == "kplanes":
+                ts = _kplanes(ts, int(problem["k"]))
             keep.append(ts)
             sptr[g] = ts.data_ptr()
     ptrs = {"b_ptrs": torch.tensor(bptr, dtype=torch.int64, device=device)}

@@ -235,6 +235,12 @@ CONFIGS = {
                              routing=("topk", 16384, 6), alpha=("const", 1.0), prob=("softmax_picks",),
                              a_std=0.1, b_std="1/sqrtK", c_std=4.0, geglu_alpha=1.702, linear_offset=1.0,
                              glu_clamp_min=-7.0, glu_clamp_max=7.0, seed=110),
+    # counter calibration: one expert, one 256-column tile, 65536 rows, so that
+    # every row of A is fetched exactly once and B (0.5 MB) stays in cache:
+    # the bytes the kernel's own direct-to-LDS loads move are known
+    "stream_gating_l1": dict(L=1, K=2048, N=256, ab="e4m3", act="none", d="bf16", c=None,
+                             routing=("multinomial", 65536), alpha=("const", 1.0),
+                             prob=("uniform",), a_std=1.0, b_std="1/sqrtK", seed=111),
     # FC1 + SwiGLU at L=64 (the forward whose backward is dswiglu_bf16_l64)
     "fc1_swiglu_l64": dict(L=64, K=2048, N=2816, ab="e4m3", act="swiglu", d="e4m3", c=None,
                            routing=("topk", 16384, 6), alpha=("const", 1.0),

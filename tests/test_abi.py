@@ -32,7 +32,8 @@ def _declared_functions():
 def test_exports_every_declared_function():
     names = _declared_functions()
     assert {"moegg_check", "moegg_run", "moegg_check_offsets", "moegg_n_out", "moegg_status_string",
-            "moegg_last_error", "moegg_abi_version", "moegg_set_grid_limit"} <= set(names)
+            "moegg_last_error", "moegg_abi_version", "moegg_set_grid_limit",
+            "moegg_sf_to_kplanes"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", mg.lib_path], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (moegg_[a-z_]+)\b", out))
     assert set(names) <= exported, set(names) - exported
@@ -50,8 +51,9 @@ def test_version_and_strings():
 
 def test_struct_layout_matches_header():
     # problem: 2 x int32, int64, 6 x int32, float -> 44 bytes, padded to 48
-    assert ctypes.sizeof(mg.moegg_problem) == 64
+    assert ctypes.sizeof(mg.moegg_problem) == 72
     assert mg.moegg_problem.valid_m.offset == 8
+    assert mg.moegg_problem.sf_layout.offset == 64
     assert ctypes.sizeof(mg.moegg_args) == 19 * 8
     assert mg.moegg_args.b_ptrs.offset == 17 * 8 and mg.moegg_args.sfb_ptrs.offset == 18 * 8
 
@@ -100,6 +102,8 @@ OK, INVALID, MISALIGNED, NOT_SUPPORTED = 0, 1, 2, 3
 CASES = [
     # (base, problem overrides, tensor overrides, expected status)
     ("gating_bf16", dict(num_groups=0), {}, INVALID),
+    ("gating_bf16", dict(sf_layout=1), {}, OK),                        # K-block planes
+    ("gating_bf16", dict(sf_layout=2), {}, INVALID),                   # unknown scale layout
     ("gating_bf16", dict(num_groups=1025), {}, INVALID),
     ("gating_bf16", dict(n=0), {}, INVALID),
     ("gating_bf16", dict(valid_m=-128), {}, INVALID),
@@ -254,3 +258,15 @@ def test_grid_limit_hook_round_trips():
         assert mg.moegg_set_grid_limit(0) == 0
     finally:
         mg.moegg_set_grid_limit(prev)
+
+
+def test_sf_to_kplanes_rejects_bad_arguments_before_any_launch():
+    """Argument rules of the scale-layout conversion (no device work: each
+    case fails validation, and rows == 0 enqueues nothing)."""
+    assert mg.moegg_sf_to_kplanes(FAKE, FAKE + 0x100000, 10, 200, None) == INVALID       # k % 128
+    assert mg.moegg_sf_to_kplanes(FAKE, FAKE + 0x100000, -1, 256, None) == INVALID        # rows < 0
+    assert mg.moegg_sf_to_kplanes(FAKE + 4, FAKE + 0x100000, 10, 256, None) == MISALIGNED
+    assert mg.moegg_sf_to_kplanes(FAKE, FAKE + 8, 10, 256, None) == MISALIGNED
+    assert mg.moegg_sf_to_kplanes(FAKE, FAKE + 16, 10, 256, None) == INVALID             # overlap
+    assert mg.moegg_sf_to_kplanes(None, FAKE, 10, 256, None) == INVALID
+    assert mg.moegg_sf_to_kplanes(FAKE, FAKE + 0x100000, 0, 256, None) == OK              # nothing to do

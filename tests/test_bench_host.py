@@ -46,15 +46,20 @@ def test_algorithmic_bytes_backward_counts_c_in_and_dprob():
     assert bench.algorithmic_bytes(case) == float(reads + writes)
 
 
-def test_traffic_lookup_needs_matching_workload_and_kernel(tmp_path, monkeypatch):
+def test_profile_lookup_needs_matching_workload_and_kernel(tmp_path, monkeypatch):
     h = bench.kernel_source_hash()
     f = tmp_path / "t.md"
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    f.write_text(f"workload: fc1_swiglu_l64\nkernel_source_sha256_16: {h}\nhbm_bytes_per_launch: 1.5e9\n")
-    assert bench.read_traffic("fc1_swiglu_l64") == 1.5e9
-    assert bench.read_traffic("fc1_swiglu_l8") is None
-    f.write_text("workload: fc1_swiglu_l64\nkernel_source_sha256_16: 0000000000000000\nhbm_bytes_per_launch: 1.5e9\n")
-    assert bench.read_traffic("fc1_swiglu_l64") is None
+    monkeypatch.setattr(bench, "PROFILE_FILE", str(f))
+    f.write_text(f"kernel_source_sha256_16: {h}\n\n```\n"
+                 "workload=fc1_swiglu_l64 hbm_bytes_per_launch=1.5e9 sclk_mhz=1875.0 mfma_busy_frac=0.57\n"
+                 "workload=fc1_swiglu_l64:rowmajor hbm_bytes_per_launch=1.6e9\n```\n")
+    assert bench.read_profile("fc1_swiglu_l64") == {"hbm_bytes_per_launch": 1.5e9, "sclk_mhz": 1875.0,
+                                                    "mfma_busy_frac": 0.57}
+    assert bench.read_profile("fc1_swiglu_l64:rowmajor") == {"hbm_bytes_per_launch": 1.6e9}
+    assert bench.read_profile("fc1_swiglu_l8") is None
+    f.write_text("kernel_source_sha256_16: 0000000000000000\n"
+                 "workload=fc1_swiglu_l64 hbm_bytes_per_launch=1.5e9\n")
+    assert bench.read_profile("fc1_swiglu_l64") is None
 
 
 def test_kernel_hash_ignores_comments(tmp_path, monkeypatch):
