@@ -55,7 +55,7 @@ typedef uint32_t v2u __attribute__((ext_vector_type(2)));   // struct defeats SR
 
 constexpr int kBK = 128;          // bytes of K per row and pipeline stage (one cache line)
 constexpr int kBandM = 8;         // m-tiles per raster band (L2 reuse of B)
-constexpr int kTPitch = 36;       // floats per row of the epilogue transpose (see quant_tile)
+constexpr int kTPitch = 36;       // floats per row of the epilogue transpose (see quant_codes)
 constexpr int kScratch = 8192;    // bytes of epilogue scratch per wave
 
 // Unrolled loop whose index is a compile-time constant (instruction
@@ -208,26 +208,25 @@ __device__ __forceinline__ T sload(const T* base, int i) {
   return ((const __attribute__((address_space(4))) T*)base)[i];
 }
 
-// Store 16 values of one row (one 32-column tile) as bf16.  This lane holds
-// columns 8j + 4*hi + [0, 4) (8 bytes each); v_permlane32_swap(x, y)
-// exchanges x of lanes 32-63 with y of lanes 0-31, so swapping the runs of
-// j = 2i and 2i + 1 leaves lane hi = 0 with columns 16i + [0, 8) and lane
-// hi = 1 with 16i + [8, 16): two 16-byte stores per lane, each instruction
-// writing 32 contiguous bytes of every row.  `base` is the tile's first
-// column in the wave's first row; `roff` the lane's row offset in bytes.
-__device__ __forceinline__ void store_bf16_tile(uint8_t* base, uint32_t roff, int hi, const float* v) {
+// 16 values of one row (one 32-column tile) as bf16, in 16-byte pieces.
+// This lane holds columns 8j + 4*hi + [0, 4) (8 bytes each);
+// v_permlane32_swap(x, y) exchanges x of lanes 32-63 with y of lanes 0-31, so
+// swapping the runs of j = 2i and 2i + 1 leaves lane hi = 0 with columns
+// 16i + [0, 8) and lane hi = 1 with 16i + [8, 16): piece q[i] is the row's
+// bytes [32 i + 16 hi, +16).
+__device__ __forceinline__ void bf16_pieces(const float* v, v4u* q) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const uint32_t a0 = bf16x2(v[8 * i + 0], v[8 * i + 1]), a1 = bf16x2(v[8 * i + 2], v[8 * i + 3]);
     const uint32_t b0 = bf16x2(v[8 * i + 4], v[8 * i + 5]), b1 = bf16x2(v[8 * i + 6], v[8 * i + 7]);
     const v2u s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
     const v2u s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-    *at(reinterpret_cast<v4u*>(base + 32 * i), roff + 16 * hi) = v4u{s0.x, s1.x, s0.y, s1.y};
+    q[i] = v4u{s0.x, s1.x, s0.y, s1.y};
   }
 }
 
 // One row's 32 bf16 of a 32-column tile into this lane's layout, runs of 4
-// at columns 8j + 4*hi (w[j], 8 bytes each): the inverse of store_bf16_tile.
+// at columns 8j + 4*hi (w[j], 8 bytes each): the inverse of bf16_pieces.
 // q[i] holds the row's bytes [32 i + 16 hi, + 16) (two 16-byte reads per
 // lane cover 32 contiguous bytes of every row); the runs are exchanged with
 // lane ^ 32.
@@ -241,17 +240,72 @@ __device__ __forceinline__ void unpack_bf16(const v4u* q, v2u* w) {
   }
 }
 
-// Store one row's 32 E4M3 codes of a 32-column tile.  This lane holds the
-// codes of columns 8j + 4*hi + [0, 4) (w[j]).  v_permlane32_swap(x, y)
-// exchanges x of lanes 32-63 with y of lanes 0-31: with x = w[j], y = w[j+2]
-// lane hi = 0 ends with (own w[j], partner's w[j]) = columns 8j + [0, 8) and
-// lane hi = 1 with (partner's w[j+2], own w[j+2]) = columns 16 + 8j + [0, 8),
-// so lane hi = 0 stores columns [0, 16) and lane hi = 1 columns [16, 32),
-// one 16-byte store each.
-__device__ __forceinline__ void store_e4m3_row(uint8_t* base, uint32_t roff, int hi, const uint32_t* w) {
+// One row's 32 E4M3 codes of a 32-column tile as this lane's 16-byte piece.
+// This lane holds the codes of columns 8j + 4*hi + [0, 4) (w[j]).
+// v_permlane32_swap(x, y) exchanges x of lanes 32-63 with y of lanes 0-31:
+// with x = w[j], y = w[j+2] lane hi = 0 ends with (own w[j], partner's w[j])
+// = columns 8j + [0, 8) and lane hi = 1 with (partner's w[j+2], own w[j+2])
+// = columns 16 + 8j + [0, 8): the piece is the row's bytes [16 hi, +16).
+__device__ __forceinline__ v4u e4m3_piece(const uint32_t* w) {
   const v2u s0 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
   const v2u s1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
-  *at(reinterpret_cast<v4u*>(base), roff + 16 * hi) = v4u{s0.x, s0.y, s1.x, s1.y};
+  return v4u{s0.x, s0.y, s1.x, s1.y};
+}
+
+// Whole-segment stores of one 32-row block of output bytes.  Lane (row l32,
+// half hi) holds, for each 32-byte column piece b < W / 32 of the block, the
+// row's bytes [32 b + 16 hi, +16) (q[b]: the layout of the pieces above).
+// Stored as they are, one instruction writes 32 rows x 32 bytes; here they
+// pass through the wave's LDS scratch `lds` (32 x W bytes) and come back so
+// that each instruction writes 1024 / W whole W-byte row segments (W / 16
+// lanes per row): the memory system takes 2x (W = 64) or 4x (W = 128) fewer,
+// larger requests.  Chunk c of row r sits at chunk slot c ^ swz(r), so that
+// the 16-lane groups of the writes (16 rows, one chunk) and of the reads
+// (whole rows) hit 16 distinct bank quads.  Only chunks below `valid` bytes
+// of a row are stored.  `base`: the block's first byte; `pitch`: bytes per
+// row.  Lanes read what other lanes wrote: wave-scope fences around a wave
+// barrier (no instructions: the LDS serves one wave's accesses in order) make
+// the compiler keep every write ahead of the reads, and this call's accesses
+// after the scratch's earlier uses and before its later ones; without them it
+// may treat a write that its own lane never reads back as dead on some paths.
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+template <int W>
+__device__ __forceinline__ void store_rows(uint8_t* base, uint32_t pitch, const v4u* q, float* lds, int lid,
+                                           uint32_t valid = W) {
+  static_assert(W == 64 || W == 128, "segment width");
+  constexpr int CPR = W / 16;                      // 16-byte chunks per row
+  auto slot = [](int r, int c) __attribute__((always_inline)) {
+    return W == 128 ? c ^ ((r >> 1) & 7) : c ^ ((r >> 2) & 3);
+  };
+  const int l32 = lid & 31, hi = lid >> 5;
+  wave_sync_lds();
+#pragma unroll
+  for (int b = 0; b < W / 32; ++b)
+    *reinterpret_cast<v4f*>(lds + l32 * (W / 4) + slot(l32, 2 * b + hi) * 4) = __builtin_bit_cast(v4f, q[b]);
+  wave_sync_lds();
+  const int c = lid % CPR;
+  // all reads in flight together (pinned here, not sunk into the store
+  // condition), then the stores
+  v4f v[W / 32];
+#pragma unroll
+  for (int k = 0; k < W / 32; ++k) {
+    const int r = k * (64 / CPR) + lid / CPR;
+    v[k] = *reinterpret_cast<const v4f*>(lds + r * (W / 4) + slot(r, c) * 4);
+  }
+#pragma unroll
+  for (int k = 0; k < W / 32; ++k) asm volatile("" : "+v"(v[k]));
+  if (static_cast<uint32_t>(c * 16) < valid) {
+#pragma unroll
+    for (int k = 0; k < W / 32; ++k) {
+      const int r = k * (64 / CPR) + lid / CPR;
+      *at(reinterpret_cast<v4u*>(base), r * pitch + c * 16) = __builtin_bit_cast(v4u, v[k]);
+    }
+  }
+  wave_sync_lds();
 }
 
 // FP8 row + column quantisation of one 32 x 32 output tile ("Grouped GEMM +
@@ -266,12 +320,11 @@ __device__ __forceinline__ void store_e4m3_row(uint8_t* base, uint32_t roff, int
 //   S: 32 floats, the inverse column scales.
 // Lanes 0-31 read rows 0-15 of column l, lanes 32-63 rows 24-31 then 16-23,
 // so that both halves of a 64-lane read hit complementary bank ranges.
-// Outputs: D at dW + roff, D_col at dcW + roff (dW, dcW: the block's first
-// column in the wave's first row; roff: the lane's row offset), the row
-// block's scale byte at sfW + sfoff.
+// Outputs: this lane's 16-byte pieces of its row of D (prow) and of D_col
+// (pcol), see e4m3_piece; the row block's scale byte at sfW + sfoff.
 // Returns the E8M0 byte of this lane's column (l % 32) block.
-__device__ __forceinline__ uint32_t quant_tile(float* T, float* S, uint8_t* dW, uint8_t* dcW, uint8_t* sfW,
-                                               uint32_t roff, uint32_t sfoff, int hi, int l32, const float* dn) {
+__device__ __forceinline__ uint32_t quant_codes(float* T, float* S, uint8_t* sfW, uint32_t sfoff, int hi, int l32,
+                                                const float* dn, v4u& prow, v4u& pcol) {
   // the previous call's cross-lane reads of T and S stay ahead of this
   // call's writes
   __builtin_amdgcn_wave_barrier();
@@ -319,11 +372,12 @@ __device__ __forceinline__ uint32_t quant_tile(float* T, float* S, uint8_t* dW, 
     wr[j] = e4m3x4_scaled(dn[4 * j], dn[4 * j + 1], dn[4 * j + 2], dn[4 * j + 3], sr);
     wc[j] = e4m3x4(dn[4 * j] * sc[j].x, dn[4 * j + 1] * sc[j].y, dn[4 * j + 2] * sc[j].z, dn[4 * j + 3] * sc[j].w);
   }
-  store_e4m3_row(dW, roff, hi, wr);
-  store_e4m3_row(dcW, roff, hi, wc);
+  prow = e4m3_piece(wr);
+  pcol = e4m3_piece(wc);
   if (hi == 0) *at(sfW, sfoff) = static_cast<uint8_t>(br);
   return bc;
 }
+
 
 // ---------------------------------------------------------------------------
 // the fused kernel
@@ -861,11 +915,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       // (raw reads q[0, 2) of the first block, q[2, 4) of the second)
       v4u nq[4];
       if (has_cols(0)) stage_x(0, 0);
+      // the outputs of a 32-row block go out in whole 128-byte row segments
+      // (store_rows through the transpose scratch): BF16 dC per column pair,
+      // FP8 dC (4 blocks of 32 columns) once both pairs are quantised
+      float* const stg = sT;
+      int lid3 = lane;
+      asm volatile("" : "+v"(lid3));
+      const uint32_t dpitch = static_cast<uint32_t>(p.n_out);                     // FP8 dC row, bytes
+      const uint32_t dvalid = static_cast<uint32_t>(max(min(128, p.n_out - 2 * nbase), 0));
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
         const uint32_t ml = tm * 32 + l32;                 // row within the wave's 128
-        const uint32_t xr = ml * static_cast<uint32_t>(ld2) * 2;   // its C_in / BF16 dC row, bytes
         float dp = 0.0f;
+        v4u rq[2 * TN] = {}, kq[2 * TN] = {};             // FP8 dC row / column pieces of the 4 blocks
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           if (!has_cols(tn)) continue;
@@ -925,9 +987,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             for (int v = 0; v < 16; ++v) {
               d0[v] = dglu(v, 0, dp);
               d1[v] = dglu(v, 1, unused);
+              // (dGeGLU: pinned in groups of eight, as in the FP8 branch below)
+              if (ACT == ACT_DGEGLU && (v & 7) == 7)
+                asm volatile("" : "+v"(d0[v - 7]), "+v"(d0[v - 6]), "+v"(d0[v - 5]), "+v"(d0[v - 4]), "+v"(d0[v - 3]),
+                             "+v"(d0[v - 2]), "+v"(d0[v - 1]), "+v"(d0[v]), "+v"(d1[v - 7]), "+v"(d1[v - 6]),
+                             "+v"(d1[v - 5]), "+v"(d1[v - 4]), "+v"(d1[v - 3]), "+v"(d1[v - 2]), "+v"(d1[v - 1]),
+                             "+v"(d1[v]), "+v"(dp));
             }
-            store_bf16_tile(dbW + 128 * tn, xr, hi, d0);
-            store_bf16_tile(dbW + 128 * tn + 64, xr, hi, d1);
             if constexpr (AMAX2) {
 #pragma unroll
               for (int v = 0; v < 16; v += 2) {
@@ -935,6 +1001,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
                 amax1 = max_abs2(amax1, d1[v], d1[v + 1]);
               }
             }
+            v4u q[4];
+            bf16_pieces(d0, q);
+            bf16_pieces(d1, q + 2);
+            store_rows<128>(dbW + 128 * tn + tm * 32 * ld2 * 2, static_cast<uint32_t>(ld2) * 2, q, stg, lid3);
           } else {
             // FP8 dC: each 32-column output block quantised by rows and
             // columns like a forward D ("Grouped GEMM + dGLU (SM100)",
@@ -942,7 +1012,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             // recomputed for the second, so that a single block of values is
             // live during a quantisation.
             const int oc = 2 * ncol;
-            const uint32_t ro = ml * static_cast<uint32_t>(p.n_out), so = ml * static_cast<uint32_t>(p.n_out >> 5);
+            const uint32_t so = ml * static_cast<uint32_t>(p.n_out >> 5);
             // (dGeGLU: the elements in groups of eight, pinned after each
             // group, so that the scheduler does not keep sixteen sigmoid
             // chains in flight at once and spill; dSwiGLU does not need it)
@@ -952,7 +1022,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
               d[v] = dglu(v, 0, dp) * nc;
               if (ACT == ACT_DGEGLU && (v & 7) == 7) asm volatile("" : "+v"(d[v - 7]), "+v"(d[v - 6]), "+v"(d[v - 5]), "+v"(d[v - 4]), "+v"(d[v - 3]), "+v"(d[v - 2]), "+v"(d[v - 1]), "+v"(d[v]), "+v"(dp));
             }
-            colw0[tn] |= quant_tile(sT, sS, dW0 + oc, dcW0 + oc, sfW0 + (oc >> 5), ro, so, hi, l32, d) << (8 * tm);
+            colw0[tn] |= quant_codes(sT, sS, sfW0 + (oc >> 5), so, hi, l32, d, rq[2 * tn], kq[2 * tn]) << (8 * tm);
             // opaque copies: the second block's terms are recomputed, not kept
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -964,9 +1034,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
               d[v] = dglu(v, 1, unused) * nc;
               if (ACT == ACT_DGEGLU && (v & 7) == 7) asm volatile("" : "+v"(d[v - 7]), "+v"(d[v - 6]), "+v"(d[v - 5]), "+v"(d[v - 4]), "+v"(d[v - 3]), "+v"(d[v - 2]), "+v"(d[v - 1]), "+v"(d[v]));
             }
-            colw1[tn] |= quant_tile(sT, sS, dW0 + oc + 32, dcW0 + oc + 32, sfW0 + (oc >> 5) + 1, ro, so, hi, l32, d)
+            colw1[tn] |= quant_codes(sT, sS, sfW0 + (oc >> 5) + 1, so, hi, l32, d, rq[2 * tn + 1], kq[2 * tn + 1])
                          << (8 * tm);
           }
+        }
+        if constexpr (OUT == OUT_E4M3) {
+          store_rows<128>(dW0 + 2 * nbase + tm * 32 * dpitch, dpitch, rq, stg, lid3, dvalid);
+          store_rows<128>(dcW0 + 2 * nbase + tm * 32 * dpitch, dpitch, kq, stg, lid3, dvalid);
         }
         dp = halves_sum(dp);
         if (hi == 0) atomicAdd(at(p.dprob + mb, 4 * ml), dp);
@@ -1028,6 +1102,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       for (int tm = 0; tm < TM; ++tm) {
         const uint32_t ml = tm * 32 + l32;
         float dp = 0.0f;
+        // dC pieces of the row's TN blocks: bf16 (2 a block) or E4M3 row and
+        // column codes (1 a block)
+        v4u dq[OUT == OUT_BF16 ? 2 * TN : TN] = {}, kq[TN] = {};
         // this row's staged C_in has landed before the LDS reads, and the
         // reads have returned before the next row's loads overwrite it
         wait_vmcnt<0>();
@@ -1071,7 +1148,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             dp += r * (c * c);
           }
           if constexpr (OUT == OUT_BF16) {
-            store_bf16_tile(p.d + (mb * p.n_out + ncol) * 2, ml * static_cast<uint32_t>(p.n_out) * 2, hi, d);
+            bf16_pieces(d, dq + 2 * tn);
             if constexpr (MX) {
 #pragma unroll
               for (int v = 0; v < 16; v += 2) amax_l = max_abs2(amax_l, d[v], d[v + 1]);
@@ -1079,10 +1156,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           } else {
 #pragma unroll
             for (int v = 0; v < 16; ++v) d[v] *= nc;
-            colw[tn] |= quant_tile(sT, sS, dW0 + ncol, dcW0 + ncol, sfW0 + (ncol >> 5), ml * static_cast<uint32_t>(p.n_out),
-                                   ml * static_cast<uint32_t>(p.n_out >> 5), hi, l32, d)
+            colw[tn] |= quant_codes(sT, sS, sfW0 + (ncol >> 5), ml * static_cast<uint32_t>(p.n_out >> 5), hi, l32, d,
+                                    dq[tn], kq[tn])
                         << (8 * tm);
           }
+        }
+        // the row's dC in whole row segments of the wave's columns
+        // (store_rows through the transpose scratch)
+        {
+          constexpr int DW = (OUT == OUT_BF16 ? 2 : 1) * 32 * TN;
+          const uint32_t dpitch = static_cast<uint32_t>(p.n_out) * (OUT == OUT_BF16 ? 2 : 1);
+          const uint32_t dvalid = static_cast<uint32_t>(max(min(DW, (OUT == OUT_BF16 ? 2 : 1) * (p.n_out - nbase)), 0));
+          uint8_t* const dB = (OUT == OUT_BF16 ? reinterpret_cast<uint8_t*>(p.d) + (mb * p.n_out + nbase) * 2
+                                               : dW0 + nbase) + tm * 32 * dpitch;
+          int lid3 = lane;
+          asm volatile("" : "+v"(lid3));
+          store_rows<DW>(dB, dpitch, dq, sT, lid3, dvalid);
+          if constexpr (OUT == OUT_E4M3)
+            store_rows<DW>(dcW0 + nbase + tm * 32 * dpitch, dpitch, kq, sT, lid3, dvalid);
         }
         dp = halves_sum(dp);
         if (hi == 0) atomicAdd(at(p.dprob + mb, 4 * ml), dp);
@@ -1108,105 +1199,128 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       // 32-column MFMA tiles into one, GeGLU a [G_b | U_b] pair
       constexpr bool PAIR = ACT == ACT_SWIGLU || ACT == ACT_GEGLU;
       constexpr int TO = PAIR ? TN / 2 : TN;
+      // Each 32-row block is stored once all its column tiles are done, in
+      // whole row segments of the wave's columns (store_rows through the
+      // transpose scratch, which is free between quantisations): C (bf16,
+      // 128 bytes a row), D (bf16: 64 or 128 bytes, E4M3: 64 bytes without
+      // pairs; E4M3 with pairs has 32 bytes a row and is stored directly).
+      // GEMM columns [nbase, nbase + 64): the last wave of an N = 32 mod 64
+      // problem has the first 32 only.
+      if (nbase < p.n) {
+        const int ocol0 = PAIR ? nbase >> 1 : nbase;              // first output column
+        const uint32_t cpitch = static_cast<uint32_t>(p.n) * 2;    // bytes per C row
+        const uint32_t dpitch = static_cast<uint32_t>(p.n_out) * (OUT == OUT_BF16 ? 2 : 1);
+        constexpr int DW = (OUT == OUT_BF16 ? 2 : 1) * 32 * TO;      // D bytes per row of the wave
+        const uint32_t cvalid = static_cast<uint32_t>(min(128, 2 * (p.n - nbase)));
+        const uint32_t dvalid = static_cast<uint32_t>(min(DW, (OUT == OUT_BF16 ? 2 : 1) * (p.n_out - ocol0)));
+        uint8_t* const cW = reinterpret_cast<uint8_t*>(p.c + mb * p.n + nbase);      // the wave's first C row
+        uint8_t* const dW = OUT == OUT_BF16 ? reinterpret_cast<uint8_t*>(p.d + (mb * p.n_out + ocol0) * 2)
+                                            : dW0 + ocol0;
+        float* const stg = sT;
+        int lid2 = lane;
+        asm volatile("" : "+v"(lid2));
+        uint32_t colw[TO];                                          // E8M0 bytes of 4 column blocks
 #pragma unroll
-      for (int to = 0; to < TO; ++to) {
-        const int gcol = nbase + (PAIR ? 64 : 32) * to;   // first GEMM column
-        if (gcol >= p.n) continue;
-        const int ocol = PAIR ? gcol >> 1 : gcol;
-        uint32_t colw = 0;                                             // E8M0 bytes of 4 column blocks
-        uint8_t* const cW = reinterpret_cast<uint8_t*>(p.c + mb * p.n + gcol);        // C store, block 0
+        for (int to = 0; to < TO; ++to) colw[to] = 0;
+        auto tile_ok = [&](int to) __attribute__((always_inline)) { return PAIR || nbase + 32 * to < p.n; };
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
           const uint32_t ml = tm * 32 + l32;
-          const uint32_t cr = ml * static_cast<uint32_t>(p.n) * 2;       // C row, bytes
-          float d[16];
-          if constexpr (ACT == ACT_SWIGLU) {
-            // pairs [X_b | G_b] of 32 columns ("Grouped GEMM + SwiGLU (SM100)",
-            // Step 2): D = prob * (alpha X) * silu(alpha G), times norm_const
-            // for FP8 output, evaluated as (X G) (prob nc alpha^2) sigmoid(alpha G)
-            const v16f& ax = acc[tm][2 * to];
-            const v16f& ag = acc[tm][2 * to + 1];
-            if (p.c) {
-              float cx[16], cg[16];
+          if (p.c) {
+            // C = alpha acc of the wave's 64 GEMM columns
+            v4u cq[4] = {};
+#pragma unroll
+            for (int t = 0; t < TN; ++t) {
+              if (!tile_ok(PAIR ? 0 : t)) continue;
+              float c[16];
+#pragma unroll
+              for (int v = 0; v < 16; ++v) c[v] = alpha * acc[tm][t][v];
+              bf16_pieces(c, cq + 2 * t);
+            }
+            store_rows<128>(cW + tm * 32 * cpitch, cpitch, cq, stg, lid2, cvalid);
+          }
+          v4u dq[OUT == OUT_BF16 ? 2 * TO : TO] = {};    // bf16 D pieces, or E4M3 row pieces
+          v4u kq[TO] = {};                               // E4M3 D_col pieces
+#pragma unroll
+          for (int to = 0; to < TO; ++to) {
+            if (!tile_ok(to)) continue;
+            const int ocol = ocol0 + 32 * to;
+            float d[16];
+            if constexpr (ACT == ACT_SWIGLU) {
+              // pairs [X_b | G_b] of 32 columns ("Grouped GEMM + SwiGLU (SM100)",
+              // Step 2): D = prob * (alpha X) * silu(alpha G), times norm_const
+              // for FP8 output, evaluated as (X G) (prob nc alpha^2) sigmoid(alpha G)
+              const v16f& ax = acc[tm][2 * to];
+              const v16f& ag = acc[tm][2 * to + 1];
+              const float f = pr[tm] * nc * (alpha * alpha);
+              const float nal = -alpha * kLog2e;
 #pragma unroll
               for (int v = 0; v < 16; ++v) {
-                cx[v] = alpha * ax[v];
-                cg[v] = alpha * ag[v];
+                const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(ag[v] * nal));
+                d[v] = (ax[v] * ag[v]) * (f * s);
               }
-              store_bf16_tile(cW, cr, hi, cx);
-              store_bf16_tile(cW + 64, cr, hi, cg);
-            }
-            const float f = pr[tm] * nc * (alpha * alpha);
-            const float nal = -alpha * kLog2e;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(ag[v] * nal));
-              d[v] = (ax[v] * ag[v]) * (f * s);
-            }
-          } else if constexpr (ACT == ACT_GEGLU) {
-            // pairs [G_b | U_b] of 32 columns, gate first ("Grouped GEMM + GLU +
-            // Hadamard", §Equations, GeGLU): both halves of C = alpha acc
-            // clamped to [glu_clamp_min, glu_clamp_max], then
-            // D = gamma prob (U + offset) G sigmoid(geglu_alpha G), times norm_const
-            const v16f& ag = acc[tm][2 * to];
-            const v16f& au = acc[tm][2 * to + 1];
-            float cg[16], cu[16];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              cg[v] = alpha * ag[v];
-              cu[v] = alpha * au[v];
-            }
-            if (p.c) {
-              store_bf16_tile(cW, cr, hi, cg);
-              store_bf16_tile(cW + 64, cr, hi, cu);
-            }
-            const float f = pr[tm] * nc * p.glu_gamma;
-            const float nga = -p.geglu_alpha * kLog2e;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const float g = fminf(fmaxf(cg[v], p.glu_clamp_min), p.glu_clamp_max);
-              const float u = fminf(fmaxf(cu[v], p.glu_clamp_min), p.glu_clamp_max);
-              const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * nga));
-              d[v] = ((u + p.linear_offset) * g) * (f * s);
-            }
-          } else {
-            float c[16];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) c[v] = alpha * acc[tm][to][v];
-            if (p.c) store_bf16_tile(cW, cr, hi, c);
-            const float f = pr[tm] * nc;
-            if constexpr (ACT == ACT_SRELU) {
-              // D = prob * (s * min(tanh(relu(C)/s), 1))^2, or prob * relu(C)^2 for s = 0
-              // ("Grouped GEMM + sReLU (SM100)", §Equations, §Tanh soft clamp)
-              const float s = p.srelu_s;
-              const float rs = s > 0.0f ? 1.0f / s : 0.0f;
+            } else if constexpr (ACT == ACT_GEGLU) {
+              // pairs [G_b | U_b] of 32 columns, gate first ("Grouped GEMM + GLU +
+              // Hadamard", §Equations, GeGLU): both halves of C = alpha acc
+              // clamped to [glu_clamp_min, glu_clamp_max], then
+              // D = gamma prob (U + offset) G sigmoid(geglu_alpha G), times norm_const
+              const v16f& ag = acc[tm][2 * to];
+              const v16f& au = acc[tm][2 * to + 1];
+              const float f = pr[tm] * nc * p.glu_gamma;
+              const float nga = -p.geglu_alpha * kLog2e;
 #pragma unroll
               for (int v = 0; v < 16; ++v) {
-                float r = fmaxf(c[v], 0.0f);
-                if (s > 0.0f) r = s * fminf(tanh_nonneg(r * rs), 1.0f);
-                d[v] = f * (r * r);
+                const float g = fminf(fmaxf(alpha * ag[v], p.glu_clamp_min), p.glu_clamp_max);
+                const float u = fminf(fmaxf(alpha * au[v], p.glu_clamp_min), p.glu_clamp_max);
+                const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * nga));
+                d[v] = ((u + p.linear_offset) * g) * (f * s);
               }
             } else {
+              const float f = pr[tm] * nc;
+              if constexpr (ACT == ACT_SRELU) {
+                // D = prob * (s * min(tanh(relu(C)/s), 1))^2, or prob * relu(C)^2 for s = 0
+                // ("Grouped GEMM + sReLU (SM100)", §Equations, §Tanh soft clamp)
+                const float s = p.srelu_s;
+                const float rs = s > 0.0f ? 1.0f / s : 0.0f;
 #pragma unroll
-              for (int v = 0; v < 16; ++v) d[v] = f * c[v];
+                for (int v = 0; v < 16; ++v) {
+                  float r = fmaxf(alpha * acc[tm][to][v], 0.0f);
+                  if (s > 0.0f) r = s * fminf(tanh_nonneg(r * rs), 1.0f);
+                  d[v] = f * (r * r);
+                }
+              } else {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) d[v] = f * (alpha * acc[tm][to][v]);
+              }
+            }
+            if constexpr (OUT == OUT_BF16) {
+              bf16_pieces(d, dq + 2 * to);
+#pragma unroll
+              for (int v = 0; v < 16; v += 2) amax_l = max_abs2(amax_l, d[v], d[v + 1]);
+            } else {
+              colw[to] |= quant_codes(sT, sS, sfW0 + (ocol >> 5), ml * static_cast<uint32_t>(p.n_out >> 5), hi, l32, d,
+                                      dq[to], kq[to])
+                          << (8 * tm);
             }
           }
-          if constexpr (OUT == OUT_BF16) {
-            store_bf16_tile(p.d + (mb * p.n_out + ocol) * 2, ml * static_cast<uint32_t>(p.n_out) * 2, hi, d);
-#pragma unroll
-            for (int v = 0; v < 16; v += 2) amax_l = max_abs2(amax_l, d[v], d[v + 1]);
+          uint8_t* const dB = dW + tm * 32 * dpitch;     // this 32-row block's first D row
+          if constexpr (OUT == OUT_E4M3 && PAIR) {
+            *at(reinterpret_cast<v4u*>(dW0 + ocol0), ml * dpitch + 16 * hi) = dq[0];
+            *at(reinterpret_cast<v4u*>(dcW0 + ocol0), ml * dpitch + 16 * hi) = kq[0];
           } else {
-            const uint32_t bc = quant_tile(sT, sS, dW0 + ocol, dcW0 + ocol, sfW0 + (ocol >> 5),
-                                           ml * static_cast<uint32_t>(p.n_out), ml * static_cast<uint32_t>(p.n_out >> 5),
-                                           hi, l32, d);
-            colw |= bc << (8 * tm);
+            store_rows<DW>(dB, dpitch, dq, stg, lid2, dvalid);
+            if constexpr (OUT == OUT_E4M3) store_rows<DW>(dcW0 + ocol0 + tm * 32 * dpitch, dpitch, kq, stg, lid2, dvalid);
           }
         }
         if constexpr (OUT == OUT_E4M3) {
           // column l32's scale bytes of the wave's 4 consecutive 32-row blocks
-          if (hi == 0)
-            *at(reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(ocol) * (vm >> 5) + mblk0), l32 * sfc_pitch) =
-                colw;
+#pragma unroll
+          for (int to = 0; to < TO; ++to) {
+            const int ocol = ocol0 + 32 * to;
+            if (tile_ok(to) && hi == 0)
+              *at(reinterpret_cast<uint32_t*>(p.sfd_col + static_cast<int64_t>(ocol) * (vm >> 5) + mblk0),
+                  l32 * sfc_pitch) = colw[to];
+          }
         }
       }
       if constexpr (OUT == OUT_BF16) {
