@@ -442,6 +442,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   __shared__ __attribute__((aligned(16))) uint32_t sSA0[SA_WORDS], sSA1[SA_WORDS];
   __shared__ __attribute__((aligned(16))) uint32_t sSB0[SB_WORDS], sSB1[SB_WORDS];
   __shared__ int32_t sTiles[1025];   // m-tiles before expert g, g = 0..L
+  __shared__ uint32_t sAmax[2];      // the current tile's amax (float bits), see flush_amax
   __shared__ float sPr[kThreads / 64][kBM / 2];   // prob of each wave's 128 rows (epilogue)
   // backward epilogues: rows 16-31 of the second staged C_in block (1 KB per wave)
   __shared__ __attribute__((aligned(16))) uint8_t sCin[kThreads / 64][1024];
@@ -478,6 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
     }
     if (lane == 0) sTiles[0] = 0;
   }
+  if (tid < 2) sAmax[tid] = 0;
   __syncthreads();
   const int m_tiles = sTiles[L];
   const int n_tiles = p.n_tiles;
@@ -1060,8 +1062,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       if constexpr (AMAX2) {
         const float wi = wave_max(amax0), wg = wave_max(amax1);
         if (lane == 0) {
-          atomicMax(reinterpret_cast<unsigned int*>(p.amax + 2 * g), __float_as_uint(wi));
-          atomicMax(reinterpret_cast<unsigned int*>(p.amax + 2 * g + 1), __float_as_uint(wg));
+          atomicMax(&sAmax[0], __float_as_uint(wi));
+          atomicMax(&sAmax[1], __float_as_uint(wg));
         }
       }
     } else if constexpr (ACT == ACT_DSRELU) {
@@ -1190,7 +1192,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       }
       if constexpr (MX && OUT == OUT_BF16) {
         const float w = wave_max(amax_l);
-        if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(p.amax + g), __float_as_uint(w));
+        if (lane == 0) atomicMax(&sAmax[0], __float_as_uint(w));
       }
     } else {
       float amax_l = 0.0f;
@@ -1325,10 +1327,34 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       }
       if constexpr (OUT == OUT_BF16) {
         const float w = wave_max(amax_l);
-        if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(p.amax + g), __float_as_uint(w));
+        if (lane == 0) atomicMax(&sAmax[0], __float_as_uint(w));
       }
     }
   };
+
+  // Per-group amax: each wave folds its value for the tile into sAmax (an
+  // LDS atomic max on the float bits, which order like the values: |D| >= 0).
+  // After the barrier that starts the workgroup's next tile (or the one
+  // after its last), lane 0 of wave 0 sends the tile's value to the group's
+  // amax with one global atomic and clears the slots: one global atomic per
+  // tile instead of one per wave, on addresses that every workgroup holding
+  // a tile of the group updates (measured: FC2 with Zipf routing spent 16 %
+  // of its time in these atomics at one per wave).
+  constexpr int NAMAX = OUT != OUT_BF16 ? 0
+                        : (ACT == ACT_DSWIGLU || ACT == ACT_DGEGLU) ? (MX ? 2 : 0)
+                        : ACT == ACT_DSRELU ? (MX ? 1 : 0)
+                                            : 1;
+  auto flush_amax = [&](int gf) __attribute__((always_inline)) {
+    if constexpr (NAMAX > 0) {
+      if (gf >= 0 && wave == 0 && lane < NAMAX) {
+        const uint32_t v = sAmax[lane];
+        sAmax[lane] = 0;
+        if (v) atomicMax(reinterpret_cast<unsigned int*>(p.amax) + NAMAX * gf + lane, v);
+      }
+    }
+  };
+  // the LDS atomics of this wave's epilogue performed before a barrier
+  auto wait_lds = []() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0xC07F); };
 
   // ---- persistent tile loop ----
   // Two LDS stages.  Every cluster ends at a workgroup barrier; waves 4-7
@@ -1352,6 +1378,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   const int nks = p.k_steps;
   int t = __builtin_amdgcn_readfirstlane(slot);
   if (t >= total) return;
+  int done_g = -1;     // group of the tile whose amax waits in sAmax
   Tile cur = tile_of(t);
   Src src = make_src(cur);
   issue(src, 0, st0);
@@ -1457,13 +1484,27 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   auto run = [&](auto mode_c) __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode_c)::value;
     while (true) {
-      const int t_next = t + nwg;
+      int t_next = t + nwg;
+      // The last pass is usually partial: its tiles are split evenly over the
+      // XCDs, each XCD's share contiguous, rather than filling the first
+      // slots (which would leave some XCDs idle and crowd the others' L2).
+      // Grids of a multiple of 8 workgroups (nwg / 8 on each XCD) only.
+      if (nwg >= 8 && (nwg & 7) == 0) {
+        const int base = t_next - slot;                 // first tile of the next pass
+        if (base < total && total - base < nwg) {
+          const int rem = total - base, xcd = wg & 7, jx = wg >> 3;
+          const int lo = rem * xcd / 8, hi8 = rem * (xcd + 1) / 8;
+          t_next = lo + jx < hi8 ? base + lo + jx : total;
+        }
+      }
       const bool has_next = t_next < total;
       const Tile nxt = tile_of(has_next ? t_next : t);
       // stage 0 (and whatever the previous epilogue left in flight) complete
       // and visible, the previous epilogue's scratch free
       wait_vmcnt<0>();
+      if constexpr (NAMAX > 0) wait_lds();
       sync();
+      flush_amax(done_g);
       if (wm) sync();
       if constexpr (MODE == 0) {
         first_pair();
@@ -1520,6 +1561,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
         wait_vmcnt<N_EARLY + N_LATE>();   // prob (issued before the next tile's first stage)
         epilogue(cur, ein);
       }
+      done_g = cur.g;
       if (!has_next) break;
       t = t_next;
       cur = nxt;
@@ -1534,6 +1576,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
   else run(std::integral_constant<int, 2>{});
   // no direct-to-LDS write may still be in flight when the workgroup ends
   wait_vmcnt<0>();
+  if constexpr (NAMAX > 0) {
+    wait_lds();
+    sync();
+    flush_amax(done_g);
+  }
 }
 
 template <int AB, int ACT, int OUT>

@@ -174,6 +174,29 @@ def test_small_parity(name):
     print(f"[gpu-case] {name} stats {stats}", flush=True)
 
 
+# The epilogue stores each 32-row block of a wave's outputs in whole row
+# segments of its 64 GEMM columns.  With N = 32 mod 64 the last wave has one
+# 32-column block only and must store half of each segment: the C store (and
+# D) of the forward sReLU, whose other paths have such a case above.
+# ("Grouped GEMM + sReLU (SM100)", §Equations: C and D cover columns [0, N).)
+HALF_SEGMENT = {
+    "half_segment_srelu_fp8_c_e4m3": ("srelu_tanh_fp4_l32", dict(ab="e4m3", L=3, K=512, N=288, clip=None, s=8.0,
+                                                                 routing=("multinomial", 400), c="bf16",
+                                                                 b_std="1/sqrtK")),
+    "half_segment_srelu_fp4_c_bf16": ("srelu_tanh_fp4_l32", dict(L=2, K=512, N=288, routing=("multinomial", 300),
+                                                                 c="bf16", d="bf16")),
+}
+
+
+@pytest.mark.parametrize("name", list(HALF_SEGMENT))
+def test_half_segment_parity(name):
+    base, over = HALF_SEGMENT[name]
+    case = synth.make_case(base, seed=1500 + sorted(HALF_SEGMENT).index(name), name=name, **over)
+    got = run_gpu(case)
+    stats = check_case(case, got)
+    print(f"[gpu-case] {name} stats {stats}", flush=True)
+
+
 # ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------
