@@ -10,7 +10,7 @@ import pytest
 import oracle
 import synth
 from oracle import formats as F
-from parity_util import acc_error_bound, amax_rule, decode_bf16, pick_row_blocks, rule1, rule2
+from parity_util import acc_error_bound, amax_rule, decode_bf16, make_refine, pick_row_blocks, rule1, rule2
 
 pytestmark = pytest.mark.gpu
 
@@ -50,10 +50,11 @@ def check_case(case, got, rows=None):
         if p["d_dtype"] == "e4m3":
             nc = float(case.arrays["norm_const"][0])
             rb = acc_error_bound(case, ref)
-            stats["d_row"] = rule2(got["d"][r], got["sfd_row"][r], ref["dc"], nc, "row", "dC/SFD_row", rb)
+            stats["d_row"] = rule2(got["d"][r], got["sfd_row"][r], ref["dc"], nc, "row", "dC/SFD_row", rb,
+                                   make_refine(case, ref, "row"))
             blocks = np.unique(r // 32)
             stats["d_col"] = rule2(got["d_col"][r], got["sfd_col"][:, blocks], ref["dc"], nc, "col",
-                                   "dC_col/SFD_col", rb)
+                                   "dC_col/SFD_col", rb, make_refine(case, ref, "col"))
             return stats
         g2 = np.repeat(grp[:, None], ref["dc"].shape[1], axis=1)
         stats["dc"] = rule1(decode_bf16(got["d"][r]), ref["dc"], g2, "dC")
@@ -73,9 +74,11 @@ def check_case(case, got, rows=None):
     else:
         nc = float(case.arrays["norm_const"][0])
         rb = acc_error_bound(case, ref)
-        stats["d_row"] = rule2(got["d"][r], got["sfd_row"][r], ref["d"], nc, "row", "D/SFD_row", rb)
+        stats["d_row"] = rule2(got["d"][r], got["sfd_row"][r], ref["d"], nc, "row", "D/SFD_row", rb,
+                               make_refine(case, ref, "row"))
         blocks = np.unique(r // 32)
-        stats["d_col"] = rule2(got["d_col"][r], got["sfd_col"][:, blocks], ref["d"], nc, "col", "D_col/SFD_col", rb)
+        stats["d_col"] = rule2(got["d_col"][r], got["sfd_col"][:, blocks], ref["d"], nc, "col", "D_col/SFD_col", rb,
+                               make_refine(case, ref, "col"))
     return stats
 
 

@@ -8,9 +8,10 @@ staged prob.  A problem small enough for the oracle has fewer tiles than the
 GPU has compute units, so these cases cap the grid at 1-3 workgroups with the
 library's testing hook (moegg_set_grid_limit): every workgroup then runs many
 tiles in a row.  The step counts 1-8 cover every load schedule (1-2, 3, odd
->= 5, even >= 4 steps per tile).  Three larger cases (> 512 tiles) run at the
+>= 5, even >= 4 steps per tile).  Five larger cases (> 512 tiles) run at the
 natural grid of one workgroup per compute unit, where each workgroup takes
-two or three tiles.  ("Grouped GEMM + Quant (SM100)", §Equations, Step 1:
+two or three tiles, including a last pass with 3 and with 255 tiles left.
+("Grouped GEMM + Quant (SM100)", §Equations, Step 1:
 rows are grouped over every expert range, whichever workgroup computes
 them.)"""
 import pytest
@@ -78,6 +79,10 @@ BIG = {
                                                  prob=("uniform",))),
     "big_dswiglu_e4m3_k3": ("dswiglu_mxfp8_l64", dict(L=4, K=384, N=512, routing=("multinomial", 70000),
                                                       prob=("uniform",))),
+    # the last, partial pass is dealt evenly over the 8 XCDs: 515 tiles leave
+    # 3 for it (most XCDs get none), 767 tiles leave 255
+    "big_gating_rem3": ("quant_gating_l4", dict(L=1, K=128, N=256, force_counts=[515 * 256])),
+    "big_gating_rem255": ("quant_gating_l4", dict(L=1, K=128, N=256, force_counts=[767 * 256], d="e4m3")),
 }
 
 
