@@ -23,7 +23,7 @@ launch stream) with the dense MXFP8 MFMA peak; `traffic`, the core clock
 under the kernel (and the roofline fraction at that clock) and the MFMA-busy
 fraction come from the committed rocprofv3 counter summary when it was taken
 on the current kernel source, else they are left out (traffic null).
-`cpu_baseline` is the float64 oracle on the host cores.
+`cpu_baseline` is the C++ float64 oracle on the host cores.
 """
 from __future__ import annotations
 
@@ -105,25 +105,22 @@ def algorithmic_bytes(case) -> float:
 
 
 def cpu_baseline(case, rows_n):
-    """The oracle as it stands on the host cores, on the first `rows_n` rows."""
+    """The C++ float64 oracle as it stands (plain loops, OpenMP over rows) on
+    the host cores, on the first `rows_n` rows of the workload."""
     import numpy as np
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
-    except Exception:
-        cores = os.cpu_count() or 1
+    from oracle import cxx
     p = case.problem
     rows_n = min(rows_n, p["valid_m"])
     rows = np.arange(rows_n)
     routed = int(case.row_valid[:rows_n].sum())
     t0 = time.perf_counter()
-    oracle.grouped_gemm(p, case.arrays, rows)
+    cxx.grouped_gemm(p, case.arrays, rows)
     dt = time.perf_counter() - t0
     flops = 2.0 * routed * p["n"] * p["k"]
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"rows [0, {rows_n}) of the workload ({routed} routed rows), one float64 numpy "
-                      f"oracle pass incl. dequantise, GEMM, SwiGLU and FP8 quantisation: {dt:.1f} s"}
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cxx.threads()), "kind": "oracle",
+            "sample": f"rows [0, {rows_n}) of the workload ({routed} routed rows), one pass of the C++ float64 "
+                      f"oracle (dequantise, GEMM, SwiGLU, FP8 row and column quantisation) on "
+                      f"{cxx.threads()} OpenMP threads: {dt:.1f} s"}
 
 
 def main():
@@ -142,7 +139,7 @@ def main():
                          "K-block planes (sf_layout KPLANES) unless a ':rowmajor' suffix asks for the row-major "
                          "(rows, K/32) layout; a ':discrete' suffix passes the expert weights as per-expert "
                          "allocations (b_ptrs / sfb_ptrs)")
-    ap.add_argument("--cpu-rows", type=int, default=40960, help="rows of the oracle CPU sample")
+    ap.add_argument("--cpu-rows", type=int, default=16384, help="rows of the oracle CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true", help="skip the launches after an L2/MALL flush")
     ap.add_argument("--profile-launches", type=int, default=0,

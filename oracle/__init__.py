@@ -9,10 +9,18 @@ evaluation of the equations on the cuDNN frontend pages "Grouped GEMM + Quant
 (``moe_grouped_block_amd``): no kernels, headers, tables, constants or
 pre/post-processing.  Neither side imports the other.
 
+The package holds two independent writings of the same definitions: the
+numpy modules here (``formats``, ``grouped``) and a plain C++ implementation
+in ``oracle/cpp`` (float64 loops, OpenMP over rows; ``cxx`` is its ctypes
+binding, built by ``cxx.build()``).  Neither calls the other; the GPU parity
+tests compare against the numpy one, the CPU baseline of the benchmark times
+the C++ one, and a CPU test checks that the two agree on every seeded recipe.
+
 Pins (tests that tie this code to something other than itself) live in
-``tests/test_oracle_*.py``; every function here is pinned, none is
-"parity unpinned", except the order of the SwiGLU blocks relative to the
-GLU+Hadamard page (a reading, see ``grouped_gemm``'s docstring).
+``tests/test_oracle_*.py`` and run on both implementations; every function
+here is pinned, none is "parity unpinned", except the order of the SwiGLU
+blocks relative to the GLU+Hadamard page (a reading, see ``grouped_gemm``'s
+docstring).
 """
 from . import formats  # noqa: F401
 from .grouped import grouped_gemm, dequantize, group_of_rows  # noqa: F401

@@ -10,6 +10,7 @@ import pytest
 import oracle
 import synth
 from oracle import formats as F
+from cases import EDGE, SMALL
 from parity_util import acc_error_bound, amax_rule, decode_bf16, make_refine, pick_row_blocks, rule1, rule2
 
 pytestmark = pytest.mark.gpu
@@ -86,86 +87,7 @@ def check_case(case, got, rows=None):
 # small cases: every output element against the oracle
 # ---------------------------------------------------------------------------
 
-SMALL = {
-    "gating_l4_full": ("quant_gating_l4", {}),
-    "swiglu_fp8_e4m3": ("fc1_swiglu_l8", dict(L=3, K=512, N=320, routing=("topk", 300, 2))),
-    "swiglu_fp8_bf16": ("fc1_swiglu_l8", dict(L=3, K=512, N=320, routing=("topk", 300, 2), d="bf16",
-                                              alpha=("uniform", 0.5, 2.0))),
-    "swiglu_fp8_nc3": ("fc1_swiglu_l8", dict(L=2, K=256, N=256, routing=("topk", 200, 2), norm_const=3.0)),
-    "swiglu_fp4_e4m3_c": ("fc1_swiglu_l8", dict(L=2, ab="e2m1x2", K=512, N=320, routing=("topk", 160, 2),
-                                                b_std=1.0, clip=6.0, c="bf16")),
-    "fc2_zipf_bf16": ("fc2_gating_l64_zipf", dict(L=9, K=384, N=320, routing=("topk_zipf", 400, 3, 1.1, 2))),
-    "gating_fp8_e4m3": ("quant_gating_l4", dict(L=3, K=256, N=288, d="e4m3", routing=("multinomial", 300))),
-    "srelu_fp4_tanh_e4m3": ("srelu_tanh_fp4_l32", dict(L=3, K=1024, N=320, routing=("multinomial", 500))),
-    "srelu_fp4_plain_bf16": ("srelu_tanh_fp4_l32", dict(L=3, K=512, N=256, routing=("multinomial", 300),
-                                                        s=0.0, d="bf16", c=None)),
-    "srelu_fp8_tanh_bf16_c": ("srelu_tanh_fp4_l32", dict(ab="e4m3", L=2, K=512, N=256, clip=None, s=8.0,
-                                                         routing=("multinomial", 300), d="bf16", c="bf16",
-                                                         b_std="1/sqrtK")),
-    "gating_bf16_ops": ("quant_gating_l4", dict(ab="bf16", K=256, N=320, a_std=1.0, b_std=0.1)),
-    "swiglu_bf16_ops_e4m3": ("fc1_swiglu_l8", dict(ab="bf16", L=2, K=192, N=256, routing=("topk", 200, 2))),
-    "dswiglu_bf16": ("dswiglu_bf16_l64", dict(L=5, K=256, N=288, routing=("topk", 200, 3),
-                                              alpha=("uniform", 0.5, 2.0), beta=("uniform", 0.5, 2.0))),
-    # block-scaled dSwiGLU ("Grouped GEMM + dGLU (SM100)", block-scaled contract):
-    # step counts 8 (even), 5 (odd), 3 and 2 exercise every load schedule
-    "dswiglu_mxfp8_e4m3": ("dswiglu_mxfp8_l64", dict(L=5, K=1024, N=288, routing=("topk", 200, 3),
-                                                     alpha=("uniform", 0.5, 2.0), beta=("uniform", 0.5, 2.0))),
-    "dswiglu_mxfp8_e4m3_odd": ("dswiglu_mxfp8_l64", dict(L=3, K=640, N=256, routing=("topk", 150, 2),
-                                                         norm_const=2.0)),
-    "dswiglu_mxfp8_bf16_amax": ("dswiglu_mxfp8_l64", dict(L=4, K=384, N=320, d="bf16", routing=("topk", 200, 2),
-                                                          alpha=("uniform", 0.5, 2.0))),
-    "dswiglu_mxfp4_e4m3": ("dswiglu_mxfp8_l64", dict(ab="e2m1x2", L=3, K=512, N=256, routing=("topk", 150, 2),
-                                                     a_std=1.0, b_std=1.0, clip=6.0)),
-    "dswiglu_mxfp4_bf16_amax": ("dswiglu_mxfp8_l64", dict(ab="e2m1x2", d="bf16", L=3, K=1024, N=288,
-                                                          routing=("topk", 150, 2), a_std=1.0, b_std=1.0,
-                                                          clip=6.0)),
-    # sReLU backward (tanh clamp s = 8 and plain s = 0), every operand family
-    "dsrelu_mxfp8_e4m3": ("dsrelu_mxfp8_l32", dict(L=3, K=1024, N=320, routing=("multinomial", 300),
-                                                   alpha=("uniform", 0.5, 2.0))),
-    "dsrelu_mxfp8_e4m3_odd_plain": ("dsrelu_mxfp8_l32", dict(L=2, K=640, N=256, routing=("multinomial", 200),
-                                                             s=0.0, norm_const=0.5)),
-    "dsrelu_mxfp4_bf16_amax": ("dsrelu_mxfp8_l32", dict(ab="e2m1x2", d="bf16", L=3, K=1024, N=288,
-                                                        routing=("multinomial", 300), a_std=1.0, b_std=1.0,
-                                                        clip=6.0)),
-    "dsrelu_bf16_ops": ("dsrelu_mxfp8_l32", dict(ab="bf16", d="bf16", L=2, K=192, N=256,
-                                                 routing=("multinomial", 200))),
-    # E2M1 operands with FP8 dC and a last wave column holding one 32-column
-    # block (N % 64 == 32): the C_in staging's half-empty row
-    "dsrelu_mxfp4_e4m3_n288": ("dsrelu_mxfp8_l32", dict(ab="e2m1x2", L=3, K=512, N=288,
-                                                        routing=("multinomial", 300), a_std=1.0, b_std=1.0,
-                                                        clip=6.0)),
-    # E5M2 operands ("Grouped GEMM + Quant", §Data Types) through the other epilogues
-    "e5m2_gating_bf16": ("quant_gating_l4", dict(ab="e5m2", L=3, K=384, N=288, routing=("multinomial", 300))),
-    "e5m2_swiglu_e4m3": ("fc1_swiglu_l8", dict(ab="e5m2", L=3, K=640, N=320, routing=("topk", 300, 2))),
-    # GeGLU forward: clamps that bite (|C| ~ 1 against bounds -1.5 / 1), other
-    # constants, every operand family, both output formats
-    "geglu_e5m2_e4m3_clamped": ("fc1_geglu_e5m2_l8", dict(L=3, K=1024, N=320, routing=("topk", 300, 2),
-                                                          glu_clamp_min=-1.5, glu_clamp_max=1.0)),
-    "geglu_fp8_bf16_consts": ("fc1_geglu_e5m2_l8", dict(ab="e4m3", d="bf16", L=3, K=384, N=256,
-                                                        routing=("topk", 200, 2), glu_gamma=0.75,
-                                                        geglu_alpha=1.25, linear_offset=0.5,
-                                                        glu_clamp_min=float("-inf"), glu_clamp_max=float("inf"),
-                                                        alpha=("uniform", 0.5, 2.0))),
-    "geglu_fp4_e4m3_c": ("fc1_geglu_e5m2_l8", dict(ab="e2m1x2", L=2, K=512, N=320, routing=("topk", 160, 2),
-                                                   b_std=1.0, clip=6.0, c="bf16", glu_clamp_min=-4.0,
-                                                   glu_clamp_max=3.0)),
-    "geglu_bf16_ops": ("fc1_geglu_e5m2_l8", dict(ab="bf16", L=2, K=192, N=256, routing=("topk", 200, 2),
-                                                 glu_clamp_min=-0.75, glu_clamp_max=0.75)),
-    # dGeGLU backward ("Grouped GEMM + dGLU (SM100)", dGeGLU): C ~ N(0, 4^2)
-    # against clamps -7 / 7, so both masks and the sigmoid tails are exercised
-    "dgeglu_mxfp8_e4m3": ("dgeglu_mxfp8_l64", dict(L=5, K=1024, N=288, routing=("topk", 200, 3),
-                                                   alpha=("uniform", 0.5, 2.0))),
-    "dgeglu_e5m2_bf16_amax": ("dgeglu_mxfp8_l64", dict(ab="e5m2", d="bf16", L=3, K=640, N=256,
-                                                       routing=("topk", 150, 2), linear_offset=0.25,
-                                                       glu_clamp_min=-3.0, glu_clamp_max=5.0)),
-    "dgeglu_mxfp4_e4m3": ("dgeglu_mxfp8_l64", dict(ab="e2m1x2", L=3, K=512, N=256, routing=("topk", 150, 2),
-                                                   a_std=1.0, b_std=1.0, clip=6.0, norm_const=2.0)),
-    "dgeglu_bf16_ops": ("dgeglu_mxfp8_l64", dict(ab="bf16", d="bf16", L=2, K=192, N=288,
-                                                 routing=("topk", 150, 2), geglu_alpha=1.0)),
-    "dgeglu_mxfp4_bf16_amax_n288": ("dgeglu_mxfp8_l64", dict(ab="e2m1x2", d="bf16", L=3, K=512, N=288,
-                                                             routing=("topk", 150, 2), a_std=1.0, b_std=1.0,
-                                                             clip=6.0)),
-}
+# SMALL: see tests/cases.py
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -204,22 +126,7 @@ def test_half_segment_parity(name):
 # edge cases
 # ---------------------------------------------------------------------------
 
-EDGE = {
-    # empty first / middle / last groups, single-row groups, a group of exactly 128
-    "edge_groups_gating": ("quant_gating_l4", dict(L=7, K=256, N=256, force_counts=[0, 1, 0, 128, 129, 0, 1])),
-    "edge_groups_swiglu_e4m3": ("fc1_swiglu_l8", dict(L=5, K=128, N=128, force_counts=[0, 1, 200, 0, 3])),
-    "edge_l1": ("quant_gating_l4", dict(L=1, K=128, N=64, force_counts=[5])),
-    "edge_n64_swiglu": ("fc1_swiglu_l8", dict(L=2, K=128, N=64, routing=("topk", 100, 1))),
-    "edge_k_one_step_fp4": ("srelu_tanh_fp4_l32", dict(L=2, K=256, N=64, routing=("multinomial", 70))),
-    "edge_k_one_step_bf16": ("dswiglu_bf16_l64", dict(L=2, K=64, N=32, routing=("topk", 50, 1))),
-    # the maximum expert count: 1024 groups, most of them empty, the first and
-    # the last one populated (the whole tile prefix and its search)
-    "edge_l1024_sparse": ("quant_gating_l4", dict(L=1024, K=128, N=64,
-                                                  force_counts=[3] + [0] * 200 + [130] + [0] * 300 + [1]
-                                                  + [0] * 400 + [257] + [0] * 119 + [2])),
-    # groups aligned to 256 rows (the pages' default padding)
-    "edge_m_aligned_256": ("fc1_swiglu_l8", dict(L=3, K=256, N=128, m_aligned=256, routing=("topk", 300, 2))),
-}
+# EDGE: see tests/cases.py
 
 
 @pytest.mark.parametrize("name", list(EDGE))

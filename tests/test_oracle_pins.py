@@ -1,6 +1,8 @@
-"""Pins of the oracle's GEMM, row->group map, epilogues and quantisation
+"""Pins of the oracles' GEMM, row->group map, epilogues and quantisation
 against closed forms, brute force, finite differences and the hand-worked
-examples in tests/golden/worked_examples.yaml.  CPU only."""
+examples in tests/golden/worked_examples.yaml.  Every pin runs on both
+oracles: the numpy one (``oracle.grouped``) and the C++ one (``oracle/cpp``,
+through ``oracle.cxx``).  CPU only."""
 import itertools
 import math
 import os
@@ -14,6 +16,25 @@ from oracle import formats as F
 from oracle import grouped as G
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.yaml")
+RCP_MAX_E4M3 = np.float32(1.0) / np.float32(448.0)
+
+
+class _Numpy:
+    """The numpy oracle under the names the pins use."""
+    grouped_gemm = staticmethod(oracle.grouped_gemm)
+    swiglu, srelu, geglu = staticmethod(G.swiglu), staticmethod(G.srelu), staticmethod(G.geglu)
+    dswiglu, dsrelu, dgeglu = staticmethod(G.dswiglu), staticmethod(G.dsrelu), staticmethod(G.dgeglu)
+    quantize_rows, quantize_cols = staticmethod(G.quantize_rows), staticmethod(G.quantize_cols)
+    e8m0_block_scale = staticmethod(G.e8m0_block_scale)
+
+
+@pytest.fixture(params=["numpy", "cpp"])
+def O(request):
+    """Each pin runs against both oracles."""
+    if request.param == "numpy":
+        return _Numpy
+    from oracle import cxx
+    return cxx
 
 
 # ---------------------------------------------------------------------------
@@ -36,7 +57,7 @@ def _const_mx(rows, k, code, byte, fp4=False):
 
 @pytest.mark.parametrize("fp4", [False, True])
 @pytest.mark.parametrize("sa,sb,alpha", [(127, 127, 1.0), (130, 120, 0.5), (100, 140, 4.0)])
-def test_all_ones_power_of_two_scales_exact(fp4, sa, sb, alpha):
+def test_all_ones_power_of_two_scales_exact(fp4, sa, sb, alpha, O):
     k, n, m = 256, 64, 8
     one = 0x22 if fp4 else 0x38
     a, sfa = _const_mx(m, k, one, sa, fp4)
@@ -44,7 +65,7 @@ def test_all_ones_power_of_two_scales_exact(fp4, sa, sb, alpha):
     ab = "e2m1x2" if fp4 else "e4m3"
     arr = dict(a=a, sfa=sfa, b=b[None], sfb=sfb[None], padded_offsets=np.array([m], np.int32),
                alpha=np.array([alpha], np.float32), prob=np.ones(m, np.float32))
-    out = oracle.grouped_gemm(_problem(1, m, n, k, ab=ab), arr)
+    out = O.grouped_gemm(_problem(1, m, n, k, ab=ab), arr)
     expect = k * alpha * 2.0 ** (sa - 127 + sb - 127)
     assert np.all(out["c"] == expect)
     assert np.all(out["d"] == expect)
@@ -77,7 +98,7 @@ def _brute_force(problem, arr):
 
 
 @pytest.mark.parametrize("ab", ["e4m3", "e2m1x2"])
-def test_gemm_vs_brute_force_tiny(ab):
+def test_gemm_vs_brute_force_tiny(ab, O):
     rng = np.random.default_rng(3)
     m, n, k, L = 6, 5 * 1, 64, 2
     fp4 = ab == "e2m1x2"
@@ -94,12 +115,12 @@ def test_gemm_vs_brute_force_tiny(ab):
                padded_offsets=np.array([4, 6], np.int32),
                alpha=np.array([0.75, -1.5], np.float32), prob=np.ones(m, np.float32))
     prob = _problem(L, m, n, k, ab=ab)
-    out = oracle.grouped_gemm(prob, arr)
+    out = O.grouped_gemm(prob, arr)
     ref = _brute_force(prob, arr)
     np.testing.assert_allclose(out["c"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
 
 
-def test_one_hot_b_selects_a_column():
+def test_one_hot_b_selects_a_column(O):
     rng = np.random.default_rng(5)
     m, k = 4, 64
     n = 32
@@ -111,7 +132,7 @@ def test_one_hot_b_selects_a_column():
     arr = dict(a=a, sfa=sfa, b=b, sfb=np.full((1, n, k // 32), 127, np.uint8),
                padded_offsets=np.array([m], np.int32), alpha=np.array([2.0], np.float32),
                prob=np.ones(m, np.float32))
-    out = oracle.grouped_gemm(_problem(1, m, n, k), arr)
+    out = O.grouped_gemm(_problem(1, m, n, k), arr)
     vals = F.decode_e4m3(a) * np.repeat(2.0 ** (sfa.astype(np.float64) - 127), 32, axis=1)
     assert np.array_equal(out["c"], 2.0 * vals[:, 1::2][:, :n])
 
@@ -126,7 +147,7 @@ def test_one_hot_b_selects_a_column():
     [5],
     [0, 0, 4],
 ])
-def test_row_group_map_bit_exact(counts):
+def test_row_group_map_bit_exact(counts, O):
     pad = 4
     L = len(counts)
     padded = [((c + pad - 1) // pad) * pad for c in counts]
@@ -141,7 +162,7 @@ def test_row_group_map_bit_exact(counts):
     arr = dict(a=a, sfa=np.full((m, 1), 127, np.uint8), b=np.full((L, n, k), 0x38, np.uint8),
                sfb=np.full((L, n, 1), 127, np.uint8), padded_offsets=po,
                alpha=(2.0 ** np.arange(L)).astype(np.float32), prob=np.ones(m, np.float32))
-    out = oracle.grouped_gemm(_problem(L, m, n, k), arr)
+    out = O.grouped_gemm(_problem(L, m, n, k), arr)
     start = 0
     for g, (c, p) in enumerate(zip(counts, padded)):
         blk = out["c"][start:start + p]
@@ -158,14 +179,14 @@ def test_row_group_map_bit_exact(counts):
 # P-d / P-h: gating and amax
 # ---------------------------------------------------------------------------
 
-def test_gating_exact_and_amax_brute_force():
+def test_gating_exact_and_amax_brute_force(O):
     rng = np.random.default_rng(9)
     m, n, k = 8, 64, 64
     arr = dict(a=np.full((m, k), 0x38, np.uint8), sfa=np.full((m, 2), 127, np.uint8),
                b=np.full((2, n, k), 0x38, np.uint8), sfb=np.full((2, n, 2), 126, np.uint8),
                padded_offsets=np.array([3, 8], np.int32), alpha=np.array([1.0, 0.25], np.float32),
                prob=rng.random(m).astype(np.float32))
-    out = oracle.grouped_gemm(_problem(2, m, n, k), arr)
+    out = O.grouped_gemm(_problem(2, m, n, k), arr)
     grp = np.array([0, 0, 0, 1, 1, 1, 1, 1])
     expect = k * 0.5 * np.array([1.0, 0.25])[grp] * arr["prob"].astype(np.float64)
     assert np.array_equal(out["d"], np.repeat(expect[:, None], n, axis=1))
@@ -174,7 +195,7 @@ def test_gating_exact_and_amax_brute_force():
         assert out["amax"][g] == bf
 
 
-def test_random_amax_is_brute_force_max():
+def test_random_amax_is_brute_force_max(O):
     rng = np.random.default_rng(12)
     m, n, k, L = 12, 64, 64, 3
     arr = dict(a=rng.integers(0, 0x7F, (m, k), dtype=np.uint8) | 0x80 * rng.integers(0, 2, (m, k), dtype=np.uint8),
@@ -183,7 +204,7 @@ def test_random_amax_is_brute_force_max():
                padded_offsets=np.array([4, 4, 12], np.int32), alpha=np.array([1, 2, 3], np.float32),
                prob=rng.random(m).astype(np.float32))
     for act, d in [("none", "bf16"), ("swiglu", "bf16"), ("srelu", "bf16")]:
-        out = oracle.grouped_gemm(_problem(L, m, n, k, act=act, d=d, s=3.0), arr)
+        out = O.grouped_gemm(_problem(L, m, n, k, act=act, d=d, s=3.0), arr)
         grp = out["group"]
         for g in range(L):
             vals = [abs(v) for r in range(m) if grp[r] == g for v in out["d"][r]]
@@ -194,31 +215,31 @@ def test_random_amax_is_brute_force_max():
 # P-e: SwiGLU closed forms
 # ---------------------------------------------------------------------------
 
-def test_swiglu_closed_forms():
+def test_swiglu_closed_forms(O):
     sig = lambda t: 1.0 / (1.0 + math.exp(-t))
     xs = [-3.0, -0.5, 0.0, 1.0, 2.5]
     gs = [-40.0, -2.0, 0.0, 0.7, 3.0, 40.0]
     for x, g in itertools.product(xs, gs):
         c = np.concatenate([np.full(32, x), np.full(32, g)])[None, :]
-        d = G.swiglu(c, np.array([0.3]))
+        d = O.swiglu(c, np.array([0.3]))
         assert np.allclose(d, 0.3 * x * g * sig(g), rtol=1e-15, atol=1e-300)
     # sigma(-t) = 1 - sigma(t): swish(g) - swish(-g) = g
     c1 = np.concatenate([np.ones(32), np.full(32, 1.7)])[None]
     c2 = np.concatenate([np.ones(32), np.full(32, -1.7)])[None]
-    assert np.allclose(G.swiglu(c1, np.ones(1)) - G.swiglu(c2, np.ones(1)), 1.7, rtol=1e-15)
+    assert np.allclose(O.swiglu(c1, np.ones(1)) - O.swiglu(c2, np.ones(1)), 1.7, rtol=1e-15)
     # large gate: swish(g) -> g; very negative gate -> 0
     c = np.concatenate([np.full(32, 2.0), np.full(32, 60.0)])[None]
-    assert np.allclose(G.swiglu(c, np.ones(1)), 120.0, rtol=1e-15)
+    assert np.allclose(O.swiglu(c, np.ones(1)), 120.0, rtol=1e-15)
 
 
-def test_swiglu_pairs_independent():
+def test_swiglu_pairs_independent(O):
     # changing pair b only changes output block b
     rng = np.random.default_rng(2)
     c = rng.standard_normal((3, 256))
-    base = G.swiglu(c, np.ones(3))
+    base = O.swiglu(c, np.ones(3))
     c2 = c.copy()
     c2[:, 128:192] += 1.0
-    d2 = G.swiglu(c2, np.ones(3))
+    d2 = O.swiglu(c2, np.ones(3))
     changed = np.any(d2 != base, axis=0)
     assert not changed[:64].any() and changed[64:96].all() and not changed[96:].any()
 
@@ -227,30 +248,30 @@ def test_swiglu_pairs_independent():
 # P-f: sReLU and the tanh soft clamp
 # ---------------------------------------------------------------------------
 
-def test_srelu_properties():
+def test_srelu_properties(O):
     rng = np.random.default_rng(4)
     c = rng.standard_normal((64, 128)) * 40
     p = rng.random(64)
     for s in [0.5, 8.0, 32.0]:
-        d = G.srelu(c, p, s)
+        d = O.srelu(c, p, s)
         assert np.all(d <= s * s * p[:, None] * (1 + 1e-15))
         assert np.all(d[c <= 0] == 0)
-    d_plain = G.srelu(c, p, 0.0)
+    d_plain = O.srelu(c, p, 0.0)
     assert np.array_equal(d_plain, p[:, None] * np.maximum(c, 0) ** 2)
-    d_big = G.srelu(c, p, 1e8)          # (r/s)^2 <= 1e-11
+    d_big = O.srelu(c, p, 1e8)          # (r/s)^2 <= 1e-11
     np.testing.assert_allclose(d_big, d_plain, rtol=1e-9)
     # small-r series: (s tanh(r/s))^2 = r^2 (1 - 2 r^2 / (3 s^2) + O(r^4/s^4))
     r = np.array([[1e-3, 1e-2, 0.05]])
     s = 8.0
     series = r ** 2 * (1 - 2 * r ** 2 / (3 * s * s))
-    np.testing.assert_allclose(G.srelu(r, np.ones(1), s), series, rtol=1e-9)
+    np.testing.assert_allclose(O.srelu(r, np.ones(1), s), series, rtol=1e-9)
 
 
 # ---------------------------------------------------------------------------
 # P-g: dSwiGLU and dprob by central finite differences of the forward
 # ---------------------------------------------------------------------------
 
-def test_dswiglu_matches_finite_differences():
+def test_dswiglu_matches_finite_differences(O):
     rng = np.random.default_rng(8)
     rows, n = 3, 64
     R = rng.standard_normal((rows, n))
@@ -264,7 +285,7 @@ def test_dswiglu_matches_finite_differences():
         f = pv[:, None, None] * inp * gate / (1 + np.exp(-gate))
         return (R.reshape(rows, n // 32, 32) * f).sum()
 
-    dc, dprob = G.dswiglu(R, X, p)
+    dc, dprob = O.dswiglu(R, X, p)
     h = 1e-6
     num = np.zeros_like(X)
     for r in range(rows):
@@ -283,13 +304,13 @@ def test_dswiglu_matches_finite_differences():
     np.testing.assert_allclose(dprob, nump, rtol=1e-7, atol=1e-9)
 
 
-def test_dswiglu_alpha_squared_and_beta_placement():
+def test_dswiglu_alpha_squared_and_beta_placement(O):
     m, k, n = 2, 32, 32
     arr = dict(a=np.full((m, k), 0x3F80, np.uint16), b=np.full((1, n, k), 0x3D00, np.uint16),
                padded_offsets=np.array([m], np.int32), alpha=np.array([3.0], np.float32),
                beta=np.array([0.25], np.float32), prob=np.array([1.0, 0.5], np.float32),
                c_in=np.full((m, 2 * n), 0x4000, np.uint16))          # 2.0 -> X = 0.5
-    out = oracle.grouped_gemm(_problem(1, m, n, k, ab="bf16", act="dswiglu"), arr)
+    out = O.grouped_gemm(_problem(1, m, n, k, ab="bf16", act="dswiglu"), arr)
     assert np.all(out["r"] == 9.0)                                   # alpha^2 * (32 * 2^-5)
     s = 1 / (1 + math.exp(-0.5))
     np.testing.assert_allclose(out["dc"][0, :32], 9.0 * 0.5 * s, rtol=1e-15)
@@ -297,7 +318,7 @@ def test_dswiglu_alpha_squared_and_beta_placement():
 
 
 @pytest.mark.parametrize("s_clamp", [0.0, 2.0])
-def test_dsrelu_matches_finite_differences(s_clamp):
+def test_dsrelu_matches_finite_differences(s_clamp, O):
     """dC and dprob of the sReLU backward against central differences of the
     forward loss L = sum R * prob * f(C), f from the sReLU page's equations."""
     rng = np.random.default_rng(9)
@@ -308,9 +329,9 @@ def test_dsrelu_matches_finite_differences(s_clamp):
     p = rng.random(rows)
 
     def loss(Cv, pv):
-        return (R * G.srelu(Cv, pv, s_clamp)).sum()
+        return (R * O.srelu(Cv, pv, s_clamp)).sum()
 
-    dc, dprob = G.dsrelu(R, C, p, s_clamp)
+    dc, dprob = O.dsrelu(R, C, p, s_clamp)
     h = 1e-6
     num = np.zeros_like(C)
     for r in range(rows):
@@ -330,7 +351,7 @@ def test_dsrelu_matches_finite_differences(s_clamp):
     assert np.all(dc[C <= 0] == 0.0)
 
 
-def test_dsrelu_through_the_gemm_closed_form():
+def test_dsrelu_through_the_gemm_closed_form(O):
     """R = alpha^2 * acc, C read without scaling: A = 1.0 (byte 127), B = 1/32
     (byte 122), K = 64 -> acc = 2, alpha 0.5 -> R = 0.5; C = 2.0, s = 0:
     dC = 0.5 * prob * 4, dprob = 0.5 * 64 columns * 4 = 128 (N = 64)."""
@@ -340,7 +361,7 @@ def test_dsrelu_through_the_gemm_closed_form():
     arr = dict(a=a, sfa=sfa, b=b.reshape(1, n, k), sfb=sfb.reshape(1, n, k // 32),
                padded_offsets=np.array([m], np.int32), alpha=np.array([0.5], np.float32),
                prob=np.array([1.0, 0.25], np.float32), c_in=np.full((m, n), 0x4000, np.uint16))
-    out = oracle.grouped_gemm(_problem(1, m, n, k, ab="e4m3", act="dsrelu", d="bf16"), arr)
+    out = O.grouped_gemm(_problem(1, m, n, k, ab="e4m3", act="dsrelu", d="bf16"), arr)
     np.testing.assert_array_equal(out["dc"], np.repeat([[2.0], [0.5]], n, axis=1))
     np.testing.assert_array_equal(out["dprob"], [128.0, 128.0])
     np.testing.assert_array_equal(out["amax"], [2.0])
@@ -358,7 +379,7 @@ def test_e5m2_is_the_upper_byte_of_binary16():
     assert got[0x3C] == 1.0 and got[0x7B] == 57344.0 and got[0x01] == 2.0 ** -16 and got[0x7C] == np.inf
 
 
-def test_dgeglu_matches_finite_differences_of_geglu():
+def test_dgeglu_matches_finite_differences_of_geglu(O):
     """Without clamps the dGeGLU backward is the derivative of the GeGLU forward:
     with L = sum R * D(C) over the GeGLU outputs, dC = dL/dC and dprob = dL/dprob
     (R indexed by output column, the pairs [gate | up] gate first)."""
@@ -370,9 +391,9 @@ def test_dgeglu_matches_finite_differences_of_geglu():
     a, off = 1.3, 0.75
 
     def loss(Cv, pv):
-        return (R * G.geglu(Cv, pv, 1.0, a, off, -np.inf, np.inf)).sum()
+        return (R * O.geglu(Cv, pv, 1.0, a, off, -np.inf, np.inf)).sum()
 
-    dc, dprob = G.dgeglu(R, C, p, a, off, -np.inf, np.inf)
+    dc, dprob = O.dgeglu(R, C, p, a, off, -np.inf, np.inf)
     h = 1e-6
     num = np.zeros_like(C)
     for r in range(rows):
@@ -387,14 +408,14 @@ def test_dgeglu_matches_finite_differences_of_geglu():
     np.testing.assert_allclose(dprob, nump, rtol=1e-7, atol=1e-9)
 
 
-def test_dgeglu_clamp_masks_closed_form():
+def test_dgeglu_clamp_masks_closed_form(O):
     """Gate above clamp_max: dgate = 0, dup uses the clamped gate; up outside
     [min, max]: dup = 0, dgate uses the clamped up; equality keeps the gradient."""
     R = np.ones((1, 32))
     c = np.zeros((1, 64))
     c[0, :32] = [9.0, 7.0, 1.0, 1.0] + [0.0] * 28          # gate
     c[0, 32:] = [2.0, 2.0, -9.0, 7.0] + [0.0] * 28         # up
-    dc, dprob = G.dgeglu(R, c, np.ones(1), 1.702, 1.0, -7.0, 7.0)
+    dc, dprob = O.dgeglu(R, c, np.ones(1), 1.702, 1.0, -7.0, 7.0)
     s7 = 1 / (1 + np.exp(-1.702 * 7.0))
     s1 = 1 / (1 + np.exp(-1.702))
     assert dc[0, 0] == 0.0                                  # gate 9 > 7
@@ -406,17 +427,17 @@ def test_dgeglu_clamp_masks_closed_form():
     np.testing.assert_allclose(dprob[0], 7 * s7 * 3 + 7 * s7 * 3 + s1 * (-6) + s1 * 8, rtol=1e-14)
 
 
-def test_geglu_is_sigmoid_gelu_times_up():
+def test_geglu_is_sigmoid_gelu_times_up(O):
     """GeGLU with offset 1, gamma 1 and no clamp: D = (U + 1) * G * sigmoid(1.702 G),
     checked against scipy's logistic function; the clamp bounds both halves."""
     from scipy.special import expit
     rng = np.random.default_rng(11)
     c = rng.standard_normal((4, 128)) * 3
     p = rng.random(4)
-    d = G.geglu(c, p, 1.0, 1.702, 1.0, -np.inf, np.inf)
+    d = O.geglu(c, p, 1.0, 1.702, 1.0, -np.inf, np.inf)
     g, u = c[:, :32], c[:, 32:64]
     np.testing.assert_allclose(d[:, :32], p[:, None] * (u + 1) * g * expit(1.702 * g), rtol=1e-13)
-    dcl = G.geglu(c, p, 2.0, 1.702, 1.0, -1.0, 1.0)
+    dcl = O.geglu(c, p, 2.0, 1.702, 1.0, -1.0, 1.0)
     gc, uc = np.clip(g, -1, 1), np.clip(u, -1, 1)
     np.testing.assert_allclose(dcl[:, :32], 2 * p[:, None] * (uc + 1) * gc * expit(1.702 * gc), rtol=1e-13)
 
@@ -438,9 +459,9 @@ def _bs_dswiglu_case(d_dtype):
     return _problem(2, m, n, k, ab="e4m3", act="dswiglu", d=d_dtype), arr
 
 
-def test_block_scaled_dswiglu_amax_pairs_closed_form():
+def test_block_scaled_dswiglu_amax_pairs_closed_form(O):
     prob_, arr = _bs_dswiglu_case("bf16")
-    out = oracle.grouped_gemm(prob_, arr)
+    out = O.grouped_gemm(prob_, arr)
     np.testing.assert_array_equal(out["r"], np.repeat([[0.5], [0.5], [2.0], [2.0]], 32, axis=1))
     assert np.all(out["dc"][:, :32] == 0.0)
     np.testing.assert_array_equal(out["dc"][:, 32], [0.5, 0.25, 2.0, 0.5])
@@ -449,9 +470,9 @@ def test_block_scaled_dswiglu_amax_pairs_closed_form():
     np.testing.assert_array_equal(out["amax2"], [[0.0, 0.5], [0.0, 2.0]])
 
 
-def test_block_scaled_dswiglu_fp8_dc_closed_form():
+def test_block_scaled_dswiglu_fp8_dc_closed_form(O):
     prob_, arr = _bs_dswiglu_case("e4m3")
-    out = oracle.grouped_gemm(prob_, arr)
+    out = O.grouped_gemm(prob_, arr)
     # input blocks all zero: byte 0, codes 0.  Gate block of row 0: amax 0.5,
     # smallest 2^e >= 0.5/448 is 2^-9 (byte 118), 0.5 / 2^-9 = 256 = E4M3 0x78;
     # row 1 (0.25): 2^-10 (byte 117), code 0x78 again
@@ -465,11 +486,11 @@ def test_block_scaled_dswiglu_fp8_dc_closed_form():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("nc", [1.0, 4.0, 0.125, 3.0])
-def test_quantization_invariants(nc):
+def test_quantization_invariants(nc, O):
     rng = np.random.default_rng(6)
     d = rng.standard_normal((64, 256)) * np.exp(rng.uniform(-8, 8, (64, 1)))
     d[5, 32:64] = 0.0                                                # an all-zero row block
-    codes, sfd = G.quantize_rows(d, nc)
+    codes, sfd = O.quantize_rows(d, nc)
     d32 = d.astype(np.float32).astype(np.float64)
     blk = np.abs(d32).reshape(64, 8, 32).max(axis=2)
     scale = F.decode_e8m0(sfd)
@@ -485,7 +506,7 @@ def test_quantization_invariants(nc):
     half_ulp = 2.0 ** (ex - 3) / 2
     assert np.all(np.abs(vals - scaled) <= half_ulp * (1 + 1e-6) + 1e-30)
     # columns: same invariants on 32-row blocks
-    ccodes, csfd = G.quantize_cols(d, nc)
+    ccodes, csfd = O.quantize_cols(d, nc)
     assert csfd.shape == (256, 2)
     cblk = np.abs(d32).reshape(2, 32, 256).max(axis=1).T
     cscale = F.decode_e8m0(csfd)
@@ -494,11 +515,11 @@ def test_quantization_invariants(nc):
     assert np.all(r2 > 224 * (1 - 1e-6)) and np.all(r2 <= 448 * (1 + 1e-6))
 
 
-def test_scale_exact_power_of_two_keeps_exponent():
+def test_scale_exact_power_of_two_keeps_exponent(O):
     # amax * rcp_max exactly 2^-3 in float32 -> byte 124 (no round-up past it)
-    amax = np.float32(2.0 ** -3) / G.RCP_MAX_E4M3
-    sf = np.float32(amax) * G.RCP_MAX_E4M3
-    byte = G.e8m0_block_scale(np.array([amax], np.float32), 1.0)[0]
+    amax = np.float32(2.0 ** -3) / RCP_MAX_E4M3
+    sf = np.float32(amax) * RCP_MAX_E4M3
+    byte = O.e8m0_block_scale(np.array([amax], np.float32), 1.0)[0]
     m, e = math.frexp(float(sf))
     assert byte == (e - 1 if m == 0.5 else e) + 127
 
@@ -555,9 +576,9 @@ with open(GOLDEN) as _f:
 
 
 @pytest.mark.parametrize("case", _CASES, ids=[c["name"] for c in _CASES])
-def test_worked_example(case):
+def test_worked_example(case, O):
     p, arr = _build(case)
-    out = oracle.grouped_gemm(p, arr)
+    out = O.grouped_gemm(p, arr)
     ev = lambda s: eval(s, {"math": math})
     if "expect_d" in case:
         for r, v in enumerate(case["expect_d"]):
