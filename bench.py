@@ -139,7 +139,7 @@ def main():
                          "K-block planes (sf_layout KPLANES) unless a ':rowmajor' suffix asks for the row-major "
                          "(rows, K/32) layout; a ':discrete' suffix passes the expert weights as per-expert "
                          "allocations (b_ptrs / sfb_ptrs)")
-    ap.add_argument("--cpu-rows", type=int, default=16384, help="rows of the oracle CPU sample")
+    ap.add_argument("--cpu-rows", type=int, default=49152, help="rows of the oracle CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true", help="skip the launches after an L2/MALL flush")
     ap.add_argument("--profile-launches", type=int, default=0,
