@@ -980,7 +980,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
                 return gate <= p.glu_clamp_max ? r * pr[tm] * uo * sg * (1.0f + p.geglu_alpha * gc * (1.0f - sg))
                                                : 0.0f;
               }
-              return (up >= p.glu_clamp_min && up <= p.glu_clamp_max) ? r * pr[tm] * gc * sg : 0.0f;
+              // evaluated in every lane, then masked by a select: left to
+              // itself the compiler branched around the sigmoid per element
+              float du = r * pr[tm] * gc * sg;
+              asm volatile("" : "+v"(du));
+              return (up >= p.glu_clamp_min && up <= p.glu_clamp_max) ? du : 0.0f;
             }
           };
           if constexpr (OUT == OUT_BF16) {
@@ -1135,19 +1139,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             cv[4 * j + 3] = __uint_as_float(w.y & 0xFFFF0000u);
           }
           float d[16];
+          // (the clamp test outside the element loop, as in the forward)
+          if (sc > 0.0f) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float r = a2 * acc[tm][tn][v];
-            float c = fmaxf(cv[v], 0.0f), fp;
-            if (sc > 0.0f) {
-              const float t = fminf(tanh_nonneg(c * rs), 1.0f);
-              c = sc * t;
-              fp = 2.0f * c * (1.0f - t * t);
-            } else {
-              fp = 2.0f * c;
+            for (int v = 0; v < 16; ++v) {
+              const float r = a2 * acc[tm][tn][v];
+              const float t = fminf(tanh_nonneg(fmaxf(cv[v], 0.0f) * rs), 1.0f);
+              const float c = sc * t;
+              d[v] = r * pr[tm] * (2.0f * c * (1.0f - t * t));
+              dp += r * (c * c);
             }
-            d[v] = r * pr[tm] * fp;
-            dp += r * (c * c);
+          } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const float r = a2 * acc[tm][tn][v];
+              const float c = fmaxf(cv[v], 0.0f);
+              d[v] = r * pr[tm] * (2.0f * c);
+              dp += r * (c * c);
+            }
           }
           if constexpr (OUT == OUT_BF16) {
             bf16_pieces(d, dq + 2 * tn);
@@ -1282,13 +1291,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
               if constexpr (ACT == ACT_SRELU) {
                 // D = prob * (s * min(tanh(relu(C)/s), 1))^2, or prob * relu(C)^2 for s = 0
                 // ("Grouped GEMM + sReLU (SM100)", §Equations, §Tanh soft clamp)
+                // (the clamp test outside the element loop: inside it, the
+                // compiler made one branch per element, which kept the sixteen
+                // tanh chains from overlapping)
                 const float s = p.srelu_s;
-                const float rs = s > 0.0f ? 1.0f / s : 0.0f;
+                if (s > 0.0f) {
+                  const float rs = 1.0f / s;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                  float r = fmaxf(alpha * acc[tm][to][v], 0.0f);
-                  if (s > 0.0f) r = s * fminf(tanh_nonneg(r * rs), 1.0f);
-                  d[v] = f * (r * r);
+                  for (int v = 0; v < 16; ++v) {
+                    const float r = fmaxf(alpha * acc[tm][to][v], 0.0f);
+                    const float c = s * fminf(tanh_nonneg(r * rs), 1.0f);
+                    d[v] = f * (c * c);
+                  }
+                } else {
+#pragma unroll
+                  for (int v = 0; v < 16; ++v) {
+                    const float r = fmaxf(alpha * acc[tm][to][v], 0.0f);
+                    d[v] = f * (r * r);
+                  }
                 }
               } else {
 #pragma unroll
