@@ -346,13 +346,28 @@ def test_full_size_discrete_fc1_l64():
     print(f"[gpu-case] fc1_swiglu_l64 discrete stats {stats}", flush=True)
 
 
+def full_size_rows(case, nblocks=16):
+    """Rows a full-size run is compared on, element by element: whole 32-row
+    blocks spread over the groups (pick_row_blocks) plus every row of the
+    largest group and of the last non-empty one (whole 32-row blocks too:
+    groups are padded to multiples of 128)."""
+    rows = set(pick_row_blocks(case, nblocks=nblocks).tolist())
+    po = np.asarray(case.arrays["padded_offsets"], np.int64)
+    starts = np.concatenate([[0], po[:-1]])
+    sizes = po - starts
+    for g in {int(np.argmax(sizes)), int(np.nonzero(sizes)[0][-1])}:
+        rows.update(range(int(starts[g]), int(po[g])))
+    return np.array(sorted(rows), np.int64)
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled(name):
     case = synth.make_case(name)
     got = run_gpu(case, fill=0x5A)
-    rows = pick_row_blocks(case, nblocks=8)
+    rows = full_size_rows(case)
     stats = check_case(case, got, rows)
+    stats["rows_compared"] = len(rows)
     p = case.problem
     pad = ~case.row_valid
     if p["act"] in ("dswiglu", "dsrelu", "dgeglu"):
