@@ -352,6 +352,7 @@ uint8_t ox_e8m0_scale(float amax, float nc) { return e8m0_scale(amax, nc); }
 int ox_activation(const ox_problem* p, int64_t rows, const double* cr, const double* prob, const double* saved,
                   double* d, double* dprob) {
   if (!p || check_problem(*p)) return 1;
+  if (!cr || !prob || !d || (backward(p->act) && (!saved || !dprob))) return reject("NULL argument");
   const int64_t n = p->n, no = n_out_of(*p);
   const int64_t sw = p->act == OX_DSRELU ? n : 2 * n;
   for (int64_t r = 0; r < rows; ++r)
@@ -361,6 +362,7 @@ int ox_activation(const ox_problem* p, int64_t rows, const double* cr, const dou
 }
 
 int ox_quantize(int axis, const double* d, int64_t rows, int64_t cols, float nc, uint8_t* codes, uint8_t* sf) {
+  if (!d || !codes || !sf) return reject("NULL argument");
   if (axis == 0) {
     if (cols % 32) return reject("row blocks need cols % 32 == 0");
     quantize_rows(d, rows, cols, nc, codes, sf);
@@ -375,6 +377,10 @@ int ox_run(const ox_problem* pp, const ox_inputs* in, const int64_t* rows, int64
   if (!pp || !in || !out || (nrows > 0 && !rows)) return reject("NULL argument");
   const ox_problem& p = *pp;
   if (check_problem(p)) return 1;
+  if (!in->a || !in->b || !in->padded_offsets || !in->alpha || !in->prob ||
+      (p.ab != OX_BF16 && (!in->sfa || !in->sfb)) || (backward(p.act) && !in->c_in) ||
+      (p.act == OX_DSWIGLU && !in->beta))
+    return reject("missing input");
   const int L = p.num_groups, n = p.n, k = p.k;
   const int64_t no = n_out_of(p), rb = row_bytes(p);
   const bool bwd = backward(p.act), mx = p.ab != OX_BF16;
