@@ -1,12 +1,16 @@
-"""Seeded sweep over the configuration space, every output against the
+"""Seeded sweeps over the configuration space, every output against the
 oracle: operand family x activation x output format x K-step count x ragged
-N x expert count x group alignment.  The cases are drawn once from a fixed
-seed (the same list on every run), each small enough for the oracle."""
+N x expert count x group alignment (x norm_const and a capped grid, so that
+workgroups walk many tiles, in the wider sweep).  The cases are drawn once
+from fixed seeds (the same lists on every run), each small enough for the
+oracle."""
 import numpy as np
 import pytest
 
 import synth
 from test_gpu_parity import check_case, run_gpu
+
+mg = pytest.importorskip("moe_grouped_block_amd")
 
 pytestmark = pytest.mark.gpu
 
@@ -57,5 +61,59 @@ CASES = draw_cases()
 def test_sweep_parity(name, base, over):
     case = synth.make_case(base, seed=5000 + CASES.index((name, base, over)), name=name, **over)
     got = run_gpu(case)
+    stats = check_case(case, got)
+    print(f"[gpu-case] {name} stats {stats}", flush=True)
+
+
+def draw_wide_cases(n=48, seed=777):
+    """Wider ranges (up to 13 column blocks, 9 K-steps, 11 experts, 1500
+    routed rows), norm_const powers of two, and for about half of the cases
+    a grid capped at 1-4 workgroups (the moegg_set_grid_limit hook)."""
+    rng = np.random.default_rng(seed)
+    acts, abs_ = list(BASE), list(KSTEP)
+    cases = []
+    for i in range(n):
+        act = acts[int(rng.integers(len(acts)))]
+        ab = abs_[int(rng.integers(len(abs_)))]
+        bwd = act.startswith("d")
+        d = "bf16" if (ab == "bf16" and bwd) else ("e4m3" if rng.random() < 0.5 else "bf16")
+        c = "bf16" if (not bwd and rng.random() < 0.3) else None
+        pair = act in ("swiglu", "geglu")
+        n_cols = int(rng.integers(1, 14)) * (64 if pair else 32)
+        k = int(rng.integers(1, 10)) * KSTEP[ab]
+        L = int(rng.integers(1, 12))
+        rows = int(rng.integers(1, 1500))
+        m_al = 256 if rng.random() < 0.25 else 128
+        if L >= 2 and rng.random() < 0.5:
+            route = dict(routing=("topk", rows, 2), prob=("softmax_picks",))
+        else:
+            route = dict(routing=("multinomial", rows), prob=("uniform",))
+        over = dict(ab=ab, d=d, c=c, L=L, K=k, N=n_cols, m_aligned=m_al, alpha=("uniform", 0.5, 2.0), **route)
+        if act == "dswiglu":
+            over["beta"] = ("uniform", 0.5, 2.0)
+        if ab == "e2m1x2":
+            over.update(a_std=1.0, b_std=1.0, clip=6.0)
+        if act in ("geglu", "dgeglu"):
+            over.update(glu_clamp_min=-2.5, glu_clamp_max=2.0)
+        if rng.random() < 0.3:
+            over["norm_const"] = float(2.0 ** int(rng.integers(-3, 4)))
+        grid = int(rng.integers(1, 5)) if rng.random() < 0.5 else 0
+        cases.append((f"wide{i:02d}_{act}_{ab}_{d}_g{grid}", BASE[act], over, grid))
+    return cases
+
+
+WIDE = draw_wide_cases()
+
+
+@pytest.mark.parametrize("idx", range(len(WIDE)), ids=[c[0] for c in WIDE])
+def test_wide_sweep_parity(idx):
+    name, base, over, grid = WIDE[idx]
+    case = synth.make_case(base, seed=9000 + idx, name=name, **over)
+    print(f"[gpu-case] {name} grid limit {grid or 'none'}", flush=True)
+    prev = mg.moegg_set_grid_limit(grid)
+    try:
+        got = run_gpu(case)
+    finally:
+        mg.moegg_set_grid_limit(prev)
     stats = check_case(case, got)
     print(f"[gpu-case] {name} stats {stats}", flush=True)
