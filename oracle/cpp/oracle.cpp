@@ -14,7 +14,9 @@
 #include <cstring>
 #include <vector>
 
+#ifdef _OPENMP
 #include <omp.h>
+#endif
 
 namespace {
 
@@ -321,7 +323,13 @@ extern "C" {
 
 const char* ox_last_error(void) { return g_error; }
 
-int ox_threads(void) { return omp_get_max_threads(); }
+int ox_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 void ox_decode(int fmt, const uint8_t* codes, int64_t count, double* out) {
   for (int64_t i = 0; i < count; ++i) {

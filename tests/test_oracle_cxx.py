@@ -150,3 +150,64 @@ def test_planted_mistake_in_cpp_oracle_is_caught(tmp_path, name, old, new, pins)
         except AssertionError:
             caught += 1
     assert caught, f"no pin caught the planted mistake {name}"
+
+
+# ---------------------------------------------------------------------------
+# the C++ oracle under the address and undefined-behaviour sanitizers
+# ---------------------------------------------------------------------------
+
+_SAN_RECIPES = ["swiglu_fp8_e4m3", "srelu_fp4_tanh_e4m3", "dswiglu_bf16", "dgeglu_e5m2_bf16_amax",
+                "dsrelu_mxfp4_e4m3_n288", "geglu_fp4_e4m3_c"]
+
+
+@pytest.fixture(scope="module")
+def sanitized_driver(tmp_path_factory):
+    """oracle.cpp + run_case.cpp built with -fsanitize=address,undefined (no
+    OpenMP), so that an out-of-bounds access or undefined operation in the
+    oracle aborts the run."""
+    d = tmp_path_factory.mktemp("asan")
+    exe = d / "run_case"
+    r = subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-ffp-contract=off",
+                        "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                        "-o", str(exe), os.path.join(cxx.HERE, "oracle.cpp"), os.path.join(cxx.HERE, "run_case.cpp")],
+                       capture_output=True, text=True)
+    if r.returncode:
+        pytest.skip("no sanitizer runtime for g++ here: " + r.stderr[-300:])
+    return exe
+
+
+@pytest.mark.parametrize("name", _SAN_RECIPES)
+def test_cpp_oracle_under_sanitizers(sanitized_driver, tmp_path, name):
+    base, over = SMALL[name]
+    case = synth.make_case(base, seed=1000 + sorted(SMALL).index(name), name=name, **over)
+    p, arr = case.problem, case.arrays
+    rows = np.arange(p["valid_m"], dtype=np.int64)
+    kv = cxx._problem(p)
+    nc = float(np.asarray(arr["norm_const"], np.float32).reshape(-1)[0]) if "norm_const" in arr else 1.0
+    with open(tmp_path / "problem.txt", "w") as f:
+        for key in ("num_groups", "valid_m", "n", "k", "ab", "act", "d_fp8", "c_out", "srelu_s", "glu_gamma",
+                    "geglu_alpha", "linear_offset", "clamp_min", "clamp_max"):
+            f.write(f"{key} {float(getattr(kv, key))!r}\n")
+        f.write(f"norm_const {nc!r}\nnrows {len(rows)}\n")
+    code_t = np.uint16 if p["ab_dtype"] == "bf16" else np.uint8
+    files = {"a": ("a", code_t), "sfa": ("sfa", np.uint8), "b": ("b", code_t), "sfb": ("sfb", np.uint8),
+             "po": ("padded_offsets", np.int32), "alpha": ("alpha", np.float32), "beta": ("beta", np.float32),
+             "prob": ("prob", np.float32), "c_in": ("c_in", np.uint16)}
+    for fname, (key, dt) in files.items():
+        if arr.get(key) is not None:
+            np.ascontiguousarray(arr[key], dtype=dt).tofile(tmp_path / f"{fname}.bin")
+    rows.tofile(tmp_path / "rows.bin")
+    r = subprocess.run([str(sanitized_driver), str(tmp_path)], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, f"sanitized oracle failed on {name}:\n{r.stderr[-3000:]}"
+    ref = cxx.grouped_gemm(p, arr)
+    m, n, no = len(rows), p["n"], cxx.n_out(p)
+    bwd = p["act"] in ("dswiglu", "dsrelu", "dgeglu")
+    got_d = np.fromfile(tmp_path / "d.out", np.float64).reshape(m, no)
+    assert np.array_equal(got_d, ref["dc" if bwd else "d"])
+    assert np.array_equal(np.fromfile(tmp_path / "cr.out", np.float64).reshape(m, n), ref["r" if bwd else "c"])
+    if "d_code" in ref:
+        assert np.array_equal(np.fromfile(tmp_path / "d_code.out", np.uint8).reshape(m, no), ref["d_code"])
+        assert np.array_equal(np.fromfile(tmp_path / "sfd_row.out", np.uint8).reshape(m, no // 32), ref["sfd_row"])
+    if "amax2" in ref or "amax" in ref:
+        want = ref.get("amax2", ref.get("amax"))
+        assert np.array_equal(np.fromfile(tmp_path / "amax.out", np.float64).reshape(want.shape), want)
