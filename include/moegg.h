@@ -10,7 +10,7 @@
  *   rows m of A in [padded_offsets[g-1], padded_offsets[g]) belong to expert g
  *   acc[m,n] = sum_k dequant(A[m,k], SFA) * dequant(B[g,n,k], SFB)
  *   C = alpha_g * acc                       (forward activations)
- *   R = alpha_g^2 * acc                     (dSwiGLU backward)
+ *   R = alpha_g^2 * acc                     (backward activations)
  *   then the activation / gating epilogue selected by `act`, and the output
  *   formatting selected by `d_dtype`:
  *     BF16  D (round to nearest even) + per-group amax = max |D| (fp32, before
@@ -54,7 +54,8 @@
  *   D, D_col (valid_m, N_out) BF16 or E4M3 codes   N_out = N/2 for SwiGLU and
  *                                                  GeGLU, 2N for dSwiGLU and
  *                                                  dGeGLU, else N
- *                                                  (dC for dSwiGLU / dsReLU)
+ *                                                  (dC for the backward
+ *                                                  activations)
  *   SFD_row (valid_m, N_out/32) E8M0; SFD_col (N_out, valid_m/32) E8M0
  *   amax    (L) fp32, written by the call (zero-filled first); for dSwiGLU /
  *           dGeGLU with MX operands and a BF16 dC, (L, 2): the max |dC| of
@@ -177,7 +178,7 @@ typedef struct moegg_args {
   const float* norm_const;       /* required iff d_dtype == E4M3 */
   const void* c_in;              /* backward: saved forward C, BF16 (valid_m, 2N) or (valid_m, N) dsReLU */
   void* c;                       /* optional C output (c_dtype BF16) */
-  void* d;                       /* D (or dC for dSwiGLU) */
+  void* d;                       /* D (or dC for the backward activations) */
   void* d_col;                   /* E4M3 only */
   uint8_t* sfd_row;              /* E4M3 only */
   uint8_t* sfd_col;              /* E4M3 only */
