@@ -102,3 +102,19 @@ EDGE = {
     # groups aligned to 256 rows (the pages' default padding)
     "edge_m_aligned_256": ("fc1_swiglu_l8", dict(L=3, K=256, N=128, m_aligned=256, routing=("topk", 300, 2))),
 }
+
+# SwiGLU over E2M1 operands with E4M3 D where a column block holds one
+# routed row whose gates lie near -88: the sigmoid of those gates is below
+# FP32's normal range, so the FP32 epilogue gives 0 where the float64 oracle
+# keeps ~1e-35 (drawn by a randomized run; seed of each case given here)
+UNDERFLOW = {
+    "underflow_swiglu_fp4_l26_zipf": ("fc1_swiglu_l8", dict(
+        ab="e2m1x2", d="e4m3", c=None, L=26, K=2816, N=1024, m_aligned=128, alpha=("uniform", 0.5, 2.0),
+        routing=("topk_zipf", 5721, 3, 1.1, 2), prob=("softmax_picks",), a_std=1.0, b_std=1.0, clip=6.0), 20163),
+    "underflow_swiglu_fp4_l59": ("fc1_swiglu_l8", dict(
+        ab="e2m1x2", d="e4m3", c=None, L=59, K=1024, N=640, m_aligned=256, alpha=("uniform", 0.5, 2.0),
+        routing=("multinomial", 5355), prob=("uniform",), a_std=1.0, b_std=1.0, clip=6.0), 20164),
+    "underflow_swiglu_fp4_l22_c_nc4": ("fc1_swiglu_l8", dict(
+        ab="e2m1x2", d="e4m3", c="bf16", L=22, K=1792, N=1216, m_aligned=128, alpha=("uniform", 0.5, 2.0),
+        routing=("multinomial", 5751), prob=("uniform",), a_std=1.0, b_std=1.0, clip=6.0, norm_const=4.0), 20242),
+}

@@ -34,8 +34,9 @@ def pytest_collection_modifyitems(config, items):
 def pytest_terminal_summary(terminalreporter):
     """Totals of the rule-2 (FP8) comparisons of the run: scale bytes checked,
     those that differ within the 1e-5 power-of-two window, those accepted only
-    under the accumulation allowance (capped per tensor), and how many of those
-    needed the matrix core's truncation term."""
+    under the accumulation allowance (capped per tensor), how many of those
+    needed the matrix core's truncation term, and the blocks that match once
+    sigmoid factors below FP32's range are taken as 0."""
     try:
         from parity_util import RULE2_LOG
     except ImportError:
@@ -46,12 +47,14 @@ def pytest_terminal_summary(terminalreporter):
     mism = sum(s["scale_boundary_mismatch"] for _, s in RULE2_LOG)
     widened = sum(s["scale_acc_allowance"] for _, s in RULE2_LOG)
     trunc = sum(s.get("scale_mfma_truncation", 0) for _, s in RULE2_LOG)
+    under = sum(s.get("scale_fp32_underflow", 0) for _, s in RULE2_LOG)
     beyond = sum(s["beyond_1ulp"] for _, s in RULE2_LOG)
     elems = sum(s["elements"] for _, s in RULE2_LOG)
     worst = max(RULE2_LOG, key=lambda x: x[1]["scale_acc_allowance"] / max(x[1]["scale_blocks"], 1))
     terminalreporter.write_line(
         f"rule 2 over {len(RULE2_LOG)} FP8 tensors: {blocks} E8M0 scale bytes, {mism} differ by one at a "
         f"power-of-two boundary, {widened} of them only inside the accumulation allowance "
-        f"({trunc} decided with the matrix core's truncation) "
+        f"({trunc} decided with the matrix core's truncation), {under} matching with FP32-underflowed sigmoid "
+        f"factors at 0 "
         f"(largest share {worst[1]['scale_acc_allowance']}/{worst[1]['scale_blocks']} in {worst[0]}); "
         f"{beyond} of {elems} codes beyond one E4M3 ULP")

@@ -26,6 +26,21 @@ nothing this way (tests/hw/mfma_f8_accumulation.hip measures it).  It is
 evaluated only for the blocks whose scale byte differs outside the FP32
 allowance (rule2's `refine`), and only at the accumulator elements that feed
 them.
+
+FP32 underflow of the sigmoid (rule2's `fragile`): the pages evaluate the
+epilogue in FP32.  The logistic of an argument t below about -87.3 is under
+FP32's smallest normal number 2^-126, and its exponential overflows FP32
+below about -88.7, so an FP32 evaluation of x * g * sigmoid(g) (SwiGLU),
+the GeGLU product or the dGLU gradients gives 0 there or a subnormal
+intermediate, while the float64 oracle keeps values near 1e-35; the
+library's exp2 / rcp flush such results to zero.  Elements whose sigmoid
+factor is below 2^-96 (t < -66.5, so that a product carrying it can fall
+under 2^-126) may therefore be 0: a block whose scale byte differs from the
+reference is accepted if the byte lies between the reference's and that of
+the reference with all those elements at 0 (any of them may have been
+flushed), and its codes are then compared with the reference requantised at
+that byte.  In every block those elements match either their code or zero.
+Blocks accepted this way are counted (`scale_fp32_underflow`).
 """
 from __future__ import annotations
 
@@ -141,6 +156,48 @@ def mfma_truncation(case, ref, lrows, acols):
     return out
 
 
+UNDERFLOW_LOG2 = -96.0      # sigmoid factors below 2^UNDERFLOW_LOG2 may underflow FP32 (module docstring)
+
+
+def sigmoid_arguments(case, ref):
+    """The logistic's argument behind every output element (the shape of
+    ref['d'], or ref['dc'] for the backward activations), or None for an
+    activation without one: the gate block of each SwiGLU pair, geglu_alpha
+    times the clamped gate of each GeGLU pair, and for dSwiGLU / dGeGLU the
+    saved gate (times beta, or geglu_alpha after the upper clamp) of each
+    output pair."""
+    p, ar = case.problem, case.arrays
+    act = p["act"]
+    if act in ("swiglu", "geglu"):
+        c = ref["c"]
+        r, n = c.shape
+        pairs = c.reshape(r, n // 64, 2, 32)
+        if act == "swiglu":
+            t = pairs[:, :, 1, :]
+        else:
+            _, ga, _, cmin, cmax = G.glu_params(p)
+            t = ga * np.clip(pairs[:, :, 0, :], cmin, cmax)
+        return t.reshape(r, n // 2)
+    if act in ("dswiglu", "dgeglu"):
+        rows, grp = ref["rows"], ref["group"]
+        x = F.decode_bf16(ar["c_in"][rows])
+        r, n2 = x.shape
+        xs = x.reshape(r, n2 // 64, 2, 32)
+        if act == "dswiglu":
+            t = np.asarray(ar["beta"], np.float64)[grp][:, None, None] * xs[:, :, 1, :]
+        else:
+            _, ga, _, _, cmax = G.glu_params(p)
+            t = ga * np.minimum(xs[:, :, 0, :], cmax)
+        return np.repeat(t[:, :, None, :], 2, axis=2).reshape(r, n2)
+    return None
+
+
+def underflow_mask(case, ref):
+    """Output elements whose sigmoid factor lies below 2^UNDERFLOW_LOG2, or None."""
+    t = sigmoid_arguments(case, ref)
+    return None if t is None else t < UNDERFLOW_LOG2 * np.log(2.0)
+
+
 def acc_columns(act, ocols):
     """GEMM (accumulator) columns that the output columns `ocols` of an
     activation depend on."""
@@ -223,7 +280,7 @@ def acc_error_bound(case, ref, extra=None):
     return np.minimum(out, 1.0)
 
 
-def rule2(gpu_codes, gpu_sf, ref_d64, nc, axis, what="", rel_bound=None, refine=None):
+def rule2(gpu_codes, gpu_sf, ref_d64, nc, axis, what="", rel_bound=None, refine=None, fragile=None):
     """Compare E4M3 codes + E8M0 scales for row blocks (axis='row', blocks of 32
     columns) or column blocks (axis='col', blocks of 32 rows; ref rows must be
     whole aligned blocks).  gpu_sf layout: (rows, cols/32) for rows,
@@ -231,54 +288,91 @@ def rule2(gpu_codes, gpu_sf, ref_d64, nc, axis, what="", rel_bound=None, refine=
     acc_error_bound) widens the power-of-two allowance of a block by the
     error its amax can carry from the accumulation; `refine` (make_refine),
     given the blocks that differ outside that allowance, returns the
-    allowance with the matrix core's exact truncation at those blocks.
+    allowance with the matrix core's exact truncation at those blocks;
+    `fragile` (underflow_mask) marks elements that FP32 may flush to 0.
     Returns a stats dict."""
-    if axis == "row":
-        ref_codes, ref_sf = G.quantize_rows(ref_d64, nc)
-        d32 = ref_d64.astype(np.float32)
-        r, n = d32.shape
-        amax = np.abs(d32).reshape(r, n // 32, 32).max(axis=2)
-        sf_bcast = lambda s: np.repeat(s, 32, axis=1)
-    else:
-        ref_codes, ref_sf_t = G.quantize_cols(ref_d64, nc)
-        ref_sf = ref_sf_t.T                       # (r/32, n)
-        gpu_sf = np.asarray(gpu_sf).T
-        d32 = ref_d64.astype(np.float32)
-        r, n = d32.shape
-        amax = np.abs(d32).reshape(r // 32, 32, n).max(axis=1)
-        sf_bcast = lambda s: np.repeat(s, 32, axis=0)
-    sf32 = (np.float32(nc) * amax.astype(np.float32)) * G.RCP_MAX_E4M3
+    gpu_sf = np.asarray(gpu_sf)
+    if axis == "col":
+        gpu_sf = gpu_sf.T                         # (r/32, n)
 
-    def tolerance(rb):
+    def reference(d64):
+        """codes, scale bytes (block layout), float32 block amax and sf of d64"""
+        d32 = d64.astype(np.float32)
+        r, n = d32.shape
+        if axis == "row":
+            codes, sf = G.quantize_rows(d64, nc)
+            amax = np.abs(d32).reshape(r, n // 32, 32).max(axis=2)
+        else:
+            codes, sf_t = G.quantize_cols(d64, nc)
+            sf = sf_t.T
+            amax = np.abs(d32).reshape(r // 32, 32, n).max(axis=1)
+        return codes, sf, amax, (np.float32(nc) * amax.astype(np.float32)) * G.RCP_MAX_E4M3
+
+    def blocks_of(x):
+        r, n = x.shape
+        return x.reshape(r, n // 32, 32) if axis == "row" else x.reshape(r // 32, 32, n)
+
+    def sf_bcast(s):
+        return np.repeat(s, 32, axis=1 if axis == "row" else 0)
+
+    def tolerance(rb, d64, amax):
         if rb is None:
             return BOUNDARY_REL
         # the computed amax is within max_e(rel_e |d_e|) of the exact one
-        err = np.asarray(rb, np.float64) * np.abs(np.asarray(ref_d64, np.float64))
-        err = err.reshape(r, n // 32, 32).max(axis=2) if axis == "row" else err.reshape(r // 32, 32, n).max(axis=1)
+        err = blocks_of(np.asarray(rb, np.float64) * np.abs(np.asarray(d64, np.float64)))
+        err = err.max(axis=2) if axis == "row" else err.max(axis=1)
         with np.errstate(divide="ignore", invalid="ignore"):
             return BOUNDARY_REL + np.where(amax > 0, err / amax, 0.0)
 
-    tol = tolerance(rel_bound)
-    gpu_sf = np.asarray(gpu_sf)
+    ref_codes, ref_sf, amax, sf32 = reference(ref_d64)
+    tol = tolerance(rel_bound, ref_d64, amax)
     mism = gpu_sf != ref_sf
     one_apart = np.abs(gpu_sf.astype(int) - ref_sf.astype(int)) == 1
     allowed = near_power_of_two(sf32, tol) & one_apart
     bad_sf = mism & ~allowed
+    # FP32 underflow of sigmoid factors: any of the fragile elements may be 0,
+    # so the block's amax lies between that of the reference with all of them
+    # at 0 and the reference's own; such a block is then compared with its
+    # codes requantised at the library's scale byte, fragile elements
+    # matching either that code or zero
+    under = np.zeros_like(bad_sf)
+    zero_ok = np.zeros(np.shape(ref_d64), bool)
+    if bad_sf.any() and fragile is not None and np.any(fragile):
+        fragile = np.asarray(fragile, bool)
+        dz = np.where(fragile, 0.0, ref_d64)
+        _, z_sf, z_amax, z_sf32 = reference(dz)
+        fb = blocks_of(fragile)
+        has_f = fb.any(axis=2) if axis == "row" else fb.any(axis=1)
+        lo, hi = np.minimum(z_sf, ref_sf).astype(int), np.maximum(z_sf, ref_sf).astype(int)
+        g = gpu_sf.astype(int)
+        z_near = near_power_of_two(z_sf32, tolerance(rel_bound, dz, z_amax))
+        in_range = ((g >= lo) & (g <= hi)) | (z_near & (np.abs(g - z_sf.astype(int)) == 1))
+        under = bad_sf & has_f & in_range
+        bad_sf &= ~under
+        if under.any():
+            ub = sf_bcast(under)
+            requant = G.quantize_block_values(np.asarray(ref_d64, np.float32), sf_bcast(gpu_sf), nc)
+            ref_codes = np.where(ub, requant, ref_codes)
+            ref_sf = np.where(under, gpu_sf, ref_sf)
+            mism = gpu_sf != ref_sf
     refined = 0
     if bad_sf.any() and refine is not None:
         refined = int(bad_sf.sum())
-        tol = tolerance(refine(np.argwhere(bad_sf)))
-        allowed = near_power_of_two(sf32, tol) & one_apart
+        tol = tolerance(refine(np.argwhere(bad_sf)), ref_d64, amax)
+        allowed = np.where(under, allowed, near_power_of_two(sf32, tol) & one_apart)
         bad_sf = mism & ~allowed
     assert not bad_sf.any(), (f"{what}: {int(bad_sf.sum())} scale bytes differ away from a "
                               f"power-of-two boundary, e.g. at {np.argwhere(bad_sf)[:5].tolist()}")
     # accepted only because of the accumulation allowance (outside the 1e-5 window)
-    widened = int((mism & allowed & ~near_power_of_two(sf32, BOUNDARY_REL)).sum())
+    widened = int((mism & allowed & ~under & ~near_power_of_two(sf32, BOUNDARY_REL)).sum())
     cap = max(1, int(ACC_ALLOW_FRAC * mism.size))
     assert widened <= cap, (f"{what}: {widened} of {mism.size} scale bytes pass only under the "
                             f"accumulation allowance (cap {cap})")
+    if fragile is not None:
+        # a fragile element may be 0 in any block
+        zero_ok = np.asarray(fragile, bool) & ((np.asarray(gpu_codes) & 0x7F) == 0)
     same = ~sf_bcast(mism)
-    ulp = np.abs(_ordinal(gpu_codes) - _ordinal(ref_codes))
+    ulp = np.where(zero_ok, 0, np.abs(_ordinal(gpu_codes) - _ordinal(ref_codes)))
     over = (ulp > 1) & same
     # elements of blocks whose scales legitimately differ: compare dequantised values
     if (~same).any():
@@ -295,7 +389,7 @@ def rule2(gpu_codes, gpu_sf, ref_d64, nc, axis, what="", rel_bound=None, refine=
                                 f"(e.g. {np.argwhere(over)[:5].tolist()})")
     st = dict(elements=int(over.size), beyond_1ulp=n_over, exact=int((ulp == 0).sum()),
               scale_boundary_mismatch=int(mism.sum()), scale_acc_allowance=widened, scale_blocks=int(mism.size),
-              scale_mfma_truncation=refined)
+              scale_mfma_truncation=refined, scale_fp32_underflow=int(under.sum()))
     RULE2_LOG.append((what, st))
     return st
 

@@ -10,8 +10,9 @@ import pytest
 import oracle
 import synth
 from oracle import formats as F
-from cases import EDGE, SMALL
-from parity_util import acc_error_bound, amax_rule, decode_bf16, make_refine, pick_row_blocks, rule1, rule2
+from cases import EDGE, SMALL, UNDERFLOW
+from parity_util import (acc_error_bound, amax_rule, decode_bf16, make_refine, pick_row_blocks, rule1, rule2,
+                         underflow_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,11 +52,12 @@ def check_case(case, got, rows=None):
         if p["d_dtype"] == "e4m3":
             nc = float(case.arrays["norm_const"][0])
             rb = acc_error_bound(case, ref)
+            fz = underflow_mask(case, ref)
             stats["d_row"] = rule2(got["d"][r], got["sfd_row"][r], ref["dc"], nc, "row", "dC/SFD_row", rb,
-                                   make_refine(case, ref, "row"))
+                                   make_refine(case, ref, "row"), fz)
             blocks = np.unique(r // 32)
             stats["d_col"] = rule2(got["d_col"][r], got["sfd_col"][:, blocks], ref["dc"], nc, "col",
-                                   "dC_col/SFD_col", rb, make_refine(case, ref, "col"))
+                                   "dC_col/SFD_col", rb, make_refine(case, ref, "col"), fz)
             return stats
         g2 = np.repeat(grp[:, None], ref["dc"].shape[1], axis=1)
         stats["dc"] = rule1(decode_bf16(got["d"][r]), ref["dc"], g2, "dC")
@@ -75,11 +77,12 @@ def check_case(case, got, rows=None):
     else:
         nc = float(case.arrays["norm_const"][0])
         rb = acc_error_bound(case, ref)
+        fz = underflow_mask(case, ref)
         stats["d_row"] = rule2(got["d"][r], got["sfd_row"][r], ref["d"], nc, "row", "D/SFD_row", rb,
-                               make_refine(case, ref, "row"))
+                               make_refine(case, ref, "row"), fz)
         blocks = np.unique(r // 32)
         stats["d_col"] = rule2(got["d_col"][r], got["sfd_col"][:, blocks], ref["d"], nc, "col", "D_col/SFD_col", rb,
-                               make_refine(case, ref, "col"))
+                               make_refine(case, ref, "col"), fz)
     return stats
 
 
@@ -127,6 +130,19 @@ def test_half_segment_parity(name):
 # ---------------------------------------------------------------------------
 
 # EDGE: see tests/cases.py
+
+
+@pytest.mark.parametrize("name", list(UNDERFLOW))
+def test_fp32_underflow_parity(name):
+    """Blocks carried by sigmoid factors below FP32's normal range: the
+    library's FP32 epilogue gives 0 there; parity holds with those elements
+    at 0 (rule 2's `fragile`), and the case does reach that path."""
+    base, over, seed = UNDERFLOW[name]
+    case = synth.make_case(base, seed=seed, name=name, **over)
+    got = run_gpu(case)
+    stats = check_case(case, got)
+    assert stats["d_col"]["scale_fp32_underflow"] > 0
+    print(f"[gpu-case] {name} stats {stats}", flush=True)
 
 
 @pytest.mark.parametrize("name", list(EDGE))

@@ -160,3 +160,100 @@ def test_refine_decides_blocks_outside_the_fp32_allowance():
     assert st["scale_mfma_truncation"] == 1 and st["scale_acc_allowance"] == 1
     with pytest.raises(AssertionError, match="away from a power-of-two boundary"):
         rule2(codes, sf, d, 1.0, "row", "planted", None, refine=lambda bad: np.zeros_like(d))
+
+
+# ---------------------------------------------------------------------------
+# FP32 underflow of sigmoid factors (parity_util module docstring)
+# ---------------------------------------------------------------------------
+
+from types import SimpleNamespace  # noqa: E402
+
+from parity_util import UNDERFLOW_LOG2, sigmoid_arguments, underflow_mask  # noqa: E402
+
+
+def _quantised(d, nc=1.0):
+    codes, sf = G.quantize_rows(d, nc)
+    return codes, sf
+
+
+def test_underflowed_block_matches_the_zeroed_reference_and_is_counted():
+    rng = np.random.default_rng(3)
+    d = rng.standard_normal((4, 64))
+    d[2, 32:] = rng.standard_normal(32) * 1e-35        # a whole row block carried by sigmoid(-88)
+    fragile = np.zeros_like(d, bool)
+    fragile[2, 32:] = True
+    # the library's FP32 result: those elements flushed to 0
+    codes, sf = _quantised(np.where(fragile, 0.0, d))
+    st = rule2(codes, sf, d, 1.0, "row", "underflow", fragile=fragile)
+    assert st["scale_fp32_underflow"] == 1 and sf[2, 1] == 0
+    with pytest.raises(AssertionError):                 # without the mask the block is a mismatch
+        rule2(codes, sf, d, 1.0, "row", "underflow")
+
+
+def test_underflow_excuses_only_the_zeroed_values():
+    rng = np.random.default_rng(4)
+    d = rng.standard_normal((4, 64))
+    d[1, :32] = 1e-35
+    fragile = np.zeros_like(d, bool)
+    fragile[1, :32] = True
+    codes, sf = _quantised(np.where(fragile, 0.0, d))
+    sf = sf.copy()
+    sf[1, 0] = 9                                         # neither the reference byte nor the zeroed one
+    with pytest.raises(AssertionError):
+        rule2(codes, sf, d, 1.0, "row", "underflow", fragile=fragile)
+    # a fragile element that is not the block's maximum changes nothing
+    d2 = rng.standard_normal((4, 64))
+    d2[0, 5] = 1e-35
+    f2 = np.zeros_like(d2, bool)
+    f2[0, 5] = True
+    codes2, sf2 = _quantised(d2)
+    assert rule2(codes2, sf2, d2, 1.0, "row", "underflow", fragile=f2)["scale_fp32_underflow"] == 0
+
+
+def _fake(act, ref, arrays=None, **problem):
+    return SimpleNamespace(problem=dict(act=act, **problem), arrays=arrays or {}), ref
+
+
+def test_sigmoid_arguments_follow_each_activation():
+    r = 2
+    c = np.arange(r * 128, dtype=np.float64).reshape(r, 128) - 200.0
+    # SwiGLU: the gate is the second block of each pair [X_b | G_b]
+    case, ref = _fake("swiglu", {"c": c})
+    t = sigmoid_arguments(case, ref)
+    assert t.shape == (r, 64)
+    assert np.array_equal(t[:, :32], c[:, 32:64]) and np.array_equal(t[:, 32:], c[:, 96:128])
+    # GeGLU: geglu_alpha times the clamped first block [G_b | U_b]
+    case, ref = _fake("geglu", {"c": c}, geglu_alpha=2.0, glu_clamp_min=-150.0, glu_clamp_max=10.0)
+    t = sigmoid_arguments(case, ref)
+    assert np.array_equal(t[:, :32], 2.0 * np.clip(c[:, :32], -150.0, 10.0))
+    # dSwiGLU: beta_g times the saved gate, for both elements of the output pair
+    x = np.zeros((r, 128), np.float32)
+    x[:, 32:64] = -100.0
+    x[:, 96:] = 3.0
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    ref = {"rows": np.arange(r), "group": np.array([0, 1])}
+    case, _ = _fake("dswiglu", ref, arrays={"c_in": bits, "beta": np.array([1.0, 0.5], np.float32)})
+    t = sigmoid_arguments(case, ref)
+    assert t.shape == (r, 128)
+    assert np.all(t[0, :64] == -100.0) and np.all(t[1, :64] == -50.0) and np.all(t[:, 64:] == [[3.0], [1.5]])
+    m = underflow_mask(case, ref)
+    assert m[0, :64].all() and not m[1].any()           # -100 < -66.5 (2^-96); -50 is not
+    assert UNDERFLOW_LOG2 * np.log(2.0) < -66.0
+    # activations without a sigmoid: no mask
+    case, ref = _fake("srelu", {"c": c})
+    assert sigmoid_arguments(case, ref) is None
+
+
+def test_a_fragile_element_may_be_zero_inside_a_matching_block():
+    d = np.zeros((1, 32))
+    d[0, 0] = 1.0                                       # block maximum, not fragile
+    d[0, 1] = 2.0 ** -8                                 # a code of its own at this scale
+    fragile = np.zeros_like(d, bool)
+    fragile[0, 1] = True
+    codes, sf = _quantised(d)
+    assert codes[0, 1] != 0
+    flushed = codes.copy()
+    flushed[0, 1] = 0
+    assert rule2(flushed, sf, d, 1.0, "row", "zeroed", fragile=fragile)["beyond_1ulp"] == 0
+    with pytest.raises(AssertionError):                 # 1 of 32 codes off: above the 0.1 % bar
+        rule2(flushed, sf, d, 1.0, "row", "zeroed")
