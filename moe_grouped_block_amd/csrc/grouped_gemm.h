@@ -136,6 +136,19 @@ __device__ __forceinline__ float tanh_nonneg(float x) {
   return x < 0.125f ? series : big;
 }
 
+// tanh(x) and sech(x)^2 = 1 - tanh(x)^2 for x >= 0, the latter free of the
+// cancellation of 1 - t*t as t approaches 1: with e = e^-2x,
+// t = (1 - e) / (1 + e) (below 1/8 the odd series, as in tanh_nonneg) and
+// sech^2 = 4 e / (1 + e)^2 for every x (no subtraction).
+__device__ __forceinline__ void tanh_sech2_nonneg(float x, float& t, float& sech2) {
+  const float x2 = x * x;
+  const float series = x * (1.0f + x2 * (-1.0f / 3.0f + x2 * (2.0f / 15.0f + x2 * (-17.0f / 315.0f))));
+  const float e = __builtin_amdgcn_exp2f(-2.0f * kLog2e * x);
+  const float r = __builtin_amdgcn_rcpf(1.0f + e);
+  t = x < 0.125f ? series : (1.0f - e) * r;
+  sech2 = (4.0f * e) * (r * r);
+}
+
 // Cross-lane helpers on the VALU (DPP and the gfx950 permlane swaps), no LDS.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
@@ -1073,7 +1086,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
     } else if constexpr (ACT == ACT_DSRELU) {
       // sReLU backward (derived from "Grouped GEMM + sReLU (SM100)",
       // §Equations / §Tanh soft clamp): R = alpha^2 acc, C the saved forward
-      // C; with t = min(tanh(relu(C)/s), 1), c = s t: dC = R prob 2 c (1 - t^2),
+      // C; with t = min(tanh(relu(C)/s), 1), c = s t: dC = R prob 2 c sech^2(relu(C)/s)
+      // (= 1 - t^2, evaluated without its cancellation near t = 1),
       // dprob += R c^2 (s = 0: c = relu(C), dC = R prob 2 c)
       const float a2 = alpha * alpha;
       const float sc = p.srelu_s;
@@ -1144,9 +1158,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
               const float r = a2 * acc[tm][tn][v];
-              const float t = fminf(tanh_nonneg(fmaxf(cv[v], 0.0f) * rs), 1.0f);
+              float t, sech2;
+              tanh_sech2_nonneg(fmaxf(cv[v], 0.0f) * rs, t, sech2);
+              t = fminf(t, 1.0f);
               const float c = sc * t;
-              d[v] = r * pr[tm] * (2.0f * c * (1.0f - t * t));
+              d[v] = r * pr[tm] * (2.0f * c * sech2);
               dp += r * (c * c);
             }
           } else {

@@ -259,16 +259,17 @@ void activation_row(const ox_problem& p, const double* c, double pr, const doubl
     case OX_DSRELU: {
       // derivative of the sReLU forward ("Grouped GEMM + sReLU (SM100)",
       // §Equations / §Tanh soft clamp): f(C) = c^2 with c = s t,
-      // t = min(tanh(relu(C)/s), 1), f'(C) = 2 c (1 - t^2) (s = 0: c = relu(C),
-      // f' = 2 c); dC = R prob f'(C), dprob += R f(C)
+      // t = min(tanh(relu(C)/s), 1), f'(C) = 2 c (1 - t^2) = 2 c sech^2(relu(C)/s)
+      // (s = 0: c = relu(C), f' = 2 c); dC = R prob f'(C), dprob += R f(C)
       double acc = 0.0;
       for (int j = 0; j < n; ++j) {
         const double r = std::max(x[j], 0.0);
         double cv, fp;
         if (p.srelu_s > 0) {
           const double t = std::min(std::tanh(r / p.srelu_s), 1.0);
+          const double ch = std::cosh(r / p.srelu_s);
           cv = p.srelu_s * t;
-          fp = 2.0 * cv * (1.0 - t * t);
+          fp = 2.0 * cv / (ch * ch);              // 1 - t^2 = sech^2, free of its cancellation near t = 1
         } else {
           cv = r;
           fp = 2.0 * r;

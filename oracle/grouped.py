@@ -208,15 +208,19 @@ def dsrelu(rmat, c_saved, prob, s: float):
     is not among the sources, so the derivative is taken from the forward's
     §Equations / §Tanh soft clamp): with f(C) = (s * tanh(relu(C)/s))^2
     (relu(C)^2 for s = 0) and the forward D = prob * f(C),
-      dC    = R * prob * f'(C),  f'(C) = 2 c (1 - t^2) for C > 0 (t = tanh(C/s),
-              c = s t), 2 relu(C) for s = 0, 0 for C <= 0
+      dC    = R * prob * f'(C),  f'(C) = 2 c (1 - t^2) = 2 c sech^2(C/s) for C > 0
+              (t = tanh(C/s), c = s t; sech^2 evaluated directly, free of the
+              cancellation of 1 - t^2 as t -> 1), 2 relu(C) for s = 0, 0 for C <= 0
       dprob = sum over the N columns of R * f(C)
     """
     r = np.maximum(c_saved, 0.0)
     if s > 0:
         t = np.minimum(np.tanh(r / s), 1.0)
         c = s * t
-        fprime = 2.0 * c * (1.0 - t * t)
+        # 1 - t^2 = sech^2(r/s), the derivative of tanh, evaluated as such:
+        # written as 1 - t*t it cancels to nothing once t rounds to 1
+        with np.errstate(over="ignore"):
+            fprime = 2.0 * c / np.cosh(r / s) ** 2
     else:
         c = r
         fprime = 2.0 * r

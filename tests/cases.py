@@ -118,3 +118,20 @@ UNDERFLOW = {
         ab="e2m1x2", d="e4m3", c="bf16", L=22, K=1792, N=1216, m_aligned=128, alpha=("uniform", 0.5, 2.0),
         routing=("multinomial", 5751), prob=("uniform",), a_std=1.0, b_std=1.0, clip=6.0, norm_const=4.0), 20242),
 }
+
+# sReLU backward deep in the tanh clamp (s = 0.5 against C_in ~ N(0, 4^2), so
+# relu(C)/s reaches ~30): the gradient's factor 1 - tanh^2 = sech^2 must be
+# evaluated without the cancellation of 1 - t*t, on both sides (drawn by
+# randomized runs; seed of each case given here)
+SATURATED = {
+    "saturated_dsrelu_fp8_l48_n352": ("dsrelu_mxfp8_l32", dict(
+        ab="e4m3", d="e4m3", c=None, L=48, K=256, N=352, m_aligned=128, alpha=("uniform", 0.5, 2.0),
+        routing=("multinomial", 5537), prob=("uniform",), s=0.5), 20041),
+    "saturated_dsrelu_fp4_l51_zipf": ("dsrelu_mxfp8_l32", dict(
+        ab="e2m1x2", d="e4m3", c=None, L=51, K=768, N=480, m_aligned=256, alpha=("uniform", 0.5, 2.0),
+        routing=("topk_zipf", 3197, 3, 1.1, 2), prob=("softmax_picks",), a_std=1.0, b_std=1.0, clip=6.0,
+        s=0.5), 20213),
+    "saturated_dsrelu_fp8_l24_bf16dc": ("dsrelu_mxfp8_l32", dict(
+        ab="e4m3", d="bf16", c=None, L=24, K=1152, N=384, m_aligned=256, alpha=("uniform", 0.5, 2.0),
+        routing=("topk", 3188, 2), prob=("softmax_picks",), s=0.5), 20261),
+}

@@ -40,7 +40,10 @@ reference is accepted if the byte lies between the reference's and that of
 the reference with all those elements at 0 (any of them may have been
 flushed), and its codes are then compared with the reference requantised at
 that byte.  In every block those elements match either their code or zero.
-Blocks accepted this way are counted (`scale_fp32_underflow`).
+Blocks accepted this way are counted (`scale_fp32_underflow`).  The same
+holds for the dsReLU gradient's factor sech^2(relu(C)/s), which FP32 loses
+once its exponential e^-2x does (x > 43.7); the mask takes it below 2^-96
+(x > 34).
 """
 from __future__ import annotations
 
@@ -193,7 +196,17 @@ def sigmoid_arguments(case, ref):
 
 
 def underflow_mask(case, ref):
-    """Output elements whose sigmoid factor lies below 2^UNDERFLOW_LOG2, or None."""
+    """Output elements whose sigmoid factor (or, for dsReLU with the tanh
+    clamp, whose factor sech^2(relu(C)/s) = 4 e^-2x / (1 + e^-2x)^2) lies
+    below 2^UNDERFLOW_LOG2, or None."""
+    p = case.problem
+    if p["act"] == "dsrelu":
+        s = float(p.get("srelu_tanh_s", 0.0))
+        if s <= 0:
+            return None
+        x = np.maximum(F.decode_bf16(case.arrays["c_in"][ref["rows"]]), 0.0) / s
+        log2_sech2 = 2.0 - 2.0 * x / np.log(2.0) - 2.0 * np.log2(1.0 + np.exp(-2.0 * x))
+        return log2_sech2 < UNDERFLOW_LOG2
     t = sigmoid_arguments(case, ref)
     return None if t is None else t < UNDERFLOW_LOG2 * np.log(2.0)
 

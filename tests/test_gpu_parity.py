@@ -10,7 +10,7 @@ import pytest
 import oracle
 import synth
 from oracle import formats as F
-from cases import EDGE, SMALL, UNDERFLOW
+from cases import EDGE, SATURATED, SMALL, UNDERFLOW
 from parity_util import (acc_error_bound, amax_rule, decode_bf16, make_refine, pick_row_blocks, rule1, rule2,
                          underflow_mask)
 
@@ -130,6 +130,17 @@ def test_half_segment_parity(name):
 # ---------------------------------------------------------------------------
 
 # EDGE: see tests/cases.py
+
+
+@pytest.mark.parametrize("name", list(SATURATED))
+def test_saturated_tanh_clamp_backward_parity(name):
+    """dsReLU with s = 0.5: most gradients sit deep in the tanh clamp, where
+    1 - tanh^2 must be evaluated as sech^2 (no cancellation) to match."""
+    base, over, seed = SATURATED[name]
+    case = synth.make_case(base, seed=seed, name=name, **over)
+    got = run_gpu(case)
+    stats = check_case(case, got)
+    print(f"[gpu-case] {name} stats {stats}", flush=True)
 
 
 @pytest.mark.parametrize("name", list(UNDERFLOW))

@@ -115,6 +115,10 @@ _MUTANTS = [
      "if (p.srelu_s > 0) r = p.srelu_s * std::min(std::tanh(r / p.srelu_s), 1.0);",
      "if (p.srelu_s > 0) r = std::min(std::tanh(r / p.srelu_s), 1.0);",
      [PP.test_srelu_properties]),
+    ("dsrelu_derivative_cancels",
+     "fp = 2.0 * cv / (ch * ch);",
+     "fp = 2.0 * cv * (1.0 - t * t);",
+     [PP.test_dsrelu_derivative_in_the_saturated_clamp]),
     ("dgeglu_up_mask_dropped",
      "d[64 * b + 32 + i] = (p.clamp_min <= up && up <= p.clamp_max) ? c[j] * pr * gc * s : 0.0;",
      "d[64 * b + 32 + i] = c[j] * pr * gc * s;",

@@ -634,3 +634,21 @@ def test_planted_block_order_swap_is_detected(monkeypatch):
     monkeypatch.setattr(G, "swiglu", swapped)
     out = oracle.grouped_gemm(p, arr)
     assert not np.allclose(out["d"][0], 1 / (1 + math.exp(-2)))
+
+
+def test_dsrelu_derivative_in_the_saturated_clamp(O):
+    """Far into the tanh clamp (relu(C)/s up to 300) the sReLU derivative's
+    factor 1 - tanh^2 = sech^2 must keep its value: checked against
+    4 e^-2x / (1 + e^-2x)^2, a form free of cancellation (an evaluation as
+    1 - t*t is 0 or all rounding error once t rounds to 1, x > ~19)."""
+    s = 0.5
+    x = np.array([0.01, 0.2, 3.0, 9.0, 15.0, 19.5, 30.0, 150.0])
+    c_saved = (x * s)[None, :]
+    R = np.ones_like(c_saved)
+    p = np.ones(1)
+    dc, _ = O.dsrelu(R, c_saved, p, s)
+    e = np.exp(-2.0 * x)
+    t = (1.0 - e) / (1.0 + e)
+    expect = 2.0 * s * t * 4.0 * e / (1.0 + e) ** 2
+    np.testing.assert_allclose(dc[0], expect, rtol=1e-12, atol=0)
+    assert dc[0, -1] > 0                                 # 4 e^-300: still a normal float64
