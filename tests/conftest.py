@@ -32,15 +32,25 @@ def pytest_collection_modifyitems(config, items):
 
 
 def pytest_terminal_summary(terminalreporter):
-    """Totals of the rule-2 (FP8) comparisons of the run: scale bytes checked,
-    those that differ within the 1e-5 power-of-two window, those accepted only
-    under the accumulation allowance (capped per tensor), how many of those
-    needed the matrix core's truncation term, and the blocks that match once
-    sigmoid factors below FP32's range are taken as 0."""
+    """Totals of the parity comparisons of the run.  Rule 2 (FP8): scale bytes
+    checked, those that differ from the oracle's, those accepted only under
+    the accumulation allowance (capped per tensor), how many of those needed
+    the matrix core's truncation and the outputs' envelopes, and the blocks
+    that match once sigmoid factors below FP32's range are taken as 0.
+    Rule 1 (BF16): elements accepted only within their accumulation
+    envelope."""
     try:
-        from parity_util import RULE2_LOG
+        from parity_util import RULE1_LOG, RULE2_LOG
     except ImportError:
         return
+    if RULE1_LOG:
+        acc = sum(a for _, a, _ in RULE1_LOG)
+        elems = sum(n for _, _, n in RULE1_LOG)
+        worst = max(RULE1_LOG, key=lambda x: x[1] / max(x[2], 1))
+        terminalreporter.write_line(
+            f"rule 1 over {len(RULE1_LOG)} BF16 tensors: {acc} of {elems} elements beyond 1e-2 of their group's "
+            f"largest output and within their accumulation envelope (largest share {worst[1]}/{worst[2]} in "
+            f"{worst[0]})")
     if not RULE2_LOG:
         return
     blocks = sum(s["scale_blocks"] for _, s in RULE2_LOG)
@@ -52,9 +62,9 @@ def pytest_terminal_summary(terminalreporter):
     elems = sum(s["elements"] for _, s in RULE2_LOG)
     worst = max(RULE2_LOG, key=lambda x: x[1]["scale_acc_allowance"] / max(x[1]["scale_blocks"], 1))
     terminalreporter.write_line(
-        f"rule 2 over {len(RULE2_LOG)} FP8 tensors: {blocks} E8M0 scale bytes, {mism} differ by one at a "
-        f"power-of-two boundary, {widened} of them only inside the accumulation allowance "
-        f"({trunc} decided with the matrix core's truncation), {under} matching with FP32-underflowed sigmoid "
-        f"factors at 0 "
+        f"rule 2 over {len(RULE2_LOG)} FP8 tensors: {blocks} E8M0 scale bytes, {mism} differ from the oracle's, "
+        f"{widened} of them only inside the accumulation allowance "
+        f"({trunc} decided with the matrix core's truncation and the outputs' envelopes), {under} matching with "
+        f"FP32-underflowed sigmoid factors at 0 "
         f"(largest share {worst[1]['scale_acc_allowance']}/{worst[1]['scale_blocks']} in {worst[0]}); "
         f"{beyond} of {elems} codes beyond one E4M3 ULP")

@@ -44,6 +44,23 @@ Blocks accepted this way are counted (`scale_fp32_underflow`).  The same
 holds for the dsReLU gradient's factor sech^2(relu(C)/s), which FP32 loses
 once its exponential e^-2x does (x > 43.7); the mask takes it below 2^-96
 (x > 34).
+
+Envelope of an output over its accumulators' error (output_envelope): an
+activation that saturates (the GeGLU clamps, sReLU's tanh clamp) keeps D
+small while C can be large, so where C has heavy cancellation and lands in
+the narrow range where D still moves, the accumulation error of C (the two
+parts above, times alpha) can move D by more than 1e-2 of the group's
+largest output.  For such an element the output_envelope is the least and
+the greatest value the activation takes while each accumulator it reads
+ranges over [acc - h, acc + h], h the FP32 ordering bound plus the 8-bit
+matrix core's truncation at that element; it is exact, as every activation
+here is monotone in each input or, for swish-type factors x sigmoid(a x),
+has its one interior extremum at a known point.  Rule 1 accepts an element
+outside its tolerance that lies within the envelope (widened by the same
+tolerance), counts it (RULE1_LOG) and allows at most RULE1_ALLOW_FRAC of
+a tensor's elements (at least one); rule 2's refine bounds a block's amax by
+the envelopes of its elements and accepts every scale byte that an amax in
+that range rounds to.
 """
 from __future__ import annotations
 
@@ -61,20 +78,45 @@ BOUNDARY_REL = 1e-5
 ACC_ALLOW_FRAC = 5e-4      # cap on scale bytes accepted only by the accumulation allowance
 
 
-def rule1(gpu, ref, grp, what=""):
-    """Return the worst per-group ratio; raise AssertionError if above tolerance."""
+RULE1_ALLOW_FRAC = 1e-3    # cap on elements accepted only by their accumulation envelope
+# every rule-1 comparison that used an envelope: (what, accepted, elements)
+RULE1_LOG = []
+
+
+def rule1(gpu, ref, grp, what="", envelope=None):
+    """Return the worst per-group ratio; raise AssertionError if above tolerance.
+
+    `envelope` (make_envelope), given the positions of the elements beyond
+    the tolerance, returns the range (lo, hi) their outputs can take under
+    the accumulation error (module docstring); an element within that range
+    widened by the tolerance passes and is counted."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    worst = 0.0
+    worst, accepted = 0.0, 0
     for g in np.unique(grp):
         sel = grp == g
         den = np.abs(ref[sel]).max() if sel.any() else 0.0
-        num = np.abs(gpu[sel] - ref[sel]).max() if sel.any() else 0.0
+        diff = np.abs(gpu[sel] - ref[sel]) if sel.any() else np.zeros(0)
+        num = diff.max() if diff.size else 0.0
         if den == 0.0:
             assert num == 0.0, f"{what}: group {g} reference is all zero but gpu differs by {num}"
             continue
+        beyond = diff > RULE1_TOL * den
+        if beyond.any() and envelope is not None:
+            pos = np.argwhere(sel)[beyond]
+            lo, hi = envelope(*pos.T)
+            gv = gpu[tuple(pos.T)]
+            ok = (gv >= lo - RULE1_TOL * den) & (gv <= hi + RULE1_TOL * den)
+            accepted += int(ok.sum())
+            diff[np.flatnonzero(beyond)[ok]] = 0.0
+            num = diff.max()
         worst = max(worst, num / den)
     assert worst <= RULE1_TOL, f"{what}: rule-1 ratio {worst:.3e} > {RULE1_TOL}"
+    cap = max(1, int(RULE1_ALLOW_FRAC * gpu.size))
+    assert accepted <= cap, (f"{what}: {accepted} of {gpu.size} elements pass only within their "
+                             f"accumulation envelope (cap {cap})")
+    if envelope is not None:
+        RULE1_LOG.append((what, accepted, int(gpu.size)))
     return worst
 
 
@@ -105,6 +147,15 @@ def near_power_of_two(sf32, tol=BOUNDARY_REL):
     r = np.round(np.log2(sf[pos]))
     out[pos] = np.abs(sf[pos] / np.exp2(r) - 1.0) < tol[pos]
     return out
+
+
+def _scale_byte(sf):
+    """E8M0 byte of the smallest power of two >= sf (float64), clamped to
+    [0, 254]; 0 for sf <= 0."""
+    sf = np.asarray(sf, np.float64)
+    mant, ex = np.frexp(np.where(sf > 0, sf, 1.0))
+    e = np.where(mant == 0.5, ex - 1, ex)
+    return np.where(sf > 0, np.clip(e + 127, 0, 254), 0)
 
 
 # FP32 accumulation error of the GEMM.  The pages accumulate the block-scaled
@@ -226,21 +277,136 @@ def acc_columns(act, ocols):
 
 
 def make_refine(case, ref, axis):
-    """rule2's `refine`: the allowance recomputed with the matrix core's exact
-    truncation at the accumulator elements of the given blocks."""
-    act = case.problem["act"]
+    """rule2's `refine`: for the given blocks ((x, y) pairs in rule2's block
+    layout), the range (lo, hi) of each block's amax when every element lies
+    anywhere in its output_envelope."""
 
     def refine(bad_blocks):
-        extra = np.zeros_like(ref["acc"])
-        for x, y in np.asarray(bad_blocks).tolist():
+        bad_blocks = np.asarray(bad_blocks, np.int64).reshape(-1, 2)
+        lo = np.zeros(len(bad_blocks))
+        hi = np.zeros(len(bad_blocks))
+        for i, (x, y) in enumerate(bad_blocks.tolist()):
             if axis == "row":
-                lrows, ocols = np.array([x]), np.arange(32 * y, 32 * y + 32)
+                lrows, ocols = np.full(32, x), np.arange(32 * y, 32 * y + 32)
             else:
-                lrows, ocols = np.arange(32 * x, 32 * x + 32), np.array([y])
-            acols = acc_columns(act, ocols)
-            extra[np.ix_(lrows, acols)] = mfma_truncation(case, ref, lrows, acols)
-        return acc_error_bound(case, ref, extra)
+                lrows, ocols = np.arange(32 * x, 32 * x + 32), np.full(32, y)
+            elo, ehi = output_envelope(case, ref, lrows, ocols)
+            least = np.where((elo <= 0) & (ehi >= 0), 0.0, np.minimum(np.abs(elo), np.abs(ehi)))
+            lo[i] = least.max()
+            hi[i] = np.maximum(np.abs(elo), np.abs(ehi)).max()
+        return lo, hi
     return refine
+
+
+def make_envelope(case, ref):
+    """rule1's `envelope` for ref['d'] (or ref['dc']) at local rows / output
+    columns."""
+    return lambda lrows, ocols: output_envelope(case, ref, lrows, ocols)
+
+
+def _swish_minimum():
+    """The point where x sigmoid(x) is least: the root of 1 + x (1 - sigmoid(x))
+    (its derivative over sigmoid(x)), by bisection on [-2, -1]."""
+    lo, hi = -2.0, -1.0
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        if 1.0 + mid * (1.0 - float(G.sigmoid(mid))) > 0.0:
+            hi = mid
+        else:
+            lo = mid
+    return 0.5 * (lo + hi)
+
+
+SWISH_MIN_AT = _swish_minimum()       # -1.2784645...
+
+
+def acc_halfwidth(case, ref, lrows, acols):
+    """Half-width h of the interval [acc - h, acc + h] around the exact
+    accumulator that holds the library's, on the grid lrows x acols: the FP32
+    ordering bound plus the 8-bit matrix core's truncation."""
+    p, ar = case.problem, case.arrays
+    ab, k = p["ab_dtype"], int(p["k"])
+    lrows, acols = np.asarray(lrows, np.int64), np.asarray(acols, np.int64)
+    grows, grp = ref["rows"][lrows], ref["group"][lrows]
+    a = np.abs(G.dequantize(ar["a"][grows], None if ab == "bf16" else ar["sfa"][grows], ab))
+    s_abs = np.zeros((len(lrows), len(acols)))
+    for g in np.unique(grp):
+        sel = grp == g
+        b = np.abs(G.dequantize(ar["b"][g][acols], None if ab == "bf16" else ar["sfb"][g][acols], ab))
+        s_abs[sel] = a[sel] @ b.T
+    return (k / 16 + 2) * U_ACC * s_abs + mfma_truncation(case, ref, lrows, acols)
+
+
+def output_envelope(case, ref, lrows, ocols):
+    """(lo, hi): for each output element (lrows[i], ocols[i]) of ref['d'] (or
+    ref['dc'] for the backward activations), the least and the greatest value
+    the oracle's activation takes while each accumulator the element reads
+    lies anywhere in [acc - h, acc + h] (acc_halfwidth), the other inputs as
+    given.  The extremes are taken over the interval ends, plus, for the
+    swish-type factor g sigmoid(a g) of SwiGLU and GeGLU, its minimum at
+    g = SWISH_MIN_AT / a when inside: each activation is linear or monotone in
+    its other input, and the clamps are monotone."""
+    p, ar = case.problem, case.arrays
+    act = p["act"]
+    lrows, ocols = np.asarray(lrows, np.int64), np.asarray(ocols, np.int64)
+    lo, hi = np.zeros(len(lrows)), np.zeros(len(lrows))
+    alpha = np.asarray(ar["alpha"], np.float64)
+    for i, (li, j) in enumerate(zip(lrows.tolist(), ocols.tolist())):
+        acols = acc_columns(act, [j])
+        h = acc_halfwidth(case, ref, [li], acols)[0]
+        acc = ref["acc"][li, acols]
+        g, row = int(ref["group"][li]), int(ref["rows"][li])
+        prob = float(np.asarray(ar["prob"], np.float64)[row])
+        sc = alpha[g] ** 2 if act in ("dswiglu", "dsrelu", "dgeglu") else alpha[g]
+        ends = [np.sort(sc * np.array([acc[q] - h[q], acc[q] + h[q]])) for q in range(len(acols))]
+        if act in ("none", "srelu"):
+            c = ends[0][:, None]
+            pr = np.full(len(c), prob)
+            v = pr[:, None] * c if act == "none" else G.srelu(c, pr, float(p.get("srelu_tanh_s", 0.0)))
+            v = v[:, 0]
+        elif act in ("swiglu", "geglu"):
+            first, second = list(ends[0]), list(ends[1])
+            if act == "swiglu":
+                # D = prob X swish(G): X first, G second
+                xs, gs = first, second
+                if gs[0] < SWISH_MIN_AT < gs[1]:
+                    gs.append(SWISH_MIN_AT)
+            else:
+                # D = gamma prob (U + offset) G sigmoid(a G): G first, U second
+                gm, ga, off, cmin, cmax = G.glu_params(p)
+                gs, xs = first, second
+                if gs[0] < SWISH_MIN_AT / ga < gs[1]:
+                    gs.append(SWISH_MIN_AT / ga)
+            combos = np.array([(x, y) for x in xs for y in gs])
+            c = np.zeros((len(combos), 64))
+            pr = np.full(len(combos), prob)
+            if act == "swiglu":
+                c[:, 0], c[:, 32] = combos[:, 0], combos[:, 1]
+                v = G.swiglu(c, pr)[:, 0]
+            else:
+                c[:, 0], c[:, 32] = combos[:, 1], combos[:, 0]
+                v = G.geglu(c, pr, gm, ga, off, cmin, cmax)[:, 0]
+        else:
+            # dC is linear in its one R element for fixed saved C
+            rv = ends[0]
+            pr = np.full(2, prob)
+            x = F.decode_bf16(ar["c_in"][row])
+            if act == "dsrelu":
+                v = G.dsrelu(rv[:, None], np.full((2, 1), x[j]), pr, float(p.get("srelu_tanh_s", 0.0)))[0][:, 0]
+            else:
+                b, lane, part = j // 64, j % 32, (j % 64) // 32
+                saved = np.zeros((2, 64))
+                saved[:, 0], saved[:, 32] = x[64 * b + lane], x[64 * b + 32 + lane]
+                rm = np.zeros((2, 32))
+                rm[:, 0] = rv
+                if act == "dswiglu":
+                    saved *= float(np.asarray(ar["beta"], np.float64)[g])
+                    v = G.dswiglu(rm, saved, pr)[0][:, 32 * part]
+                else:
+                    _, ga, off, cmin, cmax = G.glu_params(p)
+                    v = G.dgeglu(rm, saved, pr, ga, off, cmin, cmax)[0][:, 32 * part]
+        lo[i], hi[i] = v.min(), v.max()
+    return lo, hi
 
 
 def acc_error_bound(case, ref, extra=None):
@@ -370,9 +536,15 @@ def rule2(gpu_codes, gpu_sf, ref_d64, nc, axis, what="", rel_bound=None, refine=
             mism = gpu_sf != ref_sf
     refined = 0
     if bad_sf.any() and refine is not None:
-        refined = int(bad_sf.sum())
-        tol = tolerance(refine(np.argwhere(bad_sf)), ref_d64, amax)
-        allowed = np.where(under, allowed, near_power_of_two(sf32, tol) & one_apart)
+        # every byte that an amax within the blocks' envelope rounds to
+        where = np.argwhere(bad_sf)
+        refined = len(where)
+        a_lo, a_hi = refine(where)
+        b_lo = _scale_byte(nc * np.asarray(a_lo) / 448.0 * (1.0 - BOUNDARY_REL))
+        b_hi = _scale_byte(nc * np.asarray(a_hi) / 448.0 * (1.0 + BOUNDARY_REL))
+        g = gpu_sf[tuple(where.T)].astype(int)
+        ok = where[(g >= b_lo) & (g <= b_hi)]
+        allowed[tuple(ok.T)] = True
         bad_sf = mism & ~allowed
     assert not bad_sf.any(), (f"{what}: {int(bad_sf.sum())} scale bytes differ away from a "
                               f"power-of-two boundary, e.g. at {np.argwhere(bad_sf)[:5].tolist()}")

@@ -10,9 +10,10 @@ import pytest
 import oracle
 import synth
 from oracle import formats as F
-from cases import EDGE, SATURATED, SMALL, UNDERFLOW
-from parity_util import (acc_error_bound, amax_rule, decode_bf16, make_refine, pick_row_blocks, rule1, rule2,
-                         underflow_mask)
+from cases import EDGE, EXTREME, SATURATED, SMALL, UNDERFLOW
+import parity_util
+from parity_util import (acc_error_bound, amax_rule, decode_bf16, make_envelope, make_refine, pick_row_blocks,
+                         rule1, rule2, underflow_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +61,7 @@ def check_case(case, got, rows=None):
                                    "dC_col/SFD_col", rb, make_refine(case, ref, "col"), fz)
             return stats
         g2 = np.repeat(grp[:, None], ref["dc"].shape[1], axis=1)
-        stats["dc"] = rule1(decode_bf16(got["d"][r]), ref["dc"], g2, "dC")
+        stats["dc"] = rule1(decode_bf16(got["d"][r]), ref["dc"], g2, "dC", make_envelope(case, ref))
         if "amax2" in ref and rows is None:
             stats["amax2"] = amax_rule(got["amax"].reshape(-1), ref["amax2"].reshape(-1))
         if "amax" in ref and rows is None:
@@ -71,7 +72,7 @@ def check_case(case, got, rows=None):
         stats["c"] = rule1(decode_bf16(got["c"][r]), ref["c"], g2, "C")
     if p["d_dtype"] == "bf16":
         g2 = np.repeat(grp[:, None], ref["d"].shape[1], axis=1)
-        stats["d"] = rule1(decode_bf16(got["d"][r]), ref["d"], g2, "D")
+        stats["d"] = rule1(decode_bf16(got["d"][r]), ref["d"], g2, "D", make_envelope(case, ref))
         if rows is None:
             stats["amax"] = amax_rule(got["amax"], ref["amax"])
     else:
@@ -154,6 +155,22 @@ def test_fp32_underflow_parity(name):
     stats = check_case(case, got)
     assert stats["d_col"]["scale_fp32_underflow"] > 0
     print(f"[gpu-case] {name} stats {stats}", flush=True)
+
+
+@pytest.mark.parametrize("name", list(EXTREME))
+def test_extreme_range_parity(name):
+    """C large with heavy cancellation under saturating activations, or R
+    below its own accumulation error: parity holds with the outputs'
+    accumulation envelopes, and the case does reach them."""
+    base, over, seed = EXTREME[name]
+    case = synth.make_case(base, seed=seed, name=name, **over)
+    got = run_gpu(case)
+    n0 = len(parity_util.RULE1_LOG)
+    stats = check_case(case, got)
+    enveloped = sum(a for _, a, _ in parity_util.RULE1_LOG[n0:])
+    enveloped += sum(v.get("scale_mfma_truncation", 0) for v in stats.values() if isinstance(v, dict))
+    assert enveloped > 0
+    print(f"[gpu-case] {name} stats {stats} enveloped {enveloped}", flush=True)
 
 
 @pytest.mark.parametrize("name", list(EDGE))
@@ -414,7 +431,8 @@ def test_full_size_sampled(name):
                 continue
             grows = np.arange(starts[g], po[g])
             ref_g = oracle.grouped_gemm(p, case.arrays, grows)
-            worst_d = max(worst_d, rule1(d[grows], ref_g["d"], np.full(ref_g["d"].shape, g), f"D group {g}"))
+            worst_d = max(worst_d, rule1(d[grows], ref_g["d"], np.full(ref_g["d"].shape, g), f"D group {g}",
+                                         make_envelope(case, ref_g)))
             ref_amax[g] = ref_g["amax"][g]
         stats["d_all_rows"] = worst_d
         stats["amax_all_groups"] = amax_rule(got["amax"], ref_amax)

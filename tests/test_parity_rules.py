@@ -153,13 +153,46 @@ def test_accumulator_columns_of_each_activation():
 
 
 def test_refine_decides_blocks_outside_the_fp32_allowance():
-    d, codes, sf, bound = _planted(1)
+    d, codes, sf, _ = _planted(1)
+    amax = np.abs(d[0, :32]).max()
     # the planted block fails without an allowance and passes once refine
-    # supplies one for it, which is then counted
-    st = rule2(codes, sf, d, 1.0, "row", "planted", None, refine=lambda bad: bound)
+    # gives its amax a range reaching below the power of two, which is then
+    # counted
+    st = rule2(codes, sf, d, 1.0, "row", "planted", None,
+               refine=lambda bad: (np.full(len(bad), amax * (1 - 1e-3)), np.full(len(bad), amax * (1 + 1e-3))))
     assert st["scale_mfma_truncation"] == 1 and st["scale_acc_allowance"] == 1
     with pytest.raises(AssertionError, match="away from a power-of-two boundary"):
-        rule2(codes, sf, d, 1.0, "row", "planted", None, refine=lambda bad: np.zeros_like(d))
+        rule2(codes, sf, d, 1.0, "row", "planted", None,
+              refine=lambda bad: (np.full(len(bad), amax), np.full(len(bad), amax)))
+
+
+def test_refine_accepts_every_byte_of_the_amax_range():
+    # an amax range spanning four binades admits the four bytes and no other
+    d, codes, sf, _ = _planted(1)
+    amax = np.abs(d[0, :32]).max()
+    for drop, ok in ((1, True), (3, True), (4, False)):
+        sf2 = sf.copy()
+        sf2[0, 0] = sf[0, 0] + 1 - drop                  # the planted byte is already one below
+        codes2 = codes.copy()
+        codes2[0, :32] = F.encode_e4m3(np.clip(d[0, :32] * 2.0 ** (127 - int(sf2[0, 0])), -448, 448))
+        lo = np.full(1, amax / 7.0)                      # bytes from 2^-3 / 8 .. 2^-3 (x 448)
+        run = lambda: rule2(codes2, sf2, d, 1.0, "row", "range", None,   # noqa: E731
+                            refine=lambda bad: (lo, np.full(len(bad), amax)))
+        if ok:
+            assert run()["scale_mfma_truncation"] == 1
+        else:
+            with pytest.raises(AssertionError):
+                run()
+
+
+def test_scale_byte_matches_the_oracles_quantiser():
+    from parity_util import _scale_byte
+    rng = np.random.default_rng(5)
+    amax = np.concatenate([np.float32(2.0) ** rng.integers(-130, 120, 200).astype(np.float32),
+                           rng.lognormal(0, 20, 2000).astype(np.float32), np.float32([0.0, 448.0, 3e38])])
+    amax = amax[np.isfinite(amax)]
+    sf32 = (np.float32(1.0) * amax) * G.RCP_MAX_E4M3
+    assert np.array_equal(_scale_byte(sf32.astype(np.float64)), G.e8m0_block_scale(amax, 1.0).astype(int))
 
 
 # ---------------------------------------------------------------------------
@@ -257,3 +290,171 @@ def test_a_fragile_element_may_be_zero_inside_a_matching_block():
     assert rule2(flushed, sf, d, 1.0, "row", "zeroed", fragile=fragile)["beyond_1ulp"] == 0
     with pytest.raises(AssertionError):                 # 1 of 32 codes off: above the 0.1 % bar
         rule2(flushed, sf, d, 1.0, "row", "zeroed")
+
+
+# ---------------------------------------------------------------------------
+# the outputs' envelope under the accumulation error (parity_util
+# output_envelope): brute force over the accumulators' intervals
+# ---------------------------------------------------------------------------
+
+import synth  # noqa: E402
+from oracle import grouped_gemm  # noqa: E402
+import parity_util as PU  # noqa: E402
+from parity_util import SWISH_MIN_AT, acc_halfwidth, make_envelope, output_envelope, rule1  # noqa: E402
+
+
+def test_swish_minimum_point():
+    x = np.linspace(-3.0, 0.0, 3_000_001)
+    f = x * G.sigmoid(x)
+    assert abs(x[np.argmin(f)] - SWISH_MIN_AT) < 2e-6
+    assert abs(SWISH_MIN_AT + 1.2784645) < 1e-6
+
+
+ENVELOPE_CASES = {
+    "none": ("quant_gating_l4", dict(L=2, K=64, N=64, routing=("multinomial", 64))),
+    "srelu": ("srelu_tanh_fp4_l32", dict(ab="e4m3", clip=None, L=2, K=64, N=64, s=2.0, b_std=1.0,
+                                         routing=("multinomial", 64), d="bf16", c=None)),
+    "srelu_plain": ("srelu_tanh_fp4_l32", dict(ab="e4m3", clip=None, L=2, K=64, N=64, s=0.0, b_std=1.0,
+                                               routing=("multinomial", 64), d="bf16", c=None)),
+    "swiglu": ("fc1_swiglu_l8", dict(L=2, K=64, N=128, routing=("topk", 64, 2), b_std=1.0, d="bf16")),
+    "geglu": ("fc1_swiglu_l8", dict(L=2, K=64, N=128, routing=("topk", 64, 2), b_std=1.0, d="bf16", act="geglu",
+                                    glu_gamma=1.3, geglu_alpha=1.7, linear_offset=0.6, glu_clamp_min=-1.5,
+                                    glu_clamp_max=2.5)),
+    "dswiglu": ("dswiglu_mxfp8_l64", dict(L=2, K=64, N=64, routing=("topk", 64, 2), d="bf16", c_std=2.0,
+                                          beta=("uniform", 0.5, 2.0))),
+    "dgeglu": ("dswiglu_mxfp8_l64", dict(L=2, K=64, N=64, routing=("topk", 64, 2), d="bf16", act="dgeglu",
+                                         c_std=2.0, geglu_alpha=1.7, linear_offset=0.6, glu_clamp_min=-1.5,
+                                         glu_clamp_max=2.5)),
+    "dsrelu": ("dsrelu_mxfp8_l32", dict(L=2, K=64, N=64, routing=("multinomial", 64), d="bf16", c_std=2.0,
+                                        s=1.0)),
+}
+
+
+def _brute_envelope(case, ref, li, j, half):
+    """Output values over a dense grid of each accumulator interval, the
+    whole row evaluated by the oracle at every grid point."""
+    p, ar = case.problem, case.arrays
+    act = p["act"]
+    acols = PU.acc_columns(act, [j])
+    g, row = int(ref["group"][li]), int(ref["rows"][li])
+    a = float(np.asarray(ar["alpha"], np.float64)[g])
+    sc = a * a if act.startswith("d") else a
+    grids = [sc * (ref["acc"][li, q] + np.linspace(-half, half, 301)) for q in acols]
+    pts = np.array(np.meshgrid(*grids, indexing="ij")).reshape(len(grids), -1).T
+    m = sc * np.repeat(ref["acc"][li][None], len(pts), axis=0)
+    m[:, acols] = pts
+    prob = np.full(len(pts), float(np.asarray(ar["prob"], np.float64)[row]))
+    if act == "none":
+        out = prob[:, None] * m
+    elif act == "srelu":
+        out = G.srelu(m, prob, float(p["srelu_tanh_s"]))
+    elif act == "swiglu":
+        out = G.swiglu(m, prob)
+    elif act == "geglu":
+        out = G.geglu(m, prob, *G.glu_params(p))
+    else:
+        x = np.repeat(F.decode_bf16(ar["c_in"][[row]]), len(pts), axis=0)
+        if act == "dswiglu":
+            out, _ = G.dswiglu(m, float(ar["beta"][g]) * x, prob)
+        elif act == "dsrelu":
+            out, _ = G.dsrelu(m, x, prob, float(p["srelu_tanh_s"]))
+        else:
+            _, ga, off, cmin, cmax = G.glu_params(p)
+            out, _ = G.dgeglu(m, x, prob, ga, off, cmin, cmax)
+    return out[:, j].min(), out[:, j].max()
+
+
+@pytest.mark.parametrize("name", list(ENVELOPE_CASES))
+def test_output_envelope_is_the_exact_range(name, monkeypatch):
+    base, over = ENVELOPE_CASES[name]
+    case = synth.make_case(base, seed=31, name=name, **over)
+    ref = grouped_gemm(case.problem, case.arrays)
+    # a wide interval (the accumulators span about +-3), so that it crosses
+    # clamps, zero and the swish minimum
+    half = 1.5 * np.abs(ref["acc"]).mean()
+    monkeypatch.setattr(PU, "acc_halfwidth", lambda c, r, lr, ac: np.full((len(lr), len(ac)), half))
+    rng = np.random.default_rng(8)
+    out = ref["d"] if "d" in ref else ref["dc"]
+    li = rng.integers(0, out.shape[0], 12)
+    oj = rng.integers(0, out.shape[1], 12)
+    lo, hi = output_envelope(case, ref, li, oj)
+    for i in range(len(li)):
+        blo, bhi = _brute_envelope(case, ref, int(li[i]), int(oj[i]), half)
+        scale = max(abs(blo), abs(bhi), 1e-300)
+        # the grid's extremes lie inside the envelope and reach its ends
+        assert lo[i] <= blo + 1e-12 * scale and bhi <= hi[i] + 1e-12 * scale
+        assert abs(lo[i] - blo) <= 1e-3 * scale and abs(hi[i] - bhi) <= 1e-3 * scale
+        assert lo[i] <= out[li[i], oj[i]] <= hi[i]
+
+
+def test_envelope_reaches_the_swish_minimum(monkeypatch):
+    # a gate interval around the minimum of g sigmoid(g): the least output is
+    # prob X swish(SWISH_MIN_AT), not a value at the interval's ends
+    base, over = ENVELOPE_CASES["swiglu"]
+    case = synth.make_case(base, seed=31, name="swiglu", **over)
+    ref = grouped_gemm(case.problem, case.arrays)
+    li, j = 0, 3
+    a = float(case.arrays["alpha"][ref["group"][li]])
+    ref["acc"][li, j] = 2.0 / a                        # X = 2
+    ref["acc"][li, j + 32] = SWISH_MIN_AT / a + 0.1 / a  # G just right of the minimum
+    monkeypatch.setattr(PU, "acc_halfwidth", lambda c, r, lr, ac: np.full((len(lr), len(ac)), 0.5 / a))
+    lo, hi = output_envelope(case, ref, [li], [j])
+    prob = float(case.arrays["prob"][ref["rows"][li]])
+    swish = lambda g: g * G.sigmoid(g)                 # noqa: E731
+    # X over [1.5, 2.5], G over [g* - 0.4, g* + 0.6], swish < 0 there: the
+    # least product takes X = 2.5 at g*, the greatest X = 1.5 at the end
+    # where swish is largest
+    assert np.isclose(lo[0], prob * 2.5 * swish(SWISH_MIN_AT), rtol=1e-12)
+    top = max(swish(SWISH_MIN_AT - 0.4), swish(SWISH_MIN_AT + 0.6))
+    assert np.isclose(hi[0], prob * 1.5 * top, rtol=1e-12)
+
+
+def test_acc_halfwidth_parts():
+    # BF16 operands: the FP32 ordering bound alone; E4M3: plus the truncation
+    for base, over in (("gating_bf16_ops", None), ("e4m3", None)):
+        if base == "gating_bf16_ops":
+            case = synth.make_case("quant_gating_l4", seed=3, name="h", ab="bf16", K=256, N=64, a_std=1.0,
+                                   b_std=0.1, routing=("multinomial", 64))
+        else:
+            case = synth.make_case("quant_gating_l4", seed=3, name="h", K=256, N=64, routing=("multinomial", 64))
+        ref = grouped_gemm(case.problem, case.arrays)
+        p, ar = case.problem, case.arrays
+        lr, ac = np.array([0, 5]), np.array([1, 7, 9])
+        ab = p["ab_dtype"]
+        a = np.abs(G.dequantize(ar["a"][ref["rows"][lr]], None if ab == "bf16" else ar["sfa"][ref["rows"][lr]], ab))
+        want = np.zeros((2, 3))
+        for i, l in enumerate(lr):
+            g = ref["group"][l]
+            b = np.abs(G.dequantize(ar["b"][g][ac], None if ab == "bf16" else ar["sfb"][g][ac], ab))
+            want[i] = (256 / 16 + 2) * 2.0 ** -23 * (b @ a[i])
+        want += PU.mfma_truncation(case, ref, lr, ac)
+        assert np.allclose(acc_halfwidth(case, ref, lr, ac), want, rtol=1e-12, atol=0)
+        if ab == "bf16":
+            assert not PU.mfma_truncation(case, ref, lr, ac).any()
+
+
+def _rule1_planted(n):
+    rng = np.random.default_rng(2)
+    ref = rng.uniform(-1, 1, (40, 50))
+    gpu = ref.copy()
+    gpu[:n, 0] += 0.5                                  # 0.5 of the group's largest output
+    grp = np.zeros(ref.shape, int)
+    return gpu, ref, grp
+
+
+def test_rule1_accepts_only_within_the_envelope_and_counts():
+    gpu, ref, grp = _rule1_planted(1)
+    with pytest.raises(AssertionError, match="rule-1"):
+        rule1(gpu, ref, grp, "plain")
+    wide = lambda r, c: (ref[r, c] - 0.6, ref[r, c] + 0.6)           # noqa: E731
+    narrow = lambda r, c: (ref[r, c] - 0.3, ref[r, c] + 0.3)         # noqa: E731
+    n0 = len(PU.RULE1_LOG)
+    assert rule1(gpu, ref, grp, "wide", wide) <= 1e-2
+    assert PU.RULE1_LOG[n0] == ("wide", 1, gpu.size)
+    with pytest.raises(AssertionError, match="rule-1"):
+        rule1(gpu, ref, grp, "narrow", narrow)
+    # more than 1e-3 of the elements (here 2 of 2000) only within the envelope
+    gpu3, ref3, grp3 = _rule1_planted(3)
+    with pytest.raises(AssertionError, match="accumulation envelope"):
+        rule1(gpu3, ref3, grp3, "cap", lambda r, c: (ref3[r, c] - 0.6, ref3[r, c] + 0.6))
+    assert make_envelope is not None
