@@ -127,12 +127,13 @@ __device__ __forceinline__ float sigmoid_f(float x) {
 }
 
 // tanh(x) for x >= 0: odd Taylor series below 1/8 (error < 2e-10), else
-// (1 - e^-2x) / (1 + e^-2x).  Result <= 1.
+// 1 - 2 / (1 + e^2x) (one reciprocal and one fused multiply-add; e^2x
+// overflowing to infinity gives exactly 1).  Result in [0, 1] by
+// construction, so that the clamp min(tanh, 1) needs no instruction.
 __device__ __forceinline__ float tanh_nonneg(float x) {
   const float x2 = x * x;
   const float series = x * (1.0f + x2 * (-1.0f / 3.0f + x2 * (2.0f / 15.0f + x2 * (-17.0f / 315.0f))));
-  const float e = __builtin_amdgcn_exp2f(-2.0f * kLog2e * x);
-  const float big = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
+  const float big = fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(2.0f * kLog2e * x)), 1.0f);
   return x < 0.125f ? series : big;
 }
 
@@ -1253,6 +1254,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
           const uint32_t ml = tm * 32 + l32;
+          if constexpr (ACT == ACT_SRELU) {
+            // C = alpha acc, formed once for both the C store and the
+            // activation (the accumulators are not read again)
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) acc[tm][t][v] *= alpha;
+          }
+          const float ca = ACT == ACT_SRELU ? 1.0f : alpha;
           if (p.c) {
             // C = alpha acc of the wave's 64 GEMM columns
             v4u cq[4] = {};
@@ -1261,7 +1271,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
               if (!tile_ok(PAIR ? 0 : t)) continue;
               float c[16];
 #pragma unroll
-              for (int v = 0; v < 16; ++v) c[v] = alpha * acc[tm][t][v];
+              for (int v = 0; v < 16; ++v) c[v] = ca * acc[tm][t][v];
               bf16_pieces(c, cq + 2 * t);
             }
             store_rows<128>(cW + tm * 32 * cpitch, cpitch, cq, stg, lid2, cvalid);
@@ -1305,7 +1315,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             } else {
               const float f = pr[tm] * nc;
               if constexpr (ACT == ACT_SRELU) {
-                // D = prob * (s * min(tanh(relu(C)/s), 1))^2, or prob * relu(C)^2 for s = 0
+                // D = prob * (s * min(tanh(relu(C)/s), 1))^2, or prob * relu(C)^2 for s = 0,
+                // evaluated as (prob s^2) t^2 with t = tanh(relu(C)/s) <= 1
                 // ("Grouped GEMM + sReLU (SM100)", §Equations, §Tanh soft clamp)
                 // (the clamp test outside the element loop: inside it, the
                 // compiler made one branch per element, which kept the sixteen
@@ -1313,16 +1324,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
                 const float s = p.srelu_s;
                 if (s > 0.0f) {
                   const float rs = 1.0f / s;
+                  const float fs2 = f * (s * s);
 #pragma unroll
                   for (int v = 0; v < 16; ++v) {
-                    const float r = fmaxf(alpha * acc[tm][to][v], 0.0f);
-                    const float c = s * fminf(tanh_nonneg(r * rs), 1.0f);
-                    d[v] = f * (c * c);
+                    const float t = tanh_nonneg(fmaxf(acc[tm][to][v], 0.0f) * rs);
+                    d[v] = fs2 * (t * t);
                   }
                 } else {
 #pragma unroll
                   for (int v = 0; v < 16; ++v) {
-                    const float r = fmaxf(alpha * acc[tm][to][v], 0.0f);
+                    const float r = fmaxf(acc[tm][to][v], 0.0f);
                     d[v] = f * (r * r);
                   }
                 }
