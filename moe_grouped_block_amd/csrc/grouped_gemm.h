@@ -141,13 +141,14 @@ __device__ __forceinline__ float tanh_nonneg(float x) {
 // cancellation of 1 - t*t as t approaches 1: with e = e^-2x,
 // t = (1 - e) / (1 + e) (below 1/8 the odd series, as in tanh_nonneg) and
 // sech^2 = 4 e / (1 + e)^2 for every x (no subtraction).
-__device__ __forceinline__ void tanh_sech2_nonneg(float x, float& t, float& sech2) {
+__device__ __forceinline__ void tanh_sech2_nonneg(float x, float& t, float& sech2_4) {
   const float x2 = x * x;
   const float series = x * (1.0f + x2 * (-1.0f / 3.0f + x2 * (2.0f / 15.0f + x2 * (-17.0f / 315.0f))));
   const float e = __builtin_amdgcn_exp2f(-2.0f * kLog2e * x);
   const float r = __builtin_amdgcn_rcpf(1.0f + e);
-  t = x < 0.125f ? series : (1.0f - e) * r;
-  sech2 = (4.0f * e) * (r * r);
+  const float er = e * r;
+  t = x < 0.125f ? series : fmaf(-2.0f, er, 1.0f);
+  sech2_4 = er * r;
 }
 
 // Cross-lane helpers on the VALU (DPP and the gfx950 permlane swaps), no LDS.
@@ -892,6 +893,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       const float a2 = alpha * alpha;
       float beta = 1.0f;
       if constexpr (ACT == ACT_DSWIGLU) beta = p.beta[g];
+      const float nqf = OUT == OUT_E4M3 ? nc : 1.0f;     // FP8 dC carries norm_const
       const int ld2 = 2 * p.n;
       const uint16_t* const cinW = p.c_in + mb * ld2 + 2 * nbase;   // wave's first row, block pair 0
       uint8_t* const dbW = p.d + (mb * ld2 + 2 * nbase) * 2;          // BF16 dC, same layout
@@ -971,18 +973,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           };
           // dC of element v in the first (part 0) or second (part 1) block;
           // part 0 also accumulates the dprob term
+          // The row's constant factors are taken out of the element terms:
+          // dC = acc (alpha^2 prob [norm_const for FP8 dC]) (...) with the
+          // dSwiGLU input's beta in the second block's factor, and the dprob
+          // terms summed over acc, times alpha^2 [beta] once per row.
+          const float k0 = (a2 * pr[tm]) * nqf;
+          const float k1 = ACT == ACT_DSWIGLU ? k0 * beta : k0;
           auto dglu = [&](int v, int part, float& dpv) __attribute__((always_inline)) -> float {
-            const float r = a2 * acc[tm][tn][v];
+            const float av = acc[tm][tn][v];
             if constexpr (ACT == ACT_DSWIGLU) {
-              const float x = beta * bf(wi, v);
+              const float xr = bf(wi, v);              // input / beta
               const float gt = beta * bf(wg, v);
               const float sg = sigmoid_f(gt);
-              const float swish = gt * sg;
               if (part == 0) {
-                dpv += r * x * swish;
-                return r * pr[tm] * swish;
+                const float swish = gt * sg;
+                dpv = fmaf(av, xr * swish, dpv);
+                return (av * k0) * swish;
               }
-              return r * pr[tm] * x * sg * (1.0f + gt * (1.0f - sg));
+              return (av * k1) * (xr * sg * fmaf(gt, 1.0f - sg, 1.0f));
             } else {
               const float gate = bf(wi, v), up = bf(wg, v);
               const float gc = fminf(gate, p.glu_clamp_max);
@@ -990,13 +998,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
               const float sg = sigmoid_f(p.geglu_alpha * gc);
               const float uo = uc + p.linear_offset;
               if (part == 0) {
-                dpv += r * gc * sg * uo;
-                return gate <= p.glu_clamp_max ? r * pr[tm] * uo * sg * (1.0f + p.geglu_alpha * gc * (1.0f - sg))
+                dpv = fmaf(av, gc * sg * uo, dpv);
+                return gate <= p.glu_clamp_max ? (av * k0) * (uo * sg * fmaf(p.geglu_alpha * gc, 1.0f - sg, 1.0f))
                                                : 0.0f;
               }
               // evaluated in every lane, then masked by a select: left to
               // itself the compiler branched around the sigmoid per element
-              float du = r * pr[tm] * gc * sg;
+              float du = (av * k0) * (gc * sg);
               asm volatile("" : "+v"(du));
               return (up >= p.glu_clamp_min && up <= p.glu_clamp_max) ? du : 0.0f;
             }
@@ -1039,7 +1047,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             float d[16], unused = 0.0f;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              d[v] = dglu(v, 0, dp) * nc;
+              d[v] = dglu(v, 0, dp);
               if (ACT == ACT_DGEGLU && (v & 7) == 7) asm volatile("" : "+v"(d[v - 7]), "+v"(d[v - 6]), "+v"(d[v - 5]), "+v"(d[v - 4]), "+v"(d[v - 3]), "+v"(d[v - 2]), "+v"(d[v - 1]), "+v"(d[v]), "+v"(dp));
             }
             colw0[tn] |= quant_codes(sT, sS, sfW0 + (oc >> 5), so, hi, l32, d, rq[2 * tn], kq[2 * tn]) << (8 * tm);
@@ -1051,7 +1059,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             }
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              d[v] = dglu(v, 1, unused) * nc;
+              d[v] = dglu(v, 1, unused);
               if (ACT == ACT_DGEGLU && (v & 7) == 7) asm volatile("" : "+v"(d[v - 7]), "+v"(d[v - 6]), "+v"(d[v - 5]), "+v"(d[v - 4]), "+v"(d[v - 3]), "+v"(d[v - 2]), "+v"(d[v - 1]), "+v"(d[v]));
             }
             colw1[tn] |= quant_codes(sT, sS, sfW0 + (oc >> 5) + 1, so, hi, l32, d, rq[2 * tn + 1], kq[2 * tn + 1])
@@ -1062,7 +1070,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           store_rows<128>(dW0 + 2 * nbase + tm * 32 * dpitch, dpitch, rq, stg, lid3, dvalid);
           store_rows<128>(dcW0 + 2 * nbase + tm * 32 * dpitch, dpitch, kq, stg, lid3, dvalid);
         }
-        dp = halves_sum(dp);
+        dp = halves_sum(dp * (ACT == ACT_DSWIGLU ? a2 * beta : a2));
         if (hi == 0) atomicAdd(at(p.dprob + mb, 4 * ml), dp);
       }
       if constexpr (OUT == OUT_E4M3) {
@@ -1093,6 +1101,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
       const float a2 = alpha * alpha;
       const float sc = p.srelu_s;
       const float rs = sc > 0.0f ? 1.0f / sc : 0.0f;
+      const float nq = OUT == OUT_E4M3 ? nc : 1.0f;     // FP8 dC carries norm_const
       float amax_l = 0.0f;
       uint32_t colw[TN];
 #pragma unroll
@@ -1155,25 +1164,29 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           }
           float d[16];
           // (the clamp test outside the element loop, as in the forward)
+          // R = alpha^2 acc: dC = acc (alpha^2 prob 8 s [nc]) t (sech^2 / 4) and
+          // dprob += alpha^2 s^2 sum acc t^2 (s = 0: dC = acc (alpha^2 prob 2 [nc]) c,
+          // dprob += alpha^2 sum acc c^2); t <= 1 by construction
+          float sq = 0.0f;
           if (sc > 0.0f) {
+            const float k = (a2 * pr[tm]) * ((8.0f * sc) * nq);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              const float r = a2 * acc[tm][tn][v];
-              float t, sech2;
-              tanh_sech2_nonneg(fmaxf(cv[v], 0.0f) * rs, t, sech2);
-              t = fminf(t, 1.0f);
-              const float c = sc * t;
-              d[v] = r * pr[tm] * (2.0f * c * sech2);
-              dp += r * (c * c);
+              float t, s4;
+              tanh_sech2_nonneg(fmaxf(cv[v], 0.0f) * rs, t, s4);
+              d[v] = (acc[tm][tn][v] * k) * (t * s4);
+              sq = fmaf(acc[tm][tn][v], t * t, sq);
             }
+            dp = fmaf(a2 * (sc * sc), sq, dp);
           } else {
+            const float k = (a2 * pr[tm]) * (2.0f * nq);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              const float r = a2 * acc[tm][tn][v];
               const float c = fmaxf(cv[v], 0.0f);
-              d[v] = r * pr[tm] * (2.0f * c);
-              dp += r * (c * c);
+              d[v] = (acc[tm][tn][v] * k) * c;
+              sq = fmaf(acc[tm][tn][v], c * c, sq);
             }
+            dp = fmaf(a2, sq, dp);
           }
           if constexpr (OUT == OUT_BF16) {
             bf16_pieces(d, dq + 2 * tn);
@@ -1182,8 +1195,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
               for (int v = 0; v < 16; v += 2) amax_l = max_abs2(amax_l, d[v], d[v + 1]);
             }
           } else {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) d[v] *= nc;
             colw[tn] |= quant_codes(sT, sS, sfW0 + (ncol >> 5), ml * static_cast<uint32_t>(p.n_out >> 5), hi, l32, d,
                                     dq[tn], kq[tn])
                         << (8 * tm);
