@@ -137,10 +137,11 @@ __device__ __forceinline__ float tanh_nonneg(float x) {
   return x < 0.125f ? series : big;
 }
 
-// tanh(x) and sech(x)^2 = 1 - tanh(x)^2 for x >= 0, the latter free of the
-// cancellation of 1 - t*t as t approaches 1: with e = e^-2x,
-// t = (1 - e) / (1 + e) (below 1/8 the odd series, as in tanh_nonneg) and
-// sech^2 = 4 e / (1 + e)^2 for every x (no subtraction).
+// tanh(x) and sech(x)^2 / 4 = (1 - tanh(x)^2) / 4 for x >= 0, the latter
+// free of the cancellation of 1 - t*t as t approaches 1: with e = e^-2x and
+// r = 1 / (1 + e), t = (1 - e) / (1 + e) = 1 - 2 e r (in [0, 1]; below 1/8
+// the odd series, as in tanh_nonneg) and sech^2 / 4 = e / (1 + e)^2 = e r^2
+// for every x (no subtraction; the caller folds the 4 into its factors).
 __device__ __forceinline__ void tanh_sech2_nonneg(float x, float& t, float& sech2_4) {
   const float x2 = x * x;
   const float series = x * (1.0f + x2 * (-1.0f / 3.0f + x2 * (2.0f / 15.0f + x2 * (-17.0f / 315.0f))));
