@@ -579,6 +579,34 @@ def rule2(gpu_codes, gpu_sf, ref_d64, nc, axis, what="", rel_bound=None, refine=
     return st
 
 
+def row_col_consistency(got, chunk=2048):
+    """Every element of a full FP8 output, without the oracle: D (row blocks)
+    and D_col (column blocks) quantise the same FP32 values, each rounding to
+    nearest at its own block scale, so their dequantised values differ by at
+    most half an E4M3 ULP of each: at most 1/8 of the larger magnitude plus
+    2^-9 of each block scale (the subnormal step).  A tile left unwritten, a
+    NaN code or a scale byte that does not belong to its block fails.
+    Returns the number of elements checked."""
+    d, dc = np.asarray(got["d"]), np.asarray(got["d_col"])
+    sr, sc = np.asarray(got["sfd_row"]), np.asarray(got["sfd_col"])
+    rows, n = d.shape
+    assert rows % 32 == 0 and n % 32 == 0 and chunk % 32 == 0
+    bad = 0
+    for r0 in range(0, rows, chunk):
+        r1 = min(rows, r0 + chunk)
+        s_r = np.repeat(F.decode_e8m0(sr[r0:r1]), 32, axis=1)
+        s_c = np.repeat(F.decode_e8m0(sc[:, r0 // 32:r1 // 32]).T, 32, axis=0)
+        vr = F.decode_e4m3(d[r0:r1]) * s_r
+        vc = F.decode_e4m3(dc[r0:r1]) * s_c
+        tol = 0.125 * np.maximum(np.abs(vr), np.abs(vc)) + 2.0 ** -9 * (s_r + s_c)
+        ok = np.abs(vr - vc) <= tol * 1.0001
+        if not ok.all():
+            where = np.argwhere(~ok)[:5] + [r0, 0]
+            bad += int((~ok).sum())
+            raise AssertionError(f"D and D_col disagree at {bad} elements, e.g. {where.tolist()}")
+    return rows * n
+
+
 def decode_bf16(bits):
     return F.decode_bf16(bits)
 

@@ -13,7 +13,7 @@ from oracle import formats as F
 from cases import EDGE, EXTREME, SATURATED, SMALL, UNDERFLOW
 import parity_util
 from parity_util import (acc_error_bound, amax_rule, decode_bf16, make_envelope, make_refine, pick_row_blocks,
-                         rule1, rule2, underflow_mask)
+                         row_col_consistency, rule1, rule2, underflow_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -438,4 +438,7 @@ def test_full_size_sampled(name):
         stats["amax_all_groups"] = amax_rule(got["amax"], ref_amax)
     else:
         assert np.all(F.decode_e4m3(got["d"][pad]) == 0) and np.all(got["sfd_row"][pad] == 0)
+    if p["d_dtype"] == "e4m3":
+        # every element of the FP8 outputs: D and D_col consistent
+        stats["row_col_consistent"] = row_col_consistency(got)
     print(f"[gpu-case] {name} stats {stats}", flush=True)

@@ -458,3 +458,44 @@ def test_rule1_accepts_only_within_the_envelope_and_counts():
     with pytest.raises(AssertionError, match="accumulation envelope"):
         rule1(gpu3, ref3, grp3, "cap", lambda r, c: (ref3[r, c] - 0.6, ref3[r, c] + 0.6))
     assert make_envelope is not None
+
+
+# ---------------------------------------------------------------------------
+# D against D_col over every element of a full output (parity_util
+# row_col_consistency)
+# ---------------------------------------------------------------------------
+
+from parity_util import row_col_consistency  # noqa: E402
+
+
+def _fp8_outputs(seed=5):
+    case = synth.make_case("fc1_swiglu_l8", seed=seed, name="rc", L=2, K=256, N=256, routing=("topk", 200, 2))
+    ref = grouped_gemm(case.problem, case.arrays)
+    nc = float(case.arrays["norm_const"][0])
+    d, sr = G.quantize_rows(ref["d"], nc)
+    dc, sc = G.quantize_cols(ref["d"], nc)
+    return dict(d=d, d_col=dc, sfd_row=sr, sfd_col=sc)
+
+
+def test_row_and_column_quantisations_of_the_oracle_are_consistent():
+    got = _fp8_outputs()
+    assert row_col_consistency(got, chunk=64) == got["d"].size
+    # values spanning many binades, down to E4M3 subnormals at their scale
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((128, 96)) * np.exp2(rng.integers(-30, 30, (128, 96)))
+    d, sr = G.quantize_rows(x, 1.0)
+    dc, sc = G.quantize_cols(x, 1.0)
+    row_col_consistency(dict(d=d, d_col=dc, sfd_row=sr, sfd_col=sc), chunk=32)
+
+
+@pytest.mark.parametrize("plant", ["unwritten_tile", "nan_code", "foreign_scale"])
+def test_row_col_consistency_catches_planted_faults(plant):
+    got = {k: v.copy() for k, v in _fp8_outputs().items()}
+    if plant == "unwritten_tile":
+        got["d"][32:64, 32:64] = 0x5A          # a block left with the fill pattern
+    elif plant == "nan_code":
+        got["d_col"][40, 7] = 0x7F
+    else:
+        got["sfd_row"][70, 1] += 2             # a row block's scale four times too large
+    with pytest.raises(AssertionError, match="disagree"):
+        row_col_consistency(got, chunk=64)
