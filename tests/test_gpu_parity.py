@@ -441,4 +441,26 @@ def test_full_size_sampled(name):
     if p["d_dtype"] == "e4m3":
         # every element of the FP8 outputs: D and D_col consistent
         stats["row_col_consistent"] = row_col_consistency(got)
+    bwd = p["act"] in ("dswiglu", "dsrelu", "dgeglu")
+    if p.get("c_dtype") == "bf16" or (bwd and p["d_dtype"] == "bf16"):
+        # every row of the BF16 C, or of the BF16 dC and dprob, against the
+        # oracle, one group at a time
+        po = np.asarray(case.arrays["padded_offsets"], np.int64)
+        starts = np.concatenate([[0], po[:-1]])
+        worst = {}
+        for g in range(p["num_groups"]):
+            if po[g] == starts[g]:
+                continue
+            grows = np.arange(starts[g], po[g])
+            ref_g = oracle.grouped_gemm(p, case.arrays, grows)
+            if p.get("c_dtype") == "bf16":
+                r1 = rule1(decode_bf16(got["c"][grows]), ref_g["c"], np.full(ref_g["c"].shape, g), f"C group {g}")
+                worst["c_all_rows"] = max(worst.get("c_all_rows", 0.0), r1)
+            if bwd and p["d_dtype"] == "bf16":
+                r1 = rule1(decode_bf16(got["d"][grows]), ref_g["dc"], np.full(ref_g["dc"].shape, g), f"dC group {g}",
+                           make_envelope(case, ref_g))
+                worst["dc_all_rows"] = max(worst.get("dc_all_rows", 0.0), r1)
+                r1 = rule1(got["dprob"][grows], ref_g["dprob"], np.full(len(grows), g), f"dprob group {g}")
+                worst["dprob_all_rows"] = max(worst.get("dprob_all_rows", 0.0), r1)
+        stats.update(worst)
     print(f"[gpu-case] {name} stats {stats}", flush=True)
