@@ -405,6 +405,34 @@ def full_size_rows(case, nblocks=16):
 
 
 @pytest.mark.slow
+def test_full_size_every_row_fc1_l64():
+    """The L=64 FC1 + SwiGLU workload that the benchmark reports, in its
+    launch configuration (K-block plane scales), against the oracle on every
+    row: D / D_col codes and both scale planes of each expert's rows, one
+    group at a time."""
+    case = synth.make_case("fc1_swiglu_l64")
+    p = dict(case.problem, sf_layout="kplanes")
+    dev = pl.to_device(case.arrays, sf_layout="kplanes", k=p["k"])
+    outs = pl.empty_outputs(p, fill=0x5A)
+    _announce(case)
+    mg.run(p, {**pl.inputs_for(p, dev), **outs})
+    torch.cuda.synchronize()
+    got = pl.to_host(outs)
+    po = np.asarray(case.arrays["padded_offsets"], np.int64)
+    starts = np.concatenate([[0], po[:-1]])
+    total = dict(elements=0, beyond_1ulp=0, scale_blocks=0, scale_boundary_mismatch=0, scale_acc_allowance=0)
+    for g in range(p["num_groups"]):
+        if po[g] == starts[g]:
+            continue
+        st = check_case(case, got, np.arange(starts[g], po[g]))
+        for axis in ("d_row", "d_col"):
+            for k in total:
+                total[k] += st[axis][k]
+    assert total["elements"] == 2 * int(case.problem["valid_m"]) * (p["n"] // 2)
+    print(f"[gpu-case] fc1_swiglu_l64 every row {total}", flush=True)
+
+
+@pytest.mark.slow
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled(name):
     case = synth.make_case(name)
