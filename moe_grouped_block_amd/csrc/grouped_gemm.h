@@ -980,12 +980,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           // terms summed over acc, times alpha^2 [beta] once per row.
           const float k0 = (a2 * pr[tm]) * nqf;
           const float k1 = ACT == ACT_DSWIGLU ? k0 * beta : k0;
-          auto dglu = [&](int v, int part, float& dpv) __attribute__((always_inline)) -> float {
+          // the sigmoid of an element: computed by its part-0 call, which
+          // returns it in sgv, and passed to its part-1 call (sgv >= 0)
+          auto dglu = [&](int v, int part, float& dpv, float& sgv) __attribute__((always_inline)) -> float {
             const float av = acc[tm][tn][v];
             if constexpr (ACT == ACT_DSWIGLU) {
               const float xr = bf(wi, v);              // input / beta
               const float gt = beta * bf(wg, v);
-              const float sg = sigmoid_f(gt);
+              const float sg = part == 0 ? sigmoid_f(gt) : sgv;
+              sgv = sg;
               if (part == 0) {
                 const float swish = gt * sg;
                 dpv = fmaf(av, xr * swish, dpv);
@@ -996,7 +999,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
               const float gate = bf(wi, v), up = bf(wg, v);
               const float gc = fminf(gate, p.glu_clamp_max);
               const float uc = fminf(fmaxf(up, p.glu_clamp_min), p.glu_clamp_max);
-              const float sg = sigmoid_f(p.geglu_alpha * gc);
+              const float sg = part == 0 ? sigmoid_f(p.geglu_alpha * gc) : sgv;
+              sgv = sg;
               const float uo = uc + p.linear_offset;
               if (part == 0) {
                 dpv = fmaf(av, gc * sg * uo, dpv);
@@ -1014,8 +1018,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             float d0[16], d1[16], unused = 0.0f;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              d0[v] = dglu(v, 0, dp);
-              d1[v] = dglu(v, 1, unused);
+              float sgv = 0.0f;
+              d0[v] = dglu(v, 0, dp, sgv);
+              d1[v] = dglu(v, 1, unused, sgv);
               // (dGeGLU: pinned in groups of eight, as in the FP8 branch below)
               if (ACT == ACT_DGEGLU && (v & 7) == 7)
                 asm volatile("" : "+v"(d0[v - 7]), "+v"(d0[v - 6]), "+v"(d0[v - 5]), "+v"(d0[v - 4]), "+v"(d0[v - 3]),
@@ -1037,22 +1042,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
           } else {
             // FP8 dC: each 32-column output block quantised by rows and
             // columns like a forward D ("Grouped GEMM + dGLU (SM100)",
-            // block-scaled Step 3).  One block at a time, the shared terms
-            // recomputed for the second, so that a single block of values is
-            // live during a quantisation.
+            // block-scaled Step 3).  One block at a time: the sigmoids of the
+            // first block's elements are kept for the second (a transcendental
+            // pair per element saved), the other shared terms recomputed, so
+            // that a single block of values is live during a quantisation.
             const int oc = 2 * ncol;
             const uint32_t so = ml * static_cast<uint32_t>(p.n_out >> 5);
             // (dGeGLU: the elements in groups of eight, pinned after each
             // group, so that the scheduler does not keep sixteen sigmoid
             // chains in flight at once and spill; dSwiGLU does not need it)
-            float d[16], unused = 0.0f;
+            float d[16], sgk[16], unused = 0.0f;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              d[v] = dglu(v, 0, dp);
+              d[v] = dglu(v, 0, dp, sgk[v]);
               if (ACT == ACT_DGEGLU && (v & 7) == 7) asm volatile("" : "+v"(d[v - 7]), "+v"(d[v - 6]), "+v"(d[v - 5]), "+v"(d[v - 4]), "+v"(d[v - 3]), "+v"(d[v - 2]), "+v"(d[v - 1]), "+v"(d[v]), "+v"(dp));
             }
             colw0[tn] |= quant_codes(sT, sS, sfW0 + (oc >> 5), so, hi, l32, d, rq[2 * tn], kq[2 * tn]) << (8 * tm);
-            // opaque copies: the second block's terms are recomputed, not kept
+            // opaque copies: the second block's other terms are recomputed, not kept
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               asm volatile("" : "+v"(wi[j]));
@@ -1060,7 +1066,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(KernelArgs p)
             }
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              d[v] = dglu(v, 1, unused);
+              d[v] = dglu(v, 1, unused, sgk[v]);
               if (ACT == ACT_DGEGLU && (v & 7) == 7) asm volatile("" : "+v"(d[v - 7]), "+v"(d[v - 6]), "+v"(d[v - 5]), "+v"(d[v - 4]), "+v"(d[v - 3]), "+v"(d[v - 2]), "+v"(d[v - 1]), "+v"(d[v]));
             }
             colw1[tn] |= quant_codes(sT, sS, sfW0 + (oc >> 5) + 1, so, hi, l32, d, rq[2 * tn + 1], kq[2 * tn + 1])
